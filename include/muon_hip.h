@@ -1,0 +1,142 @@
+/*
+ * muon_hip.h -- C ABI of the batched Muon optimizer step for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The library orthogonalises batches of same-shaped 2-D updates with the
+ * quintic Newton-Schulz iteration and applies the Muon parameter update.
+ * Every step runs in hand-written HIP kernels on the caller's stream.
+ *
+ * Sources (page title and section):
+ *   [CS] "Muon Custom Sizing" walkthrough of the modded-nanogpt 124M record:
+ *        section 1 (Muon = SGD-momentum followed by NS orthogonalisation),
+ *        section 2.3 (attn weights viewed as 4 blocks; quintic constants,
+ *        5 rounds), section 3.1 (the contiguous (4, hdim, dim) view),
+ *        section 4 (momentum lerp forms, decoupled weight decay, effective lr).
+ *   [PG] parameter-golf train_gpt.py walkthrough, Part 1 "how the Muon
+ *        optimizer works" (zeropower_via_newtonschulz5: bf16 cast, Frobenius
+ *        normalisation, A = X X^T, B = bA + cA A, X = aX + BX; aspect factor
+ *        max(1, m/n)^0.5).
+ *
+ * Conventions shared by every entry point
+ *   - Matrices are row-major and contiguous: a batch is [batch, rows, cols].
+ *   - bf16 data is passed as `void*` holding IEEE bfloat16 bit patterns.
+ *   - All pointers are device pointers owned by the caller, 16-byte aligned.
+ *     The library never allocates or frees device memory; scratch memory is
+ *     the caller's `workspace` (size from muon_workspace_bytes, 256-byte
+ *     aligned, contents undefined before and after a call).
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *     and the call returns without synchronising.  Faults inside kernels
+ *     surface at the caller's next synchronisation.
+ *   - Arguments are validated before anything is enqueued: on any error the
+ *     call has no side effects.  batch == 0 is a valid no-op.
+ *   - Non-finite inputs propagate; they are not checked.
+ *   - Calls on different streams must use different workspaces.
+ *   - No C++ exception crosses this boundary.
+ *
+ * The NS block: with view_blocks = v, each stored rows x cols matrix is read
+ * as v contiguous blocks of rows x (cols / v) ([CS] sections 2.3 and 3.1:
+ * block k is elements [k*rows*cols/v, (k+1)*rows*cols/v) re-read row-major).
+ * A block with more rows than columns is orthogonalised in its transposed
+ * (wide) orientation; the result is returned in the stored orientation.
+ */
+#ifndef MUON_HIP_H
+#define MUON_HIP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MUON_ABI_VERSION 1
+
+typedef enum muon_status {
+    MUON_OK = 0,
+    MUON_ERR_INVALID_ARG = 1,   /* null pointer, bad scalar, bad config field */
+    MUON_ERR_SHAPE = 2,         /* rows/cols/view_blocks/batch out of range   */
+    MUON_ERR_ALIGNMENT = 3,     /* pointer not 16-byte (workspace 256) aligned */
+    MUON_ERR_WORKSPACE = 4,     /* workspace smaller than muon_workspace_bytes */
+    MUON_ERR_HIP = 5,           /* a HIP runtime call failed                  */
+    MUON_ERR_UNSUPPORTED = 6    /* current device is not gfx950               */
+} muon_status;
+
+typedef enum muon_precision {
+    /* bf16 operands everywhere, fp32 MFMA accumulation, bf16 RNE stores. */
+    MUON_PRECISION_FAST = 0,
+    /* bf16 MFMA with split operands: B = b*A + c*A*A kept as a bf16 hi+lo
+     * pair, the iterate X kept as hi+lo (about 16 significant bits), and
+     * B*X formed as Bh*Xh + Bh*Xl + Bl*Xh.  About 1.6x the MFMA work. */
+    MUON_PRECISION_ACCURATE = 1
+} muon_precision;
+
+/* Newton-Schulz settings ([PG] Part 1; constants from [CS] section 2.3). */
+typedef struct muon_ns_config {
+    int32_t ns_steps;   /* quintic iterations, 0..64 (0 returns X/(|X|_F+eps)) */
+    float a, b, c;      /* X <- a X + (b A + c A A) X with A = X X^T           */
+    float eps;          /* normaliser is |X|_F + eps, per NS block (>= 0)       */
+    int32_t precision;  /* muon_precision                                       */
+} muon_ns_config;
+
+/* Fills cfg with ns_steps 5, (a,b,c) = (3.4445, -4.7750, 2.0315), eps 1e-7,
+ * MUON_PRECISION_FAST.  No-op when cfg is NULL. */
+void muon_ns_config_default(muon_ns_config* cfg);
+
+/* Bytes of workspace that ns_orthogonalize_batched / muon_step_batched need
+ * for this shape and config (cfg NULL = defaults).  Returns 0 for batch == 0
+ * and (size_t)-1 for an invalid shape. */
+size_t muon_workspace_bytes(int64_t batch, int64_t rows, int64_t cols,
+                            int32_t view_blocks, const muon_ns_config* cfg);
+
+/*
+ * out = NS(x) for every NS block of a [batch, rows, cols] bf16 batch
+ * ([PG] Part 1; [CS] section 2.3 for view_blocks = 4).
+ *   x        in,  bf16 [batch, rows, cols]
+ *   out      out, bf16 [batch, rows, cols]; may be x itself (exact alias),
+ *            must not overlap it otherwise
+ *   cfg      NULL = defaults
+ * Each NS block is normalised by its own Frobenius norm.
+ */
+muon_status ns_orthogonalize_batched(const void* x, void* out,
+                                     int64_t batch, int64_t rows, int64_t cols,
+                                     int32_t view_blocks, const muon_ns_config* cfg,
+                                     void* workspace, size_t workspace_bytes,
+                                     void* stream);
+
+/*
+ * One Muon step for a [batch, rows, cols] batch of parameters ([CS] sections
+ * 1 and 4, [PG] Part 1), in place:
+ *   M <- M + (1 - mu)(G - M)                      (momentum buffer, fp32)
+ *   U <- G + mu (M - G)   if nesterov, else U <- M
+ *   O <- NS(U) per NS block                       (see ns_orthogonalize_batched)
+ *   P <- P (1 - lr wd wd_mul) - lr max(1, rows/cols)^0.5 lr_mul O
+ *   params     in/out fp32 [batch, rows, cols]
+ *   grads      in     bf16 [batch, rows, cols]
+ *   momentum_buf in/out fp32 [batch, rows, cols]
+ *   update_out optional out, bf16 [batch, rows, cols]: O (before lr/aspect);
+ *              NULL to skip
+ *   lr, weight_decay, momentum (mu), lr_mul, wd_mul: finite floats,
+ *              0 <= momentum <= 1
+ * params, grads, momentum_buf and update_out must not overlap.
+ */
+muon_status muon_step_batched(float* params, const void* grads, float* momentum_buf,
+                              int64_t batch, int64_t rows, int64_t cols,
+                              int32_t view_blocks,
+                              float lr, float weight_decay, float momentum,
+                              int32_t nesterov, float lr_mul, float wd_mul,
+                              const muon_ns_config* cfg, void* update_out,
+                              void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/* Text of the last error on the calling thread ("" if none).  Valid until
+ * the next call into the library from that thread. */
+const char* muon_last_error(void);
+
+/* MUON_ABI_VERSION of the built library. */
+int32_t muon_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUON_HIP_H */

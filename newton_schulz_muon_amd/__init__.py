@@ -1,0 +1,222 @@
+"""Python binding of libmuon_hip.so, the batched Muon step for MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/muon_hip.h.  PyTorch supplies
+device memory (tensors, the cached workspace) and the current stream.  There
+is no fallback: if the library is missing or the device is not gfx950 the
+calls raise.
+
+Entry points (same names as the C ABI):
+    ns_orthogonalize_batched(x, out=None, *, view_blocks=1, ...)
+    muon_step_batched(params, grads, momentum_buf, *, lr, weight_decay, momentum, ...)
+    muon_workspace_bytes(batch, rows, cols, view_blocks=1, cfg=None)
+    muon_ns_config_default(), muon_last_error(), muon_abi_version()
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional, Tuple
+
+__all__ = [
+    "MuonNSConfig", "MuonError", "LIB_PATH", "EXPORTED_SYMBOLS", "load_library",
+    "muon_ns_config_default", "muon_workspace_bytes", "ns_orthogonalize_batched",
+    "muon_step_batched", "muon_last_error", "muon_abi_version", "make_config",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmuon_hip.so")
+EXPORTED_SYMBOLS = ("muon_ns_config_default", "muon_workspace_bytes", "ns_orthogonalize_batched",
+                    "muon_step_batched", "muon_last_error", "muon_abi_version")
+
+MUON_OK = 0
+_STATUS_NAMES = {0: "MUON_OK", 1: "MUON_ERR_INVALID_ARG", 2: "MUON_ERR_SHAPE", 3: "MUON_ERR_ALIGNMENT",
+                 4: "MUON_ERR_WORKSPACE", 5: "MUON_ERR_HIP", 6: "MUON_ERR_UNSUPPORTED"}
+PRECISIONS = {"fast": 0, "accurate": 1}
+
+
+class MuonNSConfig(ctypes.Structure):
+    _fields_ = [("ns_steps", ctypes.c_int32), ("a", ctypes.c_float), ("b", ctypes.c_float),
+                ("c", ctypes.c_float), ("eps", ctypes.c_float), ("precision", ctypes.c_int32)]
+
+
+class MuonError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def load_library():
+    """Loads libmuon_hip.so (raises if it has not been built)."""
+    global _lib
+    with _lib_lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing; build it with `python -m newton_schulz_muon_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+        cfgp = ctypes.POINTER(MuonNSConfig)
+        lib.muon_ns_config_default.argtypes = [cfgp]
+        lib.muon_ns_config_default.restype = None
+        lib.muon_workspace_bytes.argtypes = [i64, i64, i64, i32, cfgp]
+        lib.muon_workspace_bytes.restype = ctypes.c_size_t
+        lib.ns_orthogonalize_batched.argtypes = [vp, vp, i64, i64, i64, i32, cfgp, vp, ctypes.c_size_t, vp]
+        lib.ns_orthogonalize_batched.restype = ctypes.c_int
+        lib.muon_step_batched.argtypes = [vp, vp, vp, i64, i64, i64, i32, f32, f32, f32, i32, f32, f32,
+                                          cfgp, vp, vp, ctypes.c_size_t, vp]
+        lib.muon_step_batched.restype = ctypes.c_int
+        lib.muon_last_error.argtypes = []
+        lib.muon_last_error.restype = ctypes.c_char_p
+        lib.muon_abi_version.argtypes = []
+        lib.muon_abi_version.restype = ctypes.c_int32
+        _lib = lib
+        return lib
+
+
+def muon_ns_config_default() -> MuonNSConfig:
+    cfg = MuonNSConfig()
+    load_library().muon_ns_config_default(ctypes.byref(cfg))
+    return cfg
+
+
+def make_config(ns_steps: int = 5, coeffs: Optional[Tuple[float, float, float]] = None,
+                eps: Optional[float] = None, precision: str = "fast") -> MuonNSConfig:
+    cfg = muon_ns_config_default()
+    cfg.ns_steps = int(ns_steps)
+    if coeffs is not None:
+        cfg.a, cfg.b, cfg.c = (float(v) for v in coeffs)
+    if eps is not None:
+        cfg.eps = float(eps)
+    if precision not in PRECISIONS:
+        raise ValueError(f"precision must be one of {sorted(PRECISIONS)}")
+    cfg.precision = PRECISIONS[precision]
+    return cfg
+
+
+def muon_last_error() -> str:
+    return load_library().muon_last_error().decode()
+
+
+def muon_abi_version() -> int:
+    return int(load_library().muon_abi_version())
+
+
+def muon_workspace_bytes(batch: int, rows: int, cols: int, view_blocks: int = 1,
+                         cfg: Optional[MuonNSConfig] = None) -> int:
+    lib = load_library()
+    n = lib.muon_workspace_bytes(int(batch), int(rows), int(cols), int(view_blocks),
+                                 ctypes.byref(cfg) if cfg is not None else None)
+    if n == ctypes.c_size_t(-1).value:
+        raise MuonError(2, lib.muon_last_error().decode())
+    return int(n)
+
+
+# ---------------------------------------------------------------- workspace cache
+_ws_cache = {}
+_ws_lock = threading.Lock()
+
+
+def _workspace(device, stream_ptr: int, nbytes: int):
+    import torch
+    if nbytes == 0:
+        return None
+    key = (device.index, stream_ptr)
+    with _ws_lock:
+        buf = _ws_cache.get(key)
+        if buf is None or buf.numel() < nbytes:
+            _ws_cache.pop(key, None)
+            buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+            _ws_cache[key] = buf
+        return buf
+
+
+def _check(status: int):
+    if status != MUON_OK:
+        raise MuonError(status, load_library().muon_last_error().decode())
+
+
+def _as3d(t, name):
+    if t.dim() == 2:
+        return t.unsqueeze(0)
+    if t.dim() != 3:
+        raise ValueError(f"{name} must be [batch, rows, cols] or [rows, cols]")
+    return t
+
+
+def _require(t, name, dtype, device=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def ns_orthogonalize_batched(x, out=None, *, view_blocks: int = 1, ns_steps: int = 5,
+                             coeffs: Optional[Tuple[float, float, float]] = None,
+                             eps: Optional[float] = None, precision: str = "fast",
+                             cfg: Optional[MuonNSConfig] = None):
+    """out = NS(x) per NS block of a bf16 [batch, rows, cols] (or [rows, cols]) tensor."""
+    import torch
+    _require(x, "x", torch.bfloat16)
+    if out is None:
+        out = torch.empty_like(x)
+    _require(out, "out", torch.bfloat16, x.device)
+    if out.shape != x.shape:
+        raise ValueError("out must have the shape of x")
+    x3, o3 = _as3d(x, "x"), _as3d(out, "out")
+    cfg = cfg if cfg is not None else make_config(ns_steps, coeffs, eps, precision)
+    B, R, C = x3.shape
+    lib = load_library()
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        nbytes = muon_workspace_bytes(B, R, C, view_blocks, cfg)
+        ws = _workspace(x.device, stream, nbytes)
+        _check(lib.ns_orthogonalize_batched(
+            x3.data_ptr(), o3.data_ptr(), B, R, C, int(view_blocks), ctypes.byref(cfg),
+            ws.data_ptr() if ws is not None else None, nbytes, stream))
+    return out
+
+
+def muon_step_batched(params, grads, momentum_buf, *, lr: float, weight_decay: float,
+                      momentum: float, nesterov: bool = True, lr_mul: float = 1.0,
+                      wd_mul: float = 1.0, view_blocks: int = 1, ns_steps: int = 5,
+                      coeffs: Optional[Tuple[float, float, float]] = None,
+                      eps: Optional[float] = None, precision: str = "fast",
+                      update_out=None, cfg: Optional[MuonNSConfig] = None):
+    """One in-place Muon step on fp32 params / bf16 grads / fp32 momentum buffers."""
+    import torch
+    _require(params, "params", torch.float32)
+    _require(grads, "grads", torch.bfloat16, params.device)
+    _require(momentum_buf, "momentum_buf", torch.float32, params.device)
+    if grads.shape != params.shape or momentum_buf.shape != params.shape:
+        raise ValueError("params, grads and momentum_buf must have one shape")
+    if update_out is not None:
+        _require(update_out, "update_out", torch.bfloat16, params.device)
+        if update_out.shape != params.shape:
+            raise ValueError("update_out must have the shape of params")
+    p3, g3, m3 = _as3d(params, "params"), _as3d(grads, "grads"), _as3d(momentum_buf, "momentum_buf")
+    cfg = cfg if cfg is not None else make_config(ns_steps, coeffs, eps, precision)
+    B, R, C = p3.shape
+    lib = load_library()
+    with torch.cuda.device(params.device):
+        stream = torch.cuda.current_stream(params.device).cuda_stream
+        nbytes = muon_workspace_bytes(B, R, C, view_blocks, cfg)
+        ws = _workspace(params.device, stream, nbytes)
+        _check(lib.muon_step_batched(
+            p3.data_ptr(), g3.data_ptr(), m3.data_ptr(), B, R, C, int(view_blocks),
+            float(lr), float(weight_decay), float(momentum), 1 if nesterov else 0,
+            float(lr_mul), float(wd_mul), ctypes.byref(cfg),
+            update_out.data_ptr() if update_out is not None else None,
+            ws.data_ptr() if ws is not None else None, nbytes, stream))
+    return params

@@ -1,0 +1,342 @@
+// C ABI of the batched Muon library: argument validation, workspace plan and
+// the launch sequence.  Host code only; the kernels live in the other sources.
+//
+// Launch sequence of one call (large blocks):
+//   k_prep            momentum + cast to the oriented padded iterate + tile norms
+//   k_norm_finalize   1/s and 1/s^2 per NS block
+//   ns_steps x { k_sym<Gram>, k_sym<Poly>, k_bx }   ping-pong between two iterates;
+//                     iteration 1 folds the normalisation into its epilogues
+//                     (A = U U^T / s^2, X1 = (a U + B U) / s), so X0 = U / s is
+//                     never materialised
+//   k_finish          NS output, or the parameter update (+ optional O)
+// Small blocks (m <= 32, m n <= 4096) run the whole step in one k_small launch.
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "muon_internal.hpp"
+
+namespace muon {
+namespace {
+
+thread_local std::string g_err;
+
+muon_status fail(muon_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+muon_status hip_fail(hipError_t e, const char* what) {
+    return fail(MUON_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+muon_ns_config default_config() {
+    muon_ns_config c;
+    c.ns_steps = 5;
+    c.a = 3.4445f;
+    c.b = -4.7750f;
+    c.c = 2.0315f;
+    c.eps = 1e-7f;
+    c.precision = MUON_PRECISION_FAST;
+    return c;
+}
+
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+muon_status validate_config(const muon_ns_config& c) {
+    if (c.ns_steps < 0 || c.ns_steps > 64)
+        return fail(MUON_ERR_INVALID_ARG, "ns_steps %d outside [0, 64]", c.ns_steps);
+    if (!std::isfinite(c.a) || !std::isfinite(c.b) || !std::isfinite(c.c))
+        return fail(MUON_ERR_INVALID_ARG, "NS coefficients must be finite");
+    if (!std::isfinite(c.eps) || c.eps < 0.f)
+        return fail(MUON_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    if (c.precision != MUON_PRECISION_FAST && c.precision != MUON_PRECISION_ACCURATE)
+        return fail(MUON_ERR_INVALID_ARG, "unknown precision %d", c.precision);
+    return MUON_OK;
+}
+
+muon_status make_plan(int64_t batch, int64_t rows, int64_t cols, int32_t v,
+                      const muon_ns_config& cfg, Plan& p) {
+    constexpr int64_t kMaxSide = int64_t(1) << 24;
+    constexpr int64_t kMaxMinSide = 16384;
+    if (batch < 0) return fail(MUON_ERR_SHAPE, "batch %lld < 0", (long long)batch);
+    if (rows < 1 || cols < 1 || rows > kMaxSide || cols > kMaxSide)
+        return fail(MUON_ERR_SHAPE, "rows %lld / cols %lld out of range", (long long)rows, (long long)cols);
+    if (v < 1 || cols % v != 0)
+        return fail(MUON_ERR_SHAPE, "view_blocks %d must be >= 1 and divide cols %lld", v, (long long)cols);
+    p = Plan();
+    p.batch = batch;
+    p.R = rows;
+    p.C = cols;
+    p.v = v;
+    p.nb = batch * v;
+    if (p.nb > 0x7fffffffLL) return fail(MUON_ERR_SHAPE, "too many NS blocks");
+    p.r = rows;
+    p.c = cols / v;
+    p.m = p.r < p.c ? p.r : p.c;
+    p.n = p.r < p.c ? p.c : p.r;
+    p.tall = p.r > p.c;
+    if (p.r * p.c > 0x7fffffffLL) return fail(MUON_ERR_SHAPE, "NS block larger than 2^31 elements");
+    p.precision = cfg.precision;
+    p.small = p.m <= kSmallMaxM && p.m * p.n <= kSmallMaxElems;
+    if (p.small) return MUON_OK;
+    if (p.m > kMaxMinSide)
+        return fail(MUON_ERR_SHAPE, "smaller side %lld exceeds %lld", (long long)p.m, (long long)kMaxMinSide);
+    p.mp = round_up(p.m, kTile);
+    p.np = round_up(p.n, kTile);
+    if (p.mp * p.np > 0x7fffffffLL) return fail(MUON_ERR_SHAPE, "padded NS block larger than 2^31 elements");
+    p.ew_tiles = (p.mp / kEwTile) * (p.np / kEwTile);
+    const bool split = cfg.precision == MUON_PRECISION_ACCURATE;
+    const double xb = double(p.nb) * double(p.mp) * double(p.np) * 2.0;
+    const double ab = double(p.nb) * double(p.mp) * double(p.mp) * 2.0;
+    if (xb * 4 + ab * 3 > 1e15) return fail(MUON_ERR_SHAPE, "workspace would exceed 1 PB");
+    size_t off = 0;
+    const size_t xbytes = size_t(p.nb) * size_t(p.mp) * size_t(p.np) * 2;
+    const size_t abytes = size_t(p.nb) * size_t(p.mp) * size_t(p.mp) * 2;
+    for (int i = 0; i < 2; ++i) { p.off_x[i] = off; off = align256(off + xbytes); }
+    if (split)
+        for (int i = 0; i < 2; ++i) { p.off_xlo[i] = off; off = align256(off + xbytes); }
+    p.off_a = off; off = align256(off + abytes);
+    p.off_b = off; off = align256(off + abytes);
+    if (split) { p.off_blo = off; off = align256(off + abytes); }
+    p.off_part = off; off = align256(off + size_t(p.nb) * size_t(p.ew_tiles) * 4);
+    p.off_scale = off; off = align256(off + size_t(p.nb) * 2 * 4);
+    p.total = off;
+    return MUON_OK;
+}
+
+muon_status check_device() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    int state = (dev >= 0 && dev < 64) ? cache[dev].load() : 0;
+    if (state == 0) {
+        hipDeviceProp_t prop;
+        const hipError_t e2 = hipGetDeviceProperties(&prop, dev);
+        if (e2 != hipSuccess) return hip_fail(e2, "hipGetDeviceProperties");
+        state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        if (dev >= 0 && dev < 64) cache[dev].store(state);
+        if (state == 2)
+            return fail(MUON_ERR_UNSUPPORTED, "device %d is %s; this library is built for gfx950", dev,
+                        prop.gcnArchName);
+    }
+    if (state == 2) return fail(MUON_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+    return MUON_OK;
+}
+
+bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0; }
+
+bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
+    if (!a || !b) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + bn && b0 < a0 + an;
+}
+
+struct Buffers {
+    uint16_t* xh[2];
+    uint16_t* xl[2];
+    uint16_t* a;
+    uint16_t* bh;
+    uint16_t* bl;
+    float* part;
+    float* scale;
+};
+
+Buffers carve(const Plan& p, void* ws) {
+    char* base = static_cast<char*>(ws);
+    const bool split = p.precision == MUON_PRECISION_ACCURATE;
+    Buffers b;
+    for (int i = 0; i < 2; ++i) {
+        b.xh[i] = reinterpret_cast<uint16_t*>(base + p.off_x[i]);
+        b.xl[i] = split ? reinterpret_cast<uint16_t*>(base + p.off_xlo[i]) : nullptr;
+    }
+    b.a = reinterpret_cast<uint16_t*>(base + p.off_a);
+    b.bh = reinterpret_cast<uint16_t*>(base + p.off_b);
+    b.bl = split ? reinterpret_cast<uint16_t*>(base + p.off_blo) : nullptr;
+    b.part = reinterpret_cast<float*>(base + p.off_part);
+    b.scale = reinterpret_cast<float*>(base + p.off_scale);
+    return b;
+}
+
+// Runs finalize + the NS loop on an iterate already written by k_prep into
+// xh[0] (and xl[0]).  Returns the buffer holding the result.
+muon_status run_ns(const Plan& p, const muon_ns_config& cfg, const Buffers& b, hipStream_t s,
+                   int* final_idx) {
+    hipError_t e = launch_norm_finalize(p, b.part, b.scale, cfg.eps, s);
+    if (e != hipSuccess) return hip_fail(e, "k_norm_finalize launch");
+    int cur = 0;
+    for (int it = 0; it < cfg.ns_steps; ++it) {
+        const float* sc = it == 0 ? b.scale : nullptr;
+        e = launch_gram(p, b.xh[cur], b.a, sc, s);
+        if (e != hipSuccess) return hip_fail(e, "k_sym<gram> launch");
+        e = launch_poly(p, b.a, b.bh, b.bl, cfg.b, cfg.c, s);
+        if (e != hipSuccess) return hip_fail(e, "k_sym<poly> launch");
+        e = launch_bx(p, b.bh, b.bl, b.xh[cur], b.xl[cur], b.xh[cur ^ 1], b.xl[cur ^ 1], cfg.a, sc, s);
+        if (e != hipSuccess) return hip_fail(e, "k_bx launch");
+        cur ^= 1;
+    }
+    *final_idx = cur;
+    return MUON_OK;
+}
+
+muon_status common_checks(const Plan& p, void* ws, size_t ws_bytes) {
+    if (p.total > 0) {
+        if (ws == nullptr || ws_bytes < p.total)
+            return fail(MUON_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws ? ws_bytes : 0,
+                        p.total);
+        if (!aligned(ws, 256)) return fail(MUON_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
+    }
+    return MUON_OK;
+}
+
+}  // namespace
+}  // namespace muon
+
+using namespace muon;
+
+extern "C" {
+
+void muon_ns_config_default(muon_ns_config* cfg) {
+    if (cfg) *cfg = default_config();
+}
+
+size_t muon_workspace_bytes(int64_t batch, int64_t rows, int64_t cols, int32_t view_blocks,
+                            const muon_ns_config* cfg_in) {
+    g_err.clear();
+    const muon_ns_config cfg = cfg_in ? *cfg_in : default_config();
+    if (validate_config(cfg) != MUON_OK) return size_t(-1);
+    Plan p;
+    if (make_plan(batch, rows, cols, view_blocks, cfg, p) != MUON_OK) return size_t(-1);
+    if (batch == 0) return 0;
+    return p.total;
+}
+
+muon_status ns_orthogonalize_batched(const void* x, void* out, int64_t batch, int64_t rows,
+                                     int64_t cols, int32_t view_blocks, const muon_ns_config* cfg_in,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+    g_err.clear();
+    const muon_ns_config cfg = cfg_in ? *cfg_in : default_config();
+    muon_status st = validate_config(cfg);
+    if (st != MUON_OK) return st;
+    Plan p;
+    st = make_plan(batch, rows, cols, view_blocks, cfg, p);
+    if (st != MUON_OK) return st;
+    if (batch == 0) return MUON_OK;
+    if (!x || !out) return fail(MUON_ERR_INVALID_ARG, "x and out must be non-null");
+    if (!aligned(x, 16) || !aligned(out, 16)) return fail(MUON_ERR_ALIGNMENT, "x and out must be 16-byte aligned");
+    const size_t bytes = size_t(batch) * size_t(rows) * size_t(cols) * 2;
+    if (x != out && overlaps(x, bytes, out, bytes))
+        return fail(MUON_ERR_INVALID_ARG, "out overlaps x without being x");
+    st = common_checks(p, workspace, workspace_bytes);
+    if (st != MUON_OK) return st;
+    st = check_device();
+    if (st != MUON_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    if (p.small) {
+        SmallStep ss;
+        ss.src = static_cast<const uint16_t*>(x);
+        ss.out = static_cast<uint16_t*>(out);
+        ss.mode = kPrepCast;
+        ss.ns_steps = cfg.ns_steps;
+        ss.a = cfg.a;
+        ss.b = cfg.b;
+        ss.c = cfg.c;
+        ss.eps = cfg.eps;
+        const hipError_t e = launch_small(p, ss, s);
+        return e == hipSuccess ? MUON_OK : hip_fail(e, "k_small launch");
+    }
+    const Buffers b = carve(p, workspace);
+    hipError_t e = launch_prep(p, kPrepCast, static_cast<const uint16_t*>(x), nullptr, 0.f, b.xh[0], b.xl[0],
+                               b.part, s);
+    if (e != hipSuccess) return hip_fail(e, "k_prep launch");
+    int fin = 0;
+    st = run_ns(p, cfg, b, s, &fin);
+    if (st != MUON_OK) return st;
+    e = launch_finish(p, b.xh[fin], b.xl[fin], cfg.ns_steps == 0 ? b.scale : nullptr, nullptr, 1.f, 0.f,
+                      static_cast<uint16_t*>(out), s);
+    return e == hipSuccess ? MUON_OK : hip_fail(e, "k_finish launch");
+}
+
+muon_status muon_step_batched(float* params, const void* grads, float* momentum_buf, int64_t batch,
+                              int64_t rows, int64_t cols, int32_t view_blocks, float lr,
+                              float weight_decay, float momentum, int32_t nesterov, float lr_mul,
+                              float wd_mul, const muon_ns_config* cfg_in, void* update_out,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    g_err.clear();
+    const muon_ns_config cfg = cfg_in ? *cfg_in : default_config();
+    muon_status st = validate_config(cfg);
+    if (st != MUON_OK) return st;
+    Plan p;
+    st = make_plan(batch, rows, cols, view_blocks, cfg, p);
+    if (st != MUON_OK) return st;
+    if (!std::isfinite(lr) || !std::isfinite(weight_decay) || !std::isfinite(lr_mul) || !std::isfinite(wd_mul))
+        return fail(MUON_ERR_INVALID_ARG, "lr, weight_decay, lr_mul and wd_mul must be finite");
+    if (!(momentum >= 0.f && momentum <= 1.f)) return fail(MUON_ERR_INVALID_ARG, "momentum must be in [0, 1]");
+    if (batch == 0) return MUON_OK;
+    if (!params || !grads || !momentum_buf)
+        return fail(MUON_ERR_INVALID_ARG, "params, grads and momentum_buf must be non-null");
+    if (!aligned(params, 16) || !aligned(grads, 16) || !aligned(momentum_buf, 16) ||
+        (update_out && !aligned(update_out, 16)))
+        return fail(MUON_ERR_ALIGNMENT, "data pointers must be 16-byte aligned");
+    const size_t n = size_t(batch) * size_t(rows) * size_t(cols);
+    if (overlaps(params, 4 * n, grads, 2 * n) || overlaps(params, 4 * n, momentum_buf, 4 * n) ||
+        overlaps(grads, 2 * n, momentum_buf, 4 * n) || overlaps(update_out, 2 * n, params, 4 * n) ||
+        overlaps(update_out, 2 * n, grads, 2 * n) || overlaps(update_out, 2 * n, momentum_buf, 4 * n))
+        return fail(MUON_ERR_INVALID_ARG, "params, grads, momentum_buf and update_out must not overlap");
+    st = common_checks(p, workspace, workspace_bytes);
+    if (st != MUON_OK) return st;
+    st = check_device();
+    if (st != MUON_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    const double aspect = std::sqrt(std::fmax(1.0, double(rows) / double(cols)));
+    const float decay = static_cast<float>(1.0 - double(lr) * double(weight_decay) * double(wd_mul));
+    const float step = static_cast<float>(double(lr) * aspect * double(lr_mul));
+    const PrepMode mode = nesterov ? kPrepNesterov : kPrepPlain;
+
+    if (p.small) {
+        SmallStep ss;
+        ss.src = static_cast<const uint16_t*>(grads);
+        ss.mom = momentum_buf;
+        ss.params = params;
+        ss.out = static_cast<uint16_t*>(update_out);
+        ss.mu = momentum;
+        ss.decay = decay;
+        ss.step = step;
+        ss.mode = mode;
+        ss.ns_steps = cfg.ns_steps;
+        ss.a = cfg.a;
+        ss.b = cfg.b;
+        ss.c = cfg.c;
+        ss.eps = cfg.eps;
+        const hipError_t e = launch_small(p, ss, s);
+        return e == hipSuccess ? MUON_OK : hip_fail(e, "k_small launch");
+    }
+    const Buffers b = carve(p, workspace);
+    hipError_t e = launch_prep(p, mode, static_cast<const uint16_t*>(grads), momentum_buf, momentum, b.xh[0],
+                               b.xl[0], b.part, s);
+    if (e != hipSuccess) return hip_fail(e, "k_prep launch");
+    int fin = 0;
+    st = run_ns(p, cfg, b, s, &fin);
+    if (st != MUON_OK) return st;
+    e = launch_finish(p, b.xh[fin], b.xl[fin], cfg.ns_steps == 0 ? b.scale : nullptr, params, decay, step,
+                      static_cast<uint16_t*>(update_out), s);
+    return e == hipSuccess ? MUON_OK : hip_fail(e, "k_finish launch");
+}
+
+const char* muon_last_error(void) { return g_err.c_str(); }
+
+int32_t muon_abi_version(void) { return MUON_ABI_VERSION; }
+
+}  // extern "C"

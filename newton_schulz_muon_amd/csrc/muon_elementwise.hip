@@ -1,0 +1,452 @@
+// HBM-bound kernels of the batched Muon step (gfx950).
+//
+//   k_prep      momentum update ("Muon Custom Sizing" walkthrough, section 4:
+//               buffer lerp towards the gradient, Nesterov look-ahead from the
+//               updated buffer) fused with the cast to the oriented, padded bf16
+//               iterate and with the per-tile sums of squares that give the
+//               Frobenius norm (parameter-golf walkthrough, Part 1: the input is
+//               divided by its norm once).  Tall blocks are transposed through LDS
+//               on the way, so orientation costs no extra pass.
+//   k_norm_finalize   per NS block: 1/(sqrt(sum) + eps) and its square, summed in
+//               a fixed order so results are run-to-run deterministic.
+//   k_finish    reads the final iterate back into stored layout and either writes
+//               the NS output or applies the decoupled-decay update
+//               P <- P (1 - lr wd wd_mul) - lr max(1, R/C)^0.5 lr_mul O
+//               ("Muon Custom Sizing" walkthrough, section 4; aspect factor from
+//               the parameter-golf walkthrough, Part 1).
+//
+// Every kernel works on 64 x 64 tiles of the oriented block with 256 threads;
+// each thread owns two rows of 8 consecutive elements, so stored rows are read
+// and written as 16-byte (bf16) or 2 x 16-byte (fp32) vectors when the stored
+// column count is a multiple of 8, and element by element otherwise.
+#include "muon_internal.hpp"
+
+namespace muon {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int T = kEwTile;
+
+struct PrepArgs {
+    const uint16_t* src;   // stored bf16 (gradients or x), this launch's first block
+    float* mom;            // stored fp32 momentum buffer
+    uint16_t* xhi;         // oriented padded [nb][mp][np]
+    uint16_t* xlo;
+    float* part;           // [nb][ew_tiles]
+    int64_t r, c, mp, np, be;
+    int64_t ew_tiles;
+    int tiles_j;
+    float mu, omm;
+};
+
+__device__ __forceinline__ float block_sum_256(float v, float* red) {
+    v = wave_sum(v);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    float s = 0.f;
+    if (threadIdx.x == 0) s = ((red[0] + red[1]) + red[2]) + red[3];
+    return s;
+}
+
+template <int MODE>
+__device__ __forceinline__ float momentum_update(float g, float* mptr, float mu, float omm) {
+    if constexpr (MODE == kPrepCast) {
+        return g;
+    } else {
+        const float m = *mptr;
+        const float mn = fmaf(omm, g - m, m);
+        *mptr = mn;
+        if constexpr (MODE == kPrepNesterov) return fmaf(mu, mn - g, g);
+        else return mn;
+    }
+}
+
+// Loads 8 stored elements (bi, bj0..bj0+7) of one block, applies the momentum
+// update and returns the update direction in u[].
+template <int MODE, bool VEC>
+__device__ __forceinline__ void load_update8(const PrepArgs& a, const uint16_t* src, float* mom,
+                                             int64_t bi, int64_t bj0, float (&u)[8], bool (&ok)[8]) {
+    if constexpr (VEC) {
+        const bool valid = (bi < a.r) && (bj0 < a.c);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { ok[e] = valid; u[e] = 0.f; }
+        if (!valid) return;
+        const int64_t off = bi * a.c + bj0;
+        const u32x4 gv = *reinterpret_cast<const u32x4*>(src + off);
+        float g[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            g[2 * q] = bf16_to_f32(static_cast<uint16_t>(gv[q] & 0xffffu));
+            g[2 * q + 1] = bf16_to_f32(static_cast<uint16_t>(gv[q] >> 16));
+        }
+        if constexpr (MODE == kPrepCast) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) u[e] = g[e];
+        } else {
+            f32x4* mp4 = reinterpret_cast<f32x4*>(mom + off);
+            f32x4 m0 = mp4[0], m1 = mp4[1];
+            float m[8] = {m0[0], m0[1], m0[2], m0[3], m1[0], m1[1], m1[2], m1[3]};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) u[e] = momentum_update<MODE>(g[e], &m[e], a.mu, a.omm);
+            mp4[0] = f32x4{m[0], m[1], m[2], m[3]};
+            mp4[1] = f32x4{m[4], m[5], m[6], m[7]};
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            ok[e] = (bi < a.r) && (bj0 + e < a.c);
+            u[e] = 0.f;
+            if (ok[e]) {
+                const int64_t off = bi * a.c + bj0 + e;
+                const float g = bf16_to_f32(src[off]);
+                u[e] = momentum_update<MODE>(g, mom ? mom + off : nullptr, a.mu, a.omm);
+            }
+        }
+    }
+}
+
+template <int MODE, bool TALL, bool VEC, bool SPLIT>
+__global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
+    __shared__ uint16_t lds_hi[TALL ? T : 1][T + 2];
+    __shared__ uint16_t lds_lo[(TALL && SPLIT) ? T : 1][T + 2];
+    __shared__ float red[4];
+
+    const int t = threadIdx.x;
+    const int64_t blk = blockIdx.y;
+    const int tile = blockIdx.x;
+    const int ti = tile / a.tiles_j, tj = tile % a.tiles_j;
+    const uint16_t* src = a.src + blk * a.be;
+    float* mom = (MODE == kPrepCast) ? nullptr : a.mom + blk * a.be;
+    uint16_t* xhi = a.xhi + blk * a.mp * a.np;
+    uint16_t* xlo = SPLIT ? a.xlo + blk * a.mp * a.np : nullptr;
+    const int rl = t >> 3;
+    const int cl = (t & 7) * 8;
+    float ss = 0.f;
+
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int row = rl + 32 * h;
+        // oriented (oi, oj) = stored (bi, bj) for wide blocks, (bj, bi) for tall ones
+        const int64_t bi = TALL ? (int64_t)tj * T + row : (int64_t)ti * T + row;
+        const int64_t bj0 = TALL ? (int64_t)ti * T + cl : (int64_t)tj * T + cl;
+        float u[8];
+        bool ok[8];
+        load_update8<MODE, VEC>(a, src, mom, bi, bj0, u, ok);
+        uint16_t hi[8], lo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            hi[e] = ok[e] ? f32_to_bf16(u[e]) : uint16_t(0);
+            const float hv = bf16_to_f32(hi[e]);
+            if constexpr (SPLIT) {
+                lo[e] = ok[e] ? f32_to_bf16(u[e] - hv) : uint16_t(0);
+                ss = fmaf(u[e], u[e], ss);
+            } else {
+                ss = fmaf(hv, hv, ss);
+            }
+        }
+        if constexpr (!TALL) {
+            const int64_t o = ((int64_t)ti * T + row) * a.np + (int64_t)tj * T + cl;
+            u32x4 w;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) w[q] = uint32_t(hi[2 * q]) | (uint32_t(hi[2 * q + 1]) << 16);
+            *reinterpret_cast<u32x4*>(xhi + o) = w;
+            if constexpr (SPLIT) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) w[q] = uint32_t(lo[2 * q]) | (uint32_t(lo[2 * q + 1]) << 16);
+                *reinterpret_cast<u32x4*>(xlo + o) = w;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                lds_hi[row][cl + e] = hi[e];
+                if constexpr (SPLIT) lds_lo[row][cl + e] = lo[e];
+            }
+        }
+    }
+
+    if constexpr (TALL) {
+        __syncthreads();
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int row = rl + 32 * h;   // oriented local row = stored local column
+            const int64_t o = ((int64_t)ti * T + row) * a.np + (int64_t)tj * T + cl;
+            u32x4 w;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                w[q] = uint32_t(lds_hi[cl + 2 * q][row]) | (uint32_t(lds_hi[cl + 2 * q + 1][row]) << 16);
+            *reinterpret_cast<u32x4*>(xhi + o) = w;
+            if constexpr (SPLIT) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    w[q] = uint32_t(lds_lo[cl + 2 * q][row]) | (uint32_t(lds_lo[cl + 2 * q + 1][row]) << 16);
+                *reinterpret_cast<u32x4*>(xlo + o) = w;
+            }
+        }
+    }
+
+    const float tot = block_sum_256(ss, red);
+    if (t == 0) a.part[blk * a.ew_tiles + tile] = tot;
+}
+
+__global__ __launch_bounds__(256) void k_norm_finalize(const float* part, float* scales,
+                                                       int64_t ew_tiles, float eps) {
+    __shared__ float red[4];
+    const int64_t blk = blockIdx.x;
+    const float* p = part + blk * ew_tiles;
+    float s = 0.f;
+    for (int64_t i = threadIdx.x; i < ew_tiles; i += 256) s += p[i];
+    const float tot = block_sum_256(s, red);
+    if (threadIdx.x == 0) {
+        const float inv = 1.0f / (sqrtf(tot) + eps);
+        scales[2 * blk] = inv;
+        scales[2 * blk + 1] = inv * inv;
+    }
+}
+
+struct FinArgs {
+    const uint16_t* xhi;   // oriented padded final iterate
+    const uint16_t* xlo;
+    const float* scale;    // [nb][2] or null
+    float* P;              // stored fp32 parameters (update mode)
+    uint16_t* out;         // stored bf16 output (NS output, or optional O)
+    int64_t r, c, mp, np, be;
+    int tiles_j;           // ceil(n / 64)
+    float decay, step;
+};
+
+template <bool UPDATE, bool VEC>
+__device__ __forceinline__ void finish_store8(const FinArgs& a, float* P, uint16_t* out,
+                                              int64_t bi, int64_t bj0, const float (&o)[8],
+                                              const uint16_t (&bits)[8], bool exact_bits) {
+    if (bi >= a.r) return;
+    if constexpr (VEC) {
+        if (bj0 >= a.c) return;
+        const int64_t off = bi * a.c + bj0;
+        if constexpr (UPDATE) {
+            f32x4* p4 = reinterpret_cast<f32x4*>(P + off);
+            f32x4 p0 = p4[0], p1 = p4[1];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                p0[e] = fmaf(-a.step, o[e], p0[e] * a.decay);
+                p1[e] = fmaf(-a.step, o[e + 4], p1[e] * a.decay);
+            }
+            p4[0] = p0;
+            p4[1] = p1;
+        }
+        if (out != nullptr) {
+            u32x4 w;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint16_t l = exact_bits ? bits[2 * q] : f32_to_bf16(o[2 * q]);
+                const uint16_t h = exact_bits ? bits[2 * q + 1] : f32_to_bf16(o[2 * q + 1]);
+                w[q] = uint32_t(l) | (uint32_t(h) << 16);
+            }
+            *reinterpret_cast<u32x4*>(out + off) = w;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if (bj0 + e >= a.c) break;
+            const int64_t off = bi * a.c + bj0 + e;
+            if constexpr (UPDATE) P[off] = fmaf(-a.step, o[e], P[off] * a.decay);
+            if (out != nullptr) out[off] = exact_bits ? bits[e] : f32_to_bf16(o[e]);
+        }
+    }
+}
+
+template <bool UPDATE, bool TALL, bool VEC, bool SPLIT>
+__global__ __launch_bounds__(256) void k_finish(FinArgs a) {
+    __shared__ float lds[TALL ? T : 1][T + 1];
+    __shared__ uint16_t ldsb[TALL ? T : 1][T + 2];
+    const int t = threadIdx.x;
+    const int64_t blk = blockIdx.y;
+    const int tile = blockIdx.x;
+    const int ti = tile / a.tiles_j, tj = tile % a.tiles_j;
+    const uint16_t* xhi = a.xhi + blk * a.mp * a.np;
+    const uint16_t* xlo = SPLIT ? a.xlo + blk * a.mp * a.np : nullptr;
+    float* P = UPDATE ? a.P + blk * a.be : nullptr;
+    uint16_t* out = a.out ? a.out + blk * a.be : nullptr;
+    const float sc = a.scale ? a.scale[2 * blk] : 1.0f;
+    const bool exact_bits = !SPLIT && a.scale == nullptr;
+    const int rl = t >> 3;
+    const int cl = (t & 7) * 8;
+
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int row = rl + 32 * h;
+        const int64_t oi = (int64_t)ti * T + row;
+        const int64_t oj = (int64_t)tj * T + cl;
+        const int64_t o = oi * a.np + oj;   // always inside the padded buffer
+        const u32x4 vh = *reinterpret_cast<const u32x4*>(xhi + o);
+        u32x4 vl = {0u, 0u, 0u, 0u};
+        if constexpr (SPLIT) vl = *reinterpret_cast<const u32x4*>(xlo + o);
+        float v[8];
+        uint16_t bits[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            bits[2 * q] = static_cast<uint16_t>(vh[q] & 0xffffu);
+            bits[2 * q + 1] = static_cast<uint16_t>(vh[q] >> 16);
+            v[2 * q] = bf16_to_f32(bits[2 * q]);
+            v[2 * q + 1] = bf16_to_f32(bits[2 * q + 1]);
+            if constexpr (SPLIT) {
+                v[2 * q] += bf16_to_f32(static_cast<uint16_t>(vl[q] & 0xffffu));
+                v[2 * q + 1] += bf16_to_f32(static_cast<uint16_t>(vl[q] >> 16));
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] *= sc;
+        if constexpr (!TALL) {
+            finish_store8<UPDATE, VEC>(a, P, out, oi, oj, v, bits, exact_bits);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                lds[row][cl + e] = v[e];
+                ldsb[row][cl + e] = bits[e];
+            }
+        }
+    }
+
+    if constexpr (TALL) {
+        __syncthreads();
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int row = rl + 32 * h;    // stored local row = oriented local column
+            const int64_t bi = (int64_t)tj * T + row;
+            const int64_t bj0 = (int64_t)ti * T + cl;
+            float v[8];
+            uint16_t bits[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                v[e] = lds[cl + e][row];
+                bits[e] = ldsb[cl + e][row];
+            }
+            finish_store8<UPDATE, VEC>(a, P, out, bi, bj0, v, bits, exact_bits);
+        }
+    }
+}
+
+template <typename F>
+hipError_t for_block_chunks(int64_t nb, F&& f) {
+    for (int64_t b0 = 0; b0 < nb; b0 += kMaxGridY) {
+        const int64_t cnt = (nb - b0) < kMaxGridY ? (nb - b0) : kMaxGridY;
+        f(b0, static_cast<unsigned>(cnt));
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+template <int MODE, bool TALL, bool VEC, bool SPLIT>
+hipError_t run_prep(const Plan& p, const PrepArgs& a, hipStream_t s) {
+    const int64_t be = p.r * p.c;
+    const int64_t pad = p.mp * p.np;
+    return for_block_chunks(p.nb, [&](int64_t b0, unsigned cnt) {
+        PrepArgs c = a;
+        c.src = a.src + b0 * be;
+        c.mom = a.mom ? a.mom + b0 * be : nullptr;
+        c.xhi = a.xhi + b0 * pad;
+        c.xlo = a.xlo ? a.xlo + b0 * pad : nullptr;
+        c.part = a.part + b0 * p.ew_tiles;
+        k_prep<MODE, TALL, VEC, SPLIT><<<dim3(static_cast<unsigned>(p.ew_tiles), cnt), dim3(256), 0, s>>>(c);
+    });
+}
+
+template <int MODE>
+hipError_t prep_mode(const Plan& p, const PrepArgs& a, hipStream_t s) {
+    const bool vec = (p.c % 8) == 0;
+    const bool split = a.xlo != nullptr;
+    if (p.tall) {
+        if (vec) return split ? run_prep<MODE, true, true, true>(p, a, s) : run_prep<MODE, true, true, false>(p, a, s);
+        return split ? run_prep<MODE, true, false, true>(p, a, s) : run_prep<MODE, true, false, false>(p, a, s);
+    }
+    if (vec) return split ? run_prep<MODE, false, true, true>(p, a, s) : run_prep<MODE, false, true, false>(p, a, s);
+    return split ? run_prep<MODE, false, false, true>(p, a, s) : run_prep<MODE, false, false, false>(p, a, s);
+}
+
+template <bool UPDATE, bool TALL, bool VEC, bool SPLIT>
+hipError_t run_finish(const Plan& p, const FinArgs& a, hipStream_t s) {
+    const int64_t be = p.r * p.c;
+    const int64_t pad = p.mp * p.np;
+    const int64_t ti = (p.m + T - 1) / T;
+    const int64_t tiles = ti * a.tiles_j;
+    return for_block_chunks(p.nb, [&](int64_t b0, unsigned cnt) {
+        FinArgs c = a;
+        c.xhi = a.xhi + b0 * pad;
+        c.xlo = a.xlo ? a.xlo + b0 * pad : nullptr;
+        c.scale = a.scale ? a.scale + 2 * b0 : nullptr;
+        c.P = a.P ? a.P + b0 * be : nullptr;
+        c.out = a.out ? a.out + b0 * be : nullptr;
+        k_finish<UPDATE, TALL, VEC, SPLIT><<<dim3(static_cast<unsigned>(tiles), cnt), dim3(256), 0, s>>>(c);
+    });
+}
+
+template <bool UPDATE>
+hipError_t finish_mode(const Plan& p, const FinArgs& a, hipStream_t s) {
+    const bool vec = (p.c % 8) == 0;
+    const bool split = a.xlo != nullptr;
+    if (p.tall) {
+        if (vec) return split ? run_finish<UPDATE, true, true, true>(p, a, s) : run_finish<UPDATE, true, true, false>(p, a, s);
+        return split ? run_finish<UPDATE, true, false, true>(p, a, s) : run_finish<UPDATE, true, false, false>(p, a, s);
+    }
+    if (vec) return split ? run_finish<UPDATE, false, true, true>(p, a, s) : run_finish<UPDATE, false, true, false>(p, a, s);
+    return split ? run_finish<UPDATE, false, false, true>(p, a, s) : run_finish<UPDATE, false, false, false>(p, a, s);
+}
+
+}  // namespace
+
+hipError_t launch_prep(const Plan& p, PrepMode mode, const uint16_t* src, float* mom, float mu,
+                       uint16_t* x_hi, uint16_t* x_lo, float* partials, hipStream_t s) {
+    PrepArgs a;
+    a.src = src;
+    a.mom = mom;
+    a.xhi = x_hi;
+    a.xlo = x_lo;
+    a.part = partials;
+    a.r = p.r;
+    a.c = p.c;
+    a.mp = p.mp;
+    a.np = p.np;
+    a.be = p.r * p.c;
+    a.ew_tiles = p.ew_tiles;
+    a.tiles_j = static_cast<int>(p.np / T);
+    a.mu = mu;
+    a.omm = 1.0f - mu;
+    switch (mode) {
+        case kPrepCast: return prep_mode<kPrepCast>(p, a, s);
+        case kPrepNesterov: return prep_mode<kPrepNesterov>(p, a, s);
+        case kPrepPlain: return prep_mode<kPrepPlain>(p, a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_norm_finalize(const Plan& p, const float* partials, float* scales, float eps,
+                                hipStream_t s) {
+    if (p.nb > 0x7fffffff) return hipErrorInvalidValue;
+    k_norm_finalize<<<dim3(static_cast<unsigned>(p.nb)), dim3(256), 0, s>>>(partials, scales, p.ew_tiles, eps);
+    return hipGetLastError();
+}
+
+hipError_t launch_finish(const Plan& p, const uint16_t* x_hi, const uint16_t* x_lo,
+                         const float* scale, float* params, float decay, float step,
+                         uint16_t* out, hipStream_t s) {
+    FinArgs a;
+    a.xhi = x_hi;
+    a.xlo = x_lo;
+    a.scale = scale;
+    a.P = params;
+    a.out = out;
+    a.r = p.r;
+    a.c = p.c;
+    a.mp = p.mp;
+    a.np = p.np;
+    a.be = p.r * p.c;
+    a.tiles_j = static_cast<int>((p.n + T - 1) / T);
+    a.decay = decay;
+    a.step = step;
+    return params ? finish_mode<true>(p, a, s) : finish_mode<false>(p, a, s);
+}
+
+}  // namespace muon

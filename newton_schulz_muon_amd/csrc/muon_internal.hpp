@@ -1,0 +1,117 @@
+// Internal declarations of the batched Muon HIP library (gfx950).
+//
+// Data layout in device memory
+//   Stored batches are row-major [batch][rows][cols].  With view_blocks = v the
+//   NS block k of a stored matrix is its contiguous elements
+//   [k*rows*cols/v, (k+1)*rows*cols/v) read as rows x (cols/v).
+//   Inside the NS loop every block lives in "oriented, padded" form: an
+//   mp x np bf16 tile-aligned matrix (mp, np multiples of 128) holding the
+//   block (or its transpose when it is tall) in the top-left m x n corner and
+//   exact zeros elsewhere.  Zero padding is invariant under the iteration
+//   (zero rows of X give zero rows and columns of A and B, and B X keeps zero
+//   columns of X zero), so the GEMM kernels never mask.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "muon_hip.h"
+
+namespace muon {
+
+constexpr int kTile = 128;          // GEMM output tile edge and padding unit
+constexpr int kEwTile = 64;         // element-wise kernels' tile edge
+constexpr int kSmallMaxM = 32;      // small fp32 path: m <= 32 ...
+constexpr int kSmallMaxElems = 4096;  // ... and m * n <= 4096
+constexpr int64_t kMaxGridY = 65535;
+
+struct Plan {
+    int64_t batch = 0, R = 0, C = 0;
+    int32_t v = 1;
+    int64_t nb = 0;              // NS blocks = batch * v
+    int64_t r = 0, c = 0;        // NS block shape as stored
+    int64_t m = 0, n = 0;        // min / max side
+    bool tall = false;           // r > c: oriented form is the transpose
+    bool small = false;          // fp32 one-workgroup-per-block path
+    int64_t mp = 0, np = 0;      // padded oriented shape
+    int32_t precision = MUON_PRECISION_FAST;
+    int64_t ew_tiles = 0;        // 64 x 64 tiles per padded block (norm partial slots)
+    // workspace byte offsets
+    size_t off_x[2] = {0, 0};    // iterate ping-pong, bf16 [nb][mp][np] (hi plane)
+    size_t off_xlo[2] = {0, 0};  // ACCURATE: lo planes
+    size_t off_a = 0;            // Gram, bf16 [nb][mp][mp]
+    size_t off_b = 0;            // polynomial, bf16 [nb][mp][mp] (hi plane)
+    size_t off_blo = 0;          // ACCURATE: lo plane of B
+    size_t off_part = 0;         // fp32 [nb][ew_tiles] partial sums of squares
+    size_t off_scale = 0;        // fp32 [nb][2]: 1/s, 1/s^2
+    size_t total = 0;
+};
+
+// ---------------------------------------------------------------- device helpers
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round-to-nearest-even float -> bf16 (gfx950 v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    __bf16 h = static_cast<__bf16>(f);
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// ---------------------------------------------------------------- launchers
+// Element-wise kernels (muon_elementwise.hip).
+enum PrepMode { kPrepCast = 0, kPrepNesterov = 1, kPrepPlain = 2 };
+
+// Reads the stored batch (bf16 x or gradients), updates the momentum buffer
+// (momentum modes), writes the oriented padded iterate X0 (bf16, hi plane;
+// lo plane too when x_lo != nullptr) and per-tile sums of squares.
+hipError_t launch_prep(const Plan& p, PrepMode mode, const uint16_t* src, float* mom,
+                       float mu, uint16_t* x_hi, uint16_t* x_lo, float* partials,
+                       hipStream_t s);
+// scales[2k] = 1/(sqrt(sum_k) + eps), scales[2k+1] = scales[2k]^2.
+hipError_t launch_norm_finalize(const Plan& p, const float* partials, float* scales, float eps,
+                                hipStream_t s);
+// Writes the final iterate back in stored layout: NS output (out, bf16) or the
+// parameter update P <- P*decay - step*O (with optional O).  `scale` (may be
+// null) multiplies X first (used when ns_steps == 0).
+hipError_t launch_finish(const Plan& p, const uint16_t* x_hi, const uint16_t* x_lo,
+                         const float* scale, float* params, float decay, float step,
+                         uint16_t* out, hipStream_t s);
+
+// MFMA kernels (ns_gemm.hip).
+// A = scale2 * X X^T   (upper tiles computed, mirrored; scale2 may be null)
+hipError_t launch_gram(const Plan& p, const uint16_t* x, uint16_t* a, const float* scale2,
+                       hipStream_t s);
+// B = b A + c A A      (A symmetric; b_lo != nullptr stores the rounding residual)
+hipError_t launch_poly(const Plan& p, const uint16_t* a, uint16_t* b_hi, uint16_t* b_lo,
+                       float cb, float cc, hipStream_t s);
+// X' = scale1 * (a X + B X)   (scale1 may be null).  ACCURATE when x_lo/b_lo given:
+// X' = scale1 * (a (Xh + Xl) + Bh Xh + Bh Xl + Bl Xh), stored as hi + lo.
+hipError_t launch_bx(const Plan& p, const uint16_t* b_hi, const uint16_t* b_lo,
+                     const uint16_t* x_hi, const uint16_t* x_lo, uint16_t* out_hi,
+                     uint16_t* out_lo, float ca, const float* scale1, hipStream_t s);
+
+// Small blocks (small_ns.hip): the whole step for one block per workgroup in fp32.
+struct SmallStep {
+    const uint16_t* src = nullptr;   // x or gradients
+    float* mom = nullptr;            // momentum buffer (step modes)
+    float* params = nullptr;         // parameters (step modes)
+    uint16_t* out = nullptr;         // NS output or optional O
+    float mu = 0.f, decay = 1.f, step = 0.f;
+    int mode = 0;                    // PrepMode
+    int ns_steps = 5;
+    float a = 0.f, b = 0.f, c = 0.f, eps = 0.f;
+};
+hipError_t launch_small(const Plan& p, const SmallStep& st, hipStream_t s);
+
+}  // namespace muon

@@ -1,0 +1,143 @@
+"""C-ABI contract checks that need no GPU: the library loads, exports every
+function include/muon_hip.h declares, and rejects bad arguments before it
+touches the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import newton_schulz_muon_amd as nsm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "muon_hip.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(nsm.LIB_PATH):
+        pytest.fail("libmuon_hip.so is not built: run `python -m newton_schulz_muon_amd.build`")
+    return nsm.load_library()
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    assert "muon_step_batched" in names and "ns_orthogonalize_batched" in names
+    assert set(names) == set(nsm.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_abi_version_matches_header(lib):
+    ver = int(re.search(r"#define MUON_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert nsm.muon_abi_version() == ver
+
+
+def test_default_config(lib):
+    cfg = nsm.muon_ns_config_default()
+    assert cfg.ns_steps == 5
+    assert (cfg.a, cfg.b, cfg.c) == pytest.approx((3.4445, -4.7750, 2.0315), abs=1e-6)
+    assert cfg.eps == pytest.approx(1e-7)
+    assert cfg.precision == 0
+
+
+def _expected_ws(nb, m, n, split=False):
+    def up(x, a):
+        return (x + a - 1) // a * a
+    mp, np_ = up(m, 128), up(n, 128)
+    xb = up(nb * mp * np_ * 2, 256)
+    ab = up(nb * mp * mp * 2, 256)
+    tiles = (mp // 64) * (np_ // 64)
+    return (4 if split else 2) * xb + (3 if split else 2) * ab + up(nb * tiles * 4, 256) + up(nb * 8, 256)
+
+
+def test_workspace_bytes(lib):
+    assert nsm.muon_workspace_bytes(0, 768, 3072) == 0
+    assert nsm.muon_workspace_bytes(32, 768, 3072) == _expected_ws(32, 768, 3072)
+    # attn view: 10 stored 768x3072 -> 40 blocks of 768x768
+    assert nsm.muon_workspace_bytes(10, 768, 3072, 4) == _expected_ws(40, 768, 768)
+    # tall blocks are stored oriented: 4096x1024 -> 1024x4096
+    assert nsm.muon_workspace_bytes(3, 4096, 1024) == _expected_ws(3, 1024, 4096)
+    # ragged shapes pad to 128
+    assert nsm.muon_workspace_bytes(2, 300, 700) == _expected_ws(2, 300, 700)
+    acc = nsm.make_config(precision="accurate")
+    assert nsm.muon_workspace_bytes(2, 300, 700, 1, acc) == _expected_ws(2, 300, 700, split=True)
+    # small blocks need no workspace
+    assert nsm.muon_workspace_bytes(11, 1, 12) == 0
+
+
+@pytest.mark.parametrize("shape", [(1, 0, 5), (1, 5, 0), (1, 8, 10, 4), (-1, 4, 4), (1, 8, 8, 0)])
+def test_workspace_bytes_rejects_bad_shapes(lib, shape):
+    b, r, c, *v = shape
+    with pytest.raises(nsm.MuonError) as e:
+        nsm.muon_workspace_bytes(b, r, c, v[0] if v else 1)
+    assert e.value.status == 2
+    assert nsm.muon_last_error()
+
+
+def _cfg(**kw):
+    cfg = nsm.muon_ns_config_default()
+    for k, v in kw.items():
+        setattr(cfg, k, v)
+    return cfg
+
+
+def test_ns_validation_before_device(lib):
+    fake = ctypes.c_void_p(1 << 20)   # never dereferenced: every call below fails validation
+    # batch 0 is a no-op even with null pointers
+    assert lib.ns_orthogonalize_batched(None, None, 0, 4, 4, 1, None, None, 0, None) == 0
+    assert lib.ns_orthogonalize_batched(None, fake, 2, 64, 64, 1, None, None, 0, None) == 1
+    assert "non-null" in nsm.muon_last_error()
+    assert lib.ns_orthogonalize_batched(fake, fake, 2, 64, 0, 1, None, None, 0, None) == 2
+    assert lib.ns_orthogonalize_batched(fake, fake, 2, 64, 66, 4, None, None, 0, None) == 2
+    assert lib.ns_orthogonalize_batched(ctypes.c_void_p((1 << 20) + 2), fake, 2, 64, 64, 1,
+                                        None, None, 0, None) == 3
+    assert lib.ns_orthogonalize_batched(fake, fake, 2, 64, 64, 1, ctypes.byref(_cfg(ns_steps=-1)),
+                                        None, 0, None) == 1
+    assert lib.ns_orthogonalize_batched(fake, fake, 2, 64, 64, 1, ctypes.byref(_cfg(precision=7)),
+                                        None, 0, None) == 1
+    assert lib.ns_orthogonalize_batched(fake, fake, 2, 64, 64, 1, ctypes.byref(_cfg(eps=-1.0)),
+                                        None, 0, None) == 1
+    # workspace missing or too small
+    assert lib.ns_orthogonalize_batched(fake, fake, 2, 64, 64, 1, None, None, 0, None) == 4
+    assert lib.ns_orthogonalize_batched(fake, fake, 2, 64, 64, 1, None, fake, 100, None) == 4
+    need = nsm.muon_workspace_bytes(2, 64, 64)
+    assert lib.ns_orthogonalize_batched(fake, fake, 2, 64, 64, 1, None,
+                                        ctypes.c_void_p((1 << 20) + 16), need, None) == 3
+    # partial overlap of out and x
+    assert lib.ns_orthogonalize_batched(fake, ctypes.c_void_p((1 << 20) + 16), 2, 64, 64, 1, None,
+                                        fake, need, None) == 1
+
+
+def test_step_validation_before_device(lib):
+    fake = ctypes.c_void_p(1 << 20)
+    other = ctypes.c_void_p(1 << 32)
+    third = ctypes.c_void_p(1 << 34)
+    f = ctypes.c_float
+    args = dict(lr=0.02, wd=0.01, mu=0.95)
+
+    def call(p, g, m, b=2, r=64, c=64, v=1, lr=0.02, wd=0.01, mu=0.95, out=None, ws=None, wsb=0):
+        return lib.muon_step_batched(p, g, m, b, r, c, v, f(lr), f(wd), f(mu), 1, f(1.0), f(1.0),
+                                     None, out, ws, wsb, None)
+    assert call(None, None, None, b=0) == 0
+    assert call(None, other, third) == 1
+    assert call(fake, other, third, mu=1.5) == 1
+    assert call(fake, other, third, lr=float("nan")) == 1
+    assert call(fake, other, third, wd=float("inf")) == 1
+    assert call(fake, fake, third) == 1        # params and grads overlap
+    assert call(fake, other, third, out=other) == 1
+    assert call(fake, other, third, c=0) == 2
+    assert call(fake, other, third) == 4       # no workspace
+    del args

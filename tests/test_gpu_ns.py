@@ -1,0 +1,177 @@
+"""GPU parity of ns_orthogonalize_batched against the fp64 oracle, plus the
+invariants the HIP path must keep (bitwise: transpose, batch position, attn view,
+determinism, aliasing, zero input, power-of-two scaling; to rounding: oddness)."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from parity import assert_ns_close, bits_to_f64, rel_fro, torch_bf16_to_bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def nsm():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the gpu-marked tests must run on an MI355X")
+    import newton_schulz_muon_amd as m
+    m.load_library()
+    return m
+
+
+def _run(nsm, bits, **kw):
+    import torch
+    x = workloads.to_device_bf16(bits)
+    out = nsm.ns_orthogonalize_batched(x, **kw)
+    torch.cuda.synchronize()
+    return torch_bf16_to_bits(out)
+
+
+def _oracle_batch(bits, view_blocks=1, steps=5, coeffs=oracle.NS_COEFFS):
+    return oracle.ns_batched(bits_to_f64(bits), view_blocks=view_blocks, steps=steps, coeffs=coeffs)
+
+
+# Shapes span several 128-tiles, ragged tails (padding), tall blocks (transposed
+# orientation), the small-block path (m <= 32) and the smallest MFMA-path block.
+SHAPES = [(64, 128), (128, 128), (256, 640), (640, 256), (300, 700), (700, 300), (33, 70), (70, 33),
+          (96, 1000), (1, 12), (16, 200), (32, 128), (12, 1)]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_ns_parity_default(nsm, shape):
+    print(f"[ns parity] shape={shape}", flush=True)
+    bits = workloads.gaussian_bits((3,) + shape, seed=shape[0] * 1000 + shape[1])
+    got = bits_to_f64(_run(nsm, bits))
+    ref = _oracle_batch(bits)
+    for i in range(3):
+        assert_ns_close(got[i], ref[i], label=f"{shape}[{i}]")
+
+
+@pytest.mark.parametrize("coeffs", [(1.0, 0.0, 0.0), (0.0, 1.0, 0.0), (0.0, 0.0, 1.0), oracle.NS_COEFFS])
+@pytest.mark.parametrize("shape", [(256, 640), (300, 200)])
+def test_ns_single_iteration_terms(nsm, coeffs, shape):
+    # One iteration with one coefficient at a time isolates the Gram, polynomial
+    # and B X kernels (and the normalisation folded into their epilogues).
+    print(f"[ns one step] shape={shape} coeffs={coeffs}", flush=True)
+    bits = workloads.gaussian_bits((2,) + shape, seed=7)
+    got = bits_to_f64(_run(nsm, bits, ns_steps=1, coeffs=coeffs))
+    ref = _oracle_batch(bits, steps=1, coeffs=coeffs)
+    for i in range(2):
+        assert rel_fro(got[i], ref[i]) < 1e-2, (coeffs, i, rel_fro(got[i], ref[i]))
+
+
+@pytest.mark.parametrize("shape", [(200, 300), (1, 12)])
+def test_ns_zero_steps_is_normalisation(nsm, shape):
+    bits = workloads.gaussian_bits((2,) + shape, seed=3, std=7.0)
+    got = bits_to_f64(_run(nsm, bits, ns_steps=0))
+    ref = _oracle_batch(bits, steps=0)
+    for i in range(2):
+        assert rel_fro(got[i], ref[i]) < 4e-3
+
+
+def test_ns_attn_view(nsm):
+    # stored 96 x 384 read as 4 contiguous 96 x 96 blocks
+    bits = workloads.gaussian_bits((3, 96, 384), seed=11)
+    got = _run(nsm, bits, view_blocks=4)
+    ref = _oracle_batch(bits, view_blocks=4)
+    for i in range(3):
+        assert_ns_close(bits_to_f64(got[i]), ref[i], view_blocks=4, label=f"view[{i}]")
+    # identical to running the [12, 96, 96] reinterpretation without the view
+    flat = _run(nsm, bits.reshape(12, 96, 96))
+    np.testing.assert_array_equal(got.reshape(12, 96, 96), flat)
+
+
+def test_ns_transpose_is_bitwise(nsm):
+    bits = workloads.gaussian_bits((2, 200, 520), seed=5)
+    a = _run(nsm, bits)
+    b = _run(nsm, np.ascontiguousarray(bits.transpose(0, 2, 1)))
+    np.testing.assert_array_equal(a, b.transpose(0, 2, 1))
+
+
+def test_ns_odd_within_rounding(nsm):
+    # NS is odd in exact arithmetic.  MFMA fp32 accumulation does not round
+    # negated sums to exactly the negated value, so -x and x agree to rounding
+    # level only (not bitwise); both must match the oracle.
+    bits = workloads.gaussian_bits((2, 256, 384), seed=6)
+    a = bits_to_f64(_run(nsm, bits))
+    b = bits_to_f64(_run(nsm, bits ^ np.uint16(0x8000)))
+    ref = _oracle_batch(bits)
+    for i in range(2):
+        assert_ns_close(a[i], ref[i], label=f"+x[{i}]")
+        assert_ns_close(b[i], -ref[i], label=f"-x[{i}]")
+        assert rel_fro(b[i], -a[i]) < 1e-2
+
+
+def test_ns_batch_position_and_determinism(nsm):
+    bits = workloads.gaussian_bits((5, 160, 416), seed=9)
+    a = _run(nsm, bits)
+    a2 = _run(nsm, bits)
+    np.testing.assert_array_equal(a, a2)
+    perm = [3, 0, 4, 1, 2]
+    b = _run(nsm, bits[perm])
+    np.testing.assert_array_equal(a[perm], b)
+    single = _run(nsm, bits[2:3])
+    np.testing.assert_array_equal(a[2:3], single)
+
+
+def test_ns_in_place_alias(nsm):
+    import torch
+    bits = workloads.gaussian_bits((2, 130, 260), seed=12)
+    ref = _run(nsm, bits)
+    for steps in (1, 5):
+        x = workloads.to_device_bf16(bits)
+        nsm.ns_orthogonalize_batched(x, out=x, ns_steps=steps)
+        torch.cuda.synchronize()
+        if steps == 5:
+            np.testing.assert_array_equal(torch_bf16_to_bits(x), ref)
+        else:
+            assert_ns_close(bits_to_f64(torch_bf16_to_bits(x))[0], _oracle_batch(bits, steps=1)[0],
+                            tol=1e-2, label="alias one step")
+
+
+def test_ns_zero_block(nsm):
+    bits = np.zeros((2, 128, 256), np.uint16)
+    bits[1] = workloads.gaussian_bits((128, 256), seed=1)
+    got = _run(nsm, bits)
+    assert np.all(got[0] == 0)
+    assert_ns_close(bits_to_f64(got[1]), _oracle_batch(bits[1:])[0], label="nonzero neighbour")
+
+
+def test_ns_scale_invariance(nsm):
+    # NS normalises first, so scaling the input by a power of two changes nothing
+    bits = workloads.gaussian_bits((2, 192, 320), seed=13)
+    scaled = workloads.f32_to_bf16_bits(workloads.bf16_bits_to_f32(bits) * np.float32(64.0))
+    np.testing.assert_array_equal(_run(nsm, bits), _run(nsm, scaled))
+
+
+def test_ns_accurate_mode(nsm):
+    bits = workloads.gaussian_bits((2, 256, 640), seed=14)
+    fast = bits_to_f64(_run(nsm, bits))
+    acc = bits_to_f64(_run(nsm, bits, precision="accurate"))
+    ref = _oracle_batch(bits)
+    for i in range(2):
+        e_fast = rel_fro(fast[i], ref[i])
+        e_acc = rel_fro(acc[i], ref[i])
+        assert e_acc < 2e-2
+        assert e_acc < e_fast, (e_acc, e_fast)
+
+
+def test_ns_rejects_misaligned_and_small_workspace(nsm):
+    import ctypes
+    import torch
+    lib = nsm.load_library()
+    x = torch.zeros((2, 128, 128), dtype=torch.bfloat16, device="cuda")
+    need = nsm.muon_workspace_bytes(2, 128, 128)
+    ws = torch.empty(need + 512, dtype=torch.uint8, device="cuda")
+    st = lib.ns_orthogonalize_batched(x.data_ptr(), x.data_ptr(), 2, 128, 128, 1, None,
+                                      ws.data_ptr(), need - 1, None)
+    assert st == 4
+    st = lib.ns_orthogonalize_batched(x.data_ptr() + 2, x.data_ptr(), 2, 128, 128, 1, None,
+                                      ws.data_ptr(), need, None)
+    assert st == 3
+    st = lib.ns_orthogonalize_batched(x.data_ptr(), x.data_ptr(), 2, 128, 128, 1, None,
+                                      ws.data_ptr() + 64, need, None)
+    assert st == 3
+    assert nsm.muon_last_error()

@@ -31,7 +31,7 @@ import numpy as np
 __all__ = [
     "f32_to_bf16_bits", "bf16_bits_to_f32", "Group", "Workload", "WORKLOADS",
     "get_workload", "grad_bits_host", "param_init_host", "momentum_warmup",
-    "grads_device", "params_device",
+    "grads_device", "params_device", "gaussian_bits", "to_device_bf16",
 ]
 
 
@@ -297,3 +297,16 @@ def params_device(wl: Workload, group: Group, device="cuda"):
     p = torch.randn((group.count, group.rows, group.cols), generator=gen, device=device,
                     dtype=torch.float32)
     return p.mul_(1.0 / float(np.sqrt(group.cols)))
+
+
+def gaussian_bits(shape, seed: int, std: float = 1.0) -> np.ndarray:
+    """bf16 bits of seeded N(0, std^2) samples of any shape (ad-hoc test inputs)."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 0xAD40C])))
+    return f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32) * np.float32(std))
+
+
+def to_device_bf16(bits: np.ndarray, device="cuda"):
+    """Uploads bf16 bit patterns as a torch.bfloat16 tensor."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.to(device).view(torch.bfloat16)
