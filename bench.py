@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Benchmark of the batched Muon step on one MI355X.
+
+A step is one pass of the whole hot path over one batch: momentum, per-block
+Frobenius normalisation, 5 quintic Newton-Schulz iterations, aspect-scaled
+decoupled-decay update, for the 124M GPT custom-sizing set: 11 gate matrices
+1x12 (first), 10 attention matrices stored 768x3072 and viewed as 4 x 768x768,
+and 22 MLP matrices 768x3072 (seeded synthetic bf16 gradients ~N(0, 1e-2),
+fp32 parameters and momentum buffers resident in HBM).
+
+Prints one JSON line.  `value` is nominal Newton-Schulz TFLOP/s of the whole
+step (5 (4 m^2 n + 2 m^3) flops per NS block, m <= n, divided by the wall-clock
+step time); matrices/s and NS blocks/s are reported beside it.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Newton-Schulz TFLOP/s and matrices/s at 32x768x3072 bf16; % of MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+WORKLOAD = "gpt124m"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_bx_gpt124m_traffic.json")
+GEMM_SOURCE = os.path.join(ROOT, "newton_schulz_muon_amd", "csrc", "ns_gemm.hip")
+
+
+def ns_flops(m: int, n: int, steps: int) -> float:
+    """Nominal NS work of one block: steps * (4 m^2 n + 2 m^3), m <= n."""
+    m, n = min(m, n), max(m, n)
+    return float(steps) * (4.0 * m * m * n + 2.0 * m ** 3)
+
+
+def bx_flops(m: int, n: int, steps: int) -> float:
+    """Work of the B X products of one block: steps * 2 m^2 n."""
+    m, n = min(m, n), max(m, n)
+    return float(steps) * 2.0 * m * m * n
+
+
+def source_digest(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic():
+    """HBM bytes per k_bx launch from the committed rocprofv3 counter runs,
+    or None when they are missing or the kernel source changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256_16") != source_digest(GEMM_SOURCE):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, seconds: float):
+    """The fp64 oracle on a bounded sample of the workload (host cores)."""
+    import numpy as np
+    import oracle
+    import workloads
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        threads = os.cpu_count() or 1
+    groups = {g.name: g for g in wl.groups}
+    plan = [("gate", i) for i in range(groups["gate"].count)]
+    for i in range(max(groups["mlp"].count, groups["attn"].count)):
+        if i < groups["mlp"].count:
+            plan.append(("mlp", i))
+        if i < groups["attn"].count:
+            plan.append(("attn", i))
+    done_flops, done_mats, used = 0.0, 0, []
+    t0 = time.perf_counter()
+    for name, i in plan:
+        g = groups[name]
+        G = workloads.bf16_bits_to_f32(workloads.grad_bits_host(wl, g, 0, [i])).astype(np.float64)
+        P = workloads.param_init_host(wl, g, [i]).astype(np.float64)
+        M = np.zeros_like(G)
+        oracle.muon_step(P, G, M, lr=wl.lr, weight_decay=wl.weight_decay, momentum=wl.momentum,
+                         view_blocks=g.view_blocks, ns_steps=wl.ns_steps)
+        r, c = g.block_shape
+        done_flops += g.view_blocks * ns_flops(r, c, wl.ns_steps)
+        done_mats += 1
+        used.append(f"{name}[{i}]")
+        if time.perf_counter() - t0 > seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 numpy oracle, one full Muon step of {done_mats} matrices "
+                      f"({', '.join(used)}) in {dt:.1f} s; {done_mats / dt:.3f} matrices/s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the kernel breakdown and NS-only passes")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="run a plain device copy of MIB MiB first (HBM counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(see DESIGN.md for how the step would shard).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import newton_schulz_muon_amd as nsm
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    nsm.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = workloads.get_workload(WORKLOAD)
+
+    if args.copy_calibration > 0:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    state = []
+    for g in wl.groups:
+        P = workloads.params_device(wl, g, dev)
+        G = workloads.grads_device(wl, g, 0, dev)
+        M = torch.zeros_like(P)
+        state.append((g, P, G, M))
+    torch.cuda.synchronize()
+
+    def step():
+        for g, P, G, M in state:
+            nsm.muon_step_batched(P, G, M, lr=wl.lr, weight_decay=wl.weight_decay, momentum=wl.momentum,
+                                  view_blocks=g.view_blocks, ns_steps=wl.ns_steps, precision=g.precision)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps, k_bx launches bracketed by hipEvents on the library's stream
+    nsm.muon_timing_collect()
+    nsm.muon_timing_enable(["bx"])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    nsm.muon_timing_enable([])
+    kt = nsm.muon_timing_collect()
+
+    ms_per_step = (t1 - t0) * 1000.0 / args.steps
+    flops_step = sum(g.view_blocks * g.count * ns_flops(*g.block_shape, wl.ns_steps) for g in wl.groups)
+    n_blocks = sum(g.n_blocks for g in wl.groups)
+    value = flops_step / (ms_per_step / 1000.0) / 1e12
+
+    mfma_groups = [g for g in wl.groups if min(g.block_shape) > 32]
+    bx_flops_step = sum(g.n_blocks * bx_flops(*g.block_shape, wl.ns_steps) for g in mfma_groups)
+    bx_launches, bx_ms = kt.get("bx", (0, 0.0))
+    roofline = None
+    if bx_launches:
+        achieved = bx_flops_step * args.steps / (bx_ms / 1000.0) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                    "traffic": load_traffic(), "kernel": "k_bx<false> (X <- a X + B X)",
+                    "launches": bx_launches, "avg_launch_ms": round(bx_ms / bx_launches, 5),
+                    "flops_per_launch_avg": bx_flops_step * args.steps / bx_launches}
+
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "124M GPT custom sizing: 11 gates 1x12 + 10 attn 768x3072 viewed as "
+                               "4x768x768 + 22 mlp 768x3072; full Muon step (momentum 0.95 Nesterov, "
+                               "5 NS steps, lr 0.05, wd 0)",
+                   "matrices": wl.n_matrices, "ns_blocks": n_blocks, "ns_steps": wl.ns_steps,
+                   "precision": "fast (bf16 MFMA, fp32 accumulate); gates on the fp32 small-block path",
+                   "nominal_ns_gflop_per_step": round(flops_step / 1e9, 2)},
+        "matrices_per_s": round(wl.n_matrices / (ms_per_step / 1000.0), 1),
+        "ns_blocks_per_s": round(n_blocks / (ms_per_step / 1000.0), 1),
+        "mfma_peak_frac_nominal": round(value / PEAK_BF16_TFLOPS, 4),
+        "roofline": roofline,
+    }
+
+    if not args.no_extras:
+        # ---- attribution pass (separate from the timed region): every kernel family timed
+        nsm.muon_timing_enable(list(nsm.KERNEL_KINDS))
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        nsm.muon_timing_enable([])
+        allk = nsm.muon_timing_collect()
+        result["kernel_ms_per_step"] = {k: round(v[1] / args.steps, 4) for k, v in allk.items()}
+        ew_bytes = sum(g.count * g.rows * g.cols for g in mfma_groups)
+        if "prep" in allk:
+            prep_ms = allk["prep"][1] / args.steps
+            result["prep_hbm_gbs"] = round(12.0 * ew_bytes / (prep_ms / 1000.0) / 1e9, 1)
+        if "finish" in allk:
+            fin_ms = allk["finish"][1] / args.steps
+            result["finish_hbm_gbs"] = round(10.0 * ew_bytes / (fin_ms / 1000.0) / 1e9, 1)
+        # ---- NS only on the metric's exact batch: 32 x 768 x 3072, no view
+        x = workloads.grads_device(workloads.get_workload("metric32"), workloads.get_workload("metric32").groups[0], 0, dev)
+        out = torch.empty_like(x)
+        for _ in range(3):
+            nsm.ns_orthogonalize_batched(x, out)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            nsm.ns_orthogonalize_batched(x, out)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        f = 32 * ns_flops(768, 3072, 5)
+        result["ns_only_32x768x3072"] = {"ms": round(ms, 4), "tflops": round(f / (ms / 1000) / 1e12, 2),
+                                         "matrices_per_s": round(32 / (ms / 1000), 1),
+                                         "mfma_peak_frac_nominal": round(f / (ms / 1000) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del x, out
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

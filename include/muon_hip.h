@@ -128,6 +128,29 @@ muon_status muon_step_batched(float* params, const void* grads, float* momentum_
                               void* workspace, size_t workspace_bytes,
                               void* stream);
 
+/* Kernel timing (diagnostics).  Kernel families of the library: */
+typedef enum muon_kernel_kind {
+    MUON_KERNEL_PREP = 0,           /* momentum + cast + tile norms            */
+    MUON_KERNEL_NORM_FINALIZE = 1,  /* per-block 1/|X|_F                       */
+    MUON_KERNEL_GRAM = 2,           /* A = X X^T                               */
+    MUON_KERNEL_POLY = 3,           /* B = b A + c A A                         */
+    MUON_KERNEL_BX = 4,             /* X <- a X + B X                          */
+    MUON_KERNEL_FINISH = 5,         /* NS output / parameter update            */
+    MUON_KERNEL_SMALL = 6,          /* whole step for small blocks             */
+    MUON_KERNEL_COUNT = 7
+} muon_kernel_kind;
+
+/* While kernel_mask has bit k set, every launch of kernel family k records a
+ * hipEvent before and after it on the stream it is launched on (events are
+ * created on first use and reused; 0 turns recording off).  Recording adds
+ * two event packets per selected launch and nothing when the mask is 0. */
+muon_status muon_timing_enable(uint32_t kernel_mask);
+
+/* Waits for every recorded event, adds launch counts and elapsed milliseconds
+ * per family into launches[MUON_KERNEL_COUNT] and total_ms[MUON_KERNEL_COUNT]
+ * (either may be NULL), and forgets the recorded launches. */
+muon_status muon_timing_collect(int64_t* launches, double* total_ms);
+
 /* Text of the last error on the calling thread ("" if none).  Valid until
  * the next call into the library from that thread. */
 const char* muon_last_error(void);

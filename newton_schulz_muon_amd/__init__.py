@@ -22,12 +22,15 @@ from typing import Optional, Tuple
 __all__ = [
     "MuonNSConfig", "MuonError", "LIB_PATH", "EXPORTED_SYMBOLS", "load_library",
     "muon_ns_config_default", "muon_workspace_bytes", "ns_orthogonalize_batched",
-    "muon_step_batched", "muon_last_error", "muon_abi_version", "make_config",
+    "muon_step_batched", "muon_timing_enable", "muon_timing_collect", "muon_last_error",
+    "muon_abi_version", "make_config", "KERNEL_KINDS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmuon_hip.so")
 EXPORTED_SYMBOLS = ("muon_ns_config_default", "muon_workspace_bytes", "ns_orthogonalize_batched",
-                    "muon_step_batched", "muon_last_error", "muon_abi_version")
+                    "muon_step_batched", "muon_timing_enable", "muon_timing_collect",
+                    "muon_last_error", "muon_abi_version")
+KERNEL_KINDS = ("prep", "norm_finalize", "gram", "poly", "bx", "finish", "small")
 
 MUON_OK = 0
 _STATUS_NAMES = {0: "MUON_OK", 1: "MUON_ERR_INVALID_ARG", 2: "MUON_ERR_SHAPE", 3: "MUON_ERR_ALIGNMENT",
@@ -70,6 +73,10 @@ def load_library():
         lib.muon_step_batched.argtypes = [vp, vp, vp, i64, i64, i64, i32, f32, f32, f32, i32, f32, f32,
                                           cfgp, vp, vp, ctypes.c_size_t, vp]
         lib.muon_step_batched.restype = ctypes.c_int
+        lib.muon_timing_enable.argtypes = [ctypes.c_uint32]
+        lib.muon_timing_enable.restype = ctypes.c_int
+        lib.muon_timing_collect.argtypes = [ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]
+        lib.muon_timing_collect.restype = ctypes.c_int
         lib.muon_last_error.argtypes = []
         lib.muon_last_error.restype = ctypes.c_char_p
         lib.muon_abi_version.argtypes = []
@@ -96,6 +103,24 @@ def make_config(ns_steps: int = 5, coeffs: Optional[Tuple[float, float, float]] 
         raise ValueError(f"precision must be one of {sorted(PRECISIONS)}")
     cfg.precision = PRECISIONS[precision]
     return cfg
+
+
+def muon_timing_enable(kinds=()) -> None:
+    """Records hipEvents around every launch of the named kernel families
+    (names from KERNEL_KINDS); an empty list turns recording off."""
+    mask = 0
+    for k in kinds:
+        mask |= 1 << KERNEL_KINDS.index(k)
+    _check(load_library().muon_timing_enable(mask))
+
+
+def muon_timing_collect() -> dict:
+    """{family: (launches, total_ms)} for the launches recorded since the last collect."""
+    n = len(KERNEL_KINDS)
+    launches = (ctypes.c_int64 * n)()
+    total = (ctypes.c_double * n)()
+    _check(load_library().muon_timing_collect(launches, total))
+    return {k: (int(launches[i]), float(total[i])) for i, k in enumerate(KERNEL_KINDS) if launches[i]}
 
 
 def muon_last_error() -> str:

@@ -12,6 +12,9 @@
 // Small blocks (m <= 32, m n <= 4096) run the whole step in one k_small launch.
 #include <atomic>
 #include <cmath>
+#include <map>
+#include <mutex>
+#include <vector>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -134,6 +137,69 @@ muon_status check_device() {
     return MUON_OK;
 }
 
+// ---------------------------------------------------------------- kernel timing
+struct TimingState {
+    std::mutex mu;
+    std::atomic<uint32_t> mask{0};
+    std::map<int, std::vector<hipEvent_t>> pool;   // per device
+    struct Rec { int kind; int dev; hipEvent_t a, b; };
+    std::vector<Rec> recs;
+};
+
+TimingState& timing() {
+    static TimingState* t = new TimingState();   // never destroyed: events outlive static teardown
+    return *t;
+}
+
+hipEvent_t pool_get(TimingState& ts, int dev) {
+    auto& v = ts.pool[dev];
+    if (!v.empty()) {
+        hipEvent_t e = v.back();
+        v.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// Records an event pair around one launch when its kernel family is selected.
+class LaunchTimer {
+  public:
+    LaunchTimer(int kind, hipStream_t s) : kind_(kind), s_(s) {
+        TimingState& ts = timing();
+        if (!(ts.mask.load() & (1u << kind))) return;
+        std::lock_guard<std::mutex> lk(ts.mu);
+        if (hipGetDevice(&dev_) != hipSuccess) return;
+        a_ = pool_get(ts, dev_);
+        b_ = pool_get(ts, dev_);
+        if (a_ && b_ && hipEventRecord(a_, s_) == hipSuccess) on_ = true;
+    }
+    void stop() {
+        if (!on_) return;
+        on_ = false;
+        TimingState& ts = timing();
+        std::lock_guard<std::mutex> lk(ts.mu);
+        if (hipEventRecord(b_, s_) == hipSuccess) ts.recs.push_back({kind_, dev_, a_, b_});
+    }
+    ~LaunchTimer() { stop(); }
+
+  private:
+    int kind_;
+    hipStream_t s_;
+    int dev_ = 0;
+    hipEvent_t a_ = nullptr, b_ = nullptr;
+    bool on_ = false;
+};
+
+template <typename F>
+hipError_t timed(int kind, hipStream_t s, F&& f) {
+    LaunchTimer t(kind, s);
+    const hipError_t e = f();
+    t.stop();
+    return e;
+}
+
 bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0; }
 
 bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
@@ -172,16 +238,18 @@ Buffers carve(const Plan& p, void* ws) {
 // xh[0] (and xl[0]).  Returns the buffer holding the result.
 muon_status run_ns(const Plan& p, const muon_ns_config& cfg, const Buffers& b, hipStream_t s,
                    int* final_idx) {
-    hipError_t e = launch_norm_finalize(p, b.part, b.scale, cfg.eps, s);
+    hipError_t e = timed(MUON_KERNEL_NORM_FINALIZE, s, [&] { return launch_norm_finalize(p, b.part, b.scale, cfg.eps, s); });
     if (e != hipSuccess) return hip_fail(e, "k_norm_finalize launch");
     int cur = 0;
     for (int it = 0; it < cfg.ns_steps; ++it) {
         const float* sc = it == 0 ? b.scale : nullptr;
-        e = launch_gram(p, b.xh[cur], b.a, sc, s);
+        e = timed(MUON_KERNEL_GRAM, s, [&] { return launch_gram(p, b.xh[cur], b.a, sc, s); });
         if (e != hipSuccess) return hip_fail(e, "k_sym<gram> launch");
-        e = launch_poly(p, b.a, b.bh, b.bl, cfg.b, cfg.c, s);
+        e = timed(MUON_KERNEL_POLY, s, [&] { return launch_poly(p, b.a, b.bh, b.bl, cfg.b, cfg.c, s); });
         if (e != hipSuccess) return hip_fail(e, "k_sym<poly> launch");
-        e = launch_bx(p, b.bh, b.bl, b.xh[cur], b.xl[cur], b.xh[cur ^ 1], b.xl[cur ^ 1], cfg.a, sc, s);
+        e = timed(MUON_KERNEL_BX, s, [&] {
+            return launch_bx(p, b.bh, b.bl, b.xh[cur], b.xl[cur], b.xh[cur ^ 1], b.xl[cur ^ 1], cfg.a, sc, s);
+        });
         if (e != hipSuccess) return hip_fail(e, "k_bx launch");
         cur ^= 1;
     }
@@ -253,18 +321,21 @@ muon_status ns_orthogonalize_batched(const void* x, void* out, int64_t batch, in
         ss.b = cfg.b;
         ss.c = cfg.c;
         ss.eps = cfg.eps;
-        const hipError_t e = launch_small(p, ss, s);
+        const hipError_t e = timed(MUON_KERNEL_SMALL, s, [&] { return launch_small(p, ss, s); });
         return e == hipSuccess ? MUON_OK : hip_fail(e, "k_small launch");
     }
     const Buffers b = carve(p, workspace);
-    hipError_t e = launch_prep(p, kPrepCast, static_cast<const uint16_t*>(x), nullptr, 0.f, b.xh[0], b.xl[0],
-                               b.part, s);
+    hipError_t e = timed(MUON_KERNEL_PREP, s, [&] {
+        return launch_prep(p, kPrepCast, static_cast<const uint16_t*>(x), nullptr, 0.f, b.xh[0], b.xl[0], b.part, s);
+    });
     if (e != hipSuccess) return hip_fail(e, "k_prep launch");
     int fin = 0;
     st = run_ns(p, cfg, b, s, &fin);
     if (st != MUON_OK) return st;
-    e = launch_finish(p, b.xh[fin], b.xl[fin], cfg.ns_steps == 0 ? b.scale : nullptr, nullptr, 1.f, 0.f,
-                      static_cast<uint16_t*>(out), s);
+    e = timed(MUON_KERNEL_FINISH, s, [&] {
+        return launch_finish(p, b.xh[fin], b.xl[fin], cfg.ns_steps == 0 ? b.scale : nullptr, nullptr, 1.f, 0.f,
+                             static_cast<uint16_t*>(out), s);
+    });
     return e == hipSuccess ? MUON_OK : hip_fail(e, "k_finish launch");
 }
 
@@ -320,19 +391,52 @@ muon_status muon_step_batched(float* params, const void* grads, float* momentum_
         ss.b = cfg.b;
         ss.c = cfg.c;
         ss.eps = cfg.eps;
-        const hipError_t e = launch_small(p, ss, s);
+        const hipError_t e = timed(MUON_KERNEL_SMALL, s, [&] { return launch_small(p, ss, s); });
         return e == hipSuccess ? MUON_OK : hip_fail(e, "k_small launch");
     }
     const Buffers b = carve(p, workspace);
-    hipError_t e = launch_prep(p, mode, static_cast<const uint16_t*>(grads), momentum_buf, momentum, b.xh[0],
-                               b.xl[0], b.part, s);
+    hipError_t e = timed(MUON_KERNEL_PREP, s, [&] {
+        return launch_prep(p, mode, static_cast<const uint16_t*>(grads), momentum_buf, momentum, b.xh[0], b.xl[0],
+                           b.part, s);
+    });
     if (e != hipSuccess) return hip_fail(e, "k_prep launch");
     int fin = 0;
     st = run_ns(p, cfg, b, s, &fin);
     if (st != MUON_OK) return st;
-    e = launch_finish(p, b.xh[fin], b.xl[fin], cfg.ns_steps == 0 ? b.scale : nullptr, params, decay, step,
-                      static_cast<uint16_t*>(update_out), s);
+    e = timed(MUON_KERNEL_FINISH, s, [&] {
+        return launch_finish(p, b.xh[fin], b.xl[fin], cfg.ns_steps == 0 ? b.scale : nullptr, params, decay, step,
+                             static_cast<uint16_t*>(update_out), s);
+    });
     return e == hipSuccess ? MUON_OK : hip_fail(e, "k_finish launch");
+}
+
+muon_status muon_timing_enable(uint32_t kernel_mask) {
+    g_err.clear();
+    if (kernel_mask >> MUON_KERNEL_COUNT) return fail(MUON_ERR_INVALID_ARG, "unknown kernel bits in mask 0x%x", kernel_mask);
+    timing().mask.store(kernel_mask);
+    return MUON_OK;
+}
+
+muon_status muon_timing_collect(int64_t* launches, double* total_ms) {
+    g_err.clear();
+    TimingState& ts = timing();
+    std::lock_guard<std::mutex> lk(ts.mu);
+    muon_status st = MUON_OK;
+    for (const auto& r : ts.recs) {
+        float ms = 0.f;
+        hipError_t e = hipEventSynchronize(r.b);
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+        if (e != hipSuccess) {
+            st = hip_fail(e, "muon_timing_collect");
+        } else {
+            if (launches) launches[r.kind] += 1;
+            if (total_ms) total_ms[r.kind] += ms;
+        }
+        ts.pool[r.dev].push_back(r.a);
+        ts.pool[r.dev].push_back(r.b);
+    }
+    ts.recs.clear();
+    return st;
 }
 
 const char* muon_last_error(void) { return g_err.c_str(); }
