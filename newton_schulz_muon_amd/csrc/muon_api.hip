@@ -4,9 +4,10 @@
 // Launch sequence of one call (large blocks):
 //   k_prep            momentum + cast to the oriented padded iterate + tile norms
 //   k_norm_finalize   1/s and 1/s^2 per NS block
-//   ns_steps x { k_sym<Gram>, k_sym<Poly>, k_bx }   ping-pong between two iterates;
+//   ns_steps x { k_sym<Gram>, k_sym<Poly>, k_bx }   ping-pong between two iterates
+//                     (k_sym<Poly> forms B' = a I + b A + c A A, k_bx X' = B' X);
 //                     iteration 1 folds the normalisation into its epilogues
-//                     (A = U U^T / s^2, X1 = (a U + B U) / s), so X0 = U / s is
+//                     (A = U U^T / s^2, X1 = B' U / s), so X0 = U / s is
 //                     never materialised
 //   k_finish          NS output, or the parameter update (+ optional O)
 // Small blocks (m <= 32, m n <= 4096) run the whole step in one k_small launch.
@@ -245,10 +246,10 @@ muon_status run_ns(const Plan& p, const muon_ns_config& cfg, const Buffers& b, h
         const float* sc = it == 0 ? b.scale : nullptr;
         e = timed(MUON_KERNEL_GRAM, s, [&] { return launch_gram(p, b.xh[cur], b.a, sc, s); });
         if (e != hipSuccess) return hip_fail(e, "k_sym<gram> launch");
-        e = timed(MUON_KERNEL_POLY, s, [&] { return launch_poly(p, b.a, b.bh, b.bl, cfg.b, cfg.c, s); });
+        e = timed(MUON_KERNEL_POLY, s, [&] { return launch_poly(p, b.a, b.bh, b.bl, cfg.a, cfg.b, cfg.c, s); });
         if (e != hipSuccess) return hip_fail(e, "k_sym<poly> launch");
         e = timed(MUON_KERNEL_BX, s, [&] {
-            return launch_bx(p, b.bh, b.bl, b.xh[cur], b.xl[cur], b.xh[cur ^ 1], b.xl[cur ^ 1], cfg.a, sc, s);
+            return launch_bx(p, b.bh, b.bl, b.xh[cur], b.xl[cur], b.xh[cur ^ 1], b.xl[cur ^ 1], sc, s);
         });
         if (e != hipSuccess) return hip_fail(e, "k_bx launch");
         cur ^= 1;

@@ -92,14 +92,14 @@ hipError_t launch_finish(const Plan& p, const uint16_t* x_hi, const uint16_t* x_
 // A = scale2 * X X^T   (upper tiles computed, mirrored; scale2 may be null)
 hipError_t launch_gram(const Plan& p, const uint16_t* x, uint16_t* a, const float* scale2,
                        hipStream_t s);
-// B = b A + c A A      (A symmetric; b_lo != nullptr stores the rounding residual)
+// B' = a I + b A + c A A   (A symmetric; b_lo != nullptr stores the rounding residual)
 hipError_t launch_poly(const Plan& p, const uint16_t* a, uint16_t* b_hi, uint16_t* b_lo,
-                       float cb, float cc, hipStream_t s);
-// X' = scale1 * (a X + B X)   (scale1 may be null).  ACCURATE when x_lo/b_lo given:
-// X' = scale1 * (a (Xh + Xl) + Bh Xh + Bh Xl + Bl Xh), stored as hi + lo.
+                       float ca, float cb, float cc, hipStream_t s);
+// X' = scale1 * B' X   (scale1 may be null; a X is carried by the diagonal of B').
+// ACCURATE when x_lo/b_lo are given: X' = scale1 * (Bh Xh + Bh Xl + Bl Xh), stored as hi + lo.
 hipError_t launch_bx(const Plan& p, const uint16_t* b_hi, const uint16_t* b_lo,
                      const uint16_t* x_hi, const uint16_t* x_lo, uint16_t* out_hi,
-                     uint16_t* out_lo, float ca, const float* scale1, hipStream_t s);
+                     uint16_t* out_lo, const float* scale1, hipStream_t s);
 
 // Small blocks (small_ns.hip): the whole step for one block per workgroup in fp32.
 struct SmallStep {
