@@ -183,7 +183,7 @@ def main():
         achieved = bx_flops_step * args.steps / (bx_ms / 1000.0) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                    "traffic": load_traffic(), "kernel": "k_bx<false> (X <- a X + B X)",
+                    "traffic": load_traffic(), "kernel": "k_gemm<kBx> (X <- B' X, B' = aI + bA + cA^2)",
                     "launches": bx_launches, "avg_launch_ms": round(bx_ms / bx_launches, 5),
                     "flops_per_launch_avg": bx_flops_step * args.steps / bx_launches}
 

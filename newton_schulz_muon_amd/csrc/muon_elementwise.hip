@@ -32,12 +32,16 @@ constexpr int T = kEwTile;
 struct PrepArgs {
     const uint16_t* src;   // stored bf16 (gradients or x), this launch's first block
     float* mom;            // stored fp32 momentum buffer
-    uint16_t* xhi;         // oriented padded [nb][mp][np]
-    uint16_t* xlo;
+    uint16_t* dh;          // padded copy in stored orientation [rp][cp] (hi, lo)
+    uint16_t* dl;
+    uint16_t* th;          // padded transposed copy [cp][rp] (hi, lo)
+    uint16_t* tl;
     float* part;           // [nb][ew_tiles]
-    int64_t r, c, mp, np, be;
+    int64_t r, c;          // stored block shape
+    int64_t rp, cp;        // padded stored-orientation shape
+    int64_t be;            // r * c
     int64_t ew_tiles;
-    int tiles_j;
+    int tiles_j;           // cp / 64
     float mu, omm;
 };
 
@@ -108,20 +112,27 @@ __device__ __forceinline__ void load_update8(const PrepArgs& a, const uint16_t* 
     }
 }
 
-template <int MODE, bool TALL, bool VEC, bool SPLIT>
+// One 64 x 64 tile of the padded stored-orientation block per workgroup.  The
+// oriented iterate X is that block for wide blocks (written through d) and its
+// transpose for tall ones (written through t, via LDS); the host passes the
+// one destination that applies and null for the other.
+template <int MODE, bool VEC, bool SPLIT>
 __global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
-    __shared__ uint16_t lds_hi[TALL ? T : 1][T + 2];
-    __shared__ uint16_t lds_lo[(TALL && SPLIT) ? T : 1][T + 2];
+    __shared__ uint16_t lds_hi[T][T + 2];
+    __shared__ uint16_t lds_lo[SPLIT ? T : 1][T + 2];
     __shared__ float red[4];
 
     const int t = threadIdx.x;
     const int64_t blk = blockIdx.y;
     const int tile = blockIdx.x;
-    const int ti = tile / a.tiles_j, tj = tile % a.tiles_j;
+    const int si = tile / a.tiles_j, sj = tile % a.tiles_j;
     const uint16_t* src = a.src + blk * a.be;
     float* mom = (MODE == kPrepCast) ? nullptr : a.mom + blk * a.be;
-    uint16_t* xhi = a.xhi + blk * a.mp * a.np;
-    uint16_t* xlo = SPLIT ? a.xlo + blk * a.mp * a.np : nullptr;
+    const int64_t pad = a.rp * a.cp;
+    uint16_t* dh = a.dh ? a.dh + blk * pad : nullptr;
+    uint16_t* dl = (SPLIT && a.dl) ? a.dl + blk * pad : nullptr;
+    uint16_t* th = a.th ? a.th + blk * pad : nullptr;
+    uint16_t* tl = (SPLIT && a.tl) ? a.tl + blk * pad : nullptr;
     const int rl = t >> 3;
     const int cl = (t & 7) * 8;
     float ss = 0.f;
@@ -129,9 +140,8 @@ __global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int row = rl + 32 * h;
-        // oriented (oi, oj) = stored (bi, bj) for wide blocks, (bj, bi) for tall ones
-        const int64_t bi = TALL ? (int64_t)tj * T + row : (int64_t)ti * T + row;
-        const int64_t bj0 = TALL ? (int64_t)ti * T + cl : (int64_t)tj * T + cl;
+        const int64_t bi = (int64_t)si * T + row;
+        const int64_t bj0 = (int64_t)sj * T + cl;
         float u[8];
         bool ok[8];
         load_update8<MODE, VEC>(a, src, mom, bi, bj0, u, ok);
@@ -147,43 +157,40 @@ __global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
                 ss = fmaf(hv, hv, ss);
             }
         }
-        if constexpr (!TALL) {
-            const int64_t o = ((int64_t)ti * T + row) * a.np + (int64_t)tj * T + cl;
+        if (dh != nullptr) {
+            const int64_t o = bi * a.cp + bj0;   // inside the padded block
             u32x4 w;
 #pragma unroll
             for (int q = 0; q < 4; ++q) w[q] = uint32_t(hi[2 * q]) | (uint32_t(hi[2 * q + 1]) << 16);
-            *reinterpret_cast<u32x4*>(xhi + o) = w;
+            *reinterpret_cast<u32x4*>(dh + o) = w;
             if constexpr (SPLIT) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) w[q] = uint32_t(lo[2 * q]) | (uint32_t(lo[2 * q + 1]) << 16);
-                *reinterpret_cast<u32x4*>(xlo + o) = w;
+                *reinterpret_cast<u32x4*>(dl + o) = w;
             }
-        } else {
+        }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                lds_hi[row][cl + e] = hi[e];
-                if constexpr (SPLIT) lds_lo[row][cl + e] = lo[e];
-            }
+        for (int e = 0; e < 8; ++e) {
+            lds_hi[row][cl + e] = hi[e];
+            if constexpr (SPLIT) lds_lo[row][cl + e] = lo[e];
         }
     }
 
-    if constexpr (TALL) {
-        __syncthreads();
+    __syncthreads();
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int row = rl + 32 * h;   // oriented local row = stored local column
-            const int64_t o = ((int64_t)ti * T + row) * a.np + (int64_t)tj * T + cl;
-            u32x4 w;
+    for (int h = 0; h < 2 && th != nullptr; ++h) {
+        const int row = rl + 32 * h;   // transposed local row = stored local column
+        const int64_t o = ((int64_t)sj * T + row) * a.rp + (int64_t)si * T + cl;
+        u32x4 w;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            w[q] = uint32_t(lds_hi[cl + 2 * q][row]) | (uint32_t(lds_hi[cl + 2 * q + 1][row]) << 16);
+        *reinterpret_cast<u32x4*>(th + o) = w;
+        if constexpr (SPLIT) {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                w[q] = uint32_t(lds_hi[cl + 2 * q][row]) | (uint32_t(lds_hi[cl + 2 * q + 1][row]) << 16);
-            *reinterpret_cast<u32x4*>(xhi + o) = w;
-            if constexpr (SPLIT) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    w[q] = uint32_t(lds_lo[cl + 2 * q][row]) | (uint32_t(lds_lo[cl + 2 * q + 1][row]) << 16);
-                *reinterpret_cast<u32x4*>(xlo + o) = w;
-            }
+                w[q] = uint32_t(lds_lo[cl + 2 * q][row]) | (uint32_t(lds_lo[cl + 2 * q + 1][row]) << 16);
+            *reinterpret_cast<u32x4*>(tl + o) = w;
         }
     }
 
@@ -339,7 +346,7 @@ hipError_t for_block_chunks(int64_t nb, F&& f) {
     return hipSuccess;
 }
 
-template <int MODE, bool TALL, bool VEC, bool SPLIT>
+template <int MODE, bool VEC, bool SPLIT>
 hipError_t run_prep(const Plan& p, const PrepArgs& a, hipStream_t s) {
     const int64_t be = p.r * p.c;
     const int64_t pad = p.mp * p.np;
@@ -347,23 +354,21 @@ hipError_t run_prep(const Plan& p, const PrepArgs& a, hipStream_t s) {
         PrepArgs c = a;
         c.src = a.src + b0 * be;
         c.mom = a.mom ? a.mom + b0 * be : nullptr;
-        c.xhi = a.xhi + b0 * pad;
-        c.xlo = a.xlo ? a.xlo + b0 * pad : nullptr;
+        c.dh = a.dh ? a.dh + b0 * pad : nullptr;
+        c.dl = a.dl ? a.dl + b0 * pad : nullptr;
+        c.th = a.th ? a.th + b0 * pad : nullptr;
+        c.tl = a.tl ? a.tl + b0 * pad : nullptr;
         c.part = a.part + b0 * p.ew_tiles;
-        k_prep<MODE, TALL, VEC, SPLIT><<<dim3(static_cast<unsigned>(p.ew_tiles), cnt), dim3(256), 0, s>>>(c);
+        k_prep<MODE, VEC, SPLIT><<<dim3(static_cast<unsigned>(p.ew_tiles), cnt), dim3(256), 0, s>>>(c);
     });
 }
 
 template <int MODE>
 hipError_t prep_mode(const Plan& p, const PrepArgs& a, hipStream_t s) {
     const bool vec = (p.c % 8) == 0;
-    const bool split = a.xlo != nullptr;
-    if (p.tall) {
-        if (vec) return split ? run_prep<MODE, true, true, true>(p, a, s) : run_prep<MODE, true, true, false>(p, a, s);
-        return split ? run_prep<MODE, true, false, true>(p, a, s) : run_prep<MODE, true, false, false>(p, a, s);
-    }
-    if (vec) return split ? run_prep<MODE, false, true, true>(p, a, s) : run_prep<MODE, false, true, false>(p, a, s);
-    return split ? run_prep<MODE, false, false, true>(p, a, s) : run_prep<MODE, false, false, false>(p, a, s);
+    const bool split = a.dl != nullptr || a.tl != nullptr;
+    if (vec) return split ? run_prep<MODE, true, true>(p, a, s) : run_prep<MODE, true, false>(p, a, s);
+    return split ? run_prep<MODE, false, true>(p, a, s) : run_prep<MODE, false, false>(p, a, s);
 }
 
 template <bool UPDATE, bool TALL, bool VEC, bool SPLIT>
@@ -402,16 +407,19 @@ hipError_t launch_prep(const Plan& p, PrepMode mode, const uint16_t* src, float*
     PrepArgs a;
     a.src = src;
     a.mom = mom;
-    a.xhi = x_hi;
-    a.xlo = x_lo;
+    // wide block: X is the stored orientation; tall block: X is its transpose
+    a.dh = p.tall ? nullptr : x_hi;
+    a.dl = p.tall ? nullptr : x_lo;
+    a.th = p.tall ? x_hi : nullptr;
+    a.tl = p.tall ? x_lo : nullptr;
     a.part = partials;
     a.r = p.r;
     a.c = p.c;
-    a.mp = p.mp;
-    a.np = p.np;
+    a.rp = p.tall ? p.np : p.mp;
+    a.cp = p.tall ? p.mp : p.np;
     a.be = p.r * p.c;
     a.ew_tiles = p.ew_tiles;
-    a.tiles_j = static_cast<int>(p.np / T);
+    a.tiles_j = static_cast<int>(a.cp / T);
     a.mu = mu;
     a.omm = 1.0f - mu;
     switch (mode) {

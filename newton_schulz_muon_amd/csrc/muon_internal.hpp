@@ -73,11 +73,10 @@ __device__ __forceinline__ float wave_sum(float v) {
 enum PrepMode { kPrepCast = 0, kPrepNesterov = 1, kPrepPlain = 2 };
 
 // Reads the stored batch (bf16 x or gradients), updates the momentum buffer
-// (momentum modes), writes the oriented padded iterate X0 (bf16, hi plane;
-// lo plane too when x_lo != nullptr) and per-tile sums of squares.
-hipError_t launch_prep(const Plan& p, PrepMode mode, const uint16_t* src, float* mom,
-                       float mu, uint16_t* x_hi, uint16_t* x_lo, float* partials,
-                       hipStream_t s);
+// (momentum modes), writes the oriented padded iterate X0 (bf16 hi plane; lo
+// plane too when x_lo != nullptr) and per-tile sums of squares.
+hipError_t launch_prep(const Plan& p, PrepMode mode, const uint16_t* src, float* mom, float mu,
+                       uint16_t* x_hi, uint16_t* x_lo, float* partials, hipStream_t s);
 // scales[2k] = 1/(sqrt(sum_k) + eps), scales[2k+1] = scales[2k]^2.
 hipError_t launch_norm_finalize(const Plan& p, const float* partials, float* scales, float eps,
                                 hipStream_t s);
@@ -96,10 +95,10 @@ hipError_t launch_gram(const Plan& p, const uint16_t* x, uint16_t* a, const floa
 hipError_t launch_poly(const Plan& p, const uint16_t* a, uint16_t* b_hi, uint16_t* b_lo,
                        float ca, float cb, float cc, hipStream_t s);
 // X' = scale1 * B' X   (scale1 may be null; a X is carried by the diagonal of B').
-// ACCURATE when x_lo/b_lo are given: X' = scale1 * (Bh Xh + Bh Xl + Bl Xh), stored as hi + lo.
-hipError_t launch_bx(const Plan& p, const uint16_t* b_hi, const uint16_t* b_lo,
-                     const uint16_t* x_hi, const uint16_t* x_lo, uint16_t* out_hi,
-                     uint16_t* out_lo, const float* scale1, hipStream_t s);
+// ACCURATE when b_lo is given: X' = scale1 * (Bh Xh + Bh Xl + Bl Xh), stored as hi + lo.
+hipError_t launch_bx(const Plan& p, const uint16_t* b_hi, const uint16_t* b_lo, const uint16_t* x_hi,
+                     const uint16_t* x_lo, uint16_t* out_hi, uint16_t* out_lo, const float* scale1,
+                     hipStream_t s);
 
 // Small blocks (small_ns.hip): the whole step for one block per workgroup in fp32.
 struct SmallStep {

@@ -3,312 +3,309 @@
 // X = a X + B X) with the coefficients of the "Muon Custom Sizing"
 // walkthrough, section 2.3, which also names a symmetric kernel for X X^T.
 //
-//   k_sym<GRAM>  A  = scale * X X^T             K = np, both operands rows of X
-//   k_sym<POLY>  B' = a I + b A + c A A^T       K = mp, A symmetric so A A = A A^T
-//   k_bx         X' = scale * B' X              K = mp, X read k-major
+// Products C[i][j] = sum_k P[i][k] Q[k][j] over an oriented padded iterate
+// X [mp][np]:
+//   Gram   A  = scale X X^T            P = X rows, Q = X^T: both read as
+//                                      k-contiguous rows of X            (K = np)
+//   poly   B' = a I + b A + c A A      P = Q = A                         (K = mp)
+//   bx     X' = scale B' X             P = B', Q = X                     (K = mp)
+// The a X term of the update is carried by the diagonal of B'
+// (a X + B X = (a I + B) X), so the B X epilogue reads nothing.
 //
-// The a X term of the update is carried by the diagonal of B' (exact in the
-// algebra: a X + B X = (a I + B) X), so k_bx has no read-modify epilogue and
-// the bf16 rounding of B' happens after the cancellation between a and the
-// diagonal of b A + c A^2 rather than before it.
+// A and B' are symmetric (their kernel computes only the upper-triangle tiles
+// ti <= tj and writes each off-diagonal tile a second time, transposed, so
+// the stored matrices are exactly symmetric).  Hence their row panels equal
+// their column panels, and poly and bx read every operand as a k-major panel
+// (k rows of 2 BT contiguous bytes: whole cache lines), like X in B X.
 //
-// A and B' are symmetric, so k_sym computes only the tiles (ti <= tj) of the
-// upper triangle and also stores each off-diagonal tile transposed.
+// Tiling: a 256-thread workgroup (2 x 2 waves) computes a BT x BT output tile
+// (BT = 256 or 128), each wave (BT/2)^2 as a grid of v_mfma_f32_32x32x16_bf16
+// accumulators.  K steps by 32 through a ring of four LDS stages, operand
+// slices fetched straight into LDS with buffer_load_dwordx4 ... lds (no
+// staging registers).  Once per step, just before its last 16-deep
+// sub-slice, every wave waits for its own loads of the next slice and then at
+// a barrier; the loads of slice k + 3 go into the stage just freed, spread
+// over that sub-slice one instruction per two MFMAs.  Fragments of sub-slice
+// u + 1 are read from LDS while the MFMAs of u run.  A k-contiguous operand
+// tile sits in LDS as rows x 32 bf16, 16-byte chunk index XOR-swizzled by the
+// row; a k-major tile as it lies in memory (BK k-rows x BT columns, 16-byte
+// chunks XOR-swizzled by 4 (row % 4)), its fragments read with
+// ds_read_b64_tr_b16, two per fragment, which transposes on the way.  Both
+// layouts are conflict-free for their reads; the swizzle is applied on the
+// global side of the DMA.
 //
-// Tiling: a 256-thread workgroup (2 x 2 waves) computes a BM x BN output tile
-// (256 x 256 or 128 x 128); each wave owns (BM/2) x (BN/2) as a grid of
-// v_mfma_f32_32x32x16_bf16 accumulators.  K steps by 64 through two LDS
-// stages: while the waves multiply stage s, the next K slice is fetched into
-// stage s^1 (rows of a k-contiguous operand by buffer_load ... lds DMA, the
-// k-major X of k_bx through registers), with one barrier per step.  Operand
-// tiles sit in LDS as rows x 64 bf16 (8 chunks of 16 bytes per row) with the
-// chunk index XOR-swizzled by the row, so 16-byte fragment reads are
-// conflict-free.  X in k_bx is k-major in memory: each thread loads 4 k-rows x
-// 8 columns and writes them transposed (8-byte LDS stores).
+// Epilogue: 32 rows of a wave's accumulators at a time are staged in LDS as
+// fp32 and read back row by row, so global stores write 256- (or 128-) byte
+// row segments.  The mirror tile of a symmetric output is staged as bf16 and
+// read back with ds_read_b64_tr_b16, two reads handing each lane 8
+// consecutive rows of one column for a 16-byte store.
 //
 // MFMA 32x32x16 lane layout: lane l supplies row (l % 32) of its operand and
 // 8 consecutive k values starting at 8 (l / 32); result element (r, c) of a
 // 32 x 32 block sits in lane 32 ((r / 4) % 2) + c, register 4 (r / 8) + r % 4.
-// The kernels pass the column operand first, so each lane ends up holding 4
-// consecutive output columns of one output row (8-byte stores).
+// The kernels pass the column operand first, so each lane holds 4 consecutive
+// output columns of one output row.
+//
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
+// (i % 4) of the 8 bytes addressed by lanes 4 e + i / 4, for e = 0..3.  With
+// lane L addressing row rb + L / 4, columns cb + 4 (L % 4) .. + 3 of a
+// row-major tile, lane i gets rows rb .. rb + 3 of column cb + i.
+#include <type_traits>
+
 #include "muon_internal.hpp"
 
 namespace muon {
 namespace {
 
-constexpr int BK = 64;
+constexpr int BK = 32;        // K slice per pipeline stage
 constexpr int NTHR = 256;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+// LDS of gfx950 has 64 banks of 4 bytes: a 16-byte read by 16 lanes, or an
+// 8-byte read by 32 lanes, is conflict-free when the lanes cover 256
+// distinct-bank bytes.
+//
+// A k-contiguous operand tile in LDS: rows of BK bf16 = 64 bytes = 4 chunks of
+// 16 bytes; chunk c of row r is stored at chunk c ^ ((r / 4) % 4).  Any 16
+// consecutive rows then cover all 64 banks for 16-byte fragment reads.
+__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 __device__ __forceinline__ int lds_off(int row, int chunk) {
-    return (row << 7) + ((chunk ^ swz(row)) << 4);
+    return (row << 6) + ((chunk ^ swz(row)) << 4);
 }
 
-template <int BM, int BN>
+template <int BT>
 struct TileCfg {
-    static constexpr int TM = BM / 2, TN = BN / 2;   // wave tile
-    static constexpr int FM = TM / 32, FN = TN / 32; // 32x32 blocks per wave
-    static constexpr int A_BYTES = BM * BK * 2;
-    static constexpr int B_BYTES = BN * BK * 2;
-    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int TW = BT / 2;               // wave tile edge
+    static constexpr int F = TW / 32;               // 32x32 blocks per wave side
+    static constexpr int OP_BYTES = BT * BK * 2;    // one operand tile
 };
 
-// Buffer resource over one matrix (raw addressing, byte offsets): loads are
-// range-checked by the hardware against `bytes`, and each lane keeps a 32-bit
-// offset instead of a 64-bit pointer.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
-}
-
-__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-}
-
-// R rows x 64 k of a k-contiguous matrix: R * 8 16-byte vectors, R / 32 per
-// thread (vector v = thread + 256 q covers row v / 8, k chunk v % 8).
-template <int R>
-struct RowTile {
-    u32x4 v[R / 32];
-    uint32_t voff[R / 32];
-
-    __device__ __forceinline__ void init(int64_t ld, int row0) {
-#pragma unroll
-        for (int q = 0; q < R / 32; ++q) {
-            const int v = threadIdx.x + NTHR * q;
-            voff[q] = static_cast<uint32_t>(((int64_t)(row0 + (v >> 3)) * ld + (v & 7) * 8) * 2);
-        }
-    }
-    // k0: first k column of the slice
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int k0) {
-#pragma unroll
-        for (int q = 0; q < R / 32; ++q) v[q] = buf_load16(r, voff[q], static_cast<uint32_t>(k0 * 2));
-    }
-    __device__ __forceinline__ void store(char* lds) const {
-#pragma unroll
-        for (int q = 0; q < R / 32; ++q) {
-            const int vi = threadIdx.x + NTHR * q;
-            *reinterpret_cast<u32x4*>(lds + lds_off(vi >> 3, vi & 7)) = v[q];
-        }
-    }
+// LDS ring depth (stages of one K slice each).  Slice k + NS - 1 is fetched
+// while slice k is multiplied and must land NS - 2 steps later.
+template <int BT, bool SPLIT_IN>
+struct RingCfg {
+    static constexpr int NS = 4;
 };
 
-// The same R x 64 tile fetched straight into LDS (buffer_load_dwordx4 ... lds):
-// an instruction of one wave fills 1 KB of LDS, lane L writing bytes
-// [16 L, 16 L + 16) of it, i.e. 8 rows x 8 chunks.  The swizzle is applied on
-// the global side: the lane whose LDS slot is (row, physical chunk p) fetches
-// logical chunk p ^ swz(row).  No registers stage the data.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor of `bytes` bytes at `base` (stride 0; loads past the
+// end return zero).
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    return i32x4{static_cast<int>(static_cast<uint32_t>(b)), static_cast<int>((b >> 32) & 0xffffu),
+                 static_cast<int>(bytes), 0x00020000};
+}
+
+// One buffer_load_dwordx4 ... lds: lane L's 16 bytes at rsrc + voff + soff go to
+// LDS byte address lds + 16 L.  It is issued as inline assembly so that the
+// compiler does not track it: the compiler would otherwise make every
+// transposing LDS read (which carries no alias information) wait for all of
+// this wave's outstanding DMA, which collapses the pipeline.  The kernel
+// orders DMA and LDS reads itself with explicit vmcnt waits and barriers.
+__device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t voff, uint32_t soff, char* lds) {
+    const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)lds));
+    asm volatile("buffer_load_dwordx4 %1, %2, %3 offen lds" ::"{m0}"(m0), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+}
+
+// An R x BK slice of a k-contiguous matrix fetched straight into LDS: one
+// instruction of one wave fills 1 KB (lane L writes bytes [16 L, 16 L + 16)),
+// i.e. 16 rows x 4 chunks.  The lane whose LDS slot is (row, physical chunk p)
+// fetches logical chunk p ^ swz(row).
 template <int R>
 struct RowDma {
-    static constexpr int PER_WAVE = R / 32;   // 1 KB windows per wave
-    uint32_t voff[PER_WAVE];
+    static constexpr int PW = R / 64;   // 1 KB windows per wave
+    const void* base;                   // the matrix; its buffer descriptor is built in load()
+    uint32_t bytes;
+    uint32_t voff[PW];
 
-    __device__ __forceinline__ void init(int64_t ld, int row0) {
+    __device__ __forceinline__ void init(const void* base_, uint32_t bytes_, int64_t ld, int row0) {
+        base = base_;
+        bytes = bytes_;
         const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
 #pragma unroll
-        for (int q = 0; q < PER_WAVE; ++q) {
-            const int row = 8 * (w * PER_WAVE + q) + (l >> 3);
-            const int chunk = (l & 7) ^ swz(row);
+        for (int q = 0; q < PW; ++q) {
+            const int row = 16 * (w * PW + q) + (l >> 2);
+            const int chunk = (l & 3) ^ swz(row);
             voff[q] = static_cast<uint32_t>(((int64_t)(row0 + row) * ld + chunk * 8) * 2);
         }
     }
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, char* lds, int k0) const {
+    // Window q of this wave (1 KB) of the slice at K offset k0.
+    __device__ __forceinline__ void load_q(char* lds, int k0, int q) const {
         const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-#pragma unroll
-        for (int q = 0; q < PER_WAVE; ++q)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                r, (__attribute__((address_space(3))) void*)(lds + (w * PER_WAVE + q) * 1024), 16, voff[q],
-                static_cast<uint32_t>(k0 * 2), 0, 0);
+        dma16(make_rsrc(base, bytes), voff[q], static_cast<uint32_t>(k0 * 2), lds + (w * PW + q) * 1024);
     }
 };
 
-// 64 k x C columns of a column-contiguous matrix: 2C sub-blocks of 4 k x 8
-// columns, C / 128 per thread.  Sub-block sb covers columns 8 (sb % (C/8)) ..
-// and k rows 4 (sb / (C/8)) ..; it is written transposed (LDS row = column).
+// A BK x C slice (BK k-rows, C columns) of a column-contiguous matrix in its
+// own layout: rows of 2C bytes, 16-byte chunk c of row r stored at chunk
+// c ^ (4 (r % 4)), so the 4 rows x 64 bytes that 32 lanes of a transposing
+// read touch land in 4 distinct 64-byte bank groups.
+// One DMA instruction of one wave fills 1 KB = 512 / C rows.
 template <int C>
-struct ColTile {
-    u32x4 v[C / 32];
-    uint32_t voff[C / 32];
-    uint32_t ldb;   // row pitch in bytes
+__device__ __forceinline__ int col_off(int row, int col) {
+    return row * (2 * C) + (((col >> 3) ^ ((row & 3) << 2)) << 4) + (((col >> 2) & 1) << 3);
+}
 
-    __device__ __forceinline__ void init(int64_t ld, int col0) {
+template <int C>
+struct ColDma {
+    static constexpr int ROWS_PER_WIN = 512 / C;
+    static constexpr int PW = BK / ROWS_PER_WIN / 4;   // 1 KB windows per wave
+    const void* base;
+    uint32_t bytes;
+    uint32_t ldb;                                      // row pitch in bytes
+    uint32_t voff[PW];
+
+    __device__ __forceinline__ void init(const void* base_, uint32_t bytes_, int64_t ld, int col0) {
+        base = base_;
+        bytes = bytes_;
         ldb = static_cast<uint32_t>(ld * 2);
+        const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
 #pragma unroll
-        for (int s = 0; s < C / 128; ++s) {
-            const int sb = threadIdx.x + NTHR * s;
-            const int jg = sb % (C / 8), kg = sb / (C / 8);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                voff[4 * s + r] = static_cast<uint32_t>(((int64_t)(kg * 4 + r) * ld + col0 + jg * 8) * 2);
+        for (int q = 0; q < PW; ++q) {
+            const int row = ROWS_PER_WIN * (w * PW + q) + l / (C / 8);
+            const int chunk = (l % (C / 8)) ^ ((row & 3) << 2);
+            voff[q] = static_cast<uint32_t>(((int64_t)row * ld + col0 + chunk * 8) * 2);
         }
     }
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int k0) {
-#pragma unroll
-        for (int q = 0; q < C / 32; ++q) v[q] = buf_load16(r, voff[q], static_cast<uint32_t>(k0) * ldb);
+    __device__ __forceinline__ void load_q(char* lds, int k0, int q) const {
+        const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        dma16(make_rsrc(base, bytes), voff[q], static_cast<uint32_t>(k0) * ldb, lds + (w * PW + q) * 1024);
     }
-    __device__ __forceinline__ void store(char* lds) const {
-#pragma unroll
-        for (int s = 0; s < C / 128; ++s) {
-            const int sb = threadIdx.x + NTHR * s;
-            const int jg = sb % (C / 8), kg = sb / (C / 8);
-#pragma unroll
-            for (int cc = 0; cc < 8; ++cc) {
-                const int p = cc >> 1;
-                const uint32_t a0 = v[4 * s][p], a1 = v[4 * s + 1][p];
-                const uint32_t a2 = v[4 * s + 2][p], a3 = v[4 * s + 3][p];
-                u32x2 w;
-                if (cc & 1) {
-                    w[0] = (a0 >> 16) | (a1 & 0xffff0000u);
-                    w[1] = (a2 >> 16) | (a3 & 0xffff0000u);
-                } else {
-                    w[0] = (a0 & 0xffffu) | (a1 << 16);
-                    w[1] = (a2 & 0xffffu) | (a3 << 16);
-                }
-                *reinterpret_cast<u32x2*>(lds + lds_off(jg * 8 + cc, kg >> 1) + ((kg & 1) << 3)) = w;
-            }
+};
+
+// The operands of one kernel: NA tiles for the output rows and NB tiles for
+// the output columns (1 + 1, or 2 + 2 hi/lo planes for the split B X).  Each
+// is either k-contiguous rows (RowDma) or k-major columns (ColDma).
+template <int BT, int NA, int NB, typename ALoader, typename BLoader>
+struct Operands {
+    ALoader a[NA];
+    BLoader b[NB];
+    static constexpr int STAGE = (NA + NB) * TileCfg<BT>::OP_BYTES;
+    static constexpr int WINDOWS = NA * ALoader::PW + NB * BLoader::PW;   // DMA instructions per wave
+    __device__ __forceinline__ static char* a_tile(char* stage, int i) { return stage + i * TileCfg<BT>::OP_BYTES; }
+    __device__ __forceinline__ static char* b_tile(char* stage, int j) {
+        return stage + (NA + j) * TileCfg<BT>::OP_BYTES;
+    }
+    // DMA instruction w (0 <= w < WINDOWS) of this wave for the slice at k0.
+    __device__ __forceinline__ void load_window(char* stage, int k0, int w) const {
+        constexpr int PA = ALoader::PW, PB = BLoader::PW;
+        if (w < NA * PA) {
+            a[w / PA].load_q(a_tile(stage, w / PA), k0, w % PA);
+        } else {
+            const int v = w - NA * PA;
+            b[v / PB].load_q(b_tile(stage, v / PB), k0, v % PB);
         }
     }
-};
-
-// Work attached to a K step (see kstep): global prefetch of the next stage and
-// the transposing LDS write of k_bx.  Plain functors rather than lambdas.
-struct NoWork {
-    __device__ __forceinline__ void operator()() const {}
-};
-
-template <int R>
-struct PrefetchRows2 {   // two row tiles by DMA (k_sym)
-    const RowDma<R>& ra;
-    const RowDma<R>& rb;
-    __amdgpu_buffer_rsrc_t rs;
-    char* lds_a;
-    char* lds_b;
-    int k0;
-    bool on;
-    __device__ __forceinline__ void operator()() const {
-        if (on) {
-            ra.load(rs, lds_a, k0);
-            rb.load(rs, lds_b, k0);
-        }
+    __device__ __forceinline__ void load(char* stage, int k0) const {
+#pragma unroll
+        for (int w = 0; w < WINDOWS; ++w) load_window(stage, k0, w);
     }
 };
 
-template <int R, int C>
-struct PrefetchRowCol {   // B' rows by DMA, X columns into registers (k_bx)
-    const RowDma<R>& rb;
-    ColTile<C>& cx;
-    __amdgpu_buffer_rsrc_t rbs, rxs;
-    char* lds_b;
-    int k0;
-    bool on;
-    __device__ __forceinline__ void operator()() const {
-        if (on) {
-            rb.load(rbs, lds_b, k0);
-            cx.load(rxs, k0);
-        }
-    }
-};
-
-template <int C>
-struct StoreCols {
-    const ColTile<C>& cx;
-    char* lds;
-    bool on;
-    __device__ __forceinline__ void operator()() const {
-        if (on) cx.store(lds);
-    }
-};
-
-template <typename F, typename G>
-struct Both {
-    const F& f;
-    const G& g;
-    __device__ __forceinline__ void operator()() const {
-        f();
-        g();
-    }
-};
-
-// Workgroups of one launch are handed to the 8 XCDs round-robin (w -> XCD
-// w % 8).  Renumbering them so that each XCD gets one contiguous range of
-// logical tiles keeps the operand panels of a matrix in a single XCD's L2.
-__device__ __forceinline__ uint32_t xcd_logical(uint32_t w, uint32_t total) {
-    const uint32_t q = total >> 3, r = total & 7, x = w & 7;
-    return x * q + (x < r ? x : r) + (w >> 3);
-}
-
-template <int FM, int FN>
-__device__ __forceinline__ void load_frags(const char* As, const char* Bs, int wr0, int wc0, int ks,
-                                           bf16x8 (&a)[FM], bf16x8 (&b)[FN]) {
+// One fragment (a 32-wide block at base, one 16-deep sub-slice ks) of an
+// operand.  From k-contiguous rows: one 16-byte read.  From a k-major tile:
+// two transposing reads (k rows ks*16 + 8 (l / 32) + 0..3 and + 4..7 of
+// index l % 32 of the block).
+template <bool KMAJOR, int BT>
+__device__ __forceinline__ bf16x8 load_frag(const char* S, int base, int ks) {
     const int lane = threadIdx.x & 63;
-    const int lr = lane & 31, ch = ks * 2 + (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(As + lds_off(wr0 + i * 32 + lr, ch));
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-        b[j] = *reinterpret_cast<const bf16x8*>(Bs + lds_off(wc0 + j * 32 + lr, ch));
+    if constexpr (!KMAJOR) {
+        return *reinterpret_cast<const bf16x8*>(S + lds_off(base + (lane & 31), ks * 2 + (lane >> 5)));
+    } else {
+        const int L = lane & 15, grp = (lane >> 4) & 1;
+        const int row = 16 * ks + 8 * (lane >> 5) + (L >> 2);
+        const int col = base + grp * 16 + 4 * (L & 3);
+        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(S + col_off<BT>(row, col)));
+        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(S + col_off<BT>(row + 4, col)));
+        const i16x8 v = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        return __builtin_bit_cast(bf16x8, v);
+    }
 }
 
-template <int FM, int FN>
-__device__ __forceinline__ void mfma_block(const bf16x8 (&a)[FM], const bf16x8 (&b)[FN],
-                                           f32x16 (&acc)[FM][FN]) {
+// The fragments of one sub-slice, read in the order the MFMAs consume them
+// (a0 with b0 .. b(F-1), then a1, a2, ...), so the reads issued last have the
+// most MFMAs of the next sub-slice to complete behind.  With DMA, the loads of
+// a stage (into `next`, K offset k1) are issued in between, a share after
+// each fragment: the reads are placed one per MFMA, so the DMA instructions
+// are spread over the sub-slice instead of stalling the wave in a burst when
+// the address queue fills.
+template <int F, bool KMAJOR_A, bool KMAJOR_B, int BT, bool DMA = false, typename Ops = void>
+__device__ __forceinline__ void load_frags(const char* As, const char* Bs, int wr0, int wc0, int ks,
+                                           bf16x8 (&a)[F], bf16x8 (&b)[F], const Ops* ops = nullptr,
+                                           char* next = nullptr, int k1 = 0) {
+    constexpr int NF = 2 * F;
+    auto dma_after = [&](int fi) {
+        if constexpr (DMA) {
+            constexpr int W = Ops::WINDOWS;
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+            for (int w = 0; w < W; ++w)
+                if (w * NF >= fi * W && w * NF < (fi + 1) * W) ops->load_window(next, k1, w);
+        }
+    };
+    a[0] = load_frag<KMAJOR_A, BT>(As, wr0, ks);
+    dma_after(0);
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+    for (int j = 0; j < F; ++j) {
+        b[j] = load_frag<KMAJOR_B, BT>(Bs, wc0 + j * 32, ks);
+        dma_after(1 + j);
+    }
+#pragma unroll
+    for (int i = 1; i < F; ++i) {
+        a[i] = load_frag<KMAJOR_A, BT>(As, wr0 + i * 32, ks);
+        dma_after(F + i);
+    }
+}
+
+template <int F>
+__device__ __forceinline__ void mfma_block(const bf16x8 (&a)[F], const bf16x8 (&b)[F], f32x16 (&acc)[F][F]) {
+#pragma unroll
+    for (int i = 0; i < F; ++i)
+#pragma unroll
+        for (int j = 0; j < F; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
 }
 
-// Scheduling pattern for one 16-deep sub-slice region: the FM + FN fragment
-// reads of the next sub-slice spread evenly between the FM * FN MFMAs.
-template <int FM, int FN>
-__device__ __forceinline__ void interleave_reads() {
+// Interleaves the F*F MFMAs of one sub-slice with the NREAD LDS reads issued
+// beside them (the fragments of the next sub-slice).
+template <int F, int NREAD>
+__device__ __forceinline__ void interleave() {
 #pragma unroll
-    for (int t = 0; t < FM + FN; ++t) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                    // LDS read
-        __builtin_amdgcn_sched_group_barrier(0x008, FM * FN / (FM + FN), 0);  // MFMA
+    for (int t = 0; t < NREAD; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                   // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, (F * F) / NREAD, 0);     // MFMA
     }
 }
 
-// One 64-deep K step of a wave: acc += A(rows) B(cols)^T over stage `st`.
-// `prefetch` issues the global loads of the next stage right after the first
-// fragment reads; `late` runs in the last sub-slice region (k_bx writes the
-// transposed X there).  Each 16-deep sub-slice is its own scheduling region
-// (sched_barrier), so the LDS reads placed between its MFMAs are the next
-// sub-slice's fragments and their latency hides behind the current MFMAs.
-template <int FM, int FN, typename Prefetch, typename Late>
-__device__ __forceinline__ void kstep(const char* As, const char* Bs, int wr0, int wc0,
-                                      f32x16 (&acc)[FM][FN], const Prefetch& prefetch, const Late& late) {
-    constexpr int KS = BK / 16;
-    bf16x8 a[2][FM], b[2][FN];
-    load_frags<FM, FN>(As, Bs, wr0, wc0, 0, a[0], b[0]);
-    prefetch();
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        const int cur = ks & 1;
-        if (ks + 1 < KS) load_frags<FM, FN>(As, Bs, wr0, wc0, ks + 1, a[cur ^ 1], b[cur ^ 1]);
-        mfma_block<FM, FN>(a[cur], b[cur], acc);
-        if (ks + 1 < KS) {
-            interleave_reads<FM, FN>();
-        } else {
-            late();
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    }
+// Waits until at most N of this wave's DMA instructions are outstanding, then
+// for every wave of the workgroup.  A bare s_barrier does not drain the
+// outstanding loads the way __syncthreads does; the empty asm statements keep
+// the compiler from moving LDS accesses across it.
+template <int N>
+__device__ __forceinline__ void wait_dma_and_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt field is 6 bits");
+    constexpr int imm = (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(imm);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
-template <int FM, int FN>
-__device__ __forceinline__ void zero_acc(f32x16 (&acc)[FM][FN]) {
+template <int F>
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[F][F]) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < F; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+        for (int j = 0; j < F; ++j)
 #pragma unroll
             for (int s = 0; s < 16; ++s) acc[i][j][s] = 0.f;
 }
@@ -320,210 +317,255 @@ __device__ __forceinline__ u32x2 pack4(const uint16_t (&h)[4]) {
     return w;
 }
 
-enum SymKind { kGram = 0, kPoly = 1, kPolySplit = 2 };
+// Workgroups of one launch are handed to the 8 XCDs round-robin (w -> XCD
+// w % 8).  Renumbering them so that each XCD gets one contiguous range of
+// logical tiles keeps the operand panels of a matrix in a single XCD's L2.
+__device__ __forceinline__ uint32_t xcd_logical(uint32_t w, uint32_t total) {
+    const uint32_t q = total >> 3, r = total & 7, x = w & 7;
+    return x * q + (x < r ? x : r) + (w >> 3);
+}
 
-struct SymArgs {
-    const uint16_t* src;     // X (Gram) or A (poly), this launch's first block
-    uint16_t* out;           // A (Gram) or B' hi (poly)
-    uint16_t* out_lo;        // B' lo (poly split)
-    const float* scale;      // [nb][2] (Gram, iteration 1) or null
-    int64_t src_stride, out_stride;
-    int64_t ld;              // row pitch of src = K
-    int64_t ldo;             // row pitch of out = mp
-    int T;                   // tiles per side
-    uint32_t tiles;          // tiles per block = T (T + 1) / 2
-    uint32_t total;          // tiles * blocks in this launch
-    uint32_t src_bytes;      // bytes of one source matrix
+// Epilogue staging, per wave and per 32-row chunk of its TW x TW tile.
+// fp32 chunk: rows of TW floats, 16-byte chunk index XOR (row % 16), so the
+// MFMA-layout writes (16 rows, one chunk) and the row-contiguous reads (one
+// row, 16 chunks) are both conflict-free.
+template <int TW>
+__device__ __forceinline__ int f32_off(int row, int col) {
+    return row * (TW * 4) + (((col >> 2) ^ (row & 15)) << 4);
+}
+// bf16 chunk for the mirror store: rows of TW bf16, 16-byte chunk index XOR
+// an even row function chosen so that the transposing reads (rows 0-3 and
+// 8-11 of a 16-row group, two adjacent chunks) hit distinct banks.
+template <int TW>
+__device__ __forceinline__ int mir_off(int row, int col) {
+    const int f = TW == 128 ? 2 * ((row & 3) | (((row >> 3) & 1) << 2))
+                            : 2 * (((row >> 1) & 1) | (((row >> 3) & 1) << 1));
+    return row * (TW * 2) + (((col >> 3) ^ f) << 4) + (((col >> 2) & 1) << 3);
+}
+
+enum Kind { kGram = 0, kPoly = 1, kPolySplit = 2, kBx = 3, kBxSplit = 4 };
+
+struct GemmArgs {
+    const uint16_t* p[2];     // row operands (hi, lo): X, A or B'
+    const uint16_t* q[2];     // column operands (hi, lo): X, A (k-contiguous) or X (k-major)
+    uint16_t* out[2];         // row-major output (hi, lo)
+    const float* scale;       // [nb][2] or null
+    int64_t p_stride, q_stride, out_stride;
+    int64_t K;                // reduction length (row pitch of k-contiguous operands)
+    int64_t ldq;              // row pitch of a k-major column operand
+    int64_t ldo;              // output row pitch
+    uint32_t p_bytes, q_bytes;
+    int T;                    // symmetric: tiles per side
+    uint32_t tiles_i;         // full: row tiles per block (ti varies fastest)
+    uint32_t tiles;           // tiles per block
+    uint32_t total;           // tiles * blocks
     float ca, cb, cc;
 };
 
 template <int KIND, int BT>
-__global__ __launch_bounds__(NTHR) void k_sym(SymArgs a) {
-    using Cfg = TileCfg<BT, BT>;
-    constexpr int FM = Cfg::FM, FN = Cfg::FN;
-    __shared__ __attribute__((aligned(16))) char lds[2 * Cfg::STAGE];
+__global__ __launch_bounds__(NTHR) void k_gemm(GemmArgs a) {
+    using Cfg = TileCfg<BT>;
+    constexpr int F = Cfg::F, TW = Cfg::TW;
+    constexpr bool SYM = KIND == kGram || KIND == kPoly || KIND == kPolySplit;
+    constexpr bool POLY = KIND == kPoly || KIND == kPolySplit;
+    constexpr bool SPLIT_IN = KIND == kBxSplit;                       // hi/lo planes of both operands
+    constexpr bool SPLIT_OUT = KIND == kPolySplit || KIND == kBxSplit;
+    // Operand layouts: X X^T reads rows of X (k-contiguous).  The other
+    // products read k-major panels only: A, B' are symmetric, so their row
+    // panels are the column panels of the same matrix, and X of B X is
+    // k-major as stored.  A k-major slice row is a whole 2 BT-byte run of
+    // full cache lines, where a k-contiguous slice row is only 2 BK bytes.
+    constexpr bool KMAJOR_A = KIND != kGram;
+    constexpr bool KMAJOR_B = KIND != kGram;
+    constexpr int NA = SPLIT_IN ? 2 : 1, NB = SPLIT_IN ? 2 : 1;
+    using ALoader = typename std::conditional<KMAJOR_A, ColDma<BT>, RowDma<BT>>::type;
+    using BLoader = typename std::conditional<KMAJOR_B, ColDma<BT>, RowDma<BT>>::type;
+    using Ops = Operands<BT, NA, NB, ALoader, BLoader>;
+    constexpr int STAGE = Ops::STAGE;
+    constexpr int LDS_BYTES = RingCfg<BT, SPLIT_IN>::NS * STAGE;
+    __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
 
     const uint32_t L = xcd_logical(blockIdx.x, a.total);
     const int64_t blk = L / a.tiles;
-    int id = static_cast<int>(L % a.tiles), ti = 0, len = a.T;
-    while (id >= len) { id -= len; ++ti; --len; }
-    const int tj = ti + id;
-    const uint16_t* src = a.src + blk * a.src_stride;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, a.src_bytes);
+    int ti, tj;
+    {
+        int id = static_cast<int>(L % a.tiles);
+        if constexpr (SYM) {
+            int t = 0, len = a.T;
+            while (id >= len) { id -= len; ++t; --len; }
+            ti = t;
+            tj = t + id;
+        } else {
+            ti = id % static_cast<int>(a.tiles_i);
+            tj = id / static_cast<int>(a.tiles_i);
+        }
+    }
     const int row0 = ti * BT, col0 = tj * BT;
     const int wave = threadIdx.x >> 6;
-    const int wr0 = (wave >> 1) * Cfg::TM, wc0 = (wave & 1) * Cfg::TN;
+    const int wr0 = (wave >> 1) * TW, wc0 = (wave & 1) * TW;
 
-    f32x16 acc[FM][FN];
-    zero_acc(acc);
+    Ops ops;
+#pragma unroll
+    for (int i = 0; i < NA; ++i) ops.a[i].init(a.p[i] + blk * a.p_stride, a.p_bytes, a.K, row0);   // K = ld (square when k-major)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) ops.b[j].init(a.q[j] + blk * a.q_stride, a.q_bytes, KMAJOR_B ? a.ldq : a.K, col0);
 
-    RowDma<BT> ra, rb;
-    ra.init(a.ld, row0);
-    rb.init(a.ld, col0);
-    ra.load(rs, lds, 0);
-    rb.load(rs, lds + Cfg::A_BYTES, 0);
-    __syncthreads();
-    const int nk = static_cast<int>(a.ld / BK);
+    f32x16 acc[F][F];
+    zero_acc<F>(acc);
+
+    // Ring of NS stages; slice kt lives in stage kt % NS.  A K step is U
+    // sub-slices (16 deep, and for the split B X three products each); the
+    // fragments of sub-slice u + 1 are read from LDS while the MFMAs of u run,
+    // so the first fragments of slice kt + 1 are read during the last
+    // sub-slice of step kt.  Just before that sub-slice every wave waits for
+    // its own loads of slice kt + 1 and then at a barrier, after which stage
+    // (kt - 1) % NS is free (all its reads were consumed by step kt - 1) and
+    // slice kt + NS - 1 is fetched into it.  Every step issues exactly one
+    // stage of loads (Ops::WINDOWS DMA instructions per wave; in the tail an
+    // in-bounds slice whose copy is never read), so the wait count is fixed.
+    constexpr int NS = RingCfg<BT, SPLIT_IN>::NS;
+    static_assert(NS >= 3, "the ring needs a stage in flight beside the two being read");
+    constexpr int KS = BK / 16;
+    constexpr int P = SPLIT_IN ? 3 : 1;          // products per step: Bh Xh (+ Bh Xl, Bl Xh)
+    constexpr int U = P * KS;
+    static_assert(U % 2 == 0, "fragment ping-pong restarts at 0 each step");
+    constexpr int NREAD = (KMAJOR_A ? 2 * F : F) + (KMAJOR_B ? 2 * F : F);
+    constexpr int W = Ops::WINDOWS;
+    const int nk = static_cast<int>(a.K / BK);
+
+#pragma unroll
+    for (int st = 0; st < NS - 1; ++st) ops.load(lds + st * STAGE, (st < nk ? st : 0) * BK);
+    bf16x8 fa[2][F], fb[2][F];
+    wait_dma_and_barrier<(NS - 2) * W>();
+    load_frags<F, KMAJOR_A, KMAJOR_B, BT>(Ops::a_tile(lds, 0), Ops::b_tile(lds, 0), wr0, wc0, 0, fa[0], fb[0]);
+
     for (int kt = 0; kt < nk; ++kt) {
-        char* cur = lds + (kt & 1) * Cfg::STAGE;
-        char* nxt = lds + ((kt & 1) ^ 1) * Cfg::STAGE;
-        const bool more = kt + 1 < nk;
-        const PrefetchRows2<BT> pf{ra, rb, rs, nxt, nxt + Cfg::A_BYTES, (kt + 1) * BK, more};
-        kstep<FM, FN>(cur, cur + Cfg::A_BYTES, wr0, wc0, acc, pf, NoWork{});
-        __syncthreads();
+        char* cur = lds + (kt % NS) * STAGE;
+        char* nxt = lds + ((kt + 1) % NS) * STAGE;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = u & 1;
+            if (u == U - 1) wait_dma_and_barrier<(NS - 3) * W>();
+            if (u + 1 < U) {
+                const int pn = (u + 1) / KS, ks = (u + 1) % KS;
+                // products: 0 = (A hi, B hi), 1 = (A hi, B lo), 2 = (A lo, B hi)
+                load_frags<F, KMAJOR_A, KMAJOR_B, BT>(Ops::a_tile(cur, pn == 2 ? 1 : 0), Ops::b_tile(cur, pn == 1 ? 1 : 0),
+                                            wr0, wc0, ks, fa[c ^ 1], fb[c ^ 1]);
+            } else {
+                const int kn = kt + NS - 1;
+                load_frags<F, KMAJOR_A, KMAJOR_B, BT, true>(Ops::a_tile(nxt, 0), Ops::b_tile(nxt, 0), wr0, wc0, 0,
+                                                            fa[c ^ 1], fb[c ^ 1], &ops, lds + (kn % NS) * STAGE,
+                                                            (kn < nk ? kn : kt) * BK);
+            }
+            mfma_block<F>(fa[c], fb[c], acc);
+            interleave<F, NREAD>();
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): no DMA may land on the epilogue staging
+    __syncthreads();
 
+    // ---- epilogue, one 32-row chunk of the wave tile at a time: the fp32
+    // accumulators go through LDS so that global stores (and the A reads of
+    // the polynomial) cover whole row segments instead of the MFMA layout's
+    // 4-column pieces of 32 rows.  All staging is wave-private; LDS accesses
+    // of one wave complete in order, so no barrier is needed.
     const int lane = threadIdx.x & 63;
     const int lr = lane & 31, lk = lane >> 5;
-    uint16_t* out = a.out + blk * a.out_stride;
-    uint16_t* out_lo = (KIND == kPolySplit) ? a.out_lo + blk * a.out_stride : nullptr;
-    const uint16_t* amat = src;   // poly: the b A term reads A itself (pitch ld == ldo)
-    const float sc = (KIND == kGram && a.scale) ? a.scale[2 * blk + 1] : 1.0f;
-    const bool mirror = ti != tj;
+    float sc = 1.0f;
+    if constexpr (KIND == kGram) {
+        if (a.scale) sc = a.scale[2 * blk + 1];
+    } else if constexpr (!POLY) {
+        if (a.scale) sc = a.scale[2 * blk];
+    }
+    const uint16_t* amat = POLY ? a.p[0] + blk * a.p_stride : nullptr;
+    uint16_t* out0 = a.out[0] + blk * a.out_stride;
+    uint16_t* out1 = SPLIT_OUT ? a.out[1] + blk * a.out_stride : nullptr;
+    constexpr int ST_F32 = 32 * TW * 4;
+    constexpr int ST_BF = SYM ? 32 * TW * 2 : 0;
+    constexpr int WAVE_LDS = ST_F32 + ST_BF * (SPLIT_OUT ? 2 : 1);
+    static_assert(4 * WAVE_LDS <= LDS_BYTES, "epilogue staging must fit in LDS");
+    char* sf = lds + wave * WAVE_LDS;
+    char* sb = sf + ST_F32;
+    char* sb_lo = sb + ST_BF;
+    const bool mirror = SYM && ti != tj;
+    constexpr int LPR = TW / 4;       // lanes per row on read-back (4 values each)
+    constexpr int RPI = 64 / LPR;     // rows per read-back instruction
+    const int rrow = lane / LPR, rcol = (lane % LPR) * 4;
+    const int64_t gcol = col0 + wc0 + rcol;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        const int r = row0 + wr0 + i * 32 + lr;
+    for (int i = 0; i < F; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            __builtin_amdgcn_sched_barrier(0);   // keep the epilogue one 32 x 32 block at a time
+        for (int j = 0; j < F; ++j)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int c0 = col0 + wc0 + j * 32 + g * 8 + lk * 4;
-                const int64_t o = (int64_t)r * a.ldo + c0;
-                uint16_t hb[4], lb[4];
-                if constexpr (KIND == kGram) {
+                const f32x4 v = {acc[i][j][g * 4 + 0], acc[i][j][g * 4 + 1], acc[i][j][g * 4 + 2],
+                                 acc[i][j][g * 4 + 3]};
+                *reinterpret_cast<f32x4*>(sf + f32_off<TW>(lr, j * 32 + g * 8 + lk * 4)) = v;
+            }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) hb[q] = f32_to_bf16(acc[i][j][g * 4 + q] * sc);
+        for (int t = 0; t < 32 / RPI; ++t) {
+            const int rr = t * RPI + rrow;
+            const int64_t grow = row0 + wr0 + i * 32 + rr;
+            const int64_t o = grow * a.ldo + gcol;
+            const f32x4 x = *reinterpret_cast<const f32x4*>(sf + f32_off<TW>(rr, rcol));
+            float am[4] = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (POLY) {
+                const u32x2 av = *reinterpret_cast<const u32x2*>(amat + o);
+                am[0] = bf16_to_f32(uint16_t(av[0] & 0xffffu));
+                am[1] = bf16_to_f32(uint16_t(av[0] >> 16));
+                am[2] = bf16_to_f32(uint16_t(av[1] & 0xffffu));
+                am[3] = bf16_to_f32(uint16_t(av[1] >> 16));
+            }
+            uint16_t hb[4], lb[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float v;
+                if constexpr (POLY) {
+                    v = fmaf(a.cc, x[e], a.cb * am[e]);
+                    if (grow == gcol + e) v += a.ca;
                 } else {
-                    const u32x2 av = *reinterpret_cast<const u32x2*>(amat + o);
-                    const float am[4] = {bf16_to_f32(uint16_t(av[0] & 0xffffu)), bf16_to_f32(uint16_t(av[0] >> 16)),
-                                         bf16_to_f32(uint16_t(av[1] & 0xffffu)), bf16_to_f32(uint16_t(av[1] >> 16))};
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        float v = fmaf(a.cc, acc[i][j][g * 4 + q], a.cb * am[q]);
-                        if (r == c0 + q) v += a.ca;
-                        hb[q] = f32_to_bf16(v);
-                        if constexpr (KIND == kPolySplit) lb[q] = f32_to_bf16(v - bf16_to_f32(hb[q]));
-                    }
+                    v = x[e] * sc;
                 }
-                *reinterpret_cast<u32x2*>(out + o) = pack4(hb);
-                if constexpr (KIND == kPolySplit) *reinterpret_cast<u32x2*>(out_lo + o) = pack4(lb);
+                hb[e] = f32_to_bf16(v);
+                if constexpr (SPLIT_OUT) lb[e] = f32_to_bf16(v - bf16_to_f32(hb[e]));
+            }
+            *reinterpret_cast<u32x2*>(out0 + o) = pack4(hb);
+            if constexpr (SPLIT_OUT) *reinterpret_cast<u32x2*>(out1 + o) = pack4(lb);
+            if constexpr (SYM) {
                 if (mirror) {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        out[(int64_t)(c0 + q) * a.ldo + r] = hb[q];
-                        if constexpr (KIND == kPolySplit) out_lo[(int64_t)(c0 + q) * a.ldo + r] = lb[q];
-                    }
+                    *reinterpret_cast<u32x2*>(sb + mir_off<TW>(rr, rcol)) = pack4(hb);
+                    if constexpr (SPLIT_OUT) *reinterpret_cast<u32x2*>(sb_lo + mir_off<TW>(rr, rcol)) = pack4(lb);
                 }
             }
         }
-    }
-}
-
-struct BxArgs {
-    const uint16_t* bh;      // B' hi [mp][mp]
-    const uint16_t* bl;      // B' lo (split)
-    const uint16_t* xh;      // X hi [mp][np]
-    const uint16_t* xl;      // X lo (split)
-    uint16_t* oh;            // X' hi
-    uint16_t* ol;            // X' lo (split)
-    const float* scale;      // [nb][2] (iteration 1) or null
-    int64_t bstride, xstride;
-    int64_t mp, np;
-    uint32_t tiles_i;        // row tiles per block (ti varies fastest)
-    uint32_t tiles;          // tiles per block
-    uint32_t total;          // tiles * blocks in this launch
-    uint32_t bbytes, xbytes; // bytes of one B' / X matrix
-};
-
-template <bool SPLIT, int BM, int BN>
-__global__ __launch_bounds__(NTHR) void k_bx(BxArgs a) {
-    using Cfg = TileCfg<BM, BN>;
-    constexpr int FM = Cfg::FM, FN = Cfg::FN;
-    constexpr int NOPS = SPLIT ? 2 : 1;            // hi (and lo) planes of each operand
-    constexpr int STAGE = NOPS * Cfg::STAGE;
-    __shared__ __attribute__((aligned(16))) char lds[2 * STAGE];
-
-    const uint32_t L = xcd_logical(blockIdx.x, a.total);
-    const int64_t blk = L / a.tiles;
-    const uint32_t tile = L % a.tiles;
-    const int ti = static_cast<int>(tile % a.tiles_i), tj = static_cast<int>(tile / a.tiles_i);
-    const __amdgpu_buffer_rsrc_t rbh_s = make_rsrc(a.bh + blk * a.bstride, a.bbytes);
-    const __amdgpu_buffer_rsrc_t rxh_s = make_rsrc(a.xh + blk * a.xstride, a.xbytes);
-    __amdgpu_buffer_rsrc_t rbl_s = rbh_s, rxl_s = rxh_s;
-    if constexpr (SPLIT) {
-        rbl_s = make_rsrc(a.bl + blk * a.bstride, a.bbytes);
-        rxl_s = make_rsrc(a.xl + blk * a.xstride, a.xbytes);
-    }
-    const int row0 = ti * BM, col0 = tj * BN;
-    const int wave = threadIdx.x >> 6;
-    const int wr0 = (wave >> 1) * Cfg::TM, wc0 = (wave & 1) * Cfg::TN;
-
-    f32x16 acc[FM][FN];
-    zero_acc(acc);
-
-    // stage layout: [Bh | Xh | Bl | Xl]; B' arrives by DMA, X through registers
-    RowDma<BM> rbh, rbl;
-    ColTile<BN> cxh, cxl;
-    rbh.init(a.mp, row0);
-    cxh.init(a.np, col0);
-    rbh.load(rbh_s, lds, 0);
-    cxh.load(rxh_s, 0);
-    if constexpr (SPLIT) {
-        rbl.init(a.mp, row0);
-        cxl.init(a.np, col0);
-        rbl.load(rbl_s, lds + Cfg::STAGE, 0);
-        cxl.load(rxl_s, 0);
-    }
-    cxh.store(lds + Cfg::A_BYTES);
-    if constexpr (SPLIT) cxl.store(lds + Cfg::STAGE + Cfg::A_BYTES);
-    __syncthreads();
-    const int nk = static_cast<int>(a.mp / BK);
-    for (int kt = 0; kt < nk; ++kt) {
-        char* cur = lds + (kt & 1) * STAGE;
-        char* nxt = lds + ((kt & 1) ^ 1) * STAGE;
-        const bool more = kt + 1 < nk;
-        const int k1 = (kt + 1) * BK;
-        const PrefetchRowCol<BM, BN> pfh{rbh, cxh, rbh_s, rxh_s, nxt, k1, more};
-        const StoreCols<BN> sth{cxh, nxt + Cfg::A_BYTES, more};
-        if constexpr (!SPLIT) {
-            kstep<FM, FN>(cur, cur + Cfg::A_BYTES, wr0, wc0, acc, pfh, sth);
-        } else {
-            const PrefetchRowCol<BM, BN> pfl{rbl, cxl, rbl_s, rxl_s, nxt + Cfg::STAGE, k1, more};
-            const StoreCols<BN> stl{cxl, nxt + Cfg::STAGE + Cfg::A_BYTES, more};
-            kstep<FM, FN>(cur, cur + Cfg::A_BYTES, wr0, wc0, acc, Both<decltype(pfh), decltype(pfl)>{pfh, pfl},
-                          NoWork{});
-            kstep<FM, FN>(cur, cur + Cfg::STAGE + Cfg::A_BYTES, wr0, wc0, acc, NoWork{}, NoWork{});  // Bh Xl
-            kstep<FM, FN>(cur + Cfg::STAGE, cur + Cfg::A_BYTES, wr0, wc0, acc, NoWork{},             // Bl Xh
-                          Both<decltype(sth), decltype(stl)>{sth, stl});
-        }
-        __syncthreads();
-    }
-
-    const int lane = threadIdx.x & 63;
-    const int lr = lane & 31, lk = lane >> 5;
-    const float sc = a.scale ? a.scale[2 * blk] : 1.0f;
-    uint16_t* oh = a.oh + blk * a.xstride;
-    uint16_t* ol = SPLIT ? a.ol + blk * a.xstride : nullptr;
+        if constexpr (SYM) {
+            // Mirror: output row (col0 + wc0 + c) gets this chunk's 32 values of
+            // column c.  Two transposing reads give lane L of 16-lane group g4
+            // rows 8 g4 .. 8 g4 + 7 of column cb + L, stored as 16 bytes.
+            if (mirror) {
+                const int L = lane & 15, g4 = lane >> 4;
+                const int srow = 8 * g4 + (L >> 2);
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        const int r = row0 + wr0 + i * 32 + lr;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            __builtin_amdgcn_sched_barrier(0);   // keep the epilogue one 32 x 32 block at a time
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int c0 = col0 + wc0 + j * 32 + g * 8 + lk * 4;
-                const int64_t o = (int64_t)r * a.np + c0;
-                uint16_t hb[4], lb[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float v = sc * acc[i][j][g * 4 + q];
-                    hb[q] = f32_to_bf16(v);
-                    if constexpr (SPLIT) lb[q] = f32_to_bf16(v - bf16_to_f32(hb[q]));
+                for (int cb = 0; cb < TW; cb += 16) {
+                    const int scol = cb + 4 * (L & 3);
+                    const int64_t o = (int64_t)(col0 + wc0 + cb + L) * a.ldo + row0 + wr0 + i * 32 + 8 * g4;
+                    const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) i16x4*)(sb + mir_off<TW>(srow, scol)));
+                    const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) i16x4*)(sb + mir_off<TW>(srow + 4, scol)));
+                    *reinterpret_cast<i16x8*>(out0 + o) = i16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+                    if constexpr (SPLIT_OUT) {
+                        const i16x4 w0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) i16x4*)(sb_lo + mir_off<TW>(srow, scol)));
+                        const i16x4 w1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) i16x4*)(sb_lo + mir_off<TW>(srow + 4, scol)));
+                        *reinterpret_cast<i16x8*>(out1 + o) =
+                            i16x8{w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+                    }
                 }
-                *reinterpret_cast<u32x2*>(oh + o) = pack4(hb);
-                if constexpr (SPLIT) *reinterpret_cast<u32x2*>(ol + o) = pack4(lb);
             }
         }
     }
@@ -532,49 +574,44 @@ __global__ __launch_bounds__(NTHR) void k_bx(BxArgs a) {
 // Every kernel instantiation is named explicitly: with implicit instantiation
 // from the launchers below, hipcc emitted host launch stubs for only some of
 // them, leaving undefined symbols in the shared library.
-template __global__ void k_sym<kGram, 128>(SymArgs);
-template __global__ void k_sym<kGram, 256>(SymArgs);
-template __global__ void k_sym<kPoly, 128>(SymArgs);
-template __global__ void k_sym<kPoly, 256>(SymArgs);
-template __global__ void k_sym<kPolySplit, 128>(SymArgs);
-template __global__ void k_bx<false, 128, 128>(BxArgs);
-template __global__ void k_bx<false, 256, 256>(BxArgs);
-template __global__ void k_bx<true, 128, 128>(BxArgs);
+template __global__ void k_gemm<kGram, 128>(GemmArgs);
+template __global__ void k_gemm<kGram, 256>(GemmArgs);
+template __global__ void k_gemm<kPoly, 128>(GemmArgs);
+template __global__ void k_gemm<kPoly, 256>(GemmArgs);
+template __global__ void k_gemm<kPolySplit, 128>(GemmArgs);
+template __global__ void k_gemm<kBx, 128>(GemmArgs);
+template __global__ void k_gemm<kBx, 256>(GemmArgs);
+template __global__ void k_gemm<kBxSplit, 128>(GemmArgs);
 
 constexpr int64_t kCUs = 256;
 
-// 256-wide symmetric tiles when the side divides and they give at least one
-// full wave of workgroups; 128 otherwise.
+// 256-wide tiles when the side divides and they give at least one full wave
+// of workgroups; 128 otherwise.
 bool use_big_sym(const Plan& p) {
     if (p.mp % 256 != 0) return false;
     const int64_t T = p.mp / 256;
     return p.nb * T * (T + 1) / 2 >= kCUs;
 }
 
-bool use_big_bx(const Plan& p) {
+bool use_big_full(const Plan& p) {
     if (p.mp % 256 != 0 || p.np % 256 != 0) return false;
     return p.nb * (p.mp / 256) * (p.np / 256) >= kCUs;
 }
 
 template <int KIND, int BT>
-hipError_t run_sym(const Plan& p, SymArgs a, hipStream_t s) {
-    a.T = static_cast<int>(p.mp / BT);
-    a.tiles = static_cast<uint32_t>(a.T * (a.T + 1) / 2);
+hipError_t run(const Plan& p, GemmArgs a, hipStream_t s) {
+    constexpr bool SYM = KIND == kGram || KIND == kPoly || KIND == kPolySplit;
+    if constexpr (SYM) {
+        a.T = static_cast<int>(p.mp / BT);
+        a.tiles = static_cast<uint32_t>(a.T * (a.T + 1) / 2);
+    } else {
+        a.tiles_i = static_cast<uint32_t>(p.mp / BT);
+        a.tiles = a.tiles_i * static_cast<uint32_t>(p.np / BT);
+    }
     const int64_t total = int64_t(a.tiles) * p.nb;
     if (total > 0x7fffffffLL) return hipErrorInvalidValue;
     a.total = static_cast<uint32_t>(total);
-    k_sym<KIND, BT><<<dim3(a.total), dim3(NTHR), 0, s>>>(a);
-    return hipGetLastError();
-}
-
-template <bool SPLIT, int BM, int BN>
-hipError_t run_bx(const Plan& p, BxArgs a, hipStream_t s) {
-    a.tiles_i = static_cast<uint32_t>(p.mp / BM);
-    a.tiles = a.tiles_i * static_cast<uint32_t>(p.np / BN);
-    const int64_t total = int64_t(a.tiles) * p.nb;
-    if (total > 0x7fffffffLL) return hipErrorInvalidValue;
-    a.total = static_cast<uint32_t>(total);
-    k_bx<SPLIT, BM, BN><<<dim3(a.total), dim3(NTHR), 0, s>>>(a);
+    k_gemm<KIND, BT><<<dim3(a.total), dim3(NTHR), 0, s>>>(a);
     return hipGetLastError();
 }
 
@@ -582,55 +619,60 @@ hipError_t run_bx(const Plan& p, BxArgs a, hipStream_t s) {
 
 hipError_t launch_gram(const Plan& p, const uint16_t* x, uint16_t* a_out, const float* scale2,
                        hipStream_t s) {
-    SymArgs a{};
-    a.src = x;
-    a.out = a_out;
+    GemmArgs a{};
+    a.p[0] = x;
+    a.q[0] = x;
+    a.out[0] = a_out;
     a.scale = scale2;
-    a.src_stride = p.mp * p.np;
+    a.p_stride = a.q_stride = p.mp * p.np;
     a.out_stride = p.mp * p.mp;
-    a.ld = p.np;
+    a.K = p.np;
     a.ldo = p.mp;
-    a.src_bytes = static_cast<uint32_t>(p.mp * p.np * 2);
-    return use_big_sym(p) ? run_sym<kGram, 256>(p, a, s) : run_sym<kGram, 128>(p, a, s);
+    a.p_bytes = a.q_bytes = static_cast<uint32_t>(p.mp * p.np * 2);
+    return use_big_sym(p) ? run<kGram, 256>(p, a, s) : run<kGram, 128>(p, a, s);
 }
 
 hipError_t launch_poly(const Plan& p, const uint16_t* a_in, uint16_t* b_hi, uint16_t* b_lo,
                        float ca, float cb, float cc, hipStream_t s) {
-    SymArgs a{};
-    a.src = a_in;
-    a.out = b_hi;
-    a.out_lo = b_lo;
-    a.src_stride = p.mp * p.mp;
+    GemmArgs a{};
+    a.p[0] = a_in;
+    a.q[0] = a_in;
+    a.out[0] = b_hi;
+    a.out[1] = b_lo;
+    a.p_stride = a.q_stride = p.mp * p.mp;
     a.out_stride = p.mp * p.mp;
-    a.ld = p.mp;
+    a.K = p.mp;
+    a.ldq = p.mp;
     a.ldo = p.mp;
+    a.p_bytes = a.q_bytes = static_cast<uint32_t>(p.mp * p.mp * 2);
     a.ca = ca;
     a.cb = cb;
     a.cc = cc;
-    a.src_bytes = static_cast<uint32_t>(p.mp * p.mp * 2);
-    if (b_lo) return run_sym<kPolySplit, 128>(p, a, s);
-    return use_big_sym(p) ? run_sym<kPoly, 256>(p, a, s) : run_sym<kPoly, 128>(p, a, s);
+    if (b_lo) return run<kPolySplit, 128>(p, a, s);
+    return use_big_sym(p) ? run<kPoly, 256>(p, a, s) : run<kPoly, 128>(p, a, s);
 }
 
-hipError_t launch_bx(const Plan& p, const uint16_t* b_hi, const uint16_t* b_lo,
-                     const uint16_t* x_hi, const uint16_t* x_lo, uint16_t* out_hi,
-                     uint16_t* out_lo, const float* scale1, hipStream_t s) {
-    BxArgs a{};
-    a.bh = b_hi;
-    a.bl = b_lo;
-    a.xh = x_hi;
-    a.xl = x_lo;
-    a.oh = out_hi;
-    a.ol = out_lo;
+hipError_t launch_bx(const Plan& p, const uint16_t* b_hi, const uint16_t* b_lo, const uint16_t* x_hi,
+                     const uint16_t* x_lo, uint16_t* out_hi, uint16_t* out_lo, const float* scale1,
+                     hipStream_t s) {
+    GemmArgs a{};
+    a.p[0] = b_hi;
+    a.p[1] = b_lo;
+    a.q[0] = x_hi;
+    a.q[1] = x_lo;
+    a.out[0] = out_hi;
+    a.out[1] = out_lo;
     a.scale = scale1;
-    a.bstride = p.mp * p.mp;
-    a.xstride = p.mp * p.np;
-    a.mp = p.mp;
-    a.np = p.np;
-    a.bbytes = static_cast<uint32_t>(p.mp * p.mp * 2);
-    a.xbytes = static_cast<uint32_t>(p.mp * p.np * 2);
-    if (b_lo) return run_bx<true, 128, 128>(p, a, s);
-    return use_big_bx(p) ? run_bx<false, 256, 256>(p, a, s) : run_bx<false, 128, 128>(p, a, s);
+    a.p_stride = p.mp * p.mp;
+    a.q_stride = p.mp * p.np;
+    a.out_stride = p.mp * p.np;
+    a.K = p.mp;
+    a.ldq = p.np;
+    a.ldo = p.np;
+    a.p_bytes = static_cast<uint32_t>(p.mp * p.mp * 2);
+    a.q_bytes = static_cast<uint32_t>(p.mp * p.np * 2);
+    if (b_lo) return run<kBxSplit, 128>(p, a, s);
+    return use_big_full(p) ? run<kBx, 256>(p, a, s) : run<kBx, 128>(p, a, s);
 }
 
 }  // namespace muon
