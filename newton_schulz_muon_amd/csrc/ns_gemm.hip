@@ -355,10 +355,16 @@ struct GemmArgs {
     int64_t ldq;              // row pitch of a k-major column operand
     int64_t ldo;              // output row pitch
     uint32_t p_bytes, q_bytes;
+    // Tile enumeration (of 256-wide tiles in quadrant mode): block-major;
+    // within a block the upper triangle row by row (symmetric) or ti fastest.
     int T;                    // symmetric: tiles per side
-    uint32_t tiles_i;         // full: row tiles per block (ti varies fastest)
+    uint32_t tiles_i;         // full: row tiles per block
     uint32_t tiles;           // tiles per block
-    uint32_t total;           // tiles * blocks
+    uint32_t total;           // workgroups of this launch
+    // Quadrant mode (128-wide kernel finishing the last partial round of a
+    // 256-wide tiling): workgroup L computes quadrant L % 4 of 256-wide tile
+    // big_base + L / 4.
+    uint32_t quad, big_base;
     float ca, cb, cc;
 };
 
@@ -386,10 +392,11 @@ __global__ __launch_bounds__(NTHR) void k_gemm(GemmArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
 
     const uint32_t L = xcd_logical(blockIdx.x, a.total);
-    const int64_t blk = L / a.tiles;
+    const uint32_t tile = a.quad ? a.big_base + L / 4 : L;
+    const int64_t blk = tile / a.tiles;
     int ti, tj;
     {
-        int id = static_cast<int>(L % a.tiles);
+        int id = static_cast<int>(tile % a.tiles);
         if constexpr (SYM) {
             int t = 0, len = a.T;
             while (id >= len) { id -= len; ++t; --len; }
@@ -398,6 +405,11 @@ __global__ __launch_bounds__(NTHR) void k_gemm(GemmArgs a) {
         } else {
             ti = id % static_cast<int>(a.tiles_i);
             tj = id / static_cast<int>(a.tiles_i);
+        }
+        if (a.quad) {
+            ti = 2 * ti + static_cast<int>((L >> 1) & 1);
+            tj = 2 * tj + static_cast<int>(L & 1);
+            if (SYM && ti > tj) return;   // lower quadrant of a diagonal tile: its mirror covers it
         }
     }
     const int row0 = ti * BT, col0 = tj * BT;
@@ -493,6 +505,17 @@ __global__ __launch_bounds__(NTHR) void k_gemm(GemmArgs a) {
     constexpr int RPI = 64 / LPR;     // rows per read-back instruction
     const int rrow = lane / LPR, rcol = (lane % LPR) * 4;
     const int64_t gcol = col0 + wc0 + rcol;
+    // The polynomial's A values of chunk i + 1 are loaded while chunk i is
+    // finished (double buffer), so their latency is exposed once, not per row.
+    constexpr int NT = 32 / RPI;      // read-back instructions per chunk
+    u32x2 abuf[2][NT];
+    auto load_a = [&](int i, u32x2 (&dst)[NT]) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            dst[t] = *reinterpret_cast<const u32x2*>(amat + (int64_t)(row0 + wr0 + i * 32 + t * RPI + rrow) * a.ldo +
+                                                     gcol);
+    };
+    if constexpr (POLY) load_a(0, abuf[0]);
 #pragma unroll
     for (int i = 0; i < F; ++i) {
         __builtin_amdgcn_sched_barrier(0);
@@ -504,16 +527,19 @@ __global__ __launch_bounds__(NTHR) void k_gemm(GemmArgs a) {
                                  acc[i][j][g * 4 + 3]};
                 *reinterpret_cast<f32x4*>(sf + f32_off<TW>(lr, j * 32 + g * 8 + lk * 4)) = v;
             }
+        if constexpr (POLY) {
+            if (i + 1 < F) load_a(i + 1, abuf[(i + 1) & 1]);
+        }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int t = 0; t < 32 / RPI; ++t) {
+        for (int t = 0; t < NT; ++t) {
             const int rr = t * RPI + rrow;
             const int64_t grow = row0 + wr0 + i * 32 + rr;
             const int64_t o = grow * a.ldo + gcol;
             const f32x4 x = *reinterpret_cast<const f32x4*>(sf + f32_off<TW>(rr, rcol));
             float am[4] = {0.f, 0.f, 0.f, 0.f};
             if constexpr (POLY) {
-                const u32x2 av = *reinterpret_cast<const u32x2*>(amat + o);
+                const u32x2 av = abuf[i & 1][t];
                 am[0] = bf16_to_f32(uint16_t(av[0] & 0xffffu));
                 am[1] = bf16_to_f32(uint16_t(av[0] >> 16));
                 am[2] = bf16_to_f32(uint16_t(av[1] & 0xffffu));
@@ -585,34 +611,64 @@ template __global__ void k_gemm<kBxSplit, 128>(GemmArgs);
 
 constexpr int64_t kCUs = 256;
 
-// 256-wide tiles when the side divides and they give at least one full wave
-// of workgroups; 128 otherwise.
-bool use_big_sym(const Plan& p) {
-    if (p.mp % 256 != 0) return false;
-    const int64_t T = p.mp / 256;
-    return p.nb * T * (T + 1) / 2 >= kCUs;
-}
+// Estimated cycles of one round of workgroups at reduction length K, from the
+// measured per-K-step loop time and the prologue + epilogue of each tiling:
+// a round is one 256-wide tile per CU, or two 128-wide tiles per CU (which
+// share the CU; per flop the 128-wide tiling is about 1.3x slower: twice the
+// operand traffic per MFMA).
+double round_cycles_big(int64_t K) { return 1305.0 * double(K / BK) + 12000.0; }
+double round_cycles_small(int64_t K) { return 812.0 * double(K / BK) + 8500.0; }
 
-bool use_big_full(const Plan& p) {
-    if (p.mp % 256 != 0 || p.np % 256 != 0) return false;
-    return p.nb * (p.mp / 256) * (p.np / 256) >= kCUs;
-}
-
-template <int KIND, int BT>
+// Tiling of one product, by the estimated duration of three plans:
+//  * 128-wide tiles throughout (512 per round);
+//  * 256-wide tiles (256 per round) with the last partial round split into
+//    128-wide quadrants in a second launch;
+//  * 256-wide tiles throughout, the last round partial.
+template <int KIND>
 hipError_t run(const Plan& p, GemmArgs a, hipStream_t s) {
     constexpr bool SYM = KIND == kGram || KIND == kPoly || KIND == kPolySplit;
-    if constexpr (SYM) {
-        a.T = static_cast<int>(p.mp / BT);
-        a.tiles = static_cast<uint32_t>(a.T * (a.T + 1) / 2);
-    } else {
-        a.tiles_i = static_cast<uint32_t>(p.mp / BT);
-        a.tiles = a.tiles_i * static_cast<uint32_t>(p.np / BT);
+    constexpr bool HAS_BIG = KIND == kGram || KIND == kPoly || KIND == kBx;
+    auto geometry = [&](int bt) {
+        if (SYM) {
+            a.T = static_cast<int>(p.mp / bt);
+            a.tiles = static_cast<uint32_t>(a.T * (a.T + 1) / 2);
+        } else {
+            a.tiles_i = static_cast<uint32_t>(p.mp / bt);
+            a.tiles = a.tiles_i * static_cast<uint32_t>(p.np / bt);
+        }
+        return int64_t(a.tiles) * p.nb;
+    };
+    auto launch = [&](int bt, int64_t total, uint32_t quad, uint32_t base) {
+        a.quad = quad;
+        a.big_base = base;
+        a.total = static_cast<uint32_t>(total);
+        if (bt == 256) {
+            if constexpr (HAS_BIG) k_gemm<KIND, 256><<<dim3(a.total), dim3(NTHR), 0, s>>>(a);
+        } else {
+            k_gemm<KIND, 128><<<dim3(a.total), dim3(NTHR), 0, s>>>(a);
+        }
+        return hipGetLastError();
+    };
+    const int64_t small = geometry(128);
+    if (small > 0x3fffffffLL) return hipErrorInvalidValue;
+    const double t_small = double((small + 2 * kCUs - 1) / (2 * kCUs)) * round_cycles_small(a.K);
+    if (HAS_BIG && p.mp % 256 == 0 && (SYM || p.np % 256 == 0)) {
+        const int64_t big = geometry(256);
+        const int64_t full = big / kCUs, tail = big % kCUs;
+        const double t_split = double(full) * round_cycles_big(a.K) +
+                               double((4 * tail + 2 * kCUs - 1) / (2 * kCUs)) * round_cycles_small(a.K);
+        const double t_big = double(full + (tail ? 1 : 0)) * round_cycles_big(a.K);
+        if (t_big <= t_split && t_big < t_small) return launch(256, big, 0, 0);
+        if (t_split < t_small) {
+            if (full > 0) {
+                const hipError_t e = launch(256, full * kCUs, 0, 0);
+                if (e != hipSuccess || tail == 0) return e;
+            }
+            return launch(128, 4 * tail, 1, static_cast<uint32_t>(full * kCUs));
+        }
+        geometry(128);
     }
-    const int64_t total = int64_t(a.tiles) * p.nb;
-    if (total > 0x7fffffffLL) return hipErrorInvalidValue;
-    a.total = static_cast<uint32_t>(total);
-    k_gemm<KIND, BT><<<dim3(a.total), dim3(NTHR), 0, s>>>(a);
-    return hipGetLastError();
+    return launch(128, small, 0, 0);
 }
 
 }  // namespace
@@ -629,7 +685,7 @@ hipError_t launch_gram(const Plan& p, const uint16_t* x, uint16_t* a_out, const 
     a.K = p.np;
     a.ldo = p.mp;
     a.p_bytes = a.q_bytes = static_cast<uint32_t>(p.mp * p.np * 2);
-    return use_big_sym(p) ? run<kGram, 256>(p, a, s) : run<kGram, 128>(p, a, s);
+    return run<kGram>(p, a, s);
 }
 
 hipError_t launch_poly(const Plan& p, const uint16_t* a_in, uint16_t* b_hi, uint16_t* b_lo,
@@ -648,8 +704,7 @@ hipError_t launch_poly(const Plan& p, const uint16_t* a_in, uint16_t* b_hi, uint
     a.ca = ca;
     a.cb = cb;
     a.cc = cc;
-    if (b_lo) return run<kPolySplit, 128>(p, a, s);
-    return use_big_sym(p) ? run<kPoly, 256>(p, a, s) : run<kPoly, 128>(p, a, s);
+    return b_lo ? run<kPolySplit>(p, a, s) : run<kPoly>(p, a, s);
 }
 
 hipError_t launch_bx(const Plan& p, const uint16_t* b_hi, const uint16_t* b_lo, const uint16_t* x_hi,
@@ -671,8 +726,7 @@ hipError_t launch_bx(const Plan& p, const uint16_t* b_hi, const uint16_t* b_lo, 
     a.ldo = p.np;
     a.p_bytes = static_cast<uint32_t>(p.mp * p.mp * 2);
     a.q_bytes = static_cast<uint32_t>(p.mp * p.np * 2);
-    if (b_lo) return run<kBxSplit, 128>(p, a, s);
-    return use_big_full(p) ? run<kBx, 256>(p, a, s) : run<kBx, 128>(p, a, s);
+    return b_lo ? run<kBxSplit>(p, a, s) : run<kBx>(p, a, s);
 }
 
 }  // namespace muon

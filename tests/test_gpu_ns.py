@@ -49,6 +49,26 @@ def test_ns_parity_default(nsm, shape):
         assert_ns_close(got[i], ref[i], label=f"{shape}[{i}]")
 
 
+# Batches large enough for 256-wide tiles with a partial last round, which is
+# finished by a second launch of 128-wide quadrants.  50 blocks of 768 x 768:
+# 300 upper-triangle tiles (256 + 44, the 44 including diagonal tiles whose
+# lower quadrant is skipped) and 450 B X tiles (256 + 194).  24 of 768 x 1536:
+# 144 symmetric tiles (all 128-wide) and 432 B X tiles (256 + 176).  Blocks
+# on both sides of each launch boundary, and the first and last, are checked.
+@pytest.mark.parametrize("batch,shape,check", [
+    (50, (768, 768), (0, 28, 29, 42, 43, 49)),
+    (24, (768, 1536), (0, 14, 15, 23)),
+    (24, (1536, 768), (0, 14, 15, 23)),
+])
+def test_ns_parity_tail_split(nsm, batch, shape, check):
+    print(f"[ns tail split] batch={batch} shape={shape}", flush=True)
+    bits = workloads.gaussian_bits((batch,) + shape, seed=batch * 7 + shape[1])
+    got = bits_to_f64(_run(nsm, bits))
+    ref = _oracle_batch(bits[list(check)])
+    for k, i in enumerate(check):
+        assert_ns_close(got[i], ref[k], label=f"{shape}[{i}]")
+
+
 @pytest.mark.parametrize("coeffs", [(1.0, 0.0, 0.0), (0.0, 1.0, 0.0), (0.0, 0.0, 1.0), oracle.NS_COEFFS])
 @pytest.mark.parametrize("shape", [(256, 640), (300, 200)])
 def test_ns_single_iteration_terms(nsm, coeffs, shape):
