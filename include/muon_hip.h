@@ -142,8 +142,11 @@ typedef enum muon_kernel_kind {
 
 /* While kernel_mask has bit k set, every launch of kernel family k records a
  * hipEvent before and after it on the stream it is launched on (events are
- * created on first use and reused; 0 turns recording off).  Recording adds
- * two event packets per selected launch and nothing when the mask is 0. */
+ * created on first use with hipEventDisableSystemFence, as they only measure
+ * time, and reused; 0 turns recording off).  Recording adds two event packets
+ * per selected launch and nothing when the mask is 0.  One launch of a family
+ * is one library-level launch: the B X product of a call may run as a bulk
+ * kernel plus a tail kernel, timed together. */
 muon_status muon_timing_enable(uint32_t kernel_mask);
 
 /* Waits for every recorded event, adds launch counts and elapsed milliseconds

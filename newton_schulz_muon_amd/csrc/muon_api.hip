@@ -159,8 +159,10 @@ hipEvent_t pool_get(TimingState& ts, int dev) {
         v.pop_back();
         return e;
     }
+    // Timing only: without the system-scope fence a record does not write back
+    // and invalidate caches, which would otherwise slow the bracketed launch.
     hipEvent_t e = nullptr;
-    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
     return e;
 }
 
