@@ -57,7 +57,6 @@
 namespace muon {
 namespace {
 
-constexpr int BK = 32;        // K slice per pipeline stage
 constexpr int NTHR = 256;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -72,26 +71,35 @@ typedef __attribute__((address_space(3))) void lds_void;
 // 8-byte read by 32 lanes, is conflict-free when the lanes cover 256
 // distinct-bank bytes.
 //
-// A k-contiguous operand tile in LDS: rows of BK bf16 = 64 bytes = 4 chunks of
-// 16 bytes; chunk c of row r is stored at chunk c ^ ((r / 4) % 4).  Any 16
+// A k-contiguous operand tile in LDS: rows of BK bf16 (2 BK bytes, BK / 8
+// chunks of 16 bytes); chunk c of row r is stored at chunk c ^ f(r) with
+// f(r) = (r / RP) mod (BK / 8), RP = 256 / (2 BK) rows per 256 bytes.  Any 16
 // consecutive rows then cover all 64 banks for 16-byte fragment reads.
-__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
+template <int BK>
+__device__ __forceinline__ int swz(int row) {
+    return (row / (128 / BK)) & (BK / 8 - 1);
+}
+template <int BK>
 __device__ __forceinline__ int lds_off(int row, int chunk) {
-    return (row << 6) + ((chunk ^ swz(row)) << 4);
+    return row * (2 * BK) + ((chunk ^ swz<BK>(row)) << 4);
 }
 
+// Pipeline of one tile size (K slice BK, NS LDS stages):
+//  * 256-wide tiles (one workgroup per CU): BK = 32 in a ring of NS = 4; the
+//    wait and barrier of a step come before its last sub-slice, and slice
+//    k + 3 is fetched into the stage just freed (it lands two steps later).
+//  * 128-wide tiles (two workgroups per CU): BK = 64 in NS = 2 stages; slice
+//    k + 1 is fetched during step k and waited for at the end of the step.
+//    The 128-byte k-contiguous rows are whole cache lines (a 64-byte row
+//    costs the same L1 miss as a full line), and the other workgroup on the
+//    CU covers the first fragment reads of each step.
 template <int BT>
 struct TileCfg {
     static constexpr int TW = BT / 2;               // wave tile edge
     static constexpr int F = TW / 32;               // 32x32 blocks per wave side
+    static constexpr int BK = BT == 256 ? 32 : 64;  // K slice per stage
+    static constexpr int NS = BT == 256 ? 4 : 2;    // LDS stages
     static constexpr int OP_BYTES = BT * BK * 2;    // one operand tile
-};
-
-// LDS ring depth (stages of one K slice each).  Slice k + NS - 1 is fetched
-// while slice k is multiplied and must land NS - 2 steps later.
-template <int BT, bool SPLIT_IN>
-struct RingCfg {
-    static constexpr int NS = 4;
 };
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -117,11 +125,13 @@ __device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t voff, uint32_t
 
 // An R x BK slice of a k-contiguous matrix fetched straight into LDS: one
 // instruction of one wave fills 1 KB (lane L writes bytes [16 L, 16 L + 16)),
-// i.e. 16 rows x 4 chunks.  The lane whose LDS slot is (row, physical chunk p)
-// fetches logical chunk p ^ swz(row).
-template <int R>
+// i.e. 512 / BK rows of BK / 8 chunks.  The lane whose LDS slot is (row,
+// physical chunk p) fetches logical chunk p ^ swz(row).
+template <int R, int BK>
 struct RowDma {
-    static constexpr int PW = R / 64;   // 1 KB windows per wave
+    static constexpr int CPR = BK / 8;               // chunks per row
+    static constexpr int RPW = 64 / CPR;             // rows per 1 KB window
+    static constexpr int PW = R / RPW / 4;           // windows per wave
     const void* base;                   // the matrix; its buffer descriptor is built in load()
     uint32_t bytes;
     uint32_t voff[PW];
@@ -132,8 +142,8 @@ struct RowDma {
         const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
 #pragma unroll
         for (int q = 0; q < PW; ++q) {
-            const int row = 16 * (w * PW + q) + (l >> 2);
-            const int chunk = (l & 3) ^ swz(row);
+            const int row = RPW * (w * PW + q) + l / CPR;
+            const int chunk = (l % CPR) ^ swz<BK>(row);
             voff[q] = static_cast<uint32_t>(((int64_t)(row0 + row) * ld + chunk * 8) * 2);
         }
     }
@@ -154,7 +164,7 @@ __device__ __forceinline__ int col_off(int row, int col) {
     return row * (2 * C) + (((col >> 3) ^ ((row & 3) << 2)) << 4) + (((col >> 2) & 1) << 3);
 }
 
-template <int C>
+template <int C, int BK>
 struct ColDma {
     static constexpr int ROWS_PER_WIN = 512 / C;
     static constexpr int PW = BK / ROWS_PER_WIN / 4;   // 1 KB windows per wave
@@ -218,7 +228,8 @@ template <bool KMAJOR, int BT>
 __device__ __forceinline__ bf16x8 load_frag(const char* S, int base, int ks) {
     const int lane = threadIdx.x & 63;
     if constexpr (!KMAJOR) {
-        return *reinterpret_cast<const bf16x8*>(S + lds_off(base + (lane & 31), ks * 2 + (lane >> 5)));
+        return *reinterpret_cast<const bf16x8*>(
+            S + lds_off<TileCfg<BT>::BK>(base + (lane & 31), ks * 2 + (lane >> 5)));
     } else {
         const int L = lane & 15, grp = (lane >> 4) & 1;
         const int row = 16 * ks + 8 * (lane >> 5) + (L >> 2);
@@ -234,22 +245,23 @@ __device__ __forceinline__ bf16x8 load_frag(const char* S, int base, int ks) {
 
 // The fragments of one sub-slice, read in the order the MFMAs consume them
 // (a0 with b0 .. b(F-1), then a1, a2, ...), so the reads issued last have the
-// most MFMAs of the next sub-slice to complete behind.  With DMA, the loads of
-// a stage (into `next`, K offset k1) are issued in between, a share after
-// each fragment: the reads are placed one per MFMA, so the DMA instructions
-// are spread over the sub-slice instead of stalling the wave in a burst when
-// the address queue fills.
-template <int F, bool KMAJOR_A, bool KMAJOR_B, int BT, bool DMA = false, typename Ops = void>
+// most MFMAs of the next sub-slice to complete behind.  With DMA, the W loads
+// of a stage (into `next`, K offset k1) are issued in between: fragment g of
+// the G fragment reads that carry them (this call's first fragment is number
+// g0) issues the windows w with w G in [g W, (g + 1) W).  The reads are placed
+// one per MFMA, so the DMA instructions are spread over the MFMA stream
+// instead of stalling the wave in a burst when the address queue fills.
+template <int F, bool KMAJOR_A, bool KMAJOR_B, int BT, bool DMA = false, int G = 1, typename Ops = void>
 __device__ __forceinline__ void load_frags(const char* As, const char* Bs, int wr0, int wc0, int ks,
                                            bf16x8 (&a)[F], bf16x8 (&b)[F], const Ops* ops = nullptr,
-                                           char* next = nullptr, int k1 = 0) {
-    constexpr int NF = 2 * F;
+                                           char* next = nullptr, int k1 = 0, int g0 = 0) {
     auto dma_after = [&](int fi) {
         if constexpr (DMA) {
             constexpr int W = Ops::WINDOWS;
+            const int g = g0 + fi;
 #pragma unroll
             for (int w = 0; w < W; ++w)
-                if (w * NF >= fi * W && w * NF < (fi + 1) * W) ops->load_window(next, k1, w);
+                if (w * G >= g * W && w * G < (g + 1) * W) ops->load_window(next, k1, w);
         }
     };
     a[0] = load_frag<KMAJOR_A, BT>(As, wr0, ks);
@@ -384,11 +396,12 @@ __global__ __launch_bounds__(NTHR) void k_gemm(GemmArgs a) {
     constexpr bool KMAJOR_A = KIND != kGram;
     constexpr bool KMAJOR_B = KIND != kGram;
     constexpr int NA = SPLIT_IN ? 2 : 1, NB = SPLIT_IN ? 2 : 1;
-    using ALoader = typename std::conditional<KMAJOR_A, ColDma<BT>, RowDma<BT>>::type;
-    using BLoader = typename std::conditional<KMAJOR_B, ColDma<BT>, RowDma<BT>>::type;
+    constexpr int BK = Cfg::BK;
+    using ALoader = typename std::conditional<KMAJOR_A, ColDma<BT, BK>, RowDma<BT, BK>>::type;
+    using BLoader = typename std::conditional<KMAJOR_B, ColDma<BT, BK>, RowDma<BT, BK>>::type;
     using Ops = Operands<BT, NA, NB, ALoader, BLoader>;
     constexpr int STAGE = Ops::STAGE;
-    constexpr int LDS_BYTES = RingCfg<BT, SPLIT_IN>::NS * STAGE;
+    constexpr int LDS_BYTES = Cfg::NS * STAGE;
     __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
 
     const uint32_t L = xcd_logical(blockIdx.x, a.total);
@@ -425,53 +438,84 @@ __global__ __launch_bounds__(NTHR) void k_gemm(GemmArgs a) {
     f32x16 acc[F][F];
     zero_acc<F>(acc);
 
-    // Ring of NS stages; slice kt lives in stage kt % NS.  A K step is U
-    // sub-slices (16 deep, and for the split B X three products each); the
-    // fragments of sub-slice u + 1 are read from LDS while the MFMAs of u run,
-    // so the first fragments of slice kt + 1 are read during the last
-    // sub-slice of step kt.  Just before that sub-slice every wave waits for
-    // its own loads of slice kt + 1 and then at a barrier, after which stage
-    // (kt - 1) % NS is free (all its reads were consumed by step kt - 1) and
-    // slice kt + NS - 1 is fetched into it.  Every step issues exactly one
-    // stage of loads (Ops::WINDOWS DMA instructions per wave; in the tail an
-    // in-bounds slice whose copy is never read), so the wait count is fixed.
-    constexpr int NS = RingCfg<BT, SPLIT_IN>::NS;
-    static_assert(NS >= 3, "the ring needs a stage in flight beside the two being read");
+    // A K step is U sub-slices (16 deep, and for the split B X three products
+    // each); the fragments of sub-slice u + 1 are read from LDS while the
+    // MFMAs of u run.  products: 0 = (A hi, B hi), 1 = (A hi, B lo), 2 = (A lo, B hi)
+    constexpr int NS = Cfg::NS;
     constexpr int KS = BK / 16;
-    constexpr int P = SPLIT_IN ? 3 : 1;          // products per step: Bh Xh (+ Bh Xl, Bl Xh)
+    constexpr int P = SPLIT_IN ? 3 : 1;
     constexpr int U = P * KS;
     static_assert(U % 2 == 0, "fragment ping-pong restarts at 0 each step");
     constexpr int NREAD = (KMAJOR_A ? 2 * F : F) + (KMAJOR_B ? 2 * F : F);
     constexpr int W = Ops::WINDOWS;
     const int nk = static_cast<int>(a.K / BK);
-
-#pragma unroll
-    for (int st = 0; st < NS - 1; ++st) ops.load(lds + st * STAGE, (st < nk ? st : 0) * BK);
     bf16x8 fa[2][F], fb[2][F];
-    wait_dma_and_barrier<(NS - 2) * W>();
-    load_frags<F, KMAJOR_A, KMAJOR_B, BT>(Ops::a_tile(lds, 0), Ops::b_tile(lds, 0), wr0, wc0, 0, fa[0], fb[0]);
+    auto frags = [&](const char* st, int u, bf16x8 (&xa)[F], bf16x8 (&xb)[F]) {
+        const int pn = u / KS, ks = u % KS;
+        load_frags<F, KMAJOR_A, KMAJOR_B, BT>(Ops::a_tile(const_cast<char*>(st), pn == 2 ? 1 : 0),
+                                              Ops::b_tile(const_cast<char*>(st), pn == 1 ? 1 : 0), wr0, wc0, ks,
+                                              xa, xb);
+    };
 
-    for (int kt = 0; kt < nk; ++kt) {
-        char* cur = lds + (kt % NS) * STAGE;
-        char* nxt = lds + ((kt + 1) % NS) * STAGE;
+    if constexpr (NS >= 3) {
+        // Ring: slice kt lives in stage kt % NS.  Just before the last
+        // sub-slice of step kt every wave waits for its own loads of slice
+        // kt + 1 and then at a barrier, after which stage (kt - 1) % NS is
+        // free (step kt - 1 consumed all its reads) and slice kt + NS - 1 is
+        // fetched into it, spread over the last sub-slice, whose reads are
+        // the first fragments of slice kt + 1.  Every step issues exactly one
+        // stage of loads (in the tail an in-bounds slice whose copy is never
+        // read), so the wait count is fixed.
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int c = u & 1;
-            if (u == U - 1) wait_dma_and_barrier<(NS - 3) * W>();
-            if (u + 1 < U) {
-                const int pn = (u + 1) / KS, ks = (u + 1) % KS;
-                // products: 0 = (A hi, B hi), 1 = (A hi, B lo), 2 = (A lo, B hi)
-                load_frags<F, KMAJOR_A, KMAJOR_B, BT>(Ops::a_tile(cur, pn == 2 ? 1 : 0), Ops::b_tile(cur, pn == 1 ? 1 : 0),
-                                            wr0, wc0, ks, fa[c ^ 1], fb[c ^ 1]);
-            } else {
-                const int kn = kt + NS - 1;
-                load_frags<F, KMAJOR_A, KMAJOR_B, BT, true>(Ops::a_tile(nxt, 0), Ops::b_tile(nxt, 0), wr0, wc0, 0,
-                                                            fa[c ^ 1], fb[c ^ 1], &ops, lds + (kn % NS) * STAGE,
-                                                            (kn < nk ? kn : kt) * BK);
+        for (int st = 0; st < NS - 1; ++st) ops.load(lds + st * STAGE, (st < nk ? st : 0) * BK);
+        wait_dma_and_barrier<(NS - 2) * W>();
+        frags(lds, 0, fa[0], fb[0]);
+        for (int kt = 0; kt < nk; ++kt) {
+            char* cur = lds + (kt % NS) * STAGE;
+            char* nxt = lds + ((kt + 1) % NS) * STAGE;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = u & 1;
+                if (u + 1 < U) {
+                    frags(cur, u + 1, fa[c ^ 1], fb[c ^ 1]);
+                } else {
+                    wait_dma_and_barrier<(NS - 3) * W>();
+                    const int kn = kt + NS - 1;
+                    load_frags<F, KMAJOR_A, KMAJOR_B, BT, true, 2 * F>(
+                        Ops::a_tile(nxt, 0), Ops::b_tile(nxt, 0), wr0, wc0, 0, fa[c ^ 1], fb[c ^ 1], &ops,
+                        lds + (kn % NS) * STAGE, (kn < nk ? kn : kt) * BK, 0);
+                }
+                mfma_block<F>(fa[c], fb[c], acc);
+                interleave<F, NREAD>();
+                __builtin_amdgcn_sched_barrier(0);
             }
-            mfma_block<F>(fa[c], fb[c], acc);
-            interleave<F, NREAD>();
+        }
+    } else {
+        // Two stages: slice kt + 1 is fetched into the other stage during step
+        // kt, spread over its first U - 1 sub-slices, and waited for at the
+        // end of the step, where a barrier also frees stage kt % 2.
+        ops.load(lds, 0);
+        wait_dma_and_barrier<0>();
+        for (int kt = 0; kt < nk; ++kt) {
+            char* cur = lds + (kt & 1) * STAGE;
+            char* nxt = lds + ((kt + 1) & 1) * STAGE;
+            const int k1 = (kt + 1 < nk ? kt + 1 : kt) * BK;
+            frags(cur, 0, fa[0], fb[0]);
             __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = u & 1;
+                if (u + 1 < U) {
+                    const int pn = (u + 1) / KS, ks = (u + 1) % KS;
+                    load_frags<F, KMAJOR_A, KMAJOR_B, BT, true, (U - 1) * 2 * F>(
+                        Ops::a_tile(cur, pn == 2 ? 1 : 0), Ops::b_tile(cur, pn == 1 ? 1 : 0), wr0, wc0, ks,
+                        fa[c ^ 1], fb[c ^ 1], &ops, nxt, k1, u * 2 * F);
+                }
+                mfma_block<F>(fa[c], fb[c], acc);
+                if (u + 1 < U) interleave<F, NREAD>();
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            wait_dma_and_barrier<0>();
         }
     }
     __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): no DMA may land on the epilogue staging
@@ -616,8 +660,8 @@ constexpr int64_t kCUs = 256;
 // a round is one 256-wide tile per CU, or two 128-wide tiles per CU (which
 // share the CU; per flop the 128-wide tiling is about 1.3x slower: twice the
 // operand traffic per MFMA).
-double round_cycles_big(int64_t K) { return 1305.0 * double(K / BK) + 12000.0; }
-double round_cycles_small(int64_t K) { return 812.0 * double(K / BK) + 8500.0; }
+double round_cycles_big(int64_t K) { return 1305.0 * double(K / 32) + 12000.0; }
+double round_cycles_small(int64_t K) { return 812.0 * double(K / 32) + 8500.0; }
 
 // Tiling of one product, by the estimated duration of three plans:
 //  * 128-wide tiles throughout (512 per round);
