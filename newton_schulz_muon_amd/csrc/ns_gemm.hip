@@ -84,21 +84,23 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
     return row * (2 * BK) + ((chunk ^ swz<BK>(row)) << 4);
 }
 
-// Pipeline of one tile size (K slice BK, NS LDS stages):
-//  * 256-wide tiles (one workgroup per CU): BK = 32 in a ring of NS = 4; the
-//    wait and barrier of a step come before its last sub-slice, and slice
-//    k + 3 is fetched into the stage just freed (it lands two steps later).
-//  * 128-wide tiles (two workgroups per CU): BK = 64 in NS = 2 stages; slice
-//    k + 1 is fetched during step k and waited for at the end of the step.
-//    The 128-byte k-contiguous rows are whole cache lines (a 64-byte row
-//    costs the same L1 miss as a full line), and the other workgroup on the
-//    CU covers the first fragment reads of each step.
-template <int BT>
+// Pipeline (K slice BK, NS LDS stages):
+//  * ring: BK = 32 in NS = 4 stages; the wait and barrier of a step come
+//    before its last sub-slice, and slice k + 3 is fetched into the stage
+//    just freed (it lands two steps later).  256-wide tiles, and the B X
+//    product at any width.
+//  * two stages: BK = 64 in NS = 2; slice k + 1 is fetched during step k and
+//    waited for at the end of the step.  128-wide Gram and polynomial tiles
+//    (two workgroups per CU): the 128-byte k-contiguous rows of X X^T are
+//    whole cache lines (a 64-byte row costs the same L1 miss as a full
+//    line), and the other workgroup on the CU covers the first fragment
+//    reads of each step.
+template <int BT, bool RING>
 struct TileCfg {
     static constexpr int TW = BT / 2;               // wave tile edge
     static constexpr int F = TW / 32;               // 32x32 blocks per wave side
-    static constexpr int BK = BT == 256 ? 32 : 64;  // K slice per stage
-    static constexpr int NS = BT == 256 ? 4 : 2;    // LDS stages
+    static constexpr int BK = RING ? 32 : 64;       // K slice per stage
+    static constexpr int NS = RING ? 4 : 2;         // LDS stages
     static constexpr int OP_BYTES = BT * BK * 2;    // one operand tile
 };
 
@@ -127,8 +129,9 @@ __device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t voff, uint32_t
 // instruction of one wave fills 1 KB (lane L writes bytes [16 L, 16 L + 16)),
 // i.e. 512 / BK rows of BK / 8 chunks.  The lane whose LDS slot is (row,
 // physical chunk p) fetches logical chunk p ^ swz(row).
-template <int R, int BK>
+template <int R, int BK_>
 struct RowDma {
+    static constexpr int BK = BK_;
     static constexpr int CPR = BK / 8;               // chunks per row
     static constexpr int RPW = 64 / CPR;             // rows per 1 KB window
     static constexpr int PW = R / RPW / 4;           // windows per wave
@@ -164,8 +167,9 @@ __device__ __forceinline__ int col_off(int row, int col) {
     return row * (2 * C) + (((col >> 3) ^ ((row & 3) << 2)) << 4) + (((col >> 2) & 1) << 3);
 }
 
-template <int C, int BK>
+template <int C, int BK_>
 struct ColDma {
+    static constexpr int BK = BK_;
     static constexpr int ROWS_PER_WIN = 512 / C;
     static constexpr int PW = BK / ROWS_PER_WIN / 4;   // 1 KB windows per wave
     const void* base;
@@ -198,11 +202,12 @@ template <int BT, int NA, int NB, typename ALoader, typename BLoader>
 struct Operands {
     ALoader a[NA];
     BLoader b[NB];
-    static constexpr int STAGE = (NA + NB) * TileCfg<BT>::OP_BYTES;
+    static constexpr int OP_BYTES = BT * ALoader::BK * 2;   // one operand tile
+    static constexpr int STAGE = (NA + NB) * OP_BYTES;
     static constexpr int WINDOWS = NA * ALoader::PW + NB * BLoader::PW;   // DMA instructions per wave
-    __device__ __forceinline__ static char* a_tile(char* stage, int i) { return stage + i * TileCfg<BT>::OP_BYTES; }
+    __device__ __forceinline__ static char* a_tile(char* stage, int i) { return stage + i * OP_BYTES; }
     __device__ __forceinline__ static char* b_tile(char* stage, int j) {
-        return stage + (NA + j) * TileCfg<BT>::OP_BYTES;
+        return stage + (NA + j) * OP_BYTES;
     }
     // DMA instruction w (0 <= w < WINDOWS) of this wave for the slice at k0.
     __device__ __forceinline__ void load_window(char* stage, int k0, int w) const {
@@ -224,12 +229,12 @@ struct Operands {
 // operand.  From k-contiguous rows: one 16-byte read.  From a k-major tile:
 // two transposing reads (k rows ks*16 + 8 (l / 32) + 0..3 and + 4..7 of
 // index l % 32 of the block).
-template <bool KMAJOR, int BT>
+template <bool KMAJOR, int BT, int BK>
 __device__ __forceinline__ bf16x8 load_frag(const char* S, int base, int ks) {
     const int lane = threadIdx.x & 63;
     if constexpr (!KMAJOR) {
         return *reinterpret_cast<const bf16x8*>(
-            S + lds_off<TileCfg<BT>::BK>(base + (lane & 31), ks * 2 + (lane >> 5)));
+            S + lds_off<BK>(base + (lane & 31), ks * 2 + (lane >> 5)));
     } else {
         const int L = lane & 15, grp = (lane >> 4) & 1;
         const int row = 16 * ks + 8 * (lane >> 5) + (L >> 2);
@@ -251,7 +256,7 @@ __device__ __forceinline__ bf16x8 load_frag(const char* S, int base, int ks) {
 // g0) issues the windows w with w G in [g W, (g + 1) W).  The reads are placed
 // one per MFMA, so the DMA instructions are spread over the MFMA stream
 // instead of stalling the wave in a burst when the address queue fills.
-template <int F, bool KMAJOR_A, bool KMAJOR_B, int BT, bool DMA = false, int G = 1, typename Ops = void>
+template <int F, bool KMAJOR_A, bool KMAJOR_B, int BT, int BK, bool DMA = false, int G = 1, typename Ops = void>
 __device__ __forceinline__ void load_frags(const char* As, const char* Bs, int wr0, int wc0, int ks,
                                            bf16x8 (&a)[F], bf16x8 (&b)[F], const Ops* ops = nullptr,
                                            char* next = nullptr, int k1 = 0, int g0 = 0) {
@@ -264,16 +269,16 @@ __device__ __forceinline__ void load_frags(const char* As, const char* Bs, int w
                 if (w * G >= g * W && w * G < (g + 1) * W) ops->load_window(next, k1, w);
         }
     };
-    a[0] = load_frag<KMAJOR_A, BT>(As, wr0, ks);
+    a[0] = load_frag<KMAJOR_A, BT, BK>(As, wr0, ks);
     dma_after(0);
 #pragma unroll
     for (int j = 0; j < F; ++j) {
-        b[j] = load_frag<KMAJOR_B, BT>(Bs, wc0 + j * 32, ks);
+        b[j] = load_frag<KMAJOR_B, BT, BK>(Bs, wc0 + j * 32, ks);
         dma_after(1 + j);
     }
 #pragma unroll
     for (int i = 1; i < F; ++i) {
-        a[i] = load_frag<KMAJOR_A, BT>(As, wr0 + i * 32, ks);
+        a[i] = load_frag<KMAJOR_A, BT, BK>(As, wr0 + i * 32, ks);
         dma_after(F + i);
     }
 }
@@ -382,7 +387,7 @@ struct GemmArgs {
 
 template <int KIND, int BT>
 __global__ __launch_bounds__(NTHR) void k_gemm(GemmArgs a) {
-    using Cfg = TileCfg<BT>;
+    using Cfg = TileCfg<BT, BT == 256 || KIND == kBx || KIND == kBxSplit>;
     constexpr int F = Cfg::F, TW = Cfg::TW;
     constexpr bool SYM = KIND == kGram || KIND == kPoly || KIND == kPolySplit;
     constexpr bool POLY = KIND == kPoly || KIND == kPolySplit;
@@ -452,7 +457,7 @@ __global__ __launch_bounds__(NTHR) void k_gemm(GemmArgs a) {
     bf16x8 fa[2][F], fb[2][F];
     auto frags = [&](const char* st, int u, bf16x8 (&xa)[F], bf16x8 (&xb)[F]) {
         const int pn = u / KS, ks = u % KS;
-        load_frags<F, KMAJOR_A, KMAJOR_B, BT>(Ops::a_tile(const_cast<char*>(st), pn == 2 ? 1 : 0),
+        load_frags<F, KMAJOR_A, KMAJOR_B, BT, BK>(Ops::a_tile(const_cast<char*>(st), pn == 2 ? 1 : 0),
                                               Ops::b_tile(const_cast<char*>(st), pn == 1 ? 1 : 0), wr0, wc0, ks,
                                               xa, xb);
     };
@@ -481,7 +486,7 @@ __global__ __launch_bounds__(NTHR) void k_gemm(GemmArgs a) {
                 } else {
                     wait_dma_and_barrier<(NS - 3) * W>();
                     const int kn = kt + NS - 1;
-                    load_frags<F, KMAJOR_A, KMAJOR_B, BT, true, 2 * F>(
+                    load_frags<F, KMAJOR_A, KMAJOR_B, BT, BK, true, 2 * F>(
                         Ops::a_tile(nxt, 0), Ops::b_tile(nxt, 0), wr0, wc0, 0, fa[c ^ 1], fb[c ^ 1], &ops,
                         lds + (kn % NS) * STAGE, (kn < nk ? kn : kt) * BK, 0);
                 }
@@ -507,7 +512,7 @@ __global__ __launch_bounds__(NTHR) void k_gemm(GemmArgs a) {
                 const int c = u & 1;
                 if (u + 1 < U) {
                     const int pn = (u + 1) / KS, ks = (u + 1) % KS;
-                    load_frags<F, KMAJOR_A, KMAJOR_B, BT, true, (U - 1) * 2 * F>(
+                    load_frags<F, KMAJOR_A, KMAJOR_B, BT, BK, true, (U - 1) * 2 * F>(
                         Ops::a_tile(cur, pn == 2 ? 1 : 0), Ops::b_tile(cur, pn == 1 ? 1 : 0), wr0, wc0, ks,
                         fa[c ^ 1], fb[c ^ 1], &ops, nxt, k1, u * 2 * F);
                 }
