@@ -195,3 +195,28 @@ def test_ns_rejects_misaligned_and_small_workspace(nsm):
                                       ws.data_ptr() + 64, need, None)
     assert st == 3
     assert nsm.muon_last_error()
+
+
+@pytest.mark.timeout(400)
+@pytest.mark.parametrize("group,index", [("sq", 0), ("wide", 7)])
+def test_ns_parity_large_dense(nsm, group, index):
+    # The large dense batch at full size (8 x 4096^2 and 8 x 4096x14336, decaying
+    # spectrum sigma_i = 1/i, ACCURATE precision as the workload runs it): the
+    # whole batch goes through the GPU and one matrix is checked against the
+    # fp64 oracle on its bf16 input (the matrix the last 256-wide round of the
+    # wide group covers, and the first square one).
+    import torch
+    wl = workloads.get_workload("large_dense")
+    g = {gr.name: gr for gr in wl.groups}[group]
+    print(f"[ns large_dense] group={group} {g.count}x{g.rows}x{g.cols} precision={g.precision} "
+          f"check index {index}", flush=True)
+    x = workloads.grads_device(wl, g, 0, torch.device("cuda:0"))
+    out = nsm.ns_orthogonalize_batched(x, precision=g.precision)
+    torch.cuda.synchronize()
+    bits = torch_bf16_to_bits(x[index:index + 1])
+    got = bits_to_f64(torch_bf16_to_bits(out[index:index + 1]))
+    del x, out
+    ref = _oracle_batch(bits)
+    print("[ns large_dense] oracle done", flush=True)
+    rel, sig = assert_ns_close(got[0], ref[0], label=f"large_dense {group}[{index}]")
+    print(f"[ns large_dense] rel {rel:.3e} sigma {sig:.3e}", flush=True)
