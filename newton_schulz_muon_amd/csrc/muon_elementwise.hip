@@ -68,58 +68,83 @@ __device__ __forceinline__ float momentum_update(float g, float* mptr, float mu,
     }
 }
 
-// Loads 8 stored elements (bi, bj0..bj0+7) of one block, applies the momentum
-// update and returns the update direction in u[].
-template <int MODE, bool VEC>
-__device__ __forceinline__ void load_update8(const PrepArgs& a, const uint16_t* src, float* mom,
-                                             int64_t bi, int64_t bj0, float (&u)[8], bool (&ok)[8]) {
-    if constexpr (VEC) {
-        const bool valid = (bi < a.r) && (bj0 < a.c);
+// 8 stored elements (bi, bj0 .. bj0 + 7) of one block as read from HBM.
+struct Raw8 {
+    u32x4 g;        // bf16 gradient / x
+    f32x4 m0, m1;   // fp32 momentum buffer
+    bool valid;
+};
+
+// Vector path: both loads of a row piece are 16-byte.
+template <int MODE>
+__device__ __forceinline__ Raw8 load8(const PrepArgs& a, const uint16_t* src, const float* mom, int64_t bi,
+                                      int64_t bj0) {
+    Raw8 r;
+    r.valid = (bi < a.r) && (bj0 < a.c);
+    r.g = u32x4{0u, 0u, 0u, 0u};
+    r.m0 = r.m1 = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (!r.valid) return r;
+    const int64_t off = bi * a.c + bj0;
+    r.g = *reinterpret_cast<const u32x4*>(src + off);
+    if constexpr (MODE != kPrepCast) {
+        r.m0 = *reinterpret_cast<const f32x4*>(mom + off);
+        r.m1 = *(reinterpret_cast<const f32x4*>(mom + off) + 1);
+    }
+    return r;
+}
+
+// Applies the momentum update to loaded elements, stores the buffer and
+// returns the update direction in u[].
+template <int MODE>
+__device__ __forceinline__ void update8(const PrepArgs& a, const Raw8& r, float* mom, int64_t bi, int64_t bj0,
+                                        float (&u)[8], bool (&ok)[8]) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) { ok[e] = valid; u[e] = 0.f; }
-        if (!valid) return;
-        const int64_t off = bi * a.c + bj0;
-        const u32x4 gv = *reinterpret_cast<const u32x4*>(src + off);
-        float g[8];
+    for (int e = 0; e < 8; ++e) { ok[e] = r.valid; u[e] = 0.f; }
+    if (!r.valid) return;
+    float g[8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            g[2 * q] = bf16_to_f32(static_cast<uint16_t>(gv[q] & 0xffffu));
-            g[2 * q + 1] = bf16_to_f32(static_cast<uint16_t>(gv[q] >> 16));
-        }
-        if constexpr (MODE == kPrepCast) {
+    for (int q = 0; q < 4; ++q) {
+        g[2 * q] = bf16_to_f32(static_cast<uint16_t>(r.g[q] & 0xffffu));
+        g[2 * q + 1] = bf16_to_f32(static_cast<uint16_t>(r.g[q] >> 16));
+    }
+    if constexpr (MODE == kPrepCast) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) u[e] = g[e];
-        } else {
-            f32x4* mp4 = reinterpret_cast<f32x4*>(mom + off);
-            f32x4 m0 = mp4[0], m1 = mp4[1];
-            float m[8] = {m0[0], m0[1], m0[2], m0[3], m1[0], m1[1], m1[2], m1[3]};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) u[e] = momentum_update<MODE>(g[e], &m[e], a.mu, a.omm);
-            mp4[0] = f32x4{m[0], m[1], m[2], m[3]};
-            mp4[1] = f32x4{m[4], m[5], m[6], m[7]};
-        }
+        for (int e = 0; e < 8; ++e) u[e] = g[e];
     } else {
+        float m[8] = {r.m0[0], r.m0[1], r.m0[2], r.m0[3], r.m1[0], r.m1[1], r.m1[2], r.m1[3]};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            ok[e] = (bi < a.r) && (bj0 + e < a.c);
-            u[e] = 0.f;
-            if (ok[e]) {
-                const int64_t off = bi * a.c + bj0 + e;
-                const float g = bf16_to_f32(src[off]);
-                u[e] = momentum_update<MODE>(g, mom ? mom + off : nullptr, a.mu, a.omm);
-            }
+        for (int e = 0; e < 8; ++e) u[e] = momentum_update<MODE>(g[e], &m[e], a.mu, a.omm);
+        f32x4* mp4 = reinterpret_cast<f32x4*>(mom + bi * a.c + bj0);
+        *mp4 = f32x4{m[0], m[1], m[2], m[3]};
+        mp4[1] = f32x4{m[4], m[5], m[6], m[7]};
+    }
+}
+
+// Scalar path (stored column count not a multiple of 8).
+template <int MODE>
+__device__ __forceinline__ void load_update8_scalar(const PrepArgs& a, const uint16_t* src, float* mom,
+                                                    int64_t bi, int64_t bj0, float (&u)[8], bool (&ok)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        ok[e] = (bi < a.r) && (bj0 + e < a.c);
+        u[e] = 0.f;
+        if (ok[e]) {
+            const int64_t off = bi * a.c + bj0 + e;
+            const float g = bf16_to_f32(src[off]);
+            u[e] = momentum_update<MODE>(g, mom ? mom + off : nullptr, a.mu, a.omm);
         }
     }
 }
 
 // One 64 x 64 tile of the padded stored-orientation block per workgroup.  The
-// oriented iterate X is that block for wide blocks (written through d) and its
-// transpose for tall ones (written through t, via LDS); the host passes the
-// one destination that applies and null for the other.
-template <int MODE, bool VEC, bool SPLIT>
+// oriented iterate X is that block for wide blocks (written through dh/dl)
+// and its transpose for tall ones (TALL: written through th/tl, via LDS).
+// Both rows' loads are issued before any store, so a thread has its whole
+// share of HBM reads in flight at once.
+template <int MODE, bool VEC, bool SPLIT, bool TALL>
 __global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
-    __shared__ uint16_t lds_hi[T][T + 2];
-    __shared__ uint16_t lds_lo[SPLIT ? T : 1][T + 2];
+    __shared__ uint16_t lds_hi[TALL ? T : 1][T + 2];
+    __shared__ uint16_t lds_lo[(TALL && SPLIT) ? T : 1][T + 2];
     __shared__ float red[4];
 
     const int t = threadIdx.x;
@@ -129,14 +154,20 @@ __global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
     const uint16_t* src = a.src + blk * a.be;
     float* mom = (MODE == kPrepCast) ? nullptr : a.mom + blk * a.be;
     const int64_t pad = a.rp * a.cp;
-    uint16_t* dh = a.dh ? a.dh + blk * pad : nullptr;
-    uint16_t* dl = (SPLIT && a.dl) ? a.dl + blk * pad : nullptr;
-    uint16_t* th = a.th ? a.th + blk * pad : nullptr;
-    uint16_t* tl = (SPLIT && a.tl) ? a.tl + blk * pad : nullptr;
+    uint16_t* dh = TALL ? nullptr : a.dh + blk * pad;
+    uint16_t* dl = (!TALL && SPLIT) ? a.dl + blk * pad : nullptr;
+    uint16_t* th = TALL ? a.th + blk * pad : nullptr;
+    uint16_t* tl = (TALL && SPLIT) ? a.tl + blk * pad : nullptr;
     const int rl = t >> 3;
     const int cl = (t & 7) * 8;
     float ss = 0.f;
 
+    Raw8 raw[2];
+    if constexpr (VEC) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            raw[h] = load8<MODE>(a, src, mom, (int64_t)si * T + rl + 32 * h, (int64_t)sj * T + cl);
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int row = rl + 32 * h;
@@ -144,7 +175,8 @@ __global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
         const int64_t bj0 = (int64_t)sj * T + cl;
         float u[8];
         bool ok[8];
-        load_update8<MODE, VEC>(a, src, mom, bi, bj0, u, ok);
+        if constexpr (VEC) update8<MODE>(a, raw[h], mom, bi, bj0, u, ok);
+        else load_update8_scalar<MODE>(a, src, mom, bi, bj0, u, ok);
         uint16_t hi[8], lo[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -157,7 +189,7 @@ __global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
                 ss = fmaf(hv, hv, ss);
             }
         }
-        if (dh != nullptr) {
+        if constexpr (!TALL) {
             const int64_t o = bi * a.cp + bj0;   // inside the padded block
             u32x4 w;
 #pragma unroll
@@ -168,29 +200,32 @@ __global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
                 for (int q = 0; q < 4; ++q) w[q] = uint32_t(lo[2 * q]) | (uint32_t(lo[2 * q + 1]) << 16);
                 *reinterpret_cast<u32x4*>(dl + o) = w;
             }
-        }
+        } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            lds_hi[row][cl + e] = hi[e];
-            if constexpr (SPLIT) lds_lo[row][cl + e] = lo[e];
+            for (int e = 0; e < 8; ++e) {
+                lds_hi[row][cl + e] = hi[e];
+                if constexpr (SPLIT) lds_lo[row][cl + e] = lo[e];
+            }
         }
     }
 
-    __syncthreads();
+    if constexpr (TALL) {
+        __syncthreads();
 #pragma unroll
-    for (int h = 0; h < 2 && th != nullptr; ++h) {
-        const int row = rl + 32 * h;   // transposed local row = stored local column
-        const int64_t o = ((int64_t)sj * T + row) * a.rp + (int64_t)si * T + cl;
-        u32x4 w;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            w[q] = uint32_t(lds_hi[cl + 2 * q][row]) | (uint32_t(lds_hi[cl + 2 * q + 1][row]) << 16);
-        *reinterpret_cast<u32x4*>(th + o) = w;
-        if constexpr (SPLIT) {
+        for (int h = 0; h < 2; ++h) {
+            const int row = rl + 32 * h;   // transposed local row = stored local column
+            const int64_t o = ((int64_t)sj * T + row) * a.rp + (int64_t)si * T + cl;
+            u32x4 w;
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                w[q] = uint32_t(lds_lo[cl + 2 * q][row]) | (uint32_t(lds_lo[cl + 2 * q + 1][row]) << 16);
-            *reinterpret_cast<u32x4*>(tl + o) = w;
+                w[q] = uint32_t(lds_hi[cl + 2 * q][row]) | (uint32_t(lds_hi[cl + 2 * q + 1][row]) << 16);
+            *reinterpret_cast<u32x4*>(th + o) = w;
+            if constexpr (SPLIT) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    w[q] = uint32_t(lds_lo[cl + 2 * q][row]) | (uint32_t(lds_lo[cl + 2 * q + 1][row]) << 16);
+                *reinterpret_cast<u32x4*>(tl + o) = w;
+            }
         }
     }
 
@@ -224,22 +259,40 @@ struct FinArgs {
     float decay, step;
 };
 
+// Parameters of 8 stored elements (bi, bj0 .. bj0 + 7), vector path.
+struct P8 {
+    f32x4 p0, p1;
+};
+
 template <bool UPDATE, bool VEC>
-__device__ __forceinline__ void finish_store8(const FinArgs& a, float* P, uint16_t* out,
-                                              int64_t bi, int64_t bj0, const float (&o)[8],
-                                              const uint16_t (&bits)[8], bool exact_bits) {
+__device__ __forceinline__ P8 load_p8(const FinArgs& a, const float* P, int64_t bi, int64_t bj0) {
+    P8 r{f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    if constexpr (UPDATE && VEC) {
+        if (bi < a.r && bj0 < a.c) {
+            const f32x4* p4 = reinterpret_cast<const f32x4*>(P + bi * a.c + bj0);
+            r.p0 = *p4;
+            r.p1 = *(p4 + 1);
+        }
+    }
+    return r;
+}
+
+template <bool UPDATE, bool VEC>
+__device__ __forceinline__ void finish_store8(const FinArgs& a, float* P, uint16_t* out, int64_t bi, int64_t bj0,
+                                              const P8& pv, const float (&o)[8], const uint16_t (&bits)[8],
+                                              bool exact_bits) {
     if (bi >= a.r) return;
     if constexpr (VEC) {
         if (bj0 >= a.c) return;
         const int64_t off = bi * a.c + bj0;
         if constexpr (UPDATE) {
-            f32x4* p4 = reinterpret_cast<f32x4*>(P + off);
-            f32x4 p0 = p4[0], p1 = p4[1];
+            f32x4 p0 = pv.p0, p1 = pv.p1;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 p0[e] = fmaf(-a.step, o[e], p0[e] * a.decay);
                 p1[e] = fmaf(-a.step, o[e + 4], p1[e] * a.decay);
             }
+            f32x4* p4 = reinterpret_cast<f32x4*>(P + off);
             p4[0] = p0;
             p4[1] = p1;
         }
@@ -264,6 +317,10 @@ __device__ __forceinline__ void finish_store8(const FinArgs& a, float* P, uint16
     }
 }
 
+// One 64 x 64 tile of the oriented block per workgroup; both rows' loads (the
+// final iterate, and for the update the parameters) are issued before any
+// store.  (Non-temporal loads and stores here measured slower: 5.0-5.3 TB/s
+// against 5.6.)
 template <bool UPDATE, bool TALL, bool VEC, bool SPLIT>
 __global__ __launch_bounds__(256) void k_finish(FinArgs a) {
     __shared__ float lds[TALL ? T : 1][T + 1];
@@ -281,32 +338,38 @@ __global__ __launch_bounds__(256) void k_finish(FinArgs a) {
     const int rl = t >> 3;
     const int cl = (t & 7) * 8;
 
+    u32x4 vh[2], vl[2];
+    P8 pv[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int64_t o = ((int64_t)ti * T + rl + 32 * h) * a.np + (int64_t)tj * T + cl;   // inside the padded buffer
+        vh[h] = *reinterpret_cast<const u32x4*>(xhi + o);
+        vl[h] = u32x4{0u, 0u, 0u, 0u};
+        if constexpr (SPLIT) vl[h] = *reinterpret_cast<const u32x4*>(xlo + o);
+        if constexpr (!TALL) pv[h] = load_p8<UPDATE, VEC>(a, P, (int64_t)ti * T + rl + 32 * h, (int64_t)tj * T + cl);
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int row = rl + 32 * h;
         const int64_t oi = (int64_t)ti * T + row;
         const int64_t oj = (int64_t)tj * T + cl;
-        const int64_t o = oi * a.np + oj;   // always inside the padded buffer
-        const u32x4 vh = *reinterpret_cast<const u32x4*>(xhi + o);
-        u32x4 vl = {0u, 0u, 0u, 0u};
-        if constexpr (SPLIT) vl = *reinterpret_cast<const u32x4*>(xlo + o);
         float v[8];
         uint16_t bits[8];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            bits[2 * q] = static_cast<uint16_t>(vh[q] & 0xffffu);
-            bits[2 * q + 1] = static_cast<uint16_t>(vh[q] >> 16);
+            bits[2 * q] = static_cast<uint16_t>(vh[h][q] & 0xffffu);
+            bits[2 * q + 1] = static_cast<uint16_t>(vh[h][q] >> 16);
             v[2 * q] = bf16_to_f32(bits[2 * q]);
             v[2 * q + 1] = bf16_to_f32(bits[2 * q + 1]);
             if constexpr (SPLIT) {
-                v[2 * q] += bf16_to_f32(static_cast<uint16_t>(vl[q] & 0xffffu));
-                v[2 * q + 1] += bf16_to_f32(static_cast<uint16_t>(vl[q] >> 16));
+                v[2 * q] += bf16_to_f32(static_cast<uint16_t>(vl[h][q] & 0xffffu));
+                v[2 * q + 1] += bf16_to_f32(static_cast<uint16_t>(vl[h][q] >> 16));
             }
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] *= sc;
         if constexpr (!TALL) {
-            finish_store8<UPDATE, VEC>(a, P, out, oi, oj, v, bits, exact_bits);
+            finish_store8<UPDATE, VEC>(a, P, out, oi, oj, pv[h], v, bits, exact_bits);
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -317,6 +380,9 @@ __global__ __launch_bounds__(256) void k_finish(FinArgs a) {
     }
 
     if constexpr (TALL) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            pv[h] = load_p8<UPDATE, VEC>(a, P, (int64_t)tj * T + rl + 32 * h, (int64_t)ti * T + cl);
         __syncthreads();
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -330,7 +396,7 @@ __global__ __launch_bounds__(256) void k_finish(FinArgs a) {
                 v[e] = lds[cl + e][row];
                 bits[e] = ldsb[cl + e][row];
             }
-            finish_store8<UPDATE, VEC>(a, P, out, bi, bj0, v, bits, exact_bits);
+            finish_store8<UPDATE, VEC>(a, P, out, bi, bj0, pv[h], v, bits, exact_bits);
         }
     }
 }
@@ -346,7 +412,7 @@ hipError_t for_block_chunks(int64_t nb, F&& f) {
     return hipSuccess;
 }
 
-template <int MODE, bool VEC, bool SPLIT>
+template <int MODE, bool VEC, bool SPLIT, bool TALL>
 hipError_t run_prep(const Plan& p, const PrepArgs& a, hipStream_t s) {
     const int64_t be = p.r * p.c;
     const int64_t pad = p.mp * p.np;
@@ -359,16 +425,21 @@ hipError_t run_prep(const Plan& p, const PrepArgs& a, hipStream_t s) {
         c.th = a.th ? a.th + b0 * pad : nullptr;
         c.tl = a.tl ? a.tl + b0 * pad : nullptr;
         c.part = a.part + b0 * p.ew_tiles;
-        k_prep<MODE, VEC, SPLIT><<<dim3(static_cast<unsigned>(p.ew_tiles), cnt), dim3(256), 0, s>>>(c);
+        k_prep<MODE, VEC, SPLIT, TALL><<<dim3(static_cast<unsigned>(p.ew_tiles), cnt), dim3(256), 0, s>>>(c);
     });
+}
+
+template <int MODE, bool TALL>
+hipError_t prep_orient(const Plan& p, const PrepArgs& a, hipStream_t s) {
+    const bool vec = (p.c % 8) == 0;
+    const bool split = a.dl != nullptr || a.tl != nullptr;
+    if (vec) return split ? run_prep<MODE, true, true, TALL>(p, a, s) : run_prep<MODE, true, false, TALL>(p, a, s);
+    return split ? run_prep<MODE, false, true, TALL>(p, a, s) : run_prep<MODE, false, false, TALL>(p, a, s);
 }
 
 template <int MODE>
 hipError_t prep_mode(const Plan& p, const PrepArgs& a, hipStream_t s) {
-    const bool vec = (p.c % 8) == 0;
-    const bool split = a.dl != nullptr || a.tl != nullptr;
-    if (vec) return split ? run_prep<MODE, true, true>(p, a, s) : run_prep<MODE, true, false>(p, a, s);
-    return split ? run_prep<MODE, false, true>(p, a, s) : run_prep<MODE, false, false>(p, a, s);
+    return p.tall ? prep_orient<MODE, true>(p, a, s) : prep_orient<MODE, false>(p, a, s);
 }
 
 template <bool UPDATE, bool TALL, bool VEC, bool SPLIT>
