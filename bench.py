@@ -111,6 +111,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the kernel breakdown and NS-only passes")
+    ap.add_argument("--api", choices=("multi", "batched"), default="multi",
+                    help="multi: one muon_step_multi call per step over all matrices (default); "
+                         "batched: one muon_step_batched call per shape group")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run a plain device copy of MIB MiB first (HBM counter calibration)")
     args = ap.parse_args()
@@ -149,7 +152,15 @@ def main():
         state.append((g, P, G, M))
     torch.cuda.synchronize()
 
+    # every matrix of the workload, each a [rows, cols] slice of its group's stack
+    matrices = [dict(params=P[i], grads=G[i], momentum_buf=M[i], view_blocks=g.view_blocks)
+                for g, P, G, M in state for i in range(g.count)]
+
     def step():
+        if args.api == "multi":
+            nsm.muon_step_multi(matrices, lr=wl.lr, weight_decay=wl.weight_decay, momentum=wl.momentum,
+                                ns_steps=wl.ns_steps, precision="fast")
+            return
         for g, P, G, M in state:
             nsm.muon_step_batched(P, G, M, lr=wl.lr, weight_decay=wl.weight_decay, momentum=wl.momentum,
                                   view_blocks=g.view_blocks, ns_steps=wl.ns_steps, precision=g.precision)

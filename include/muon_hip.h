@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 1
+#define MUON_ABI_VERSION 2
 
 typedef enum muon_status {
     MUON_OK = 0,
@@ -127,6 +127,50 @@ muon_status muon_step_batched(float* params, const void* grads, float* momentum_
                               const muon_ns_config* cfg, void* update_out,
                               void* workspace, size_t workspace_bytes,
                               void* stream);
+
+/* One parameter matrix of a multi-matrix step, each with its own buffers
+ * (row-major, contiguous).  The pages' optimizer steps every matrix with its
+ * own lr_mul / wd_mul ([CS] section 4); params, grads, momentum_buf and
+ * update_out are as in muon_step_batched for a batch of one. */
+typedef struct muon_matrix {
+    float* params;          /* in/out fp32 [rows, cols]                      */
+    const void* grads;      /* in     bf16 [rows, cols]                      */
+    float* momentum_buf;    /* in/out fp32 [rows, cols]                      */
+    void* update_out;       /* optional out bf16 [rows, cols] (O); NULL skips */
+    int64_t rows, cols;
+    int32_t view_blocks;    /* as in muon_step_batched                       */
+    float lr_mul, wd_mul;   /* finite                                        */
+} muon_matrix;
+
+/* Bytes of workspace muon_step_multi needs for these matrices and config
+ * (cfg NULL = defaults); 0 when count is 0 or every block is small, and
+ * (size_t)-1 for an invalid matrix shape or count. */
+size_t muon_step_multi_workspace_bytes(const muon_matrix* mats, int32_t count,
+                                       const muon_ns_config* cfg);
+
+/*
+ * One Muon step for `count` matrices of any shapes, each with its own buffers
+ * (the multi-matrix form of muon_step_batched; [CS] sections 1, 2.2 and 4):
+ * per matrix i, the update of muon_step_batched with its rows, cols,
+ * view_blocks, lr_mul and wd_mul and the shared lr, weight_decay, momentum,
+ * nesterov and cfg.  Matrices of one (rows, cols, view_blocks) shape are
+ * stepped as one batch.  Batches whose NS blocks have the same padded
+ * smaller side run their Newton-Schulz loops together, products of equal
+ * reduction length sharing kernel launches, while their workspaces together
+ * stay within 160 MB (so they stay cache-resident); the others run one after
+ * the other and reuse one workspace region.  Each matrix's result is bitwise
+ * the one muon_step_batched gives it.
+ *   mats     host array of `count` descriptors, read during the call only
+ *   No two buffers of any matrices may overlap (MUON_ERR_INVALID_ARG).
+ *   Alignment: 16 bytes when a matrix's NS blocks take the vector path (more
+ *   than 32 rows and columns or more than 4096 elements, and cols/view_blocks
+ *   a multiple of 8), else 4 bytes (fp32) and 2 bytes (bf16).
+ */
+muon_status muon_step_multi(const muon_matrix* mats, int32_t count,
+                            float lr, float weight_decay, float momentum,
+                            int32_t nesterov, const muon_ns_config* cfg,
+                            void* workspace, size_t workspace_bytes,
+                            void* stream);
 
 /* Kernel timing (diagnostics).  Kernel families of the library: */
 typedef enum muon_kernel_kind {

@@ -9,7 +9,9 @@ calls raise.
 Entry points (same names as the C ABI):
     ns_orthogonalize_batched(x, out=None, *, view_blocks=1, ...)
     muon_step_batched(params, grads, momentum_buf, *, lr, weight_decay, momentum, ...)
+    muon_step_multi(matrices, *, lr, weight_decay, momentum, ...)
     muon_workspace_bytes(batch, rows, cols, view_blocks=1, cfg=None)
+    muon_step_multi_workspace_bytes(matrices, cfg=None)
     muon_ns_config_default(), muon_last_error(), muon_abi_version()
 """
 from __future__ import annotations
@@ -22,14 +24,15 @@ from typing import Optional, Tuple
 __all__ = [
     "MuonNSConfig", "MuonError", "LIB_PATH", "EXPORTED_SYMBOLS", "load_library",
     "muon_ns_config_default", "muon_workspace_bytes", "ns_orthogonalize_batched",
-    "muon_step_batched", "muon_timing_enable", "muon_timing_collect", "muon_last_error",
-    "muon_abi_version", "make_config", "KERNEL_KINDS",
+    "muon_step_batched", "muon_step_multi", "muon_step_multi_workspace_bytes", "MuonMatrix",
+    "muon_timing_enable", "muon_timing_collect", "muon_last_error", "muon_abi_version", "make_config",
+    "KERNEL_KINDS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmuon_hip.so")
 EXPORTED_SYMBOLS = ("muon_ns_config_default", "muon_workspace_bytes", "ns_orthogonalize_batched",
-                    "muon_step_batched", "muon_timing_enable", "muon_timing_collect",
-                    "muon_last_error", "muon_abi_version")
+                    "muon_step_batched", "muon_step_multi_workspace_bytes", "muon_step_multi",
+                    "muon_timing_enable", "muon_timing_collect", "muon_last_error", "muon_abi_version")
 KERNEL_KINDS = ("prep", "norm_finalize", "gram", "poly", "bx", "finish", "small")
 
 MUON_OK = 0
@@ -41,6 +44,13 @@ PRECISIONS = {"fast": 0, "accurate": 1}
 class MuonNSConfig(ctypes.Structure):
     _fields_ = [("ns_steps", ctypes.c_int32), ("a", ctypes.c_float), ("b", ctypes.c_float),
                 ("c", ctypes.c_float), ("eps", ctypes.c_float), ("precision", ctypes.c_int32)]
+
+
+class MuonMatrix(ctypes.Structure):
+    """muon_matrix of the C ABI: one matrix of a multi-matrix step."""
+    _fields_ = [("params", ctypes.c_void_p), ("grads", ctypes.c_void_p), ("momentum_buf", ctypes.c_void_p),
+                ("update_out", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("view_blocks", ctypes.c_int32), ("lr_mul", ctypes.c_float), ("wd_mul", ctypes.c_float)]
 
 
 class MuonError(RuntimeError):
@@ -73,6 +83,11 @@ def load_library():
         lib.muon_step_batched.argtypes = [vp, vp, vp, i64, i64, i64, i32, f32, f32, f32, i32, f32, f32,
                                           cfgp, vp, vp, ctypes.c_size_t, vp]
         lib.muon_step_batched.restype = ctypes.c_int
+        matp = ctypes.POINTER(MuonMatrix)
+        lib.muon_step_multi_workspace_bytes.argtypes = [matp, i32, cfgp]
+        lib.muon_step_multi_workspace_bytes.restype = ctypes.c_size_t
+        lib.muon_step_multi.argtypes = [matp, i32, f32, f32, f32, i32, cfgp, vp, ctypes.c_size_t, vp]
+        lib.muon_step_multi.restype = ctypes.c_int
         lib.muon_timing_enable.argtypes = [ctypes.c_uint32]
         lib.muon_timing_enable.restype = ctypes.c_int
         lib.muon_timing_collect.argtypes = [ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]
@@ -245,3 +260,70 @@ def muon_step_batched(params, grads, momentum_buf, *, lr: float, weight_decay: f
             update_out.data_ptr() if update_out is not None else None,
             ws.data_ptr() if ws is not None else None, nbytes, stream))
     return params
+
+
+def _matrix_array(matrices, device):
+    """ctypes array of MuonMatrix from (params, grads, momentum_buf) tuples or dicts with
+    those keys and optional update_out, view_blocks, lr_mul, wd_mul."""
+    import torch
+    arr = (MuonMatrix * max(1, len(matrices)))()
+    keep = []
+    for i, m in enumerate(matrices):
+        if not isinstance(m, dict):
+            m = dict(zip(("params", "grads", "momentum_buf"), m))
+        P, G, M = m["params"], m["grads"], m["momentum_buf"]
+        _require(P, f"matrices[{i}].params", torch.float32, device)
+        _require(G, f"matrices[{i}].grads", torch.bfloat16, device)
+        _require(M, f"matrices[{i}].momentum_buf", torch.float32, device)
+        if P.dim() != 2 or G.shape != P.shape or M.shape != P.shape:
+            raise ValueError(f"matrices[{i}]: params, grads and momentum_buf must be one [rows, cols] shape")
+        out = m.get("update_out")
+        if out is not None:
+            _require(out, f"matrices[{i}].update_out", torch.bfloat16, device)
+            if out.shape != P.shape:
+                raise ValueError(f"matrices[{i}].update_out must have the shape of params")
+        e = arr[i]
+        e.params, e.grads, e.momentum_buf = P.data_ptr(), G.data_ptr(), M.data_ptr()
+        e.update_out = out.data_ptr() if out is not None else None
+        e.rows, e.cols = P.shape
+        e.view_blocks = int(m.get("view_blocks", 1))
+        e.lr_mul = float(m.get("lr_mul", 1.0))
+        e.wd_mul = float(m.get("wd_mul", 1.0))
+        keep.append(m)
+    return arr, keep
+
+
+def muon_step_multi_workspace_bytes(matrices, cfg: Optional[MuonNSConfig] = None) -> int:
+    if not matrices:
+        return 0
+    first = matrices[0] if isinstance(matrices[0], dict) else {"params": matrices[0][0]}
+    arr, _ = _matrix_array(matrices, first["params"].device)
+    lib = load_library()
+    n = lib.muon_step_multi_workspace_bytes(arr, len(matrices), ctypes.byref(cfg) if cfg is not None else None)
+    if n == ctypes.c_size_t(-1).value:
+        raise MuonError(2, lib.muon_last_error().decode())
+    return int(n)
+
+
+def muon_step_multi(matrices, *, lr: float, weight_decay: float, momentum: float, nesterov: bool = True,
+                    ns_steps: int = 5, coeffs: Optional[Tuple[float, float, float]] = None,
+                    eps: Optional[float] = None, precision: str = "fast", cfg: Optional[MuonNSConfig] = None):
+    """One in-place Muon step on a list of matrices, each (params fp32, grads bf16, momentum fp32)
+    [rows, cols] or a dict with those keys and optional update_out, view_blocks, lr_mul, wd_mul."""
+    import torch
+    if not matrices:
+        return
+    first = matrices[0] if isinstance(matrices[0], dict) else {"params": matrices[0][0]}
+    device = first["params"].device
+    arr, _keep = _matrix_array(matrices, device)
+    cfg = cfg if cfg is not None else make_config(ns_steps, coeffs, eps, precision)
+    lib = load_library()
+    with torch.cuda.device(device):
+        stream = torch.cuda.current_stream(device).cuda_stream
+        nbytes = lib.muon_step_multi_workspace_bytes(arr, len(matrices), ctypes.byref(cfg))
+        if nbytes == ctypes.c_size_t(-1).value:
+            raise MuonError(2, lib.muon_last_error().decode())
+        ws = _workspace(device, stream, int(nbytes))
+        _check(lib.muon_step_multi(arr, len(matrices), float(lr), float(weight_decay), float(momentum),
+                                   1 if nesterov else 0, ctypes.byref(cfg),
+                                   ws.data_ptr() if ws is not None else None, int(nbytes), stream))

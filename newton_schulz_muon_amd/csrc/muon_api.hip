@@ -11,6 +11,7 @@
 //                     never materialised
 //   k_finish          NS output, or the parameter update (+ optional O)
 // Small blocks (m <= 32, m n <= 4096) run the whole step in one k_small launch.
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <map>
@@ -270,6 +271,154 @@ muon_status common_checks(const Plan& p, void* ws, size_t ws_bytes) {
     return MUON_OK;
 }
 
+
+// ---------------------------------------------------------------- multi-matrix step
+// Matrices of one (rows, cols, view_blocks) shape, stepped as one batch.
+struct ShapeGroup {
+    int64_t R = 0, C = 0;
+    int32_t v = 1;
+    std::vector<int32_t> mats;   // indices into the caller's array
+    Plan plan;
+    int wave = 0;          // groups of one wave run their NS loops together
+    size_t ws_off = 0;     // offset of its workspace within the (shared) wave region
+};
+
+// Working-set budget of one wave: the NS workspaces of the groups that share
+// launches stay resident in the 256 MB Infinity Cache only if together they
+// fit well inside it (interleaving two groups of 141 MB and 234 MB measured
+// slower than running them one after the other).
+constexpr size_t kWaveBudget = size_t(160) << 20;
+
+muon_status plan_multi(const muon_matrix* mats, int32_t count, const muon_ns_config& cfg,
+                       std::vector<ShapeGroup>& groups, size_t& total) {
+    groups.clear();
+    total = 0;
+    if (count < 0) return fail(MUON_ERR_INVALID_ARG, "count %d < 0", count);
+    if (count > 0 && mats == nullptr) return fail(MUON_ERR_INVALID_ARG, "matrices must be non-null");
+    std::map<std::tuple<int64_t, int64_t, int32_t>, size_t> index;
+    for (int32_t i = 0; i < count; ++i) {
+        const muon_matrix& m = mats[i];
+        Plan probe;
+        const muon_status st = make_plan(1, m.rows, m.cols, m.view_blocks, cfg, probe);
+        if (st != MUON_OK) return fail(st, "matrix %d: %s", i, g_err.c_str());
+        const auto key = std::make_tuple(m.rows, m.cols, m.view_blocks);
+        auto it = index.find(key);
+        if (it == index.end()) {
+            it = index.emplace(key, groups.size()).first;
+            ShapeGroup g;
+            g.R = m.rows;
+            g.C = m.cols;
+            g.v = m.view_blocks;
+            groups.push_back(g);
+        }
+        groups[it->second].mats.push_back(i);
+    }
+    for (ShapeGroup& g : groups) {
+        const muon_status st = make_plan(int64_t(g.mats.size()), g.R, g.C, g.v, cfg, g.plan);
+        if (st != MUON_OK) return st;
+    }
+    // Waves: a large group joins the first wave of its padded side m (the
+    // products share launches by m) whose workspace stays within the budget
+    // and which has room for it; else it opens a new wave.  Waves run one
+    // after the other and reuse one workspace region.
+    struct WaveInfo { int64_t mp; size_t bytes; int n; };
+    std::vector<WaveInfo> waves;
+    for (ShapeGroup& g : groups) {
+        if (g.plan.small) continue;
+        const size_t need = align256(g.plan.total);
+        int w = -1;
+        for (size_t k = 0; k < waves.size() && w < 0; ++k)
+            if (waves[k].mp == g.plan.mp && waves[k].n < kMaxGemmProblems && waves[k].bytes + need <= kWaveBudget)
+                w = int(k);
+        if (w < 0) {
+            w = int(waves.size());
+            waves.push_back({g.plan.mp, 0, 0});
+        }
+        g.wave = w;
+        g.ws_off = waves[w].bytes;
+        waves[w].bytes += need;
+        waves[w].n += 1;
+    }
+    for (const WaveInfo& w : waves) total = std::max(total, w.bytes);
+    return MUON_OK;
+}
+
+// Vector-path blocks (not small, block width a multiple of 8) are read and
+// written in 16-byte pieces; the others element by element.
+muon_status check_multi_buffers(const muon_matrix* mats, int32_t count, const std::vector<ShapeGroup>& groups) {
+    struct Range { uintptr_t a, b; int32_t mat; };
+    std::vector<Range> ranges;
+    ranges.reserve(size_t(count) * 4);
+    std::vector<char> vec16(size_t(count), 0);
+    for (const ShapeGroup& g : groups)
+        for (int32_t i : g.mats) vec16[i] = !g.plan.small && g.plan.c % 8 == 0;
+    for (int32_t i = 0; i < count; ++i) {
+        const muon_matrix& m = mats[i];
+        if (!m.params || !m.grads || !m.momentum_buf)
+            return fail(MUON_ERR_INVALID_ARG, "matrix %d: params, grads and momentum_buf must be non-null", i);
+        const uintptr_t a32 = vec16[i] ? 16 : 4, a16 = vec16[i] ? 16 : 2;
+        if (!aligned(m.params, a32) || !aligned(m.grads, a16) || !aligned(m.momentum_buf, a32) ||
+            (m.update_out && !aligned(m.update_out, a16)))
+            return fail(MUON_ERR_ALIGNMENT, "matrix %d: data pointers must be %s aligned", i,
+                        vec16[i] ? "16-byte" : "element-");
+        if (!std::isfinite(m.lr_mul) || !std::isfinite(m.wd_mul))
+            return fail(MUON_ERR_INVALID_ARG, "matrix %d: lr_mul and wd_mul must be finite", i);
+        const size_t n = size_t(m.rows) * size_t(m.cols);
+        auto add = [&](const void* p, size_t bytes) {
+            const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+            ranges.push_back({a, a + bytes, i});
+        };
+        add(m.params, 4 * n);
+        add(m.grads, 2 * n);
+        add(m.momentum_buf, 4 * n);
+        if (m.update_out) add(m.update_out, 2 * n);
+    }
+    std::sort(ranges.begin(), ranges.end(), [](const Range& x, const Range& y) { return x.a < y.a; });
+    for (size_t k = 1; k < ranges.size(); ++k)
+        if (ranges[k].a < ranges[k - 1].b)
+            return fail(MUON_ERR_INVALID_ARG, "buffers of matrices %d and %d overlap", ranges[k - 1].mat,
+                        ranges[k].mat);
+    return MUON_OK;
+}
+
+// Offsets a group's buffers to the blocks of matrices [m0, m0 + cnt).
+Buffers chunk_buffers(const Plan& p, const Buffers& b, int64_t m0) {
+    Buffers c = b;
+    const int64_t blk0 = m0 * p.v;
+    const size_t xe = size_t(p.mp) * size_t(p.np);
+    for (int i = 0; i < 2; ++i) {
+        c.xh[i] = b.xh[i] + blk0 * xe;
+        c.xl[i] = b.xl[i] ? b.xl[i] + blk0 * xe : nullptr;
+    }
+    c.part = b.part + blk0 * p.ew_tiles;
+    c.scale = b.scale + 2 * blk0;
+    return c;
+}
+
+Plan chunk_plan(const Plan& p, int64_t cnt) {
+    Plan c = p;
+    c.batch = cnt;
+    c.nb = cnt * p.v;
+    return c;
+}
+
+MatTable make_table(const muon_matrix* mats, const ShapeGroup& g, size_t m0, size_t cnt, float lr, float wd,
+                    double aspect) {
+    MatTable t;
+    t.n = static_cast<int>(cnt);
+    t.v = g.v;
+    for (size_t k = 0; k < cnt; ++k) {
+        const muon_matrix& m = mats[g.mats[m0 + k]];
+        t.src[k] = static_cast<const uint16_t*>(m.grads);
+        t.mom[k] = m.momentum_buf;
+        t.P[k] = m.params;
+        t.out[k] = static_cast<uint16_t*>(m.update_out);
+        t.decay[k] = static_cast<float>(1.0 - double(lr) * double(wd) * double(m.wd_mul));
+        t.step[k] = static_cast<float>(double(lr) * aspect * double(m.lr_mul));
+    }
+    return t;
+}
+
 }  // namespace
 }  // namespace muon
 
@@ -411,6 +560,171 @@ muon_status muon_step_batched(float* params, const void* grads, float* momentum_
                              static_cast<uint16_t*>(update_out), s);
     });
     return e == hipSuccess ? MUON_OK : hip_fail(e, "k_finish launch");
+}
+
+size_t muon_step_multi_workspace_bytes(const muon_matrix* mats, int32_t count, const muon_ns_config* cfg_in) {
+    g_err.clear();
+    const muon_ns_config cfg = cfg_in ? *cfg_in : default_config();
+    if (validate_config(cfg) != MUON_OK) return size_t(-1);
+    std::vector<ShapeGroup> groups;
+    size_t total = 0;
+    if (plan_multi(mats, count, cfg, groups, total) != MUON_OK) return size_t(-1);
+    return total;
+}
+
+muon_status muon_step_multi(const muon_matrix* mats, int32_t count, float lr, float weight_decay, float momentum,
+                            int32_t nesterov, const muon_ns_config* cfg_in, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+    g_err.clear();
+    const muon_ns_config cfg = cfg_in ? *cfg_in : default_config();
+    muon_status st = validate_config(cfg);
+    if (st != MUON_OK) return st;
+    if (!std::isfinite(lr) || !std::isfinite(weight_decay))
+        return fail(MUON_ERR_INVALID_ARG, "lr and weight_decay must be finite");
+    if (!(momentum >= 0.f && momentum <= 1.f)) return fail(MUON_ERR_INVALID_ARG, "momentum must be in [0, 1]");
+    std::vector<ShapeGroup> groups;
+    size_t total = 0;
+    st = plan_multi(mats, count, cfg, groups, total);
+    if (st != MUON_OK) return st;
+    if (count == 0) return MUON_OK;
+    st = check_multi_buffers(mats, count, groups);
+    if (st != MUON_OK) return st;
+    if (total > 0) {
+        if (workspace == nullptr || workspace_bytes < total)
+            return fail(MUON_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
+                        total);
+        if (!aligned(workspace, 256)) return fail(MUON_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
+    }
+    st = check_device();
+    if (st != MUON_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const PrepMode mode = nesterov ? kPrepNesterov : kPrepPlain;
+
+    // Small groups: the whole step in one launch per pointer table.
+    for (const ShapeGroup& g : groups) {
+        if (!g.plan.small) continue;
+        const double aspect = std::sqrt(std::fmax(1.0, double(g.R) / double(g.C)));
+        for (size_t m0 = 0; m0 < g.mats.size(); m0 += kTabMax) {
+            const size_t cnt = std::min<size_t>(kTabMax, g.mats.size() - m0);
+            const MatTable tab = make_table(mats, g, m0, cnt, lr, weight_decay, aspect);
+            const Plan pc = chunk_plan(g.plan, int64_t(cnt));
+            SmallStep ss;
+            ss.mu = momentum;
+            ss.mode = mode;
+            ss.ns_steps = cfg.ns_steps;
+            ss.a = cfg.a;
+            ss.b = cfg.b;
+            ss.c = cfg.c;
+            ss.eps = cfg.eps;
+            const hipError_t e = timed(MUON_KERNEL_SMALL, s, [&] { return launch_small(pc, ss, s, &tab); });
+            if (e != hipSuccess) return hip_fail(e, "k_small launch");
+        }
+    }
+
+    // Large groups, one wave after the other.
+    int nwaves = 0;
+    for (const ShapeGroup& g : groups)
+        if (!g.plan.small) nwaves = std::max(nwaves, g.wave + 1);
+    std::vector<Buffers> bufs(groups.size());
+    for (int w = 0; w < nwaves; ++w) {
+        std::vector<size_t> wave;
+        for (size_t gi = 0; gi < groups.size(); ++gi)
+            if (!groups[gi].plan.small && groups[gi].wave == w) wave.push_back(gi);
+
+        // Momentum + cast to the iterate, per group in chunks of pointer tables.
+        for (size_t gi : wave) {
+            const ShapeGroup& g = groups[gi];
+            const Plan& p = g.plan;
+            const double aspect = std::sqrt(std::fmax(1.0, double(g.R) / double(g.C)));
+            bufs[gi] = carve(p, static_cast<char*>(workspace) + g.ws_off);
+            for (size_t m0 = 0; m0 < g.mats.size(); m0 += kTabMax) {
+                const size_t cnt = std::min<size_t>(kTabMax, g.mats.size() - m0);
+                const MatTable tab = make_table(mats, g, m0, cnt, lr, weight_decay, aspect);
+                const Plan pc = chunk_plan(p, int64_t(cnt));
+                const Buffers bc = chunk_buffers(p, bufs[gi], int64_t(m0));
+                const hipError_t e = timed(MUON_KERNEL_PREP, s, [&] {
+                    return launch_prep(pc, mode, nullptr, nullptr, momentum, bc.xh[0], bc.xl[0], bc.part, s, &tab);
+                });
+                if (e != hipSuccess) return hip_fail(e, "k_prep launch");
+            }
+            const hipError_t e = timed(MUON_KERNEL_NORM_FINALIZE, s, [&] {
+                return launch_norm_finalize(p, bufs[gi].part, bufs[gi].scale, cfg.eps, s);
+            });
+            if (e != hipSuccess) return hip_fail(e, "k_norm_finalize launch");
+        }
+
+        // NS iterations: products of equal reduction length share launches.
+        auto buckets = [&](auto key) {
+            std::vector<std::vector<size_t>> out;
+            std::map<int64_t, size_t> at;
+            for (size_t gi : wave) {
+                const int64_t k = key(groups[gi].plan);
+                auto it = at.find(k);
+                if (it == at.end() || out[it->second].size() == size_t(kMaxGemmProblems)) {
+                    at[k] = out.size();
+                    out.emplace_back();
+                    it = at.find(k);
+                }
+                out[it->second].push_back(gi);
+            }
+            return out;
+        };
+        const auto by_np = buckets([](const Plan& p) { return p.np; });
+        const auto by_mp = buckets([](const Plan& p) { return p.mp; });
+        int cur = 0;
+        for (int it = 0; it < cfg.ns_steps; ++it) {
+            for (const auto& bk : by_np) {
+                GramOp ops[kMaxGemmProblems];
+                for (size_t k = 0; k < bk.size(); ++k) {
+                    const Buffers& b = bufs[bk[k]];
+                    ops[k] = GramOp{&groups[bk[k]].plan, b.xh[cur], b.a, it == 0 ? b.scale : nullptr};
+                }
+                const hipError_t e = timed(MUON_KERNEL_GRAM, s, [&] { return launch_gram(ops, int(bk.size()), s); });
+                if (e != hipSuccess) return hip_fail(e, "k_gemm<gram> launch");
+            }
+            for (const auto& bk : by_mp) {
+                PolyOp ops[kMaxGemmProblems];
+                for (size_t k = 0; k < bk.size(); ++k) {
+                    const Buffers& b = bufs[bk[k]];
+                    ops[k] = PolyOp{&groups[bk[k]].plan, b.a, b.bh, b.bl};
+                }
+                const hipError_t e = timed(MUON_KERNEL_POLY, s, [&] {
+                    return launch_poly(ops, int(bk.size()), cfg.a, cfg.b, cfg.c, s);
+                });
+                if (e != hipSuccess) return hip_fail(e, "k_gemm<poly> launch");
+            }
+            for (const auto& bk : by_mp) {
+                BxOp ops[kMaxGemmProblems];
+                for (size_t k = 0; k < bk.size(); ++k) {
+                    const Buffers& b = bufs[bk[k]];
+                    ops[k] = BxOp{&groups[bk[k]].plan, b.bh, b.bl, b.xh[cur], b.xl[cur], b.xh[cur ^ 1],
+                                  b.xl[cur ^ 1], it == 0 ? b.scale : nullptr};
+                }
+                const hipError_t e = timed(MUON_KERNEL_BX, s, [&] { return launch_bx(ops, int(bk.size()), s); });
+                if (e != hipSuccess) return hip_fail(e, "k_gemm<bx> launch");
+            }
+            cur ^= 1;
+        }
+
+        // Update, per group in chunks.
+        for (size_t gi : wave) {
+            const ShapeGroup& g = groups[gi];
+            const Plan& p = g.plan;
+            const double aspect = std::sqrt(std::fmax(1.0, double(g.R) / double(g.C)));
+            for (size_t m0 = 0; m0 < g.mats.size(); m0 += kTabMax) {
+                const size_t cnt = std::min<size_t>(kTabMax, g.mats.size() - m0);
+                const MatTable tab = make_table(mats, g, m0, cnt, lr, weight_decay, aspect);
+                const Plan pc = chunk_plan(p, int64_t(cnt));
+                const Buffers bc = chunk_buffers(p, bufs[gi], int64_t(m0));
+                const hipError_t e = timed(MUON_KERNEL_FINISH, s, [&] {
+                    return launch_finish(pc, bc.xh[cur], bc.xl[cur], cfg.ns_steps == 0 ? bc.scale : nullptr, nullptr,
+                                         1.f, 0.f, nullptr, s, &tab);
+                });
+                if (e != hipSuccess) return hip_fail(e, "k_finish launch");
+            }
+        }
+    }
+    return MUON_OK;
 }
 
 muon_status muon_timing_enable(uint32_t kernel_mask) {

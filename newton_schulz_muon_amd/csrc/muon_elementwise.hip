@@ -30,6 +30,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int T = kEwTile;
 
 struct PrepArgs {
+    MatTable tab;          // per-matrix buffers (tab.n > 0) or strided (src, mom)
     const uint16_t* src;   // stored bf16 (gradients or x), this launch's first block
     float* mom;            // stored fp32 momentum buffer
     uint16_t* dh;          // padded copy in stored orientation [rp][cp] (hi, lo)
@@ -151,8 +152,16 @@ __global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
     const int64_t blk = blockIdx.y;
     const int tile = blockIdx.x;
     const int si = tile / a.tiles_j, sj = tile % a.tiles_j;
-    const uint16_t* src = a.src + blk * a.be;
-    float* mom = (MODE == kPrepCast) ? nullptr : a.mom + blk * a.be;
+    const uint16_t* src;
+    float* mom = nullptr;
+    if (a.tab.n > 0) {
+        const int64_t mi = blk / a.tab.v, sub = blk % a.tab.v;
+        src = a.tab.src[mi] + sub * a.be;
+        if constexpr (MODE != kPrepCast) mom = a.tab.mom[mi] + sub * a.be;
+    } else {
+        src = a.src + blk * a.be;
+        if constexpr (MODE != kPrepCast) mom = a.mom + blk * a.be;
+    }
     const int64_t pad = a.rp * a.cp;
     uint16_t* dh = TALL ? nullptr : a.dh + blk * pad;
     uint16_t* dl = (!TALL && SPLIT) ? a.dl + blk * pad : nullptr;
@@ -249,6 +258,7 @@ __global__ __launch_bounds__(256) void k_norm_finalize(const float* part, float*
 }
 
 struct FinArgs {
+    MatTable tab;          // per-matrix buffers and scalars (tab.n > 0) or strided (P, out)
     const uint16_t* xhi;   // oriented padded final iterate
     const uint16_t* xlo;
     const float* scale;    // [nb][2] or null
@@ -280,7 +290,7 @@ __device__ __forceinline__ P8 load_p8(const FinArgs& a, const float* P, int64_t 
 template <bool UPDATE, bool VEC>
 __device__ __forceinline__ void finish_store8(const FinArgs& a, float* P, uint16_t* out, int64_t bi, int64_t bj0,
                                               const P8& pv, const float (&o)[8], const uint16_t (&bits)[8],
-                                              bool exact_bits) {
+                                              bool exact_bits, float decay, float step) {
     if (bi >= a.r) return;
     if constexpr (VEC) {
         if (bj0 >= a.c) return;
@@ -289,8 +299,8 @@ __device__ __forceinline__ void finish_store8(const FinArgs& a, float* P, uint16
             f32x4 p0 = pv.p0, p1 = pv.p1;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                p0[e] = fmaf(-a.step, o[e], p0[e] * a.decay);
-                p1[e] = fmaf(-a.step, o[e + 4], p1[e] * a.decay);
+                p0[e] = fmaf(-step, o[e], p0[e] * decay);
+                p1[e] = fmaf(-step, o[e + 4], p1[e] * decay);
             }
             f32x4* p4 = reinterpret_cast<f32x4*>(P + off);
             p4[0] = p0;
@@ -311,7 +321,7 @@ __device__ __forceinline__ void finish_store8(const FinArgs& a, float* P, uint16
         for (int e = 0; e < 8; ++e) {
             if (bj0 + e >= a.c) break;
             const int64_t off = bi * a.c + bj0 + e;
-            if constexpr (UPDATE) P[off] = fmaf(-a.step, o[e], P[off] * a.decay);
+            if constexpr (UPDATE) P[off] = fmaf(-step, o[e], P[off] * decay);
             if (out != nullptr) out[off] = exact_bits ? bits[e] : f32_to_bf16(o[e]);
         }
     }
@@ -331,8 +341,19 @@ __global__ __launch_bounds__(256) void k_finish(FinArgs a) {
     const int ti = tile / a.tiles_j, tj = tile % a.tiles_j;
     const uint16_t* xhi = a.xhi + blk * a.mp * a.np;
     const uint16_t* xlo = SPLIT ? a.xlo + blk * a.mp * a.np : nullptr;
-    float* P = UPDATE ? a.P + blk * a.be : nullptr;
-    uint16_t* out = a.out ? a.out + blk * a.be : nullptr;
+    float* P = nullptr;
+    uint16_t* out = nullptr;
+    float decay = a.decay, step = a.step;
+    if (a.tab.n > 0) {
+        const int64_t mi = blk / a.tab.v, sub = blk % a.tab.v;
+        if constexpr (UPDATE) P = a.tab.P[mi] + sub * a.be;
+        out = a.tab.out[mi] ? a.tab.out[mi] + sub * a.be : nullptr;
+        decay = a.tab.decay[mi];
+        step = a.tab.step[mi];
+    } else {
+        if constexpr (UPDATE) P = a.P + blk * a.be;
+        out = a.out ? a.out + blk * a.be : nullptr;
+    }
     const float sc = a.scale ? a.scale[2 * blk] : 1.0f;
     const bool exact_bits = !SPLIT && a.scale == nullptr;
     const int rl = t >> 3;
@@ -369,7 +390,7 @@ __global__ __launch_bounds__(256) void k_finish(FinArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] *= sc;
         if constexpr (!TALL) {
-            finish_store8<UPDATE, VEC>(a, P, out, oi, oj, pv[h], v, bits, exact_bits);
+            finish_store8<UPDATE, VEC>(a, P, out, oi, oj, pv[h], v, bits, exact_bits, decay, step);
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -396,7 +417,7 @@ __global__ __launch_bounds__(256) void k_finish(FinArgs a) {
                 v[e] = lds[cl + e][row];
                 bits[e] = ldsb[cl + e][row];
             }
-            finish_store8<UPDATE, VEC>(a, P, out, bi, bj0, pv[h], v, bits, exact_bits);
+            finish_store8<UPDATE, VEC>(a, P, out, bi, bj0, pv[h], v, bits, exact_bits, decay, step);
         }
     }
 }
@@ -418,7 +439,7 @@ hipError_t run_prep(const Plan& p, const PrepArgs& a, hipStream_t s) {
     const int64_t pad = p.mp * p.np;
     return for_block_chunks(p.nb, [&](int64_t b0, unsigned cnt) {
         PrepArgs c = a;
-        c.src = a.src + b0 * be;
+        c.src = a.src ? a.src + b0 * be : nullptr;
         c.mom = a.mom ? a.mom + b0 * be : nullptr;
         c.dh = a.dh ? a.dh + b0 * pad : nullptr;
         c.dl = a.dl ? a.dl + b0 * pad : nullptr;
@@ -474,8 +495,13 @@ hipError_t finish_mode(const Plan& p, const FinArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_prep(const Plan& p, PrepMode mode, const uint16_t* src, float* mom, float mu,
-                       uint16_t* x_hi, uint16_t* x_lo, float* partials, hipStream_t s) {
+                       uint16_t* x_hi, uint16_t* x_lo, float* partials, hipStream_t s, const MatTable* tab) {
     PrepArgs a;
+    if (tab != nullptr) {
+        if (tab->n < 1 || tab->n > kTabMax || tab->v != p.v || p.nb != int64_t(tab->n) * tab->v)
+            return hipErrorInvalidValue;
+        a.tab = *tab;
+    }
     a.src = src;
     a.mom = mom;
     // wide block: X is the stored orientation; tall block: X is its transpose
@@ -510,8 +536,13 @@ hipError_t launch_norm_finalize(const Plan& p, const float* partials, float* sca
 
 hipError_t launch_finish(const Plan& p, const uint16_t* x_hi, const uint16_t* x_lo,
                          const float* scale, float* params, float decay, float step,
-                         uint16_t* out, hipStream_t s) {
+                         uint16_t* out, hipStream_t s, const MatTable* tab) {
     FinArgs a;
+    if (tab != nullptr) {
+        if (tab->n < 1 || tab->n > kTabMax || tab->v != p.v || p.nb != int64_t(tab->n) * tab->v)
+            return hipErrorInvalidValue;
+        a.tab = *tab;
+    }
     a.xhi = x_hi;
     a.xlo = x_lo;
     a.scale = scale;
@@ -525,7 +556,8 @@ hipError_t launch_finish(const Plan& p, const uint16_t* x_hi, const uint16_t* x_
     a.tiles_j = static_cast<int>((p.n + T - 1) / T);
     a.decay = decay;
     a.step = step;
-    return params ? finish_mode<true>(p, a, s) : finish_mode<false>(p, a, s);
+    const bool update = params != nullptr || (a.tab.n > 0 && a.tab.P[0] != nullptr);
+    return update ? finish_mode<true>(p, a, s) : finish_mode<false>(p, a, s);
 }
 
 }  // namespace muon

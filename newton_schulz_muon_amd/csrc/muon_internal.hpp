@@ -69,6 +69,22 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // ---------------------------------------------------------------- launchers
+// Per-matrix addressing of one element-wise or small-block launch.  n == 0:
+// the batch is strided (each operand's base + block * r * c).  n > 0: matrix
+// i of the launch (i < n <= kTabMax) has its own buffers, NS block b is
+// sub-block b % v of matrix b / v, and the update scalars are per matrix.
+constexpr int kTabMax = 32;
+struct MatTable {
+    int n = 0;
+    int v = 1;
+    const uint16_t* src[kTabMax];   // gradients (or x)
+    float* mom[kTabMax];            // momentum buffers
+    float* P[kTabMax];              // parameters
+    uint16_t* out[kTabMax];         // NS output / optional O (entries may be null)
+    float decay[kTabMax];           // 1 - lr wd wd_mul
+    float step[kTabMax];            // lr aspect lr_mul
+};
+
 // Element-wise kernels (muon_elementwise.hip).
 enum PrepMode { kPrepCast = 0, kPrepNesterov = 1, kPrepPlain = 2 };
 
@@ -76,7 +92,8 @@ enum PrepMode { kPrepCast = 0, kPrepNesterov = 1, kPrepPlain = 2 };
 // (momentum modes), writes the oriented padded iterate X0 (bf16 hi plane; lo
 // plane too when x_lo != nullptr) and per-tile sums of squares.
 hipError_t launch_prep(const Plan& p, PrepMode mode, const uint16_t* src, float* mom, float mu,
-                       uint16_t* x_hi, uint16_t* x_lo, float* partials, hipStream_t s);
+                       uint16_t* x_hi, uint16_t* x_lo, float* partials, hipStream_t s,
+                       const MatTable* tab = nullptr);
 // scales[2k] = 1/(sqrt(sum_k) + eps), scales[2k+1] = scales[2k]^2.
 hipError_t launch_norm_finalize(const Plan& p, const float* partials, float* scales, float eps,
                                 hipStream_t s);
@@ -85,9 +102,38 @@ hipError_t launch_norm_finalize(const Plan& p, const float* partials, float* sca
 // null) multiplies X first (used when ns_steps == 0).
 hipError_t launch_finish(const Plan& p, const uint16_t* x_hi, const uint16_t* x_lo,
                          const float* scale, float* params, float decay, float step,
-                         uint16_t* out, hipStream_t s);
+                         uint16_t* out, hipStream_t s, const MatTable* tab = nullptr);
 
-// MFMA kernels (ns_gemm.hip).
+// MFMA kernels (ns_gemm.hip).  Each launcher takes 1 to 4 products of one
+// kind that share the reduction length; their tiles run in one launch (two
+// when the last round is split into quadrants).
+struct GramOp {
+    const Plan* plan;
+    const uint16_t* x;
+    uint16_t* a;
+    const float* scale2;
+};
+struct PolyOp {
+    const Plan* plan;
+    const uint16_t* a;
+    uint16_t* b_hi;
+    uint16_t* b_lo;
+};
+struct BxOp {
+    const Plan* plan;
+    const uint16_t* b_hi;
+    const uint16_t* b_lo;
+    const uint16_t* x_hi;
+    const uint16_t* x_lo;
+    uint16_t* out_hi;
+    uint16_t* out_lo;
+    const float* scale1;
+};
+constexpr int kMaxGemmProblems = 4;
+hipError_t launch_gram(const GramOp* ops, int n, hipStream_t s);
+hipError_t launch_poly(const PolyOp* ops, int n, float ca, float cb, float cc, hipStream_t s);
+hipError_t launch_bx(const BxOp* ops, int n, hipStream_t s);
+// Single-product forms.
 // A = scale2 * X X^T   (upper tiles computed, mirrored; scale2 may be null)
 hipError_t launch_gram(const Plan& p, const uint16_t* x, uint16_t* a, const float* scale2,
                        hipStream_t s);
@@ -111,6 +157,7 @@ struct SmallStep {
     int ns_steps = 5;
     float a = 0.f, b = 0.f, c = 0.f, eps = 0.f;
 };
-hipError_t launch_small(const Plan& p, const SmallStep& st, hipStream_t s);
+// With a table, src/mom/params/out/decay/step come from it (per matrix).
+hipError_t launch_small(const Plan& p, const SmallStep& st, hipStream_t s, const MatTable* tab = nullptr);
 
 }  // namespace muon

@@ -362,9 +362,14 @@ __device__ __forceinline__ int mir_off(int row, int col) {
 
 enum Kind { kGram = 0, kPoly = 1, kPolySplit = 2, kBx = 3, kBxSplit = 4 };
 
-struct GemmArgs {
+// One product of a launch: a batch of same-shaped blocks.  A launch may carry
+// up to kMaxProblems of them (same kind, same tiling), enumerated one after
+// the other, so that several parameter shapes fill the CUs together.
+constexpr int kMaxProblems = 4;
+
+struct GemmProblem {
     const uint16_t* p[2];     // row operands (hi, lo): X, A or B'
-    const uint16_t* q[2];     // column operands (hi, lo): X, A (k-contiguous) or X (k-major)
+    const uint16_t* q[2];     // column operands (hi, lo): X or A or X
     uint16_t* out[2];         // row-major output (hi, lo)
     const float* scale;       // [nb][2] or null
     int64_t p_stride, q_stride, out_stride;
@@ -377,6 +382,12 @@ struct GemmArgs {
     int T;                    // symmetric: tiles per side
     uint32_t tiles_i;         // full: row tiles per block
     uint32_t tiles;           // tiles per block
+    uint32_t first;           // index of this problem's first tile in the launch
+};
+
+struct GemmArgs {
+    GemmProblem pr[kMaxProblems];
+    int n;                    // problems in this launch
     uint32_t total;           // workgroups of this launch
     // Quadrant mode (128-wide kernel finishing the last partial round of a
     // 256-wide tiling): workgroup L computes quadrant L % 4 of 256-wide tile
@@ -386,7 +397,7 @@ struct GemmArgs {
 };
 
 template <int KIND, int BT>
-__global__ __launch_bounds__(NTHR) void k_gemm(GemmArgs a) {
+__global__ __launch_bounds__(NTHR) void k_gemm(GemmArgs args) {
     using Cfg = TileCfg<BT, BT == 256 || KIND == kBx || KIND == kBxSplit>;
     constexpr int F = Cfg::F, TW = Cfg::TW;
     constexpr bool SYM = KIND == kGram || KIND == kPoly || KIND == kPolySplit;
@@ -409,8 +420,13 @@ __global__ __launch_bounds__(NTHR) void k_gemm(GemmArgs a) {
     constexpr int LDS_BYTES = Cfg::NS * STAGE;
     __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
 
-    const uint32_t L = xcd_logical(blockIdx.x, a.total);
-    const uint32_t tile = a.quad ? a.big_base + L / 4 : L;
+    const uint32_t L = xcd_logical(blockIdx.x, args.total);
+    const uint32_t tile_all = args.quad ? args.big_base + L / 4 : L;
+    int pi = 0;
+    for (int i = 1; i < args.n; ++i)
+        if (tile_all >= args.pr[i].first) pi = i;
+    const GemmProblem& a = args.pr[pi];
+    const uint32_t tile = tile_all - a.first;
     const int64_t blk = tile / a.tiles;
     int ti, tj;
     {
@@ -424,7 +440,7 @@ __global__ __launch_bounds__(NTHR) void k_gemm(GemmArgs a) {
             ti = id % static_cast<int>(a.tiles_i);
             tj = id / static_cast<int>(a.tiles_i);
         }
-        if (a.quad) {
+        if (args.quad) {
             ti = 2 * ti + static_cast<int>((L >> 1) & 1);
             tj = 2 * tj + static_cast<int>(L & 1);
             if (SYM && ti > tj) return;   // lower quadrant of a diagonal tile: its mirror covers it
@@ -599,8 +615,8 @@ __global__ __launch_bounds__(NTHR) void k_gemm(GemmArgs a) {
             for (int e = 0; e < 4; ++e) {
                 float v;
                 if constexpr (POLY) {
-                    v = fmaf(a.cc, x[e], a.cb * am[e]);
-                    if (grow == gcol + e) v += a.ca;
+                    v = fmaf(args.cc, x[e], args.cb * am[e]);
+                    if (grow == gcol + e) v += args.ca;
                 } else {
                     v = x[e] * sc;
                 }
@@ -668,24 +684,34 @@ constexpr int64_t kCUs = 256;
 double round_cycles_big(int64_t K) { return 1305.0 * double(K / 32) + 12000.0; }
 double round_cycles_small(int64_t K) { return 812.0 * double(K / 32) + 8500.0; }
 
-// Tiling of one product, by the estimated duration of three plans:
+// Tiling of one launch (n products of one kind), by the estimated duration
+// of three plans over all their tiles together:
 //  * 128-wide tiles throughout (512 per round);
 //  * 256-wide tiles (256 per round) with the last partial round split into
 //    128-wide quadrants in a second launch;
 //  * 256-wide tiles throughout, the last round partial.
+// The products share the reduction length K (the caller groups them so).
 template <int KIND>
-hipError_t run(const Plan& p, GemmArgs a, hipStream_t s) {
+hipError_t run(const Plan* const* plans, GemmArgs a, hipStream_t s) {
     constexpr bool SYM = KIND == kGram || KIND == kPoly || KIND == kPolySplit;
     constexpr bool HAS_BIG = KIND == kGram || KIND == kPoly || KIND == kBx;
     auto geometry = [&](int bt) {
-        if (SYM) {
-            a.T = static_cast<int>(p.mp / bt);
-            a.tiles = static_cast<uint32_t>(a.T * (a.T + 1) / 2);
-        } else {
-            a.tiles_i = static_cast<uint32_t>(p.mp / bt);
-            a.tiles = a.tiles_i * static_cast<uint32_t>(p.np / bt);
+        int64_t first = 0;
+        for (int i = 0; i < a.n; ++i) {
+            GemmProblem& g = a.pr[i];
+            const Plan& p = *plans[i];
+            if (SYM) {
+                g.T = static_cast<int>(p.mp / bt);
+                g.tiles = static_cast<uint32_t>(g.T * (g.T + 1) / 2);
+            } else {
+                g.tiles_i = static_cast<uint32_t>(p.mp / bt);
+                g.tiles = g.tiles_i * static_cast<uint32_t>(p.np / bt);
+            }
+            g.first = static_cast<uint32_t>(first);
+            first += int64_t(g.tiles) * p.nb;
+            if (first > 0x3fffffffLL) return int64_t(-1);
         }
-        return int64_t(a.tiles) * p.nb;
+        return first;
     };
     auto launch = [&](int bt, int64_t total, uint32_t quad, uint32_t base) {
         a.quad = quad;
@@ -698,15 +724,21 @@ hipError_t run(const Plan& p, GemmArgs a, hipStream_t s) {
         }
         return hipGetLastError();
     };
+    const int64_t K = a.pr[0].K;
+    bool big_ok = HAS_BIG;
+    for (int i = 0; i < a.n; ++i) {
+        if (a.pr[i].K != K) return hipErrorInvalidValue;
+        big_ok = big_ok && plans[i]->mp % 256 == 0 && (SYM || plans[i]->np % 256 == 0);
+    }
     const int64_t small = geometry(128);
-    if (small > 0x3fffffffLL) return hipErrorInvalidValue;
-    const double t_small = double((small + 2 * kCUs - 1) / (2 * kCUs)) * round_cycles_small(a.K);
-    if (HAS_BIG && p.mp % 256 == 0 && (SYM || p.np % 256 == 0)) {
+    if (small < 0) return hipErrorInvalidValue;
+    const double t_small = double((small + 2 * kCUs - 1) / (2 * kCUs)) * round_cycles_small(K);
+    if (big_ok) {
         const int64_t big = geometry(256);
         const int64_t full = big / kCUs, tail = big % kCUs;
-        const double t_split = double(full) * round_cycles_big(a.K) +
-                               double((4 * tail + 2 * kCUs - 1) / (2 * kCUs)) * round_cycles_small(a.K);
-        const double t_big = double(full + (tail ? 1 : 0)) * round_cycles_big(a.K);
+        const double t_split = double(full) * round_cycles_big(K) +
+                               double((4 * tail + 2 * kCUs - 1) / (2 * kCUs)) * round_cycles_small(K);
+        const double t_big = double(full + (tail ? 1 : 0)) * round_cycles_big(K);
         if (t_big <= t_split && t_big < t_small) return launch(256, big, 0, 0);
         if (t_split < t_small) {
             if (full > 0) {
@@ -722,60 +754,102 @@ hipError_t run(const Plan& p, GemmArgs a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_gram(const Plan& p, const uint16_t* x, uint16_t* a_out, const float* scale2,
-                       hipStream_t s) {
+hipError_t launch_gram(const GramOp* ops, int n, hipStream_t s) {
+    if (n < 1 || n > kMaxProblems) return hipErrorInvalidValue;
     GemmArgs a{};
-    a.p[0] = x;
-    a.q[0] = x;
-    a.out[0] = a_out;
-    a.scale = scale2;
-    a.p_stride = a.q_stride = p.mp * p.np;
-    a.out_stride = p.mp * p.mp;
-    a.K = p.np;
-    a.ldo = p.mp;
-    a.p_bytes = a.q_bytes = static_cast<uint32_t>(p.mp * p.np * 2);
-    return run<kGram>(p, a, s);
+    const Plan* plans[kMaxProblems];
+    a.n = n;
+    for (int i = 0; i < n; ++i) {
+        const Plan& p = *ops[i].plan;
+        GemmProblem& g = a.pr[i];
+        plans[i] = &p;
+        g.p[0] = ops[i].x;
+        g.q[0] = ops[i].x;
+        g.out[0] = ops[i].a;
+        g.scale = ops[i].scale2;
+        g.p_stride = g.q_stride = p.mp * p.np;
+        g.out_stride = p.mp * p.mp;
+        g.K = p.np;
+        g.ldo = p.mp;
+        g.p_bytes = g.q_bytes = static_cast<uint32_t>(p.mp * p.np * 2);
+    }
+    return run<kGram>(plans, a, s);
 }
 
-hipError_t launch_poly(const Plan& p, const uint16_t* a_in, uint16_t* b_hi, uint16_t* b_lo,
-                       float ca, float cb, float cc, hipStream_t s) {
+hipError_t launch_poly(const PolyOp* ops, int n, float ca, float cb, float cc, hipStream_t s) {
+    if (n < 1 || n > kMaxProblems) return hipErrorInvalidValue;
     GemmArgs a{};
-    a.p[0] = a_in;
-    a.q[0] = a_in;
-    a.out[0] = b_hi;
-    a.out[1] = b_lo;
-    a.p_stride = a.q_stride = p.mp * p.mp;
-    a.out_stride = p.mp * p.mp;
-    a.K = p.mp;
-    a.ldq = p.mp;
-    a.ldo = p.mp;
-    a.p_bytes = a.q_bytes = static_cast<uint32_t>(p.mp * p.mp * 2);
+    const Plan* plans[kMaxProblems];
+    a.n = n;
     a.ca = ca;
     a.cb = cb;
     a.cc = cc;
-    return b_lo ? run<kPolySplit>(p, a, s) : run<kPoly>(p, a, s);
+    const bool split = ops[0].b_lo != nullptr;
+    for (int i = 0; i < n; ++i) {
+        const Plan& p = *ops[i].plan;
+        GemmProblem& g = a.pr[i];
+        if ((ops[i].b_lo != nullptr) != split) return hipErrorInvalidValue;
+        plans[i] = &p;
+        g.p[0] = ops[i].a;
+        g.q[0] = ops[i].a;
+        g.out[0] = ops[i].b_hi;
+        g.out[1] = ops[i].b_lo;
+        g.p_stride = g.q_stride = p.mp * p.mp;
+        g.out_stride = p.mp * p.mp;
+        g.K = p.mp;
+        g.ldq = p.mp;
+        g.ldo = p.mp;
+        g.p_bytes = g.q_bytes = static_cast<uint32_t>(p.mp * p.mp * 2);
+    }
+    return split ? run<kPolySplit>(plans, a, s) : run<kPoly>(plans, a, s);
+}
+
+hipError_t launch_bx(const BxOp* ops, int n, hipStream_t s) {
+    if (n < 1 || n > kMaxProblems) return hipErrorInvalidValue;
+    GemmArgs a{};
+    const Plan* plans[kMaxProblems];
+    a.n = n;
+    const bool split = ops[0].b_lo != nullptr;
+    for (int i = 0; i < n; ++i) {
+        const Plan& p = *ops[i].plan;
+        GemmProblem& g = a.pr[i];
+        if ((ops[i].b_lo != nullptr) != split) return hipErrorInvalidValue;
+        plans[i] = &p;
+        g.p[0] = ops[i].b_hi;
+        g.p[1] = ops[i].b_lo;
+        g.q[0] = ops[i].x_hi;
+        g.q[1] = ops[i].x_lo;
+        g.out[0] = ops[i].out_hi;
+        g.out[1] = ops[i].out_lo;
+        g.scale = ops[i].scale1;
+        g.p_stride = p.mp * p.mp;
+        g.q_stride = p.mp * p.np;
+        g.out_stride = p.mp * p.np;
+        g.K = p.mp;
+        g.ldq = p.np;
+        g.ldo = p.np;
+        g.p_bytes = static_cast<uint32_t>(p.mp * p.mp * 2);
+        g.q_bytes = static_cast<uint32_t>(p.mp * p.np * 2);
+    }
+    return split ? run<kBxSplit>(plans, a, s) : run<kBx>(plans, a, s);
+}
+
+hipError_t launch_gram(const Plan& p, const uint16_t* x, uint16_t* a_out, const float* scale2, hipStream_t s) {
+    const GramOp op{&p, x, a_out, scale2};
+    return launch_gram(&op, 1, s);
+}
+
+hipError_t launch_poly(const Plan& p, const uint16_t* a_in, uint16_t* b_hi, uint16_t* b_lo, float ca, float cb,
+                       float cc, hipStream_t s) {
+    const PolyOp op{&p, a_in, b_hi, b_lo};
+    return launch_poly(&op, 1, ca, cb, cc, s);
 }
 
 hipError_t launch_bx(const Plan& p, const uint16_t* b_hi, const uint16_t* b_lo, const uint16_t* x_hi,
                      const uint16_t* x_lo, uint16_t* out_hi, uint16_t* out_lo, const float* scale1,
                      hipStream_t s) {
-    GemmArgs a{};
-    a.p[0] = b_hi;
-    a.p[1] = b_lo;
-    a.q[0] = x_hi;
-    a.q[1] = x_lo;
-    a.out[0] = out_hi;
-    a.out[1] = out_lo;
-    a.scale = scale1;
-    a.p_stride = p.mp * p.mp;
-    a.q_stride = p.mp * p.np;
-    a.out_stride = p.mp * p.np;
-    a.K = p.mp;
-    a.ldq = p.np;
-    a.ldo = p.np;
-    a.p_bytes = static_cast<uint32_t>(p.mp * p.mp * 2);
-    a.q_bytes = static_cast<uint32_t>(p.mp * p.np * 2);
-    return b_lo ? run<kBxSplit>(p, a, s) : run<kBx>(p, a, s);
+    const BxOp op{&p, b_hi, b_lo, x_hi, x_lo, out_hi, out_lo, scale1};
+    return launch_bx(&op, 1, s);
 }
 
 }  // namespace muon

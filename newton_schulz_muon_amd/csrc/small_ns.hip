@@ -16,6 +16,7 @@ namespace muon {
 namespace {
 
 struct SmallArgs {
+    MatTable tab;     // per-matrix buffers and scalars (tab.n > 0) or strided
     const uint16_t* src;
     float* mom;
     float* P;
@@ -37,7 +38,30 @@ __global__ __launch_bounds__(256) void k_small(SmallArgs a) {
     __shared__ float red[4];
 
     const int t = threadIdx.x;
-    const int64_t base = (int64_t)blockIdx.x * a.be;
+    const int64_t blk = blockIdx.x;
+    const uint16_t* src;
+    float* mom = nullptr;
+    float* P = nullptr;
+    uint16_t* out;
+    float decay = a.decay, step = a.step;
+    if (a.tab.n > 0) {
+        const int64_t mi = blk / a.tab.v, sub = blk % a.tab.v;
+        src = a.tab.src[mi] + sub * a.be;
+        if constexpr (MODE != kPrepCast) {
+            mom = a.tab.mom[mi] + sub * a.be;
+            P = a.tab.P[mi] + sub * a.be;
+        }
+        out = a.tab.out[mi] ? a.tab.out[mi] + sub * a.be : nullptr;
+        decay = a.tab.decay[mi];
+        step = a.tab.step[mi];
+    } else {
+        src = a.src + blk * a.be;
+        if constexpr (MODE != kPrepCast) {
+            mom = a.mom + blk * a.be;
+            P = a.P + blk * a.be;
+        }
+        out = a.out ? a.out + blk * a.be : nullptr;
+    }
     const int c = a.c, m = a.m, n = a.n;
     const int be = static_cast<int>(a.be);
     float* X = buf0;
@@ -46,12 +70,12 @@ __global__ __launch_bounds__(256) void k_small(SmallArgs a) {
     float ss = 0.f;
     for (int e = t; e < be; e += 256) {
         const int bi = e / c, bj = e % c;
-        const float g = bf16_to_f32(a.src[base + e]);
+        const float g = bf16_to_f32(src[e]);
         float u = g;
         if constexpr (MODE != kPrepCast) {
-            const float mo = a.mom[base + e];
+            const float mo = mom[e];
             const float mn = fmaf(a.omm, g - mo, mo);
-            a.mom[base + e] = mn;
+            mom[e] = mn;
             u = (MODE == kPrepNesterov) ? fmaf(a.mu, mn - g, g) : mn;
         }
         const int oi = a.tall ? bj : bi, oj = a.tall ? bi : bj;
@@ -98,19 +122,24 @@ __global__ __launch_bounds__(256) void k_small(SmallArgs a) {
         const int oi = a.tall ? bj : bi, oj = a.tall ? bi : bj;
         const float o = X[oi * n + oj];
         if constexpr (MODE == kPrepCast) {
-            a.out[base + e] = f32_to_bf16(o);
+            out[e] = f32_to_bf16(o);
         } else {
-            a.P[base + e] = fmaf(-a.step, o, a.P[base + e] * a.decay);
-            if (a.out) a.out[base + e] = f32_to_bf16(o);
+            P[e] = fmaf(-step, o, P[e] * decay);
+            if (out) out[e] = f32_to_bf16(o);
         }
     }
 }
 
 }  // namespace
 
-hipError_t launch_small(const Plan& p, const SmallStep& st, hipStream_t s) {
+hipError_t launch_small(const Plan& p, const SmallStep& st, hipStream_t s, const MatTable* tab) {
     if (p.nb > 0x7fffffff || p.m > kSmallMaxM || p.m * p.n > kSmallMaxElems) return hipErrorInvalidValue;
     SmallArgs a{};
+    if (tab != nullptr) {
+        if (tab->n < 1 || tab->n > kTabMax || tab->v != p.v || p.nb != int64_t(tab->n) * tab->v)
+            return hipErrorInvalidValue;
+        a.tab = *tab;
+    }
     a.src = st.src;
     a.mom = st.mom;
     a.P = st.params;

@@ -142,3 +142,77 @@ def test_step_validation_before_device(lib):
     assert call(fake, other, third, c=0) == 2
     assert call(fake, other, third) == 4       # no workspace
     del args
+
+
+def _mat(p, g, m, rows, cols, v=1, out=None, lr_mul=1.0, wd_mul=1.0):
+    e = nsm.MuonMatrix()
+    e.params, e.grads, e.momentum_buf, e.update_out = p, g, m, out
+    e.rows, e.cols, e.view_blocks, e.lr_mul, e.wd_mul = rows, cols, v, lr_mul, wd_mul
+    return e
+
+
+def _mats(*entries):
+    arr = (nsm.MuonMatrix * len(entries))()
+    for i, e in enumerate(entries):
+        arr[i] = e
+    return arr
+
+
+def test_multi_workspace_bytes(lib):
+    base = 1 << 30
+    # 3 mlp-like, 2 attn (view 4), 1 gate: groups by (rows, cols, view)
+    es = [_mat(base + i * (1 << 26), base + i * (1 << 26) + (1 << 24), base + i * (1 << 26) + (1 << 25), 768, 3072)
+          for i in range(3)]
+    es += [_mat(base + (3 + i) * (1 << 26), base + (3 + i) * (1 << 26) + (1 << 24),
+                base + (3 + i) * (1 << 26) + (1 << 25), 768, 3072, 4) for i in range(2)]
+    es += [_mat(base + 6 * (1 << 26), base + 6 * (1 << 26) + 4096, base + 6 * (1 << 26) + 8192, 1, 12)]
+    arr = _mats(*es)
+    got = lib.muon_step_multi_workspace_bytes(arr, len(es), None)
+    assert got == _expected_ws(3, 768, 3072) + _expected_ws(8, 768, 768)
+    assert lib.muon_step_multi_workspace_bytes(arr, 0, None) == 0
+    bad = _mats(_mat(base, base + 4096, base + 8192, 8, 10, 4))
+    assert lib.muon_step_multi_workspace_bytes(bad, 1, None) == ctypes.c_size_t(-1).value
+
+
+def test_multi_validation_before_device(lib):
+    f = ctypes.c_float
+    base = 1 << 30
+
+    def call(arr, n, lr=0.02, ws=None, wsb=0):
+        return lib.muon_step_multi(arr, n, f(lr), f(0.01), f(0.95), 1, None, ws, wsb, None)
+    good = _mats(_mat(base, base + (1 << 20), base + (1 << 21), 64, 64),
+                 _mat(base + (1 << 22), base + (1 << 22) + (1 << 20), base + (1 << 22) + (1 << 21), 64, 64))
+    assert call(None, 0) == 0
+    assert call(None, 2) == 1                                  # null array
+    assert call(good, 2, lr=float("nan")) == 1
+    assert call(good, 2) == 4                                  # no workspace
+    # the second matrix's params overlap the first one's momentum buffer
+    ov = _mats(_mat(base, base + (1 << 20), base + (1 << 21), 64, 64),
+               _mat(base + (1 << 21) + 64, base + (1 << 23), base + (1 << 24), 64, 64))
+    assert call(ov, 2) == 1
+    assert "overlap" in nsm.muon_last_error()
+    mis = _mats(_mat(base + 4, base + (1 << 20), base + (1 << 21), 64, 64))
+    assert call(mis, 1) == 3
+    inf = _mats(_mat(base, base + (1 << 20), base + (1 << 21), 64, 64, lr_mul=float("inf")))
+    assert call(inf, 1) == 1
+    shp = _mats(_mat(base, base + (1 << 20), base + (1 << 21), 0, 64))
+    assert call(shp, 1) == 2
+    nul = _mats(_mat(None, base + (1 << 20), base + (1 << 21), 64, 64))
+    assert call(nul, 1) == 1
+
+
+def test_multi_alignment_by_path(lib):
+    # A 1x12 gate takes the element-wise small path: 8-byte offsets are fine
+    # (they are what slices of a stacked [n, 1, 12] batch give).  The call
+    # still fails, on the overlap planted in the second and third matrices,
+    # before any device work.
+    f = ctypes.c_float
+    base = 1 << 30
+    arr = _mats(_mat(base + 48, base + 4096 + 24, base + 8192 + 48, 1, 12),
+                _mat(base + (1 << 20), base + (1 << 21), base + (1 << 22), 64, 64),
+                _mat(base + (1 << 20) + 64, base + (1 << 23), base + (1 << 24), 64, 64))
+    assert lib.muon_step_multi(arr, 3, f(0.02), f(0.01), f(0.95), 1, None, None, 0, None) == 1
+    assert "overlap" in nsm.muon_last_error()
+    # the same offset on a vector-path matrix is rejected
+    arr = _mats(_mat(base + (1 << 20) + 8, base + (1 << 21), base + (1 << 22), 64, 64))
+    assert lib.muon_step_multi(arr, 1, f(0.02), f(0.01), f(0.95), 1, None, None, 0, None) == 3

@@ -1,0 +1,99 @@
+"""GPU checks of muon_step_multi, the pointer-array step over matrices of any
+shapes: each matrix's parameters, momentum buffer and NS output must be
+bitwise the ones muon_step_batched gives it (whose parity with the fp64
+oracle the other GPU tests establish), whatever the grouping and launch
+sharing.  Cases: the 124M custom-sizing set (gates, attn view, mlp: B'X and
+the polynomial of attn and mlp share launches), mixed shapes with per-matrix
+lr_mul / wd_mul and tall blocks, ACCURATE precision, and a shape group larger
+than one pointer table."""
+import pytest
+
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def nsm():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the gpu-marked tests must run on an MI355X")
+    import newton_schulz_muon_amd as m
+    m.load_library()
+    return m
+
+
+def _state(shapes, seed):
+    """Separate per-matrix tensors (each its own allocation) for a list of
+    (rows, cols, view_blocks, lr_mul, wd_mul)."""
+    import torch
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    mats = []
+    for r, c, v, lm, wm in shapes:
+        P = torch.randn((r, c), generator=gen, device="cuda") / c ** 0.5
+        G = (torch.randn((r, c), generator=gen, device="cuda") * 1e-2).to(torch.bfloat16)
+        M = torch.randn((r, c), generator=gen, device="cuda") * 1e-3
+        mats.append(dict(params=P, grads=G, momentum_buf=M, update_out=torch.empty_like(G),
+                         view_blocks=v, lr_mul=lm, wd_mul=wm))
+    return mats
+
+
+def _clone(mats):
+    return [{k: (v.clone() if hasattr(v, "clone") else v) for k, v in m.items()} for m in mats]
+
+
+def _reference(nsm, mats, steps, **kw):
+    """muon_step_batched on each matrix alone (a batch of one)."""
+    for _ in range(steps):
+        for m in mats:
+            nsm.muon_step_batched(m["params"], m["grads"], m["momentum_buf"], view_blocks=m["view_blocks"],
+                                  lr_mul=m["lr_mul"], wd_mul=m["wd_mul"], update_out=m["update_out"], **kw)
+
+
+def _check_equal(got, ref, label):
+    import torch
+    torch.cuda.synchronize()
+    for i, (g, r) in enumerate(zip(got, ref)):
+        for k in ("params", "momentum_buf", "update_out"):
+            assert torch.equal(g[k].view(torch.int16) if g[k].dtype == torch.bfloat16 else g[k].view(torch.int32),
+                               r[k].view(torch.int16) if r[k].dtype == torch.bfloat16 else r[k].view(torch.int32)), \
+                f"{label}: matrix {i} ({tuple(g['params'].shape)}, view {g['view_blocks']}) differs in {k}"
+
+
+def _run_case(nsm, shapes, seed, steps=2, precision="fast", label=""):
+    print(f"[multi] {label}: {len(shapes)} matrices, precision={precision}", flush=True)
+    mats = _state(shapes, seed)
+    ref = _clone(mats)
+    kw = dict(lr=0.02, weight_decay=0.01, momentum=0.95, precision=precision)
+    for _ in range(steps):
+        nsm.muon_step_multi(mats, **kw)
+    _reference(nsm, ref, steps, **kw)
+    _check_equal(mats, ref, label)
+
+
+def test_multi_gpt124m_set(nsm):
+    wl = workloads.get_workload("gpt124m")
+    shapes = []
+    for g in wl.groups:
+        shapes += [(g.rows, g.cols, g.view_blocks, 1.0, 1.0)] * g.count
+    _run_case(nsm, shapes, seed=1, label="124M custom sizing")
+
+
+def test_multi_mixed_shapes_and_multipliers(nsm):
+    shapes = [(512, 512, 1, 1.0, 1.0), (512, 256, 1, 0.5, 2.0), (256, 512, 1, 1.0, 0.0), (512, 512, 1, 2.0, 1.0),
+              (1024, 512, 1, 1.0, 1.0), (512, 1024, 1, 1.5, 0.5), (1, 12, 1, 1.0, 1.0), (96, 384, 4, 1.0, 1.0),
+              (300, 700, 1, 1.0, 1.0), (700, 300, 1, 0.7, 1.3), (33, 70, 1, 1.0, 1.0), (1536, 768, 1, 1.0, 1.0),
+              (768, 1536, 1, 1.0, 1.0)]
+    _run_case(nsm, shapes, seed=2, label="mixed")
+
+
+def test_multi_accurate(nsm):
+    shapes = [(256, 640, 1, 1.0, 1.0), (640, 256, 1, 1.0, 1.0), (256, 640, 1, 0.5, 2.0), (256, 256, 1, 1.0, 1.0)]
+    _run_case(nsm, shapes, seed=3, precision="accurate", label="accurate")
+
+
+def test_multi_many_matrices_one_shape(nsm):
+    # 40 matrices of one shape: the shape group spans two pointer tables (32 + 8)
+    shapes = [(64, 128, 1, 1.0 + 0.01 * i, 1.0) for i in range(40)] + [(1, 12, 1, 1.0, 1.0)] * 35
+    _run_case(nsm, shapes, seed=4, label="many")
