@@ -22,8 +22,8 @@ namespace muon {
 
 constexpr int kTile = 128;          // GEMM output tile edge and padding unit
 constexpr int kEwTile = 64;         // element-wise kernels' tile edge
-constexpr int kSmallMaxM = 32;      // small fp32 path: m <= 32 ...
-constexpr int kSmallMaxElems = 4096;  // ... and m * n <= 4096
+constexpr int kSmallMaxM = 64;      // small fp32 path: m <= 64 ...
+constexpr int kSmallMaxElems = 8192;  // ... and m * n <= 8192
 constexpr int64_t kMaxGridY = 65535;
 
 struct Plan {

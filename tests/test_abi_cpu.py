@@ -99,26 +99,26 @@ def test_ns_validation_before_device(lib):
     fake = ctypes.c_void_p(1 << 20)   # never dereferenced: every call below fails validation
     # batch 0 is a no-op even with null pointers
     assert lib.ns_orthogonalize_batched(None, None, 0, 4, 4, 1, None, None, 0, None) == 0
-    assert lib.ns_orthogonalize_batched(None, fake, 2, 64, 64, 1, None, None, 0, None) == 1
+    assert lib.ns_orthogonalize_batched(None, fake, 2, 128, 128, 1, None, None, 0, None) == 1
     assert "non-null" in nsm.muon_last_error()
-    assert lib.ns_orthogonalize_batched(fake, fake, 2, 64, 0, 1, None, None, 0, None) == 2
-    assert lib.ns_orthogonalize_batched(fake, fake, 2, 64, 66, 4, None, None, 0, None) == 2
-    assert lib.ns_orthogonalize_batched(ctypes.c_void_p((1 << 20) + 2), fake, 2, 64, 64, 1,
+    assert lib.ns_orthogonalize_batched(fake, fake, 2, 128, 0, 1, None, None, 0, None) == 2
+    assert lib.ns_orthogonalize_batched(fake, fake, 2, 128, 66, 4, None, None, 0, None) == 2
+    assert lib.ns_orthogonalize_batched(ctypes.c_void_p((1 << 20) + 2), fake, 2, 128, 128, 1,
                                         None, None, 0, None) == 3
-    assert lib.ns_orthogonalize_batched(fake, fake, 2, 64, 64, 1, ctypes.byref(_cfg(ns_steps=-1)),
+    assert lib.ns_orthogonalize_batched(fake, fake, 2, 128, 128, 1, ctypes.byref(_cfg(ns_steps=-1)),
                                         None, 0, None) == 1
-    assert lib.ns_orthogonalize_batched(fake, fake, 2, 64, 64, 1, ctypes.byref(_cfg(precision=7)),
+    assert lib.ns_orthogonalize_batched(fake, fake, 2, 128, 128, 1, ctypes.byref(_cfg(precision=7)),
                                         None, 0, None) == 1
-    assert lib.ns_orthogonalize_batched(fake, fake, 2, 64, 64, 1, ctypes.byref(_cfg(eps=-1.0)),
+    assert lib.ns_orthogonalize_batched(fake, fake, 2, 128, 128, 1, ctypes.byref(_cfg(eps=-1.0)),
                                         None, 0, None) == 1
     # workspace missing or too small
-    assert lib.ns_orthogonalize_batched(fake, fake, 2, 64, 64, 1, None, None, 0, None) == 4
-    assert lib.ns_orthogonalize_batched(fake, fake, 2, 64, 64, 1, None, fake, 100, None) == 4
-    need = nsm.muon_workspace_bytes(2, 64, 64)
-    assert lib.ns_orthogonalize_batched(fake, fake, 2, 64, 64, 1, None,
+    assert lib.ns_orthogonalize_batched(fake, fake, 2, 128, 128, 1, None, None, 0, None) == 4
+    assert lib.ns_orthogonalize_batched(fake, fake, 2, 128, 128, 1, None, fake, 100, None) == 4
+    need = nsm.muon_workspace_bytes(2, 128, 128)
+    assert lib.ns_orthogonalize_batched(fake, fake, 2, 128, 128, 1, None,
                                         ctypes.c_void_p((1 << 20) + 16), need, None) == 3
     # partial overlap of out and x
-    assert lib.ns_orthogonalize_batched(fake, ctypes.c_void_p((1 << 20) + 16), 2, 64, 64, 1, None,
+    assert lib.ns_orthogonalize_batched(fake, ctypes.c_void_p((1 << 20) + 16), 2, 128, 128, 1, None,
                                         fake, need, None) == 1
 
 
@@ -129,7 +129,7 @@ def test_step_validation_before_device(lib):
     f = ctypes.c_float
     args = dict(lr=0.02, wd=0.01, mu=0.95)
 
-    def call(p, g, m, b=2, r=64, c=64, v=1, lr=0.02, wd=0.01, mu=0.95, out=None, ws=None, wsb=0):
+    def call(p, g, m, b=2, r=128, c=128, v=1, lr=0.02, wd=0.01, mu=0.95, out=None, ws=None, wsb=0):
         return lib.muon_step_batched(p, g, m, b, r, c, v, f(lr), f(wd), f(mu), 1, f(1.0), f(1.0),
                                      None, out, ws, wsb, None)
     assert call(None, None, None, b=0) == 0
@@ -180,24 +180,24 @@ def test_multi_validation_before_device(lib):
 
     def call(arr, n, lr=0.02, ws=None, wsb=0):
         return lib.muon_step_multi(arr, n, f(lr), f(0.01), f(0.95), 1, None, ws, wsb, None)
-    good = _mats(_mat(base, base + (1 << 20), base + (1 << 21), 64, 64),
-                 _mat(base + (1 << 22), base + (1 << 22) + (1 << 20), base + (1 << 22) + (1 << 21), 64, 64))
+    good = _mats(_mat(base, base + (1 << 20), base + (1 << 21), 128, 128),
+                 _mat(base + (1 << 22), base + (1 << 22) + (1 << 20), base + (1 << 22) + (1 << 21), 128, 128))
     assert call(None, 0) == 0
     assert call(None, 2) == 1                                  # null array
     assert call(good, 2, lr=float("nan")) == 1
     assert call(good, 2) == 4                                  # no workspace
     # the second matrix's params overlap the first one's momentum buffer
-    ov = _mats(_mat(base, base + (1 << 20), base + (1 << 21), 64, 64),
-               _mat(base + (1 << 21) + 64, base + (1 << 23), base + (1 << 24), 64, 64))
+    ov = _mats(_mat(base, base + (1 << 20), base + (1 << 21), 128, 128),
+               _mat(base + (1 << 21) + 64, base + (1 << 23), base + (1 << 24), 128, 128))
     assert call(ov, 2) == 1
     assert "overlap" in nsm.muon_last_error()
-    mis = _mats(_mat(base + 4, base + (1 << 20), base + (1 << 21), 64, 64))
+    mis = _mats(_mat(base + 4, base + (1 << 20), base + (1 << 21), 128, 128))
     assert call(mis, 1) == 3
-    inf = _mats(_mat(base, base + (1 << 20), base + (1 << 21), 64, 64, lr_mul=float("inf")))
+    inf = _mats(_mat(base, base + (1 << 20), base + (1 << 21), 128, 128, lr_mul=float("inf")))
     assert call(inf, 1) == 1
-    shp = _mats(_mat(base, base + (1 << 20), base + (1 << 21), 0, 64))
+    shp = _mats(_mat(base, base + (1 << 20), base + (1 << 21), 0, 128))
     assert call(shp, 1) == 2
-    nul = _mats(_mat(None, base + (1 << 20), base + (1 << 21), 64, 64))
+    nul = _mats(_mat(None, base + (1 << 20), base + (1 << 21), 128, 128))
     assert call(nul, 1) == 1
 
 
@@ -209,10 +209,10 @@ def test_multi_alignment_by_path(lib):
     f = ctypes.c_float
     base = 1 << 30
     arr = _mats(_mat(base + 48, base + 4096 + 24, base + 8192 + 48, 1, 12),
-                _mat(base + (1 << 20), base + (1 << 21), base + (1 << 22), 64, 64),
-                _mat(base + (1 << 20) + 64, base + (1 << 23), base + (1 << 24), 64, 64))
+                _mat(base + (1 << 20), base + (1 << 21), base + (1 << 22), 128, 128),
+                _mat(base + (1 << 20) + 64, base + (1 << 23), base + (1 << 24), 128, 128))
     assert lib.muon_step_multi(arr, 3, f(0.02), f(0.01), f(0.95), 1, None, None, 0, None) == 1
     assert "overlap" in nsm.muon_last_error()
     # the same offset on a vector-path matrix is rejected
-    arr = _mats(_mat(base + (1 << 20) + 8, base + (1 << 21), base + (1 << 22), 64, 64))
+    arr = _mats(_mat(base + (1 << 20) + 8, base + (1 << 21), base + (1 << 22), 128, 128))
     assert lib.muon_step_multi(arr, 1, f(0.02), f(0.01), f(0.95), 1, None, None, 0, None) == 3

@@ -34,9 +34,13 @@ def _oracle_batch(bits, view_blocks=1, steps=5, coeffs=oracle.NS_COEFFS):
 
 
 # Shapes span several 128-tiles, ragged tails (padding), tall blocks (transposed
-# orientation), the small-block path (m <= 32) and the smallest MFMA-path block.
+# orientation), the small-block path (m <= 64 and m n <= 8192: every 16-row
+# tile count, ragged k, 16-byte and element-wise global access, wide and tall)
+# and the smallest MFMA-path blocks beside its limits (m = 65; m = 64 with
+# m n = 8256).
 SHAPES = [(64, 128), (128, 128), (256, 640), (640, 256), (300, 700), (700, 300), (33, 70), (70, 33),
-          (96, 1000), (1, 12), (16, 200), (32, 128), (12, 1)]
+          (96, 1000), (1, 12), (16, 200), (32, 128), (12, 1), (65, 130), (64, 129), (129, 64), (8, 1024),
+          (1, 8192), (37, 221), (221, 37), (128, 64), (1024, 8), (48, 168), (4, 2048)]
 
 
 @pytest.mark.parametrize("shape", SHAPES)
