@@ -197,7 +197,10 @@ def main():
     n_blocks = sum(g.n_blocks for g in wl.groups)
     value = flops_step / (ms_per_step / 1000.0) / 1e12
 
-    mfma_groups = [g for g in wl.groups if min(g.block_shape) > 32]
+    # Blocks with m <= 64 and m n <= 8192 take the one-launch fp32 small-block
+    # path and issue no B'X launch.
+    mfma_groups = [g for g in wl.groups
+                   if not (min(g.block_shape) <= 64 and g.block_shape[0] * g.block_shape[1] <= 8192)]
     bx_flops_step = sum(g.n_blocks * bx_flops(*g.block_shape, wl.ns_steps) for g in mfma_groups)
     bx_launches, bx_ms = kt.get("bx", (0, 0.0))
     roofline = None
@@ -261,6 +264,36 @@ def main():
                                          "matrices_per_s": round(32 / (ms / 1000), 1),
                                          "mfma_peak_frac_nominal": round(f / (ms / 1000) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         del x, out
+        # ---- AdamW for the same model's embedding, head and scalars (the other
+        # optimizer of the step): 26 bytes of HBM traffic per element.
+        awl = workloads.ADAM_WORKLOADS["gpt124m_adam"]
+        tens = []
+        for i in range(len(awl.tensors)):
+            P = workloads.adam_params_device(awl, i, dev)
+            tens.append(dict(params=P, grads=workloads.adam_grads_device(awl, i, 0, dev),
+                             exp_avg=torch.zeros_like(P), exp_avg_sq=torch.zeros_like(P), step=1))
+
+        def adam_step():
+            nsm.adamw_step_multi(tens, lr=awl.lr, betas=awl.betas, eps=awl.eps, weight_decay=awl.weight_decay)
+            for t in tens:
+                t["step"] += 1
+        for _ in range(3):
+            adam_step()
+        torch.cuda.synchronize()
+        nsm.muon_timing_enable(["adamw"])
+        for _ in range(args.steps):
+            adam_step()
+        torch.cuda.synchronize()
+        nsm.muon_timing_enable([])
+        n_l, a_ms = nsm.muon_timing_collect().get("adamw", (0, 0.0))
+        if n_l:
+            ms = a_ms / n_l
+            gbs = 26.0 * awl.numel / (ms / 1000.0) / 1e9
+            result["adamw_gpt124m"] = {"kernel": "k_adamw", "elements": awl.numel, "launches": n_l,
+                                       "avg_launch_ms": round(ms, 5), "bound": "hbm", "achieved": round(gbs, 1),
+                                       "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                       "bytes_per_element": 26}
+        del tens
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

@@ -16,6 +16,10 @@
  *        optimizer works" (zeropower_via_newtonschulz5: bf16 cast, Frobenius
  *        normalisation, A = X X^T, B = bA + cA A, X = aX + BX; aspect factor
  *        max(1, m/n)^0.5).
+ *   [DA] the article on moving the Adam gradient reduce-scatter of
+ *        modded-nanogpt's DistAdam into a backward hook (record of
+ *        2025-10-31), "change two": the per-parameter AdamW body of
+ *        DistAdam.step, used for the parameters Muon does not take.
  *
  * Conventions shared by every entry point
  *   - Matrices are row-major and contiguous: a batch is [batch, rows, cols].
@@ -49,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 2
+#define MUON_ABI_VERSION 3
 
 typedef enum muon_status {
     MUON_OK = 0,
@@ -162,15 +166,51 @@ size_t muon_step_multi_workspace_bytes(const muon_matrix* mats, int32_t count,
  * the one muon_step_batched gives it.
  *   mats     host array of `count` descriptors, read during the call only
  *   No two buffers of any matrices may overlap (MUON_ERR_INVALID_ARG).
- *   Alignment: 16 bytes when a matrix's NS blocks take the vector path (more
- *   than 32 rows and columns or more than 4096 elements, and cols/view_blocks
- *   a multiple of 8), else 4 bytes (fp32) and 2 bytes (bf16).
+ *   Alignment: 16 bytes when a matrix's NS blocks take the matrix-core path
+ *   (more than 64 rows and columns, or more than 8192 elements) and
+ *   cols/view_blocks is a multiple of 8; else 4 bytes (fp32) and 2 bytes
+ *   (bf16).  Blocks with at most 64 rows or columns and 8192 elements run
+ *   the whole step in one fp32 workgroup each and use 16-byte accesses only
+ *   where the buffers allow.
  */
 muon_status muon_step_multi(const muon_matrix* mats, int32_t count,
                             float lr, float weight_decay, float momentum,
                             int32_t nesterov, const muon_ns_config* cfg,
                             void* workspace, size_t workspace_bytes,
                             void* stream);
+
+/* One tensor of an AdamW step (any shape, stored contiguously). */
+typedef struct muon_adam_tensor {
+    float* params;          /* in/out fp32 [numel]                                */
+    const void* grads;      /* in     bf16 [numel]                                */
+    float* exp_avg;         /* in/out fp32 [numel], first moment                  */
+    float* exp_avg_sq;      /* in/out fp32 [numel], second moment                 */
+    int64_t numel;          /* >= 0; 0 skips the tensor (pointers may be NULL)    */
+    int64_t step;           /* t, the tensor's step count after this step's
+                               increment (>= 1; 1 when the moments start at 0)    */
+    float lr_mul, wd_mul;   /* finite                                             */
+} muon_adam_tensor;
+
+/*
+ * One AdamW step ([DA] DistAdam.step, on one GPU: the whole tensor is the
+ * rank's slice) for `count` tensors, in place, per element:
+ *   p <- p (1 - lr lr_mul weight_decay wd_mul)     (skipped when weight_decay == 0)
+ *   m <- beta1 m + (1 - beta1) g
+ *   v <- beta2 v + (1 - beta2) g^2
+ *   p <- p - lr lr_mul (1 - beta2^t)^0.5 / (1 - beta1^t) * m / (sqrt(v) + eps)
+ * eps is added before the second-moment bias correction, as [DA] orders it
+ * (torch's AdamW adds it after).  The 124M record uses lr 0.008,
+ * betas (0.8, 0.95), eps 1e-8 ([CS] section 4).
+ *   tensors  host array of `count` descriptors, read during the call only
+ *   lr, weight_decay finite; eps finite and >= 0; 0 <= beta1, beta2 < 1
+ *   Buffers: 4-byte (fp32) / 2-byte (bf16) aligned; 16-byte aligned buffers
+ *   move 8 elements per access.  No two buffers of any tensors may overlap
+ *   (MUON_ERR_INVALID_ARG).  count == 0 is a valid no-op.
+ * All tensors run in one launch per 24 tensors; the call needs no workspace.
+ */
+muon_status adamw_step_multi(const muon_adam_tensor* tensors, int32_t count,
+                             float lr, float beta1, float beta2, float eps,
+                             float weight_decay, void* stream);
 
 /* Kernel timing (diagnostics).  Kernel families of the library: */
 typedef enum muon_kernel_kind {
@@ -181,7 +221,8 @@ typedef enum muon_kernel_kind {
     MUON_KERNEL_BX = 4,             /* X <- a X + B X                          */
     MUON_KERNEL_FINISH = 5,         /* NS output / parameter update            */
     MUON_KERNEL_SMALL = 6,          /* whole step for small blocks             */
-    MUON_KERNEL_COUNT = 7
+    MUON_KERNEL_ADAMW = 7,          /* AdamW step (adamw_step_multi)           */
+    MUON_KERNEL_COUNT = 8
 } muon_kernel_kind;
 
 /* While kernel_mask has bit k set, every launch of kernel family k records a

@@ -10,6 +10,7 @@ Entry points (same names as the C ABI):
     ns_orthogonalize_batched(x, out=None, *, view_blocks=1, ...)
     muon_step_batched(params, grads, momentum_buf, *, lr, weight_decay, momentum, ...)
     muon_step_multi(matrices, *, lr, weight_decay, momentum, ...)
+    adamw_step_multi(tensors, *, lr, betas, eps, weight_decay)
     muon_workspace_bytes(batch, rows, cols, view_blocks=1, cfg=None)
     muon_step_multi_workspace_bytes(matrices, cfg=None)
     muon_ns_config_default(), muon_last_error(), muon_abi_version()
@@ -25,6 +26,7 @@ __all__ = [
     "MuonNSConfig", "MuonError", "LIB_PATH", "EXPORTED_SYMBOLS", "load_library",
     "muon_ns_config_default", "muon_workspace_bytes", "ns_orthogonalize_batched",
     "muon_step_batched", "muon_step_multi", "muon_step_multi_workspace_bytes", "MuonMatrix",
+    "adamw_step_multi", "MuonAdamTensor",
     "muon_timing_enable", "muon_timing_collect", "muon_last_error", "muon_abi_version", "make_config",
     "KERNEL_KINDS",
 ]
@@ -32,8 +34,8 @@ __all__ = [
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmuon_hip.so")
 EXPORTED_SYMBOLS = ("muon_ns_config_default", "muon_workspace_bytes", "ns_orthogonalize_batched",
                     "muon_step_batched", "muon_step_multi_workspace_bytes", "muon_step_multi",
-                    "muon_timing_enable", "muon_timing_collect", "muon_last_error", "muon_abi_version")
-KERNEL_KINDS = ("prep", "norm_finalize", "gram", "poly", "bx", "finish", "small")
+                    "adamw_step_multi", "muon_timing_enable", "muon_timing_collect", "muon_last_error", "muon_abi_version")
+KERNEL_KINDS = ("prep", "norm_finalize", "gram", "poly", "bx", "finish", "small", "adamw")
 
 MUON_OK = 0
 _STATUS_NAMES = {0: "MUON_OK", 1: "MUON_ERR_INVALID_ARG", 2: "MUON_ERR_SHAPE", 3: "MUON_ERR_ALIGNMENT",
@@ -51,6 +53,13 @@ class MuonMatrix(ctypes.Structure):
     _fields_ = [("params", ctypes.c_void_p), ("grads", ctypes.c_void_p), ("momentum_buf", ctypes.c_void_p),
                 ("update_out", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
                 ("view_blocks", ctypes.c_int32), ("lr_mul", ctypes.c_float), ("wd_mul", ctypes.c_float)]
+
+
+class MuonAdamTensor(ctypes.Structure):
+    """muon_adam_tensor of the C ABI: one tensor of an AdamW step."""
+    _fields_ = [("params", ctypes.c_void_p), ("grads", ctypes.c_void_p), ("exp_avg", ctypes.c_void_p),
+                ("exp_avg_sq", ctypes.c_void_p), ("numel", ctypes.c_int64), ("step", ctypes.c_int64),
+                ("lr_mul", ctypes.c_float), ("wd_mul", ctypes.c_float)]
 
 
 class MuonError(RuntimeError):
@@ -88,6 +97,9 @@ def load_library():
         lib.muon_step_multi_workspace_bytes.restype = ctypes.c_size_t
         lib.muon_step_multi.argtypes = [matp, i32, f32, f32, f32, i32, cfgp, vp, ctypes.c_size_t, vp]
         lib.muon_step_multi.restype = ctypes.c_int
+        adamp = ctypes.POINTER(MuonAdamTensor)
+        lib.adamw_step_multi.argtypes = [adamp, i32, f32, f32, f32, f32, f32, vp]
+        lib.adamw_step_multi.restype = ctypes.c_int
         lib.muon_timing_enable.argtypes = [ctypes.c_uint32]
         lib.muon_timing_enable.restype = ctypes.c_int
         lib.muon_timing_collect.argtypes = [ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]
@@ -327,3 +339,36 @@ def muon_step_multi(matrices, *, lr: float, weight_decay: float, momentum: float
         _check(lib.muon_step_multi(arr, len(matrices), float(lr), float(weight_decay), float(momentum),
                                    1 if nesterov else 0, ctypes.byref(cfg),
                                    ws.data_ptr() if ws is not None else None, int(nbytes), stream))
+
+
+def adamw_step_multi(tensors, *, lr: float, betas: Tuple[float, float], eps: float, weight_decay: float):
+    """One in-place AdamW step (DistAdam.step of the pages, decay first) on a list of tensors.
+
+    Each entry is a dict with params (fp32), grads (bf16), exp_avg and exp_avg_sq (fp32), all
+    contiguous and of one shape, step (the tensor's step count after the increment, >= 1) and
+    optional lr_mul, wd_mul."""
+    import torch
+    if not tensors:
+        return
+    device = tensors[0]["params"].device
+    arr = (MuonAdamTensor * len(tensors))()
+    for i, t in enumerate(tensors):
+        P, G, M, V = t["params"], t["grads"], t["exp_avg"], t["exp_avg_sq"]
+        _require(P, f"tensors[{i}].params", torch.float32, device)
+        _require(G, f"tensors[{i}].grads", torch.bfloat16, device)
+        _require(M, f"tensors[{i}].exp_avg", torch.float32, device)
+        _require(V, f"tensors[{i}].exp_avg_sq", torch.float32, device)
+        if not (G.shape == P.shape and M.shape == P.shape and V.shape == P.shape):
+            raise ValueError(f"tensors[{i}]: params, grads, exp_avg and exp_avg_sq must have one shape")
+        e = arr[i]
+        e.params, e.grads, e.exp_avg, e.exp_avg_sq = P.data_ptr(), G.data_ptr(), M.data_ptr(), V.data_ptr()
+        e.numel = P.numel()
+        e.step = int(t["step"])
+        e.lr_mul = float(t.get("lr_mul", 1.0))
+        e.wd_mul = float(t.get("wd_mul", 1.0))
+    lib = load_library()
+    b1, b2 = betas
+    with torch.cuda.device(device):
+        stream = torch.cuda.current_stream(device).cuda_stream
+        _check(lib.adamw_step_multi(arr, len(tensors), float(lr), float(b1), float(b2), float(eps),
+                                    float(weight_decay), stream))

@@ -21,7 +21,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libmuon_hip.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["muon_api.hip", "muon_elementwise.hip", "ns_gemm.hip", "small_ns.hip"]
+SOURCES = ["muon_api.hip", "muon_elementwise.hip", "ns_gemm.hip", "small_ns.hip", "adamw.hip"]
 
 # -packed-fp32-ops: never emit v_pk_{add,mul,fma}_f32 (the host pass warns that
 # it does not know the feature; that is harmless).

@@ -10,7 +10,8 @@
 //                     (A = U U^T / s^2, X1 = B' U / s), so X0 = U / s is
 //                     never materialised
 //   k_finish          NS output, or the parameter update (+ optional O)
-// Small blocks (m <= 32, m n <= 4096) run the whole step in one k_small launch.
+// Small blocks (m <= 64, m n <= 8192) run the whole step in one k_small launch.
+// adamw_step_multi runs one k_adamw launch per 24 tensors.
 #include <algorithm>
 #include <atomic>
 #include <cmath>
@@ -723,6 +724,73 @@ muon_status muon_step_multi(const muon_matrix* mats, int32_t count, float lr, fl
                 if (e != hipSuccess) return hip_fail(e, "k_finish launch");
             }
         }
+    }
+    return MUON_OK;
+}
+
+muon_status adamw_step_multi(const muon_adam_tensor* tensors, int32_t count, float lr, float beta1, float beta2,
+                             float eps, float weight_decay, void* stream) {
+    g_err.clear();
+    if (count < 0) return fail(MUON_ERR_SHAPE, "count must be >= 0");
+    if (count == 0) return MUON_OK;
+    if (tensors == nullptr) return fail(MUON_ERR_INVALID_ARG, "tensors must be non-null");
+    if (!std::isfinite(lr) || !std::isfinite(weight_decay))
+        return fail(MUON_ERR_INVALID_ARG, "lr and weight_decay must be finite");
+    if (!std::isfinite(eps) || eps < 0.f) return fail(MUON_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    if (!(beta1 >= 0.f && beta1 < 1.f) || !(beta2 >= 0.f && beta2 < 1.f))
+        return fail(MUON_ERR_INVALID_ARG, "betas must be in [0, 1)");
+    struct Range { uintptr_t a, b; int32_t t; };
+    std::vector<Range> ranges;
+    std::vector<AdamEntry> entries;
+    for (int32_t i = 0; i < count; ++i) {
+        const muon_adam_tensor& x = tensors[i];
+        if (x.numel < 0) return fail(MUON_ERR_SHAPE, "tensor %d: numel must be >= 0", i);
+        if (x.numel == 0) continue;
+        if (!x.params || !x.grads || !x.exp_avg || !x.exp_avg_sq)
+            return fail(MUON_ERR_INVALID_ARG, "tensor %d: params, grads, exp_avg and exp_avg_sq must be non-null", i);
+        if (!aligned(x.params, 4) || !aligned(x.exp_avg, 4) || !aligned(x.exp_avg_sq, 4) || !aligned(x.grads, 2))
+            return fail(MUON_ERR_ALIGNMENT, "tensor %d: buffers must be element-aligned", i);
+        if (x.step < 1) return fail(MUON_ERR_INVALID_ARG, "tensor %d: step must be >= 1", i);
+        if (!std::isfinite(x.lr_mul) || !std::isfinite(x.wd_mul))
+            return fail(MUON_ERR_INVALID_ARG, "tensor %d: lr_mul and wd_mul must be finite", i);
+        const size_t n = size_t(x.numel);
+        if (n > (size_t(1) << 46)) return fail(MUON_ERR_SHAPE, "tensor %d: numel too large", i);
+        auto add = [&](const void* p, size_t bytes) {
+            const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+            ranges.push_back({a, a + bytes, i});
+        };
+        add(x.params, 4 * n);
+        add(x.grads, 2 * n);
+        add(x.exp_avg, 4 * n);
+        add(x.exp_avg_sq, 4 * n);
+        AdamEntry e{};
+        e.p = x.params;
+        e.g = static_cast<const uint16_t*>(x.grads);
+        e.m = x.exp_avg;
+        e.v = x.exp_avg_sq;
+        e.numel = x.numel;
+        e.vec = aligned(x.params, 16) && aligned(x.grads, 16) && aligned(x.exp_avg, 16) && aligned(x.exp_avg_sq, 16);
+        // Per-tensor constants in double ([DA]): decay first, bias corrections in the step size.
+        const double lr_eff = double(lr) * double(x.lr_mul);
+        e.decay = weight_decay != 0.f ? float(1.0 - lr_eff * double(weight_decay) * double(x.wd_mul)) : 1.0f;
+        const double t = double(x.step);
+        const double bias1 = 1.0 - std::pow(double(beta1), t), bias2 = 1.0 - std::pow(double(beta2), t);
+        e.step = float(lr_eff * std::sqrt(bias2) / bias1);
+        entries.push_back(e);
+    }
+    std::sort(ranges.begin(), ranges.end(), [](const Range& x, const Range& y) { return x.a < y.a; });
+    for (size_t k = 1; k < ranges.size(); ++k)
+        if (ranges[k].a < ranges[k - 1].b)
+            return fail(MUON_ERR_INVALID_ARG, "buffers of tensors %d and %d overlap", ranges[k - 1].t, ranges[k].t);
+    if (entries.empty()) return MUON_OK;
+    muon_status st = check_device();
+    if (st != MUON_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (size_t i0 = 0; i0 < entries.size(); i0 += kAdamTab) {
+        const int n = int(std::min<size_t>(kAdamTab, entries.size() - i0));
+        const hipError_t e =
+            timed(MUON_KERNEL_ADAMW, s, [&] { return launch_adamw(entries.data() + i0, n, beta1, beta2, eps, s); });
+        if (e != hipSuccess) return hip_fail(e, "k_adamw launch");
     }
     return MUON_OK;
 }

@@ -146,6 +146,24 @@ hipError_t launch_bx(const Plan& p, const uint16_t* b_hi, const uint16_t* b_lo, 
                      const uint16_t* x_lo, uint16_t* out_hi, uint16_t* out_lo, const float* scale1,
                      hipStream_t s);
 
+// AdamW for the non-matrix parameters (adamw.hip): one launch over up to
+// kAdamTab tensors.  decay = 1 - lr lr_mul wd wd_mul (exactly 1 when wd = 0),
+// step = lr lr_mul (1 - beta2^t)^0.5 / (1 - beta1^t); vec: all four buffers
+// 16-byte aligned.  first_chunk is filled in by the launcher.
+constexpr int kAdamTab = 24;
+struct AdamEntry {
+    float* p;
+    const uint16_t* g;
+    float* m;
+    float* v;
+    int64_t numel;
+    uint32_t first_chunk;
+    int32_t vec;
+    float decay, step;
+};
+int64_t adamw_chunks(int64_t numel);
+hipError_t launch_adamw(const AdamEntry* entries, int n, float beta1, float beta2, float eps, hipStream_t s);
+
 // Small blocks (small_ns.hip): the whole step for one block per workgroup in fp32.
 struct SmallStep {
     const uint16_t* src = nullptr;   // x or gradients

@@ -216,3 +216,51 @@ def test_multi_alignment_by_path(lib):
     # the same offset on a vector-path matrix is rejected
     arr = _mats(_mat(base + (1 << 20) + 8, base + (1 << 21), base + (1 << 22), 128, 128))
     assert lib.muon_step_multi(arr, 1, f(0.02), f(0.01), f(0.95), 1, None, None, 0, None) == 3
+
+
+def _adam(p, g, m, v, numel, step=1, lr_mul=1.0, wd_mul=1.0):
+    e = nsm.MuonAdamTensor()
+    e.params, e.grads, e.exp_avg, e.exp_avg_sq = p, g, m, v
+    e.numel, e.step, e.lr_mul, e.wd_mul = numel, step, lr_mul, wd_mul
+    return e
+
+
+def _adams(*entries):
+    arr = (nsm.MuonAdamTensor * len(entries))()
+    for i, e in enumerate(entries):
+        arr[i] = e
+    return arr
+
+
+def test_adamw_validation_before_device(lib):
+    f = ctypes.c_float
+    base = 1 << 30
+    mb = 1 << 20
+
+    def call(arr, n, lr=0.008, b1=0.8, b2=0.95, eps=1e-8, wd=0.0):
+        return lib.adamw_step_multi(arr, n, f(lr), f(b1), f(b2), f(eps), f(wd), None)
+    good = _adams(_adam(base, base + mb, base + 2 * mb, base + 3 * mb, 1000),
+                  _adam(base + 4 * mb, base + 5 * mb, base + 6 * mb, base + 7 * mb, 768, step=3))
+    assert call(None, 0) == 0
+    assert call(None, 2) == 1                                   # null array
+    assert call(good, -1) == 2
+    assert call(good, 2, lr=float("nan")) == 1
+    assert call(good, 2, wd=float("inf")) == 1
+    assert call(good, 2, eps=-1.0) == 1
+    assert call(good, 2, b1=1.0) == 1
+    assert call(good, 2, b2=-0.1) == 1
+    # tensors with numel 0 are skipped (null pointers allowed): nothing to do, no device work
+    assert call(_adams(_adam(None, None, None, None, 0), _adam(None, None, None, None, 0)), 2) == 0
+    assert call(_adams(_adam(base, base + mb, base + 2 * mb, base + 3 * mb, -5)), 1) == 2
+    assert call(_adams(_adam(None, base + mb, base + 2 * mb, base + 3 * mb, 10)), 1) == 1
+    assert call(_adams(_adam(base, base + mb, base + 2 * mb, base + 3 * mb, 10, step=0)), 1) == 1
+    assert call(_adams(_adam(base, base + mb, base + 2 * mb, base + 3 * mb, 10, lr_mul=float("nan"))), 1) == 1
+    assert call(_adams(_adam(base + 2, base + mb, base + 2 * mb, base + 3 * mb, 10)), 1) == 3
+    assert call(_adams(_adam(base, base + mb + 1, base + 2 * mb, base + 3 * mb, 10)), 1) == 3
+    # exp_avg of the second tensor overlaps params of the first
+    ov = _adams(_adam(base, base + mb, base + 2 * mb, base + 3 * mb, 1000),
+                _adam(base + 4 * mb, base + 5 * mb, base + 400, base + 7 * mb, 10))
+    assert call(ov, 2) == 1
+    assert "overlap" in nsm.muon_last_error()
+    # params and grads of one tensor overlap
+    assert call(_adams(_adam(base, base + 1000, base + 2 * mb, base + 3 * mb, 1000)), 1) == 1

@@ -6,6 +6,7 @@ import pytest
 import torch
 
 import oracle
+import workloads
 from test_oracle_pins import _read_golden
 
 B1, B2 = oracle.ADAM_BETAS
@@ -20,6 +21,16 @@ def test_constants_match_pages():
     assert oracle.ADAM_LR == h["adam_lr"]
     assert oracle.ADAM_BETAS == (h["adam_beta1"], h["adam_beta2"])
     assert oracle.ADAM_EPS == h["adam_eps"]
+
+
+def test_adam_workload_matches_pages():
+    h = _read_golden("hyperparameters.txt")
+    wl = workloads.ADAM_WORKLOADS["gpt124m_adam"]
+    assert (wl.lr, wl.betas, wl.eps) == (h["adam_lr"], (h["adam_beta1"], h["adam_beta2"]), h["adam_eps"])
+    shapes = dict(wl.tensors)
+    vocab, dim = int(h["model_vocab_size"]), int(h["model_dim"])
+    assert shapes["embed"] == (vocab, dim) and shapes["lm_head"] == (vocab, dim)
+    assert shapes["scalars"] == (4 * int(h["model_num_layers"]),)
 
 
 def test_scalars_closed_form():

@@ -15,6 +15,11 @@ every gradient is a seeded random stand-in with the shapes the pages describe):
 * parameter-golf train_gpt.py walkthrough, the starter model description
   (9 layers, width 512, 8 heads with 4 KV heads) and Part 1 (matrix_lr 0.04,
   momentum warm-up from 0.85 to 0.95 over the first 500 steps).
+* AdamW workload: the same Custom Sizing page, section 4 (a DistAdam steps the
+  scalar, head and embedding parameters with lr 0.008, betas (0.8, 0.95),
+  eps 1e-8) and the model it trains (vocab_size 50257, model_dim 768,
+  num_layers 12).  The pages give no scalar count and no Adam weight decay:
+  48 scalars (4 per layer) and weight decay 0 are this workload's readings.
 
 bf16 values are carried as raw uint16 bit patterns.  The float32 -> bf16
 encoder below is IEEE round-to-nearest-even on the upper 16 bits, written from
@@ -32,6 +37,8 @@ __all__ = [
     "f32_to_bf16_bits", "bf16_bits_to_f32", "Group", "Workload", "WORKLOADS",
     "get_workload", "grad_bits_host", "param_init_host", "momentum_warmup",
     "grads_device", "params_device", "gaussian_bits", "to_device_bf16",
+    "AdamWorkload", "ADAM_WORKLOADS", "adam_grad_bits_host", "adam_param_host", "adam_grads_device",
+    "adam_params_device",
 ]
 
 
@@ -310,3 +317,66 @@ def to_device_bf16(bits: np.ndarray, device="cuda"):
     import torch
     t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
     return t.to(device).view(torch.bfloat16)
+
+
+# --------------------------------------------------------------------------
+# AdamW workloads (the non-matrix parameters of the same models)
+# --------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class AdamWorkload:
+    name: str
+    description: str
+    tensors: Tuple[Tuple[str, Tuple[int, ...]], ...]   # (name, shape)
+    lr: float
+    betas: Tuple[float, float]
+    eps: float
+    weight_decay: float
+    grad_std: float
+    seed: int
+
+    @property
+    def numel(self) -> int:
+        return sum(int(np.prod(shape)) for _, shape in self.tensors)
+
+
+ADAM_WORKLOADS: Dict[str, AdamWorkload] = {
+    "gpt124m_adam": AdamWorkload(
+        name="gpt124m_adam",
+        description="124M record's DistAdam params: embed 50257x768, lm_head 50257x768, 48 scalars; "
+                    "bf16 grads ~N(0,1e-3^2); lr 0.008, betas (0.8, 0.95), eps 1e-8, wd 0",
+        tensors=(("embed", (50257, 768)), ("lm_head", (50257, 768)), ("scalars", (48,))),
+        lr=0.008, betas=(0.8, 0.95), eps=1e-8, weight_decay=0.0, grad_std=1e-3, seed=20251205),
+}
+
+
+def adam_grad_bits_host(wl: AdamWorkload, index: int, step: int, numel: Optional[int] = None) -> np.ndarray:
+    """bf16 bits of the gradient of tensor `index` (flattened; first `numel` elements)."""
+    shape = wl.tensors[index][1]
+    n = int(np.prod(shape)) if numel is None else numel
+    rng = _rng(wl.seed, step, index, salt=2)
+    return f32_to_bf16_bits(rng.standard_normal(n, dtype=np.float32) * np.float32(wl.grad_std))
+
+
+def adam_param_host(wl: AdamWorkload, index: int, numel: Optional[int] = None) -> np.ndarray:
+    shape = wl.tensors[index][1]
+    n = int(np.prod(shape)) if numel is None else numel
+    rng = _rng(wl.seed, 0, index, salt=3)
+    return rng.standard_normal(n, dtype=np.float32) * np.float32(0.02)
+
+
+def adam_grads_device(wl: AdamWorkload, index: int, step: int, device="cuda"):
+    """bf16 gradient of tensor `index`, with its shape, drawn on `device`."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(_torch_seed(wl.seed, "adam-grad", step, index))
+    shape = wl.tensors[index][1]
+    g = torch.randn(shape, generator=gen, device=device, dtype=torch.float32).mul_(wl.grad_std)
+    return g.to(torch.bfloat16)
+
+
+def adam_params_device(wl: AdamWorkload, index: int, device="cuda"):
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(_torch_seed(wl.seed, "adam-param", index))
+    shape = wl.tensors[index][1]
+    return torch.randn(shape, generator=gen, device=device, dtype=torch.float32).mul_(0.02)
