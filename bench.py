@@ -33,6 +33,8 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 WORKLOAD = "gpt124m"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_bx_gpt124m_traffic.json")
 GEMM_SOURCE = os.path.join(ROOT, "newton_schulz_muon_amd", "csrc", "ns_gemm.hip")
+ADAM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_adamw_gpt124m_traffic.json")
+ADAM_SOURCE = os.path.join(ROOT, "newton_schulz_muon_amd", "csrc", "adamw.hip")
 
 
 def ns_flops(m: int, n: int, steps: int) -> float:
@@ -52,15 +54,15 @@ def source_digest(path: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def load_traffic():
-    """HBM bytes per k_bx launch from the committed rocprofv3 counter runs,
-    or None when they are missing or the kernel source changed since."""
+def load_traffic(path: str = TRAFFIC_FILE, source: str = GEMM_SOURCE):
+    """HBM bytes per launch of a kernel from the committed rocprofv3 counter
+    runs, or None when they are missing or the kernel source changed since."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha256_16") != source_digest(GEMM_SOURCE):
+    if t.get("source_sha256_16") != source_digest(source):
         return None
     return t.get("bytes_per_launch")
 
@@ -292,6 +294,7 @@ def main():
             result["adamw_gpt124m"] = {"kernel": "k_adamw", "elements": awl.numel, "launches": n_l,
                                        "avg_launch_ms": round(ms, 5), "bound": "hbm", "achieved": round(gbs, 1),
                                        "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                       "traffic": load_traffic(ADAM_TRAFFIC_FILE, ADAM_SOURCE),
                                        "bytes_per_element": 26}
         del tens
 

@@ -22,7 +22,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kThreads = 256;
-constexpr int kGroupsPerThread = 4;                                   // 8-element groups
+constexpr int kGroupsPerThread = 1;   // 8-element groups per thread (1 measured fastest; 2, 4, 8 slower)
 constexpr int64_t kAdamChunk = int64_t(kThreads) * kGroupsPerThread * 8;
 
 struct AdamArgs {
