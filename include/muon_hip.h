@@ -16,6 +16,11 @@
  *        optimizer works" (zeropower_via_newtonschulz5: bf16 cast, Frobenius
  *        normalisation, A = X X^T, B = bA + cA A, X = aX + BX; aspect factor
  *        max(1, m/n)^0.5).
+ *   [SH] the guide to the utils module of distributed_shampoo in
+ *        modded-nanogpt's optimization track, section "tensor math
+ *        utilities: dimension merging, blocking and distributed allocation"
+ *        (merge_small_dims: reshaping a >2-D parameter, e.g. a convolution
+ *        kernel, into the 2-D matrix a Muon-style optimizer works on).
  *   [DA] the article on moving the Adam gradient reduce-scatter of
  *        modded-nanogpt's DistAdam into a backward hook (record of
  *        2025-10-31), "change two": the per-parameter AdamW body of
@@ -211,6 +216,30 @@ typedef struct muon_adam_tensor {
 muon_status adamw_step_multi(const muon_adam_tensor* tensors, int32_t count,
                              float lr, float beta1, float beta2, float eps,
                              float weight_decay, void* stream);
+
+#define MUON_MAX_DIMS 16
+
+/*
+ * Merged shape of a contiguous tensor ([SH] merge_small_dims), so that a
+ * parameter of any rank can be stepped as the 2-D matrix it views as
+ * (e.g. a (32, 3, 64, 64) convolution kernel as 96 x 4096 at threshold 8192):
+ *   - ndim == 0 gives (1); a zero extent gives (0); extents equal to 1 are
+ *     dropped, and if all are 1 the result is (1);
+ *   - walking from the last extent towards the first, the next extent is
+ *     folded into the one being formed while their product is <= threshold
+ *     and the shape still has more than target_ndim extents; an extent above
+ *     the threshold is never split;
+ *   - target_ndim == 0 means no target: the squeezed shape is returned.
+ * Merging adjacent extents of a row-major tensor is a reinterpretation: the
+ * merged tensor is a view of the same memory.
+ *   shape        in, ndim extents (0 <= ndim <= MUON_MAX_DIMS), each >= 0
+ *   threshold    >= 1
+ *   merged       out, room for max(ndim, 1) extents
+ *   merged_ndim  out
+ * Host-only: needs no device.
+ */
+muon_status muon_merge_small_dims(const int64_t* shape, int32_t ndim, int64_t threshold,
+                                  int32_t target_ndim, int64_t* merged, int32_t* merged_ndim);
 
 /* Kernel timing (diagnostics).  Kernel families of the library: */
 typedef enum muon_kernel_kind {

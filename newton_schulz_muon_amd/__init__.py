@@ -11,6 +11,7 @@ Entry points (same names as the C ABI):
     muon_step_batched(params, grads, momentum_buf, *, lr, weight_decay, momentum, ...)
     muon_step_multi(matrices, *, lr, weight_decay, momentum, ...)
     adamw_step_multi(tensors, *, lr, betas, eps, weight_decay)
+    muon_merge_small_dims(shape, threshold, target_ndim=2)
     muon_workspace_bytes(batch, rows, cols, view_blocks=1, cfg=None)
     muon_step_multi_workspace_bytes(matrices, cfg=None)
     muon_ns_config_default(), muon_last_error(), muon_abi_version()
@@ -26,7 +27,7 @@ __all__ = [
     "MuonNSConfig", "MuonError", "LIB_PATH", "EXPORTED_SYMBOLS", "load_library",
     "muon_ns_config_default", "muon_workspace_bytes", "ns_orthogonalize_batched",
     "muon_step_batched", "muon_step_multi", "muon_step_multi_workspace_bytes", "MuonMatrix",
-    "adamw_step_multi", "MuonAdamTensor",
+    "adamw_step_multi", "MuonAdamTensor", "muon_merge_small_dims",
     "muon_timing_enable", "muon_timing_collect", "muon_last_error", "muon_abi_version", "make_config",
     "KERNEL_KINDS",
 ]
@@ -34,7 +35,7 @@ __all__ = [
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmuon_hip.so")
 EXPORTED_SYMBOLS = ("muon_ns_config_default", "muon_workspace_bytes", "ns_orthogonalize_batched",
                     "muon_step_batched", "muon_step_multi_workspace_bytes", "muon_step_multi",
-                    "adamw_step_multi", "muon_timing_enable", "muon_timing_collect", "muon_last_error", "muon_abi_version")
+                    "adamw_step_multi", "muon_merge_small_dims", "muon_timing_enable", "muon_timing_collect", "muon_last_error", "muon_abi_version")
 KERNEL_KINDS = ("prep", "norm_finalize", "gram", "poly", "bx", "finish", "small", "adamw")
 
 MUON_OK = 0
@@ -100,6 +101,9 @@ def load_library():
         adamp = ctypes.POINTER(MuonAdamTensor)
         lib.adamw_step_multi.argtypes = [adamp, i32, f32, f32, f32, f32, f32, vp]
         lib.adamw_step_multi.restype = ctypes.c_int
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        lib.muon_merge_small_dims.argtypes = [i64p, i32, i64, i32, i64p, ctypes.POINTER(ctypes.c_int32)]
+        lib.muon_merge_small_dims.restype = ctypes.c_int
         lib.muon_timing_enable.argtypes = [ctypes.c_uint32]
         lib.muon_timing_enable.restype = ctypes.c_int
         lib.muon_timing_collect.argtypes = [ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]
@@ -274,9 +278,14 @@ def muon_step_batched(params, grads, momentum_buf, *, lr: float, weight_decay: f
     return params
 
 
-def _matrix_array(matrices, device):
+MERGE_THRESHOLD = 8192   # merge_small_dims threshold for >2-D parameters (the pages' conv example)
+
+
+def _matrix_array(matrices, device, merge_threshold: int = MERGE_THRESHOLD):
     """ctypes array of MuonMatrix from (params, grads, momentum_buf) tuples or dicts with
-    those keys and optional update_out, view_blocks, lr_mul, wd_mul."""
+    those keys and optional update_out, view_blocks, lr_mul, wd_mul.  A parameter of another
+    rank is stepped as the 2-D matrix muon_merge_small_dims(shape, merge_threshold, 2) views it
+    as (the same memory); one that does not merge to 2-D is rejected."""
     import torch
     arr = (MuonMatrix * max(1, len(matrices)))()
     keep = []
@@ -287,8 +296,16 @@ def _matrix_array(matrices, device):
         _require(P, f"matrices[{i}].params", torch.float32, device)
         _require(G, f"matrices[{i}].grads", torch.bfloat16, device)
         _require(M, f"matrices[{i}].momentum_buf", torch.float32, device)
-        if P.dim() != 2 or G.shape != P.shape or M.shape != P.shape:
-            raise ValueError(f"matrices[{i}]: params, grads and momentum_buf must be one [rows, cols] shape")
+        if G.shape != P.shape or M.shape != P.shape:
+            raise ValueError(f"matrices[{i}]: params, grads and momentum_buf must have one shape")
+        if P.dim() == 2:
+            rows, cols = P.shape
+        else:
+            merged = muon_merge_small_dims(tuple(P.shape), merge_threshold, 2)
+            if len(merged) != 2:
+                raise ValueError(f"matrices[{i}]: shape {tuple(P.shape)} merges to {merged} at threshold "
+                                 f"{merge_threshold}, not to a 2-D matrix")
+            rows, cols = merged
         out = m.get("update_out")
         if out is not None:
             _require(out, f"matrices[{i}].update_out", torch.bfloat16, device)
@@ -297,7 +314,7 @@ def _matrix_array(matrices, device):
         e = arr[i]
         e.params, e.grads, e.momentum_buf = P.data_ptr(), G.data_ptr(), M.data_ptr()
         e.update_out = out.data_ptr() if out is not None else None
-        e.rows, e.cols = P.shape
+        e.rows, e.cols = rows, cols
         e.view_blocks = int(m.get("view_blocks", 1))
         e.lr_mul = float(m.get("lr_mul", 1.0))
         e.wd_mul = float(m.get("wd_mul", 1.0))
@@ -305,11 +322,12 @@ def _matrix_array(matrices, device):
     return arr, keep
 
 
-def muon_step_multi_workspace_bytes(matrices, cfg: Optional[MuonNSConfig] = None) -> int:
+def muon_step_multi_workspace_bytes(matrices, cfg: Optional[MuonNSConfig] = None,
+                                    merge_threshold: int = MERGE_THRESHOLD) -> int:
     if not matrices:
         return 0
     first = matrices[0] if isinstance(matrices[0], dict) else {"params": matrices[0][0]}
-    arr, _ = _matrix_array(matrices, first["params"].device)
+    arr, _ = _matrix_array(matrices, first["params"].device, merge_threshold)
     lib = load_library()
     n = lib.muon_step_multi_workspace_bytes(arr, len(matrices), ctypes.byref(cfg) if cfg is not None else None)
     if n == ctypes.c_size_t(-1).value:
@@ -319,15 +337,17 @@ def muon_step_multi_workspace_bytes(matrices, cfg: Optional[MuonNSConfig] = None
 
 def muon_step_multi(matrices, *, lr: float, weight_decay: float, momentum: float, nesterov: bool = True,
                     ns_steps: int = 5, coeffs: Optional[Tuple[float, float, float]] = None,
-                    eps: Optional[float] = None, precision: str = "fast", cfg: Optional[MuonNSConfig] = None):
+                    eps: Optional[float] = None, precision: str = "fast", cfg: Optional[MuonNSConfig] = None,
+                    merge_threshold: int = MERGE_THRESHOLD):
     """One in-place Muon step on a list of matrices, each (params fp32, grads bf16, momentum fp32)
-    [rows, cols] or a dict with those keys and optional update_out, view_blocks, lr_mul, wd_mul."""
+    or a dict with those keys and optional update_out, view_blocks, lr_mul, wd_mul.  Parameters
+    that are not 2-D are stepped as their muon_merge_small_dims view (merge_threshold, target 2)."""
     import torch
     if not matrices:
         return
     first = matrices[0] if isinstance(matrices[0], dict) else {"params": matrices[0][0]}
     device = first["params"].device
-    arr, _keep = _matrix_array(matrices, device)
+    arr, _keep = _matrix_array(matrices, device, merge_threshold)
     cfg = cfg if cfg is not None else make_config(ns_steps, coeffs, eps, precision)
     lib = load_library()
     with torch.cuda.device(device):
@@ -372,3 +392,15 @@ def adamw_step_multi(tensors, *, lr: float, betas: Tuple[float, float], eps: flo
         stream = torch.cuda.current_stream(device).cuda_stream
         _check(lib.adamw_step_multi(arr, len(tensors), float(lr), float(b1), float(b2), float(eps),
                                     float(weight_decay), stream))
+
+
+def muon_merge_small_dims(shape, threshold: int, target_ndim: int = 2) -> Tuple[int, ...]:
+    """Merged shape of a contiguous tensor (the C ABI's muon_merge_small_dims);
+    target_ndim 0 means no target."""
+    lib = load_library()
+    shape = [int(s) for s in shape]
+    arr = (ctypes.c_int64 * max(1, len(shape)))(*shape)
+    out = (ctypes.c_int64 * max(1, len(shape)))()
+    nd = ctypes.c_int32(0)
+    _check(lib.muon_merge_small_dims(arr, len(shape), int(threshold), int(target_ndim), out, ctypes.byref(nd)))
+    return tuple(int(out[i]) for i in range(nd.value))

@@ -795,6 +795,57 @@ muon_status adamw_step_multi(const muon_adam_tensor* tensors, int32_t count, flo
     return MUON_OK;
 }
 
+muon_status muon_merge_small_dims(const int64_t* shape, int32_t ndim, int64_t threshold, int32_t target_ndim,
+                                  int64_t* merged, int32_t* merged_ndim) {
+    g_err.clear();
+    if (ndim < 0 || ndim > MUON_MAX_DIMS) return fail(MUON_ERR_SHAPE, "ndim must be in [0, %d]", MUON_MAX_DIMS);
+    if ((ndim > 0 && shape == nullptr) || merged == nullptr || merged_ndim == nullptr)
+        return fail(MUON_ERR_INVALID_ARG, "shape, merged and merged_ndim must be non-null");
+    if (threshold < 1) return fail(MUON_ERR_INVALID_ARG, "threshold must be >= 1");
+    if (target_ndim < 0) return fail(MUON_ERR_INVALID_ARG, "target_ndim must be >= 1, or 0 for no target");
+    for (int32_t i = 0; i < ndim; ++i)
+        if (shape[i] < 0) return fail(MUON_ERR_SHAPE, "extent %d is negative", i);
+    auto put1 = [&](int64_t v) {
+        merged[0] = v;
+        *merged_ndim = 1;
+        return MUON_OK;
+    };
+    if (ndim == 0) return put1(1);                       // a 0-D tensor is 1-D
+    for (int32_t i = 0; i < ndim; ++i)
+        if (shape[i] == 0) return put1(0);               // empty
+    int64_t sq[MUON_MAX_DIMS];
+    int32_t ns = 0;
+    for (int32_t i = 0; i < ndim; ++i)
+        if (shape[i] != 1) sq[ns++] = shape[i];          // size-1 extents squeezed out
+    if (ns == 0) return put1(1);
+    if (target_ndim == 0) {                              // no target: no merging
+        for (int32_t i = 0; i < ns; ++i) merged[i] = sq[i];
+        *merged_ndim = ns;
+        return MUON_OK;
+    }
+    // Walk from the last extent to the first.  `cur` is the extent being
+    // formed; out[] collects finished extents right to left.  The next extent
+    // folds into `cur` while the shape still has more than target_ndim
+    // extents and the product stays within the threshold.
+    int64_t out[MUON_MAX_DIMS];
+    int32_t nout = 0;
+    int64_t cur = sq[ns - 1];
+    for (int32_t i = ns - 2; i >= 0; --i) {
+        const int64_t count = int64_t(i) + 2 + nout;
+        const bool fits = sq[i] <= threshold / cur;     // sq[i] * cur <= threshold, without overflow
+        if (count > target_ndim && fits) {
+            cur *= sq[i];
+        } else {
+            out[nout++] = cur;
+            cur = sq[i];
+        }
+    }
+    out[nout++] = cur;
+    for (int32_t i = 0; i < nout; ++i) merged[i] = out[nout - 1 - i];
+    *merged_ndim = nout;
+    return MUON_OK;
+}
+
 muon_status muon_timing_enable(uint32_t kernel_mask) {
     g_err.clear();
     if (kernel_mask >> MUON_KERNEL_COUNT) return fail(MUON_ERR_INVALID_ARG, "unknown kernel bits in mask 0x%x", kernel_mask);

@@ -97,3 +97,46 @@ def test_multi_many_matrices_one_shape(nsm):
     # 40 matrices of one shape: the shape group spans two pointer tables (32 + 8)
     shapes = [(64, 128, 1, 1.0 + 0.01 * i, 1.0) for i in range(40)] + [(1, 12, 1, 1.0, 1.0)] * 35
     _run_case(nsm, shapes, seed=4, label="many")
+
+
+def test_multi_merged_conv_kernels_match_oracle(nsm):
+    """>2-D parameters are stepped as the 2-D matrix merge_small_dims gives
+    (threshold 8192): a (32, 3, 64, 64) convolution kernel as 96 x 4096 (the
+    pages' example, matrix-core path), (8, 4, 5, 5) as 8 x 100 and
+    (16, 1, 3, 3) as 16 x 9 (small-block path).  Checked against the fp64
+    oracle's step on the oracle's own merged view."""
+    import numpy as np
+    import torch
+    import oracle
+    from oracle.shape_oracle import merge_small_dims
+    from parity import (MOMENTUM_TOL, NS_REL_TOL, assert_ns_close, bits_to_f64, rel_fro,
+                        torch_bf16_to_bits)
+    shapes = [(32, 3, 64, 64), (8, 4, 5, 5), (16, 1, 3, 3)]
+    rng = np.random.default_rng(31)
+    mats, host = [], []
+    for k, shp in enumerate(shapes):
+        P0 = (rng.standard_normal(shp) * 0.02).astype(np.float32)
+        gb = workloads.gaussian_bits(shp, seed=700 + k, std=1e-2)
+        P = torch.from_numpy(P0).cuda()
+        mats.append(dict(params=P, grads=workloads.to_device_bf16(gb), momentum_buf=torch.zeros_like(P),
+                         update_out=torch.empty(shp, dtype=torch.bfloat16, device="cuda")))
+        host.append((P0, gb))
+    print("[multi merge] conv-shaped parameters", flush=True)
+    nsm.muon_step_multi(mats, lr=0.02, weight_decay=0.01, momentum=0.95)
+    torch.cuda.synchronize()
+    for shp, m, (P0, gb) in zip(shapes, mats, host):
+        r, c = merge_small_dims(shp, 8192, 2)
+        assert nsm.muon_merge_small_dims(shp, 8192, 2) == (r, c)
+        P_ref, M_ref, O_ref = oracle.muon_step(P0.reshape(1, r, c), bits_to_f64(gb).reshape(1, r, c),
+                                               np.zeros((1, r, c)), lr=0.02, weight_decay=0.01, momentum=0.95)
+        O_got = bits_to_f64(torch_bf16_to_bits(m["update_out"])).reshape(r, c)
+        assert_ns_close(O_got, O_ref[0], label=f"{shp} as {r}x{c}")
+        assert rel_fro(m["momentum_buf"].cpu().numpy().reshape(r, c), M_ref[0]) <= MOMENTUM_TOL
+        lr_eff = float(np.float32(0.02)) * oracle.aspect_factor(r, c)
+        bound = NS_REL_TOL * lr_eff * np.linalg.norm(O_ref) + 4 * 2.0 ** -24 * np.linalg.norm(P_ref)
+        assert np.linalg.norm(m["params"].cpu().numpy().reshape(r, c) - P_ref[0]) <= bound
+    # a tensor that cannot merge to 2-D at this threshold is rejected before any work
+    bad = torch.zeros((4096, 3, 4096), device="cuda")
+    with pytest.raises(ValueError):
+        nsm.muon_step_multi([dict(params=bad, grads=bad.to(torch.bfloat16), momentum_buf=bad.clone())],
+                            lr=0.02, weight_decay=0.0, momentum=0.95)
