@@ -681,7 +681,12 @@ constexpr int64_t kCUs = 256;
 // a round is one 256-wide tile per CU, or two 128-wide tiles per CU (which
 // share the CU; per flop the 128-wide tiling is about 1.3x slower: twice the
 // operand traffic per MFMA).
-double round_cycles_big(int64_t K) { return 1305.0 * double(K / 32) + 12000.0; }
+// A 256-wide symmetric tile also stores its mirror (twice the bytes of a B'X
+// tile), and when a launch is one round every workgroup stores at once, at
+// the HBM limit: 25000 rather than 12000 fixed cycles (measured on the 124M
+// attn Gram and polynomial, 240 tiles at K = 768, which run 1.8% faster per
+// step as 128-wide tiles).
+double round_cycles_big(int64_t K, bool sym) { return 1305.0 * double(K / 32) + (sym ? 25000.0 : 12000.0); }
 double round_cycles_small(int64_t K) { return 812.0 * double(K / 32) + 8500.0; }
 
 // Tiling of one launch (n products of one kind), by the estimated duration
@@ -736,9 +741,10 @@ hipError_t run(const Plan* const* plans, GemmArgs a, hipStream_t s) {
     if (big_ok) {
         const int64_t big = geometry(256);
         const int64_t full = big / kCUs, tail = big % kCUs;
-        const double t_split = double(full) * round_cycles_big(K) +
+        const double rb = round_cycles_big(K, SYM);
+        const double t_split = double(full) * rb +
                                double((4 * tail + 2 * kCUs - 1) / (2 * kCUs)) * round_cycles_small(K);
-        const double t_big = double(full + (tail ? 1 : 0)) * round_cycles_big(K);
+        const double t_big = double(full + (tail ? 1 : 0)) * rb;
         if (t_big <= t_split && t_big < t_small) return launch(256, big, 0, 0);
         if (t_split < t_small) {
             if (full > 0) {

@@ -55,14 +55,19 @@ def test_ns_parity_default(nsm, shape):
 
 # Batches large enough for 256-wide tiles with a partial last round, which is
 # finished by a second launch of 128-wide quadrants.  50 blocks of 768 x 768:
-# 300 upper-triangle tiles (256 + 44, the 44 including diagonal tiles whose
-# lower quadrant is skipped) and 450 B X tiles (256 + 194).  24 of 768 x 1536:
-# 144 symmetric tiles (all 128-wide) and 432 B X tiles (256 + 176).  Blocks
-# on both sides of each launch boundary, and the first and last, are checked.
+# the symmetric products run as 128-wide tiles (at K = 768 two 128-wide rounds
+# cost what one 256-wide round does), the 450 B X tiles as 256 + 194.  24 of
+# 768 x 1536: 144 symmetric tiles (all 128-wide) and 432 B X tiles (256 + 176).
+# 50 of 768 x 3072: 300 upper-triangle Gram tiles at K = 3072 (256 + 44, the
+# 44 including diagonal tiles whose lower quadrant is skipped; blocks 42 and
+# 43 straddle the launch boundary) and 1800 B X tiles (1792 + 8, block 49).
+# Blocks on both sides of each launch boundary, and the first and last, are
+# checked.
 @pytest.mark.parametrize("batch,shape,check", [
     (50, (768, 768), (0, 28, 29, 42, 43, 49)),
     (24, (768, 1536), (0, 14, 15, 23)),
     (24, (1536, 768), (0, 14, 15, 23)),
+    (50, (768, 3072), (0, 42, 43, 49)),
 ])
 def test_ns_parity_tail_split(nsm, batch, shape, check):
     print(f"[ns tail split] batch={batch} shape={shape}", flush=True)
