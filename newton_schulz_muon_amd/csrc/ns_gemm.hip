@@ -62,6 +62,7 @@ constexpr int NTHR = 256;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -360,6 +361,17 @@ __device__ __forceinline__ int mir_off(int row, int col) {
     return row * (TW * 2) + (((col >> 3) ^ f) << 4) + (((col >> 2) & 1) << 3);
 }
 
+// bf16 chunk of the B X epilogue: rows of TW bf16 (CH = TW / 8 chunks of 16
+// bytes), chunk index XOR (row % CH) and the two 8-byte halves of a chunk
+// swapped on rows CH..2 CH - 1.  The MFMA-layout writes (8 bytes by each of
+// 32 rows x 2 lanes) then cover 64 distinct banks for TW = 128, and the
+// row reads (16 bytes, CH lanes per row) each cover a whole row.
+template <int TW>
+__device__ __forceinline__ int bst_off(int row, int col) {
+    constexpr int CH = TW / 8;
+    return row * (TW * 2) + (((col >> 3) ^ (row & (CH - 1))) << 4) + ((((col >> 2) & 1) ^ ((row / CH) & 1)) << 3);
+}
+
 enum Kind { kGram = 0, kPoly = 1, kPolySplit = 2, kBx = 3, kBxSplit = 4 };
 
 // One product of a launch: a batch of same-shaped blocks.  A launch may carry
@@ -583,6 +595,31 @@ __global__ __launch_bounds__(NTHR) void k_gemm(GemmArgs args) {
     if constexpr (POLY) load_a(0, abuf[0]);
 #pragma unroll
     for (int i = 0; i < F; ++i) {
+        if constexpr (KIND == kBx) {
+            // B X: the rounded bf16 values go through LDS (half the bytes of
+            // fp32 staging) and leave as 16-byte pieces of rows.
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < F; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    uint16_t hb[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) hb[e] = f32_to_bf16(acc[i][j][g * 4 + e] * sc);
+                    *reinterpret_cast<u32x2*>(sf + bst_off<TW>(lr, j * 32 + g * 8 + lk * 4)) = pack4(hb);
+                }
+            __builtin_amdgcn_sched_barrier(0);
+            constexpr int CH = TW / 8, RPB = 64 / CH;
+            const int brow = lane / CH, bch = lane % CH;
+#pragma unroll
+            for (int t = 0; t < 32 / RPB; ++t) {
+                const int rr = t * RPB + brow;
+                u32x4 v = *reinterpret_cast<const u32x4*>(sf + rr * (TW * 2) + ((bch ^ (rr & (CH - 1))) << 4));
+                if ((rr / CH) & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+                *reinterpret_cast<u32x4*>(out0 + (int64_t)(row0 + wr0 + i * 32 + rr) * a.ldo + col0 + wc0 + 8 * bch) = v;
+            }
+            continue;
+        }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < F; ++j)
