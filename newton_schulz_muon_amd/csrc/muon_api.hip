@@ -4,8 +4,9 @@
 // Launch sequence of one call (large blocks):
 //   k_prep            momentum + cast to the oriented padded iterate + tile norms
 //   k_norm_finalize   1/s and 1/s^2 per NS block
-//   ns_steps x { k_sym<Gram>, k_sym<Poly>, k_bx }   ping-pong between two iterates
-//                     (k_sym<Poly> forms B' = a I + b A + c A A, k_bx X' = B' X);
+//   ns_steps x { k_gemm<kGram>, k_gemm<kPoly>, k_gemm<kBx> }   ping-pong between
+//                     two iterates (kPoly forms B' = a I + b A + c A A, kBx
+//                     X' = B' X);
 //                     iteration 1 folds the normalisation into its epilogues
 //                     (A = U U^T / s^2, X1 = B' U / s), so X0 = U / s is
 //                     never materialised
@@ -249,13 +250,13 @@ muon_status run_ns(const Plan& p, const muon_ns_config& cfg, const Buffers& b, h
     for (int it = 0; it < cfg.ns_steps; ++it) {
         const float* sc = it == 0 ? b.scale : nullptr;
         e = timed(MUON_KERNEL_GRAM, s, [&] { return launch_gram(p, b.xh[cur], b.a, sc, s); });
-        if (e != hipSuccess) return hip_fail(e, "k_sym<gram> launch");
+        if (e != hipSuccess) return hip_fail(e, "k_gemm<gram> launch");
         e = timed(MUON_KERNEL_POLY, s, [&] { return launch_poly(p, b.a, b.bh, b.bl, cfg.a, cfg.b, cfg.c, s); });
-        if (e != hipSuccess) return hip_fail(e, "k_sym<poly> launch");
+        if (e != hipSuccess) return hip_fail(e, "k_gemm<poly> launch");
         e = timed(MUON_KERNEL_BX, s, [&] {
             return launch_bx(p, b.bh, b.bl, b.xh[cur], b.xl[cur], b.xh[cur ^ 1], b.xl[cur ^ 1], sc, s);
         });
-        if (e != hipSuccess) return hip_fail(e, "k_bx launch");
+        if (e != hipSuccess) return hip_fail(e, "k_gemm<bx> launch");
         cur ^= 1;
     }
     *final_idx = cur;
