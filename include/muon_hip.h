@@ -39,7 +39,9 @@
  *   - Arguments are validated before anything is enqueued: on any error the
  *     call has no side effects.  batch == 0 is a valid no-op.
  *   - Non-finite inputs propagate; they are not checked.
- *   - Calls on different streams must use different workspaces.
+ *   - Calls on different streams must use different workspaces.  The part of
+ *     a workspace a call uses must not overlap its data buffers
+ *     (MUON_ERR_INVALID_ARG).
  *   - No C++ exception crosses this boundary.
  *
  * The NS block: with view_blocks = v, each stored rows x cols matrix is read

@@ -347,7 +347,8 @@ muon_status plan_multi(const muon_matrix* mats, int32_t count, const muon_ns_con
 
 // Vector-path blocks (not small, block width a multiple of 8) are read and
 // written in 16-byte pieces; the others element by element.
-muon_status check_multi_buffers(const muon_matrix* mats, int32_t count, const std::vector<ShapeGroup>& groups) {
+muon_status check_multi_buffers(const muon_matrix* mats, int32_t count, const std::vector<ShapeGroup>& groups,
+                                const void* workspace, size_t ws_bytes) {
     struct Range { uintptr_t a, b; int32_t mat; };
     std::vector<Range> ranges;
     ranges.reserve(size_t(count) * 4);
@@ -375,11 +376,18 @@ muon_status check_multi_buffers(const muon_matrix* mats, int32_t count, const st
         add(m.momentum_buf, 4 * n);
         if (m.update_out) add(m.update_out, 2 * n);
     }
+    if (workspace != nullptr && ws_bytes > 0) {
+        const uintptr_t a = reinterpret_cast<uintptr_t>(workspace);
+        ranges.push_back({a, a + ws_bytes, -1});
+    }
     std::sort(ranges.begin(), ranges.end(), [](const Range& x, const Range& y) { return x.a < y.a; });
     for (size_t k = 1; k < ranges.size(); ++k)
         if (ranges[k].a < ranges[k - 1].b)
-            return fail(MUON_ERR_INVALID_ARG, "buffers of matrices %d and %d overlap", ranges[k - 1].mat,
-                        ranges[k].mat);
+            return (ranges[k - 1].mat < 0 || ranges[k].mat < 0)
+                       ? fail(MUON_ERR_INVALID_ARG, "the workspace overlaps buffers of matrix %d",
+                              ranges[k - 1].mat < 0 ? ranges[k].mat : ranges[k - 1].mat)
+                       : fail(MUON_ERR_INVALID_ARG, "buffers of matrices %d and %d overlap", ranges[k - 1].mat,
+                              ranges[k].mat);
     return MUON_OK;
 }
 
@@ -461,6 +469,8 @@ muon_status ns_orthogonalize_batched(const void* x, void* out, int64_t batch, in
         return fail(MUON_ERR_INVALID_ARG, "out overlaps x without being x");
     st = common_checks(p, workspace, workspace_bytes);
     if (st != MUON_OK) return st;
+    if (p.total > 0 && (overlaps(workspace, p.total, x, bytes) || overlaps(workspace, p.total, out, bytes)))
+        return fail(MUON_ERR_INVALID_ARG, "workspace overlaps x or out");
     st = check_device();
     if (st != MUON_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -521,6 +531,10 @@ muon_status muon_step_batched(float* params, const void* grads, float* momentum_
         return fail(MUON_ERR_INVALID_ARG, "params, grads, momentum_buf and update_out must not overlap");
     st = common_checks(p, workspace, workspace_bytes);
     if (st != MUON_OK) return st;
+    if (p.total > 0 &&
+        (overlaps(workspace, p.total, params, 4 * n) || overlaps(workspace, p.total, grads, 2 * n) ||
+         overlaps(workspace, p.total, momentum_buf, 4 * n) || overlaps(workspace, p.total, update_out, 2 * n)))
+        return fail(MUON_ERR_INVALID_ARG, "workspace overlaps a data buffer");
     st = check_device();
     if (st != MUON_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -589,7 +603,7 @@ muon_status muon_step_multi(const muon_matrix* mats, int32_t count, float lr, fl
     st = plan_multi(mats, count, cfg, groups, total);
     if (st != MUON_OK) return st;
     if (count == 0) return MUON_OK;
-    st = check_multi_buffers(mats, count, groups);
+    st = check_multi_buffers(mats, count, groups, total > 0 ? workspace : nullptr, total);
     if (st != MUON_OK) return st;
     if (total > 0) {
         if (workspace == nullptr || workspace_bytes < total)

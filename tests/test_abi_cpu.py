@@ -264,3 +264,27 @@ def test_adamw_validation_before_device(lib):
     assert "overlap" in nsm.muon_last_error()
     # params and grads of one tensor overlap
     assert call(_adams(_adam(base, base + 1000, base + 2 * mb, base + 3 * mb, 1000)), 1) == 1
+
+
+def test_workspace_must_not_overlap_data(lib):
+    # Valid calls in every other respect; each fails on the overlap before any device work.
+    f = ctypes.c_float
+    base = 1 << 32
+    need = nsm.muon_workspace_bytes(2, 128, 128)
+    n = 2 * 128 * 128
+    P, G, M = base, base + 8 * n, base + 16 * n
+    ws = base + 24 * n
+    # workspace starting inside momentum_buf
+    assert lib.muon_step_batched(P, G, M, 2, 128, 128, 1, f(0.02), f(0.01), f(0.95), 1, f(1.0), f(1.0),
+                                 None, None, ctypes.c_void_p(M + 256), need, None) == 1
+    assert "workspace" in nsm.muon_last_error()
+    # ns: workspace covering x
+    assert lib.ns_orthogonalize_batched(ctypes.c_void_p(G), ctypes.c_void_p(ws), 2, 128, 128, 1, None,
+                                        ctypes.c_void_p(G - 256), need, None) == 1
+    # multi: workspace overlapping the second matrix's grads
+    arr = _mats(_mat(base, base + (1 << 20), base + (1 << 21), 128, 128),
+                _mat(base + (1 << 22), base + (1 << 23), base + (1 << 24), 128, 128))
+    wsb = lib.muon_step_multi_workspace_bytes(arr, 2, None)
+    assert lib.muon_step_multi(arr, 2, f(0.02), f(0.01), f(0.95), 1, None, ctypes.c_void_p(base + (1 << 23) - 256),
+                               wsb, None) == 1
+    assert "workspace overlaps" in nsm.muon_last_error()
