@@ -32,9 +32,11 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 WORKLOAD = "gpt124m"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_bx_gpt124m_traffic.json")
+LOOP_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_ns_loop_gpt124m_traffic.json")
 GEMM_SOURCE = os.path.join(ROOT, "newton_schulz_muon_amd", "csrc", "ns_gemm.hip")
 ADAM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_adamw_gpt124m_traffic.json")
 ADAM_SOURCE = os.path.join(ROOT, "newton_schulz_muon_amd", "csrc", "adamw.hip")
+SETTLE_CALLS = 12              # calls before warm-up that let the automatic NS schedule choose
 
 
 def ns_flops(m: int, n: int, steps: int) -> float:
@@ -116,6 +118,9 @@ def main():
     ap.add_argument("--api", choices=("multi", "batched"), default="multi",
                     help="multi: one muon_step_multi call per step over all matrices (default); "
                          "batched: one muon_step_batched call per shape group")
+    ap.add_argument("--ns-schedule", choices=("auto", "persistent", "per_product"), default="auto",
+                    help="auto: the library's per-shape choice (default); persistent: all NS iterations of "
+                         "a wave in one launch; per_product: three launches per iteration")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run a plain device copy of MIB MiB first (HBM counter calibration)")
     args = ap.parse_args()
@@ -133,6 +138,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     nsm.load_library()
+    nsm.muon_set_ns_schedule(args.ns_schedule)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     wl = workloads.get_workload(WORKLOAD)
@@ -167,6 +173,13 @@ def main():
             nsm.muon_step_batched(P, G, M, lr=wl.lr, weight_decay=wl.weight_decay, momentum=wl.momentum,
                                   view_blocks=g.view_blocks, ns_steps=wl.ns_steps, precision=g.precision)
 
+    # The library's automatic NS schedule times its first ten calls per set of
+    # shapes (alternating the per-product launches and the persistent loop)
+    # and keeps the faster one once those calls' events have completed: let it
+    # settle, synchronising after each call, before the warm-up proper.
+    for _ in range(SETTLE_CALLS):
+        step()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -179,12 +192,12 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
 
-    # ---- roofline region: the same K steps again, each B'X call bracketed by a
-    # hipEvent pair on the library's stream.  Every event record costs a
-    # dispatch bubble of ~4.4 us (two per call, ~88 us per step), which is why
-    # `value` comes from the uninstrumented region above.
+    # ---- roofline region: the same K steps again, each NS-loop (or, per
+    # product, B'X) call bracketed by a hipEvent pair on the library's stream.
+    # Every event record costs a short dispatch bubble, which is why `value`
+    # comes from the uninstrumented region above.
     nsm.muon_timing_collect()
-    nsm.muon_timing_enable(["bx"])
+    nsm.muon_timing_enable(["bx", "ns_loop"])
     torch.cuda.synchronize()
     r0 = time.perf_counter()
     for _ in range(args.steps):
@@ -205,8 +218,21 @@ def main():
                    if not (min(g.block_shape) <= 64 and g.block_shape[0] * g.block_shape[1] <= 8192)]
     bx_flops_step = sum(g.n_blocks * bx_flops(*g.block_shape, wl.ns_steps) for g in mfma_groups)
     bx_launches, bx_ms = kt.get("bx", (0, 0.0))
+    loop_launches, loop_ms = kt.get("ns_loop", (0, 0.0))
     roofline = None
-    if bx_launches:
+    if loop_launches:
+        # one launch runs every NS iteration of a wave: nominal NS flops of the
+        # MFMA-path blocks per launch over its duration
+        loop_flops_step = sum(g.n_blocks * ns_flops(*g.block_shape, wl.ns_steps) for g in mfma_groups)
+        achieved = loop_flops_step * args.steps / (loop_ms / 1000.0) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                    "traffic": load_traffic(LOOP_TRAFFIC_FILE),
+                    "kernel": "k_ns_loop (every NS iteration: X X^T, aI + bA + cA^2, B' X; nominal flops)",
+                    "launches": loop_launches, "avg_launch_ms": round(loop_ms / loop_launches, 5),
+                    "flops_per_launch_avg": loop_flops_step * args.steps / loop_launches,
+                    "region_ms_per_step": round((r1 - r0) * 1000.0 / args.steps, 4)}
+    elif bx_launches:
         achieved = bx_flops_step * args.steps / (bx_ms / 1000.0) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
@@ -226,6 +252,7 @@ def main():
                    "matrices": wl.n_matrices, "ns_blocks": n_blocks, "ns_steps": wl.ns_steps,
                    "precision": "fast (bf16 MFMA, fp32 accumulate); gates on the fp32 small-block path",
                    "nominal_ns_gflop_per_step": round(flops_step / 1e9, 2)},
+        "ns_schedule": args.ns_schedule, "settle_calls": SETTLE_CALLS,
         "matrices_per_s": round(wl.n_matrices / (ms_per_step / 1000.0), 1),
         "ns_blocks_per_s": round(n_blocks / (ms_per_step / 1000.0), 1),
         "mfma_peak_frac_nominal": round(value / PEAK_BF16_TFLOPS, 4),
@@ -251,6 +278,9 @@ def main():
         # ---- NS only on the metric's exact batch: 32 x 768 x 3072, no view
         x = workloads.grads_device(workloads.get_workload("metric32"), workloads.get_workload("metric32").groups[0], 0, dev)
         out = torch.empty_like(x)
+        for _ in range(SETTLE_CALLS):
+            nsm.ns_orthogonalize_batched(x, out)
+            torch.cuda.synchronize()
         for _ in range(3):
             nsm.ns_orthogonalize_batched(x, out)
         torch.cuda.synchronize()
@@ -261,8 +291,15 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / args.steps
+        nsm.muon_timing_collect()
+        nsm.muon_timing_enable(["ns_loop", "gram"])
+        nsm.ns_orthogonalize_batched(x, out)
+        torch.cuda.synchronize()
+        nsm.muon_timing_enable([])
+        used = "persistent" if "ns_loop" in nsm.muon_timing_collect() else "per_product"
         f = 32 * ns_flops(768, 3072, 5)
         result["ns_only_32x768x3072"] = {"ms": round(ms, 4), "tflops": round(f / (ms / 1000) / 1e12, 2),
+                                         "schedule": used,
                                          "matrices_per_s": round(32 / (ms / 1000), 1),
                                          "mfma_peak_frac_nominal": round(f / (ms / 1000) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         del x, out

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 3
+#define MUON_ABI_VERSION 4
 
 typedef enum muon_status {
     MUON_OK = 0,
@@ -243,6 +243,28 @@ muon_status adamw_step_multi(const muon_adam_tensor* tensors, int32_t count,
 muon_status muon_merge_small_dims(const int64_t* shape, int32_t ndim, int64_t threshold,
                                   int32_t target_ndim, int64_t* merged, int32_t* merged_ndim);
 
+/* Schedule of the Newton-Schulz iterations of large blocks (process-wide).
+ * Two schedules give bitwise the same results:
+ *   per-product: each iteration launches the Gram, polynomial and B X
+ *     products in turn;
+ *   persistent: all iterations of the blocks of a call (of a wave, in
+ *     muon_step_multi) run in one launch of one workgroup per CU, which take
+ *     runs of 256-wide tiles of the three products from a precomputed queue
+ *     and wait on per-block completion counters kept in the workspace.  It
+ *     needs FAST precision and both padded sides of every block batch
+ *     multiples of 256; other calls use the per-product schedule.
+ * mode 0 (default): automatic, per set of block shapes and counts: the first
+ *   10 calls with a new set alternate the two schedules under hipEvent timing
+ *   (recorded on the call's stream) and, once those events have completed,
+ *   later calls use the one with the lower best time;
+ * mode 1: per-product always;  mode 2: persistent wherever it applies.
+ * The persistent schedule keeps one device copy of the queue of each distinct
+ * set (built with hipMalloc and hipMemcpy by the first call that needs it)
+ * until the process ends; beyond 64 such sets (256 for the automatic
+ * choice), calls with a new set use the per-product schedule.
+ * Returns MUON_ERR_INVALID_ARG for any other mode. */
+muon_status muon_set_ns_schedule(int32_t mode);
+
 /* Kernel timing (diagnostics).  Kernel families of the library: */
 typedef enum muon_kernel_kind {
     MUON_KERNEL_PREP = 0,           /* momentum + cast + tile norms            */
@@ -253,7 +275,8 @@ typedef enum muon_kernel_kind {
     MUON_KERNEL_FINISH = 5,         /* NS output / parameter update            */
     MUON_KERNEL_SMALL = 6,          /* whole step for small blocks             */
     MUON_KERNEL_ADAMW = 7,          /* AdamW step (adamw_step_multi)           */
-    MUON_KERNEL_COUNT = 8
+    MUON_KERNEL_NS_LOOP = 8,        /* all NS iterations in one launch         */
+    MUON_KERNEL_COUNT = 9
 } muon_kernel_kind;
 
 /* While kernel_mask has bit k set, every launch of kernel family k records a

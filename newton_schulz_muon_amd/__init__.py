@@ -29,14 +29,16 @@ __all__ = [
     "muon_step_batched", "muon_step_multi", "muon_step_multi_workspace_bytes", "MuonMatrix",
     "adamw_step_multi", "MuonAdamTensor", "muon_merge_small_dims",
     "muon_timing_enable", "muon_timing_collect", "muon_last_error", "muon_abi_version", "make_config",
-    "KERNEL_KINDS",
+    "muon_set_ns_schedule", "KERNEL_KINDS", "NS_SCHEDULES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmuon_hip.so")
 EXPORTED_SYMBOLS = ("muon_ns_config_default", "muon_workspace_bytes", "ns_orthogonalize_batched",
                     "muon_step_batched", "muon_step_multi_workspace_bytes", "muon_step_multi",
-                    "adamw_step_multi", "muon_merge_small_dims", "muon_timing_enable", "muon_timing_collect", "muon_last_error", "muon_abi_version")
-KERNEL_KINDS = ("prep", "norm_finalize", "gram", "poly", "bx", "finish", "small", "adamw")
+                    "adamw_step_multi", "muon_merge_small_dims", "muon_set_ns_schedule", "muon_timing_enable",
+                    "muon_timing_collect", "muon_last_error", "muon_abi_version")
+KERNEL_KINDS = ("prep", "norm_finalize", "gram", "poly", "bx", "finish", "small", "adamw", "ns_loop")
+NS_SCHEDULES = {"auto": 0, "per_product": 1, "persistent": 2}
 
 MUON_OK = 0
 _STATUS_NAMES = {0: "MUON_OK", 1: "MUON_ERR_INVALID_ARG", 2: "MUON_ERR_SHAPE", 3: "MUON_ERR_ALIGNMENT",
@@ -104,6 +106,8 @@ def load_library():
         i64p = ctypes.POINTER(ctypes.c_int64)
         lib.muon_merge_small_dims.argtypes = [i64p, i32, i64, i32, i64p, ctypes.POINTER(ctypes.c_int32)]
         lib.muon_merge_small_dims.restype = ctypes.c_int
+        lib.muon_set_ns_schedule.argtypes = [i32]
+        lib.muon_set_ns_schedule.restype = ctypes.c_int
         lib.muon_timing_enable.argtypes = [ctypes.c_uint32]
         lib.muon_timing_enable.restype = ctypes.c_int
         lib.muon_timing_collect.argtypes = [ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]
@@ -134,6 +138,17 @@ def make_config(ns_steps: int = 5, coeffs: Optional[Tuple[float, float, float]] 
         raise ValueError(f"precision must be one of {sorted(PRECISIONS)}")
     cfg.precision = PRECISIONS[precision]
     return cfg
+
+
+def muon_set_ns_schedule(schedule: str) -> None:
+    """Process-wide schedule of the NS iterations of large blocks: "auto" (the
+    default: per set of shapes, the faster of the two after a few timed
+    calls), "per_product" (three launches per iteration) or "persistent" (one
+    launch for all iterations where the shapes allow).  Results are bitwise
+    equal."""
+    if schedule not in NS_SCHEDULES:
+        raise ValueError(f"schedule must be one of {sorted(NS_SCHEDULES)}")
+    _check(load_library().muon_set_ns_schedule(NS_SCHEDULES[schedule]))
 
 
 def muon_timing_enable(kinds=()) -> None:

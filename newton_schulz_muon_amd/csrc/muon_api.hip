@@ -117,6 +117,7 @@ muon_status make_plan(int64_t batch, int64_t rows, int64_t cols, int32_t v,
     if (split) { p.off_blo = off; off = align256(off + abytes); }
     p.off_part = off; off = align256(off + size_t(p.nb) * size_t(p.ew_tiles) * 4);
     p.off_scale = off; off = align256(off + size_t(p.nb) * 2 * 4);
+    p.off_sync = off; off += ns_loop_sync_bytes(p.nb);
     p.total = off;
     return MUON_OK;
 }
@@ -222,6 +223,7 @@ struct Buffers {
     uint16_t* bl;
     float* part;
     float* scale;
+    uint32_t* sync;
 };
 
 Buffers carve(const Plan& p, void* ws) {
@@ -237,6 +239,7 @@ Buffers carve(const Plan& p, void* ws) {
     b.bl = split ? reinterpret_cast<uint16_t*>(base + p.off_blo) : nullptr;
     b.part = reinterpret_cast<float*>(base + p.off_part);
     b.scale = reinterpret_cast<float*>(base + p.off_scale);
+    b.sync = reinterpret_cast<uint32_t*>(base + p.off_sync);
     return b;
 }
 
@@ -246,6 +249,15 @@ muon_status run_ns(const Plan& p, const muon_ns_config& cfg, const Buffers& b, h
                    int* final_idx) {
     hipError_t e = timed(MUON_KERNEL_NORM_FINALIZE, s, [&] { return launch_norm_finalize(p, b.part, b.scale, cfg.eps, s); });
     if (e != hipSuccess) return hip_fail(e, "k_norm_finalize launch");
+    const NsLoopProblem lp{&p, {b.xh[0], b.xh[1]}, b.a, b.bh, b.scale, b.sync};
+    const NsChoice ch = ns_schedule_begin(&lp, 1, cfg.ns_steps, s);
+    if (ch.persistent) {
+        e = timed(MUON_KERNEL_NS_LOOP, s, [&] { return launch_ns_loop(&lp, 1, cfg.ns_steps, cfg.a, cfg.b, cfg.c, s); });
+        if (e != hipSuccess) return hip_fail(e, "k_ns_loop launch");
+        ns_schedule_end(ch, s);
+        *final_idx = cfg.ns_steps & 1;
+        return MUON_OK;
+    }
     int cur = 0;
     for (int it = 0; it < cfg.ns_steps; ++it) {
         const float* sc = it == 0 ? b.scale : nullptr;
@@ -259,6 +271,7 @@ muon_status run_ns(const Plan& p, const muon_ns_config& cfg, const Buffers& b, h
         if (e != hipSuccess) return hip_fail(e, "k_gemm<bx> launch");
         cur ^= 1;
     }
+    ns_schedule_end(ch, s);
     *final_idx = cur;
     return MUON_OK;
 }
@@ -688,7 +701,21 @@ muon_status muon_step_multi(const muon_matrix* mats, int32_t count, float lr, fl
         const auto by_np = buckets([](const Plan& p) { return p.np; });
         const auto by_mp = buckets([](const Plan& p) { return p.mp; });
         int cur = 0;
-        for (int it = 0; it < cfg.ns_steps; ++it) {
+        std::vector<NsLoopProblem> lps;
+        for (size_t gi : wave) {
+            const Buffers& b = bufs[gi];
+            lps.push_back(NsLoopProblem{&groups[gi].plan, {b.xh[0], b.xh[1]}, b.a, b.bh, b.scale, b.sync});
+        }
+        const NsChoice ch = ns_schedule_begin(lps.data(), int(lps.size()), cfg.ns_steps, s);
+        const bool loop = ch.persistent;
+        if (loop) {
+            const hipError_t e = timed(MUON_KERNEL_NS_LOOP, s, [&] {
+                return launch_ns_loop(lps.data(), int(lps.size()), cfg.ns_steps, cfg.a, cfg.b, cfg.c, s);
+            });
+            if (e != hipSuccess) return hip_fail(e, "k_ns_loop launch");
+            cur = cfg.ns_steps & 1;
+        }
+        for (int it = 0; it < (loop ? 0 : cfg.ns_steps); ++it) {
             for (const auto& bk : by_np) {
                 GramOp ops[kMaxGemmProblems];
                 for (size_t k = 0; k < bk.size(); ++k) {
@@ -721,6 +748,7 @@ muon_status muon_step_multi(const muon_matrix* mats, int32_t count, float lr, fl
             }
             cur ^= 1;
         }
+        ns_schedule_end(ch, s);
 
         // Update, per group in chunks.
         for (size_t gi : wave) {
@@ -858,6 +886,13 @@ muon_status muon_merge_small_dims(const int64_t* shape, int32_t ndim, int64_t th
     out[nout++] = cur;
     for (int32_t i = 0; i < nout; ++i) merged[i] = out[nout - 1 - i];
     *merged_ndim = nout;
+    return MUON_OK;
+}
+
+muon_status muon_set_ns_schedule(int32_t mode) {
+    g_err.clear();
+    if (mode < 0 || mode > 2) return fail(MUON_ERR_INVALID_ARG, "schedule mode %d is not 0, 1 or 2", mode);
+    set_ns_schedule(mode);
     return MUON_OK;
 }
 

@@ -13,6 +13,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <vector>
 #include <stdint.h>
 #include <stddef.h>
 
@@ -45,6 +46,7 @@ struct Plan {
     size_t off_blo = 0;          // ACCURATE: lo plane of B
     size_t off_part = 0;         // fp32 [nb][ew_tiles] partial sums of squares
     size_t off_scale = 0;        // fp32 [nb][2]: 1/s, 1/s^2
+    size_t off_sync = 0;         // u32 counters of the persistent NS loop (ns_loop_sync_bytes)
     size_t total = 0;
 };
 
@@ -145,6 +147,41 @@ hipError_t launch_poly(const Plan& p, const uint16_t* a, uint16_t* b_hi, uint16_
 hipError_t launch_bx(const Plan& p, const uint16_t* b_hi, const uint16_t* b_lo, const uint16_t* x_hi,
                      const uint16_t* x_lo, uint16_t* out_hi, uint16_t* out_lo, const float* scale1,
                      hipStream_t s);
+
+// Persistent NS loop (ns_gemm.hip): every iteration of the three products
+// of up to kMaxNsLoopProblems block batches in one launch of one workgroup
+// per CU, which take tiles from a precomputed queue and wait on per-block
+// completion counters.  Each problem brings a sync region of
+// ns_loop_sync_bytes(nb) (the launcher zeroes it first).  Iteration t reads
+// x[t % 2] and writes x[(t + 1) % 2]; the first one applies `scale` as the
+// per-product launches do.
+struct NsLoopProblem {
+    const Plan* plan;
+    uint16_t* x[2];
+    uint16_t* a;
+    uint16_t* b;
+    const float* scale;
+    uint32_t* sync;
+};
+constexpr int kMaxNsLoopProblems = 8;
+// Whether launch_ns_loop takes these problems: FAST precision, both padded
+// sides multiples of 256, 1 <= ns_steps, at most kMaxNsLoopProblems.
+bool ns_loop_eligible(const NsLoopProblem* probs, int n, int ns_steps);
+// Which schedule runs the NS iterations of these problems on stream s (see
+// set_ns_schedule); the caller launches it between begin and end.
+struct NsChoice {
+    bool persistent = false;
+    int trial = -1;                            // timed trial call of the automatic choice
+    const std::vector<int64_t>* key = nullptr;
+};
+NsChoice ns_schedule_begin(const NsLoopProblem* probs, int n, int ns_steps, hipStream_t s);
+void ns_schedule_end(const NsChoice& c, hipStream_t s);
+size_t ns_loop_sync_bytes(int64_t total_blocks);
+hipError_t launch_ns_loop(const NsLoopProblem* probs, int n, int ns_steps, float ca, float cb, float cc,
+                          hipStream_t s);
+// 0: automatic per set of shapes (default); 1: per-product launches only;
+// 2: the persistent loop wherever eligible.
+void set_ns_schedule(int mode);
 
 // AdamW for the non-matrix parameters (adamw.hip): one launch over up to
 // kAdamTab tensors.  decay = 1 - lr lr_mul wd wd_mul (exactly 1 when wd = 0),

@@ -50,7 +50,16 @@
 // (i % 4) of the 8 bytes addressed by lanes 4 e + i / 4, for e = 0..3.  With
 // lane L addressing row rb + L / 4, columns cb + 4 (L % 4) .. + 3 of a
 // row-major tile, lane i gets rows rb .. rb + 3 of column cb + i.
+#include <algorithm>
+#include <atomic>
+#include <functional>
+#include <map>
+#include <mutex>
+#include <queue>
+#include <set>
+#include <tuple>
 #include <type_traits>
+#include <vector>
 
 #include "muon_internal.hpp"
 
@@ -140,10 +149,10 @@ struct RowDma {
     uint32_t bytes;
     uint32_t voff[PW];
 
-    __device__ __forceinline__ void init(const void* base_, uint32_t bytes_, int64_t ld, int row0) {
+    __device__ __forceinline__ void init(const void* base_, uint32_t bytes_, int64_t ld, int row0, int tid) {
         base = base_;
         bytes = bytes_;
-        const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+        const int w = tid >> 6, l = tid & 63;
 #pragma unroll
         for (int q = 0; q < PW; ++q) {
             const int row = RPW * (w * PW + q) + l / CPR;
@@ -152,8 +161,8 @@ struct RowDma {
         }
     }
     // Window q of this wave (1 KB) of the slice at K offset k0.
-    __device__ __forceinline__ void load_q(char* lds, int k0, int q) const {
-        const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    __device__ __forceinline__ void load_q(char* lds, int k0, int q, int tid) const {
+        const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
         dma16(make_rsrc(base, bytes), voff[q], static_cast<uint32_t>(k0 * 2), lds + (w * PW + q) * 1024);
     }
 };
@@ -178,11 +187,11 @@ struct ColDma {
     uint32_t ldb;                                      // row pitch in bytes
     uint32_t voff[PW];
 
-    __device__ __forceinline__ void init(const void* base_, uint32_t bytes_, int64_t ld, int col0) {
+    __device__ __forceinline__ void init(const void* base_, uint32_t bytes_, int64_t ld, int col0, int tid) {
         base = base_;
         bytes = bytes_;
         ldb = static_cast<uint32_t>(ld * 2);
-        const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+        const int w = tid >> 6, l = tid & 63;
 #pragma unroll
         for (int q = 0; q < PW; ++q) {
             const int row = ROWS_PER_WIN * (w * PW + q) + l / (C / 8);
@@ -190,8 +199,8 @@ struct ColDma {
             voff[q] = static_cast<uint32_t>(((int64_t)row * ld + col0 + chunk * 8) * 2);
         }
     }
-    __device__ __forceinline__ void load_q(char* lds, int k0, int q) const {
-        const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    __device__ __forceinline__ void load_q(char* lds, int k0, int q, int tid) const {
+        const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
         dma16(make_rsrc(base, bytes), voff[q], static_cast<uint32_t>(k0) * ldb, lds + (w * PW + q) * 1024);
     }
 };
@@ -211,18 +220,18 @@ struct Operands {
         return stage + (NA + j) * OP_BYTES;
     }
     // DMA instruction w (0 <= w < WINDOWS) of this wave for the slice at k0.
-    __device__ __forceinline__ void load_window(char* stage, int k0, int w) const {
+    __device__ __forceinline__ void load_window(char* stage, int k0, int w, int tid) const {
         constexpr int PA = ALoader::PW, PB = BLoader::PW;
         if (w < NA * PA) {
-            a[w / PA].load_q(a_tile(stage, w / PA), k0, w % PA);
+            a[w / PA].load_q(a_tile(stage, w / PA), k0, w % PA, tid);
         } else {
             const int v = w - NA * PA;
-            b[v / PB].load_q(b_tile(stage, v / PB), k0, v % PB);
+            b[v / PB].load_q(b_tile(stage, v / PB), k0, v % PB, tid);
         }
     }
-    __device__ __forceinline__ void load(char* stage, int k0) const {
+    __device__ __forceinline__ void load(char* stage, int k0, int tid) const {
 #pragma unroll
-        for (int w = 0; w < WINDOWS; ++w) load_window(stage, k0, w);
+        for (int w = 0; w < WINDOWS; ++w) load_window(stage, k0, w, tid);
     }
 };
 
@@ -231,8 +240,8 @@ struct Operands {
 // two transposing reads (k rows ks*16 + 8 (l / 32) + 0..3 and + 4..7 of
 // index l % 32 of the block).
 template <bool KMAJOR, int BT, int BK>
-__device__ __forceinline__ bf16x8 load_frag(const char* S, int base, int ks) {
-    const int lane = threadIdx.x & 63;
+__device__ __forceinline__ bf16x8 load_frag(const char* S, int base, int ks, int tid) {
+    const int lane = tid & 63;
     if constexpr (!KMAJOR) {
         return *reinterpret_cast<const bf16x8*>(
             S + lds_off<BK>(base + (lane & 31), ks * 2 + (lane >> 5)));
@@ -259,7 +268,7 @@ __device__ __forceinline__ bf16x8 load_frag(const char* S, int base, int ks) {
 // instead of stalling the wave in a burst when the address queue fills.
 template <int F, bool KMAJOR_A, bool KMAJOR_B, int BT, int BK, bool DMA = false, int G = 1, typename Ops = void>
 __device__ __forceinline__ void load_frags(const char* As, const char* Bs, int wr0, int wc0, int ks,
-                                           bf16x8 (&a)[F], bf16x8 (&b)[F], const Ops* ops = nullptr,
+                                           bf16x8 (&a)[F], bf16x8 (&b)[F], int tid, const Ops* ops = nullptr,
                                            char* next = nullptr, int k1 = 0, int g0 = 0) {
     auto dma_after = [&](int fi) {
         if constexpr (DMA) {
@@ -267,19 +276,19 @@ __device__ __forceinline__ void load_frags(const char* As, const char* Bs, int w
             const int g = g0 + fi;
 #pragma unroll
             for (int w = 0; w < W; ++w)
-                if (w * G >= g * W && w * G < (g + 1) * W) ops->load_window(next, k1, w);
+                if (w * G >= g * W && w * G < (g + 1) * W) ops->load_window(next, k1, w, tid);
         }
     };
-    a[0] = load_frag<KMAJOR_A, BT, BK>(As, wr0, ks);
+    a[0] = load_frag<KMAJOR_A, BT, BK>(As, wr0, ks, tid);
     dma_after(0);
 #pragma unroll
     for (int j = 0; j < F; ++j) {
-        b[j] = load_frag<KMAJOR_B, BT, BK>(Bs, wc0 + j * 32, ks);
+        b[j] = load_frag<KMAJOR_B, BT, BK>(Bs, wc0 + j * 32, ks, tid);
         dma_after(1 + j);
     }
 #pragma unroll
     for (int i = 1; i < F; ++i) {
-        a[i] = load_frag<KMAJOR_A, BT, BK>(As, wr0 + i * 32, ks);
+        a[i] = load_frag<KMAJOR_A, BT, BK>(As, wr0 + i * 32, ks, tid);
         dma_after(F + i);
     }
 }
@@ -408,8 +417,38 @@ struct GemmArgs {
     float ca, cb, cc;
 };
 
+// One output tile of one product, its pointers already offset to the block.
+struct TileJob {
+    const uint16_t* p[2];     // row operands (hi, lo): X, A or B'
+    const uint16_t* q[2];     // column operands (hi, lo): X, A or X
+    uint16_t* out[2];         // row-major output (hi, lo)
+    const float* scale;       // epilogue factor of X X^T or B X, or null (1)
+    uint32_t p_bytes, q_bytes;
+    int64_t K;                // reduction length (row pitch of k-contiguous operands)
+    int64_t ldq;              // row pitch of a k-major column operand
+    int64_t ldo;              // output row pitch
+    int ti, tj;               // tile row and column (in tiles of BT)
+};
+
+// LDS bytes of one tile of KIND at width BT (the operand stages; the
+// epilogue staging reuses them).
 template <int KIND, int BT>
-__global__ __launch_bounds__(NTHR) void k_gemm(GemmArgs args) {
+constexpr int tile_lds_bytes() {
+    using Cfg = TileCfg<BT, BT == 256 || KIND == kBx || KIND == kBxSplit>;
+    return Cfg::NS * (KIND == kBxSplit ? 4 : 2) * Cfg::OP_BYTES;
+}
+
+// Computes one BT x BT output tile with the 256 threads of the workgroup,
+// using `lds` (tile_lds_bytes<KIND, BT>() bytes) for the operand stages and
+// the epilogue.  All LDS traffic of the previous use of `lds` must be
+// finished (a barrier) before the call.
+template <int KIND, int BT, bool OPAQUE_TID = false>
+__device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca, float cb, float cc) {
+    // In a loop over tiles the thread index is made opaque per tile, so that
+    // the compiler does not hoist the lane-dependent address arithmetic of
+    // every product out of the loop (and spill it).
+    int tid = static_cast<int>(threadIdx.x);
+    if constexpr (OPAQUE_TID) asm volatile("" : "+v"(tid));
     using Cfg = TileCfg<BT, BT == 256 || KIND == kBx || KIND == kBxSplit>;
     constexpr int F = Cfg::F, TW = Cfg::TW;
     constexpr bool SYM = KIND == kGram || KIND == kPoly || KIND == kPolySplit;
@@ -430,43 +469,17 @@ __global__ __launch_bounds__(NTHR) void k_gemm(GemmArgs args) {
     using Ops = Operands<BT, NA, NB, ALoader, BLoader>;
     constexpr int STAGE = Ops::STAGE;
     constexpr int LDS_BYTES = Cfg::NS * STAGE;
-    __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
-
-    const uint32_t L = xcd_logical(blockIdx.x, args.total);
-    const uint32_t tile_all = args.quad ? args.big_base + L / 4 : L;
-    int pi = 0;
-    for (int i = 1; i < args.n; ++i)
-        if (tile_all >= args.pr[i].first) pi = i;
-    const GemmProblem& a = args.pr[pi];
-    const uint32_t tile = tile_all - a.first;
-    const int64_t blk = tile / a.tiles;
-    int ti, tj;
-    {
-        int id = static_cast<int>(tile % a.tiles);
-        if constexpr (SYM) {
-            int t = 0, len = a.T;
-            while (id >= len) { id -= len; ++t; --len; }
-            ti = t;
-            tj = t + id;
-        } else {
-            ti = id % static_cast<int>(a.tiles_i);
-            tj = id / static_cast<int>(a.tiles_i);
-        }
-        if (args.quad) {
-            ti = 2 * ti + static_cast<int>((L >> 1) & 1);
-            tj = 2 * tj + static_cast<int>(L & 1);
-            if (SYM && ti > tj) return;   // lower quadrant of a diagonal tile: its mirror covers it
-        }
-    }
+    static_assert(LDS_BYTES == tile_lds_bytes<KIND, BT>(), "LDS size");
+    const int ti = a.ti, tj = a.tj;
     const int row0 = ti * BT, col0 = tj * BT;
-    const int wave = threadIdx.x >> 6;
+    const int wave = tid >> 6;
     const int wr0 = (wave >> 1) * TW, wc0 = (wave & 1) * TW;
 
     Ops ops;
 #pragma unroll
-    for (int i = 0; i < NA; ++i) ops.a[i].init(a.p[i] + blk * a.p_stride, a.p_bytes, a.K, row0);   // K = ld (square when k-major)
+    for (int i = 0; i < NA; ++i) ops.a[i].init(a.p[i], a.p_bytes, a.K, row0, tid);   // K = ld (square when k-major)
 #pragma unroll
-    for (int j = 0; j < NB; ++j) ops.b[j].init(a.q[j] + blk * a.q_stride, a.q_bytes, KMAJOR_B ? a.ldq : a.K, col0);
+    for (int j = 0; j < NB; ++j) ops.b[j].init(a.q[j], a.q_bytes, KMAJOR_B ? a.ldq : a.K, col0, tid);
 
     f32x16 acc[F][F];
     zero_acc<F>(acc);
@@ -487,7 +500,7 @@ __global__ __launch_bounds__(NTHR) void k_gemm(GemmArgs args) {
         const int pn = u / KS, ks = u % KS;
         load_frags<F, KMAJOR_A, KMAJOR_B, BT, BK>(Ops::a_tile(const_cast<char*>(st), pn == 2 ? 1 : 0),
                                               Ops::b_tile(const_cast<char*>(st), pn == 1 ? 1 : 0), wr0, wc0, ks,
-                                              xa, xb);
+                                              xa, xb, tid);
     };
 
     if constexpr (NS >= 3) {
@@ -500,7 +513,7 @@ __global__ __launch_bounds__(NTHR) void k_gemm(GemmArgs args) {
         // stage of loads (in the tail an in-bounds slice whose copy is never
         // read), so the wait count is fixed.
 #pragma unroll
-        for (int st = 0; st < NS - 1; ++st) ops.load(lds + st * STAGE, (st < nk ? st : 0) * BK);
+        for (int st = 0; st < NS - 1; ++st) ops.load(lds + st * STAGE, (st < nk ? st : 0) * BK, tid);
         wait_dma_and_barrier<(NS - 2) * W>();
         frags(lds, 0, fa[0], fb[0]);
         for (int kt = 0; kt < nk; ++kt) {
@@ -515,7 +528,7 @@ __global__ __launch_bounds__(NTHR) void k_gemm(GemmArgs args) {
                     wait_dma_and_barrier<(NS - 3) * W>();
                     const int kn = kt + NS - 1;
                     load_frags<F, KMAJOR_A, KMAJOR_B, BT, BK, true, 2 * F>(
-                        Ops::a_tile(nxt, 0), Ops::b_tile(nxt, 0), wr0, wc0, 0, fa[c ^ 1], fb[c ^ 1], &ops,
+                        Ops::a_tile(nxt, 0), Ops::b_tile(nxt, 0), wr0, wc0, 0, fa[c ^ 1], fb[c ^ 1], tid, &ops,
                         lds + (kn % NS) * STAGE, (kn < nk ? kn : kt) * BK, 0);
                 }
                 mfma_block<F>(fa[c], fb[c], acc);
@@ -527,7 +540,7 @@ __global__ __launch_bounds__(NTHR) void k_gemm(GemmArgs args) {
         // Two stages: slice kt + 1 is fetched into the other stage during step
         // kt, spread over its first U - 1 sub-slices, and waited for at the
         // end of the step, where a barrier also frees stage kt % 2.
-        ops.load(lds, 0);
+        ops.load(lds, 0, tid);
         wait_dma_and_barrier<0>();
         for (int kt = 0; kt < nk; ++kt) {
             char* cur = lds + (kt & 1) * STAGE;
@@ -542,7 +555,7 @@ __global__ __launch_bounds__(NTHR) void k_gemm(GemmArgs args) {
                     const int pn = (u + 1) / KS, ks = (u + 1) % KS;
                     load_frags<F, KMAJOR_A, KMAJOR_B, BT, BK, true, (U - 1) * 2 * F>(
                         Ops::a_tile(cur, pn == 2 ? 1 : 0), Ops::b_tile(cur, pn == 1 ? 1 : 0), wr0, wc0, ks,
-                        fa[c ^ 1], fb[c ^ 1], &ops, nxt, k1, u * 2 * F);
+                        fa[c ^ 1], fb[c ^ 1], tid, &ops, nxt, k1, u * 2 * F);
                 }
                 mfma_block<F>(fa[c], fb[c], acc);
                 if (u + 1 < U) interleave<F, NREAD>();
@@ -559,17 +572,12 @@ __global__ __launch_bounds__(NTHR) void k_gemm(GemmArgs args) {
     // the polynomial) cover whole row segments instead of the MFMA layout's
     // 4-column pieces of 32 rows.  All staging is wave-private; LDS accesses
     // of one wave complete in order, so no barrier is needed.
-    const int lane = threadIdx.x & 63;
+    const int lane = tid & 63;
     const int lr = lane & 31, lk = lane >> 5;
-    float sc = 1.0f;
-    if constexpr (KIND == kGram) {
-        if (a.scale) sc = a.scale[2 * blk + 1];
-    } else if constexpr (!POLY) {
-        if (a.scale) sc = a.scale[2 * blk];
-    }
-    const uint16_t* amat = POLY ? a.p[0] + blk * a.p_stride : nullptr;
-    uint16_t* out0 = a.out[0] + blk * a.out_stride;
-    uint16_t* out1 = SPLIT_OUT ? a.out[1] + blk * a.out_stride : nullptr;
+    const float sc = a.scale ? *a.scale : 1.0f;
+    const uint16_t* amat = POLY ? a.p[0] : nullptr;
+    uint16_t* out0 = a.out[0];
+    uint16_t* out1 = SPLIT_OUT ? a.out[1] : nullptr;
     constexpr int ST_F32 = 32 * TW * 4;
     constexpr int ST_BF = SYM ? 32 * TW * 2 : 0;
     constexpr int WAVE_LDS = ST_F32 + ST_BF * (SPLIT_OUT ? 2 : 1);
@@ -652,8 +660,8 @@ __global__ __launch_bounds__(NTHR) void k_gemm(GemmArgs args) {
             for (int e = 0; e < 4; ++e) {
                 float v;
                 if constexpr (POLY) {
-                    v = fmaf(args.cc, x[e], args.cb * am[e]);
-                    if (grow == gcol + e) v += args.ca;
+                    v = fmaf(cc, x[e], cb * am[e]);
+                    if (grow == gcol + e) v += ca;
                 } else {
                     v = x[e] * sc;
                 }
@@ -697,6 +705,268 @@ __global__ __launch_bounds__(NTHR) void k_gemm(GemmArgs args) {
             }
         }
     }
+}
+
+template <int KIND, int BT>
+__global__ __launch_bounds__(NTHR) void k_gemm(GemmArgs args) {
+    constexpr bool SYM = KIND == kGram || KIND == kPoly || KIND == kPolySplit;
+    constexpr bool SPLIT_IN = KIND == kBxSplit;
+    constexpr bool SPLIT_OUT = KIND == kPolySplit || KIND == kBxSplit;
+    __shared__ __attribute__((aligned(16))) char lds[tile_lds_bytes<KIND, BT>()];
+
+    const uint32_t L = xcd_logical(blockIdx.x, args.total);
+    const uint32_t tile_all = args.quad ? args.big_base + L / 4 : L;
+    int pi = 0;
+    for (int i = 1; i < args.n; ++i)
+        if (tile_all >= args.pr[i].first) pi = i;
+    const GemmProblem& a = args.pr[pi];
+    const uint32_t tile = tile_all - a.first;
+    const int64_t blk = tile / a.tiles;
+    int ti, tj;
+    {
+        int id = static_cast<int>(tile % a.tiles);
+        if constexpr (SYM) {
+            int t = 0, len = a.T;
+            while (id >= len) { id -= len; ++t; --len; }
+            ti = t;
+            tj = t + id;
+        } else {
+            ti = id % static_cast<int>(a.tiles_i);
+            tj = id / static_cast<int>(a.tiles_i);
+        }
+        if (args.quad) {
+            ti = 2 * ti + static_cast<int>((L >> 1) & 1);
+            tj = 2 * tj + static_cast<int>(L & 1);
+            if (SYM && ti > tj) return;   // lower quadrant of a diagonal tile: its mirror covers it
+        }
+    }
+    TileJob j;
+    j.p[0] = a.p[0] + blk * a.p_stride;
+    j.p[1] = SPLIT_IN ? a.p[1] + blk * a.p_stride : nullptr;
+    j.q[0] = a.q[0] + blk * a.q_stride;
+    j.q[1] = SPLIT_IN ? a.q[1] + blk * a.q_stride : nullptr;
+    j.out[0] = a.out[0] + blk * a.out_stride;
+    j.out[1] = SPLIT_OUT ? a.out[1] + blk * a.out_stride : nullptr;
+    j.scale = nullptr;
+    if constexpr (KIND == kGram) {
+        if (a.scale) j.scale = a.scale + 2 * blk + 1;
+    } else if constexpr (KIND == kBx || KIND == kBxSplit) {
+        if (a.scale) j.scale = a.scale + 2 * blk;
+    }
+    j.p_bytes = a.p_bytes;
+    j.q_bytes = a.q_bytes;
+    j.K = a.K;
+    j.ldq = a.ldq;
+    j.ldo = a.ldo;
+    j.ti = ti;
+    j.tj = tj;
+    gemm_tile<KIND, BT>(j, lds, args.ca, args.cb, args.cc);
+}
+
+// ---------------------------------------------------------------- persistent NS loop
+// One launch runs every iteration of the Gram, polynomial and B X products of
+// up to kMaxNsLoopProblems block batches, as 256-wide tiles.  Each workgroup
+// (one per CU) takes the next item of its queue (an atomic head), waits until
+// the item's block has completed every tile of the product before it
+// (done[block] reaches the item's count), computes the tile and adds one to
+// done[block].  Items are listed in an order in which each depends only on
+// items listed before it in the same queue, and an item is taken only by a
+// running workgroup, so the lowest unfinished item can always proceed.  A wait
+// longer than kSpinTicks sets the error word and every workgroup leaves.
+struct PersistProblem {
+    const uint16_t* x[2];
+    uint16_t* a;
+    uint16_t* b;
+    const float* scale;
+    uint32_t* done;           // [nb] completion counters, kSyncStride words apart
+    int32_t mp, np;
+    uint32_t first_blk;       // global index of its first block
+    uint32_t nsym, nbx;       // tiles per block: symmetric products, B X
+};
+
+struct PersistArgs {
+    PersistProblem pr[kMaxNsLoopProblems];
+    int n;
+    int nq;                   // queues: 1, or 8 (workgroup w serves queue w % 8)
+    const uint2* items;       // x = global block | (tiles - 1) << 28, y = first tile | product << 22 | iteration << 24
+    uint32_t qbase[9];        // queue q is items[qbase[q], qbase[q + 1])
+    uint32_t* sync;           // queue heads 0..7, then the error word and an XCD mismatch flag
+    int local_sync;           // 8 queues served by the workgroups of one XCD each
+    float ca, cb, cc;
+};
+
+// Counters of the loop each sit on their own 128-byte line (kSyncStride
+// words apart): queue heads 0..7, then the error word, then per block.
+constexpr uint32_t kSyncStride = 32;
+constexpr uint64_t kSpinTicks = 100000000;   // 1 s of the 100 MHz real-time counter
+constexpr uint32_t kItemEnd = 0xffffffffu;
+constexpr uint32_t kBlockMask = 0x0fffffffu;   // item.x: block; the top 4 bits: tiles in the item - 1
+
+__global__ __launch_bounds__(NTHR) void k_ns_loop(PersistArgs args) {
+    constexpr int LDS = tile_lds_bytes<kBx, 256>();
+    static_assert(tile_lds_bytes<kGram, 256>() <= LDS && tile_lds_bytes<kPoly, 256>() <= LDS, "LDS size");
+    __shared__ __attribute__((aligned(16))) char lds[LDS];
+    __shared__ uint2 s_item;
+    // The loop's control flow is uniform across the workgroup: wave 0 does the
+    // queue and counter work with all its lanes (lane 0 alone adds 1 in each
+    // atomic, the others add 0) and every value that steers the loop is read
+    // with readfirstlane.  (Lane-divergent code at the head and the end of
+    // this loop let the compiler split it into separate loops for lane 0 and
+    // the other lanes, which never meet at the barriers again.)
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    const uint32_t one = (threadIdx.x & 63) == 0 ? 1u : 0u;
+    // With 8 queues, workgroup w serves queue w % 8, which gives every queue
+    // the same number of workgroups; the launcher enables local_sync only
+    // where workgroup w runs on XCD w % 8 (checked once per device), so a
+    // queue's tiles, and hence its blocks' buffers, stay in one XCD's L2.
+    const uint32_t xcc = __builtin_amdgcn_s_getreg((20) | (0 << 6) | (3 << 11)) & 7u;   // HW_REG_XCC_ID
+    const int q = args.nq == 8 ? static_cast<int>(blockIdx.x & 7) : 0;
+    const uint32_t qb = args.qbase[q], qlen = args.qbase[q + 1] - qb;
+    uint32_t* const err = args.sync + kSyncStride * 8;
+    if (args.local_sync && wave == 0 && xcc != (blockIdx.x & 7))
+        __hip_atomic_fetch_or(err + 1, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t* prev_done = nullptr;    // counter of the item this workgroup finished last ...
+    uint32_t prev_tiles = 0;          // ... and its tile count
+    // The queue index of the next item is taken just before each tile's
+    // stores are waited for, so that the atomic's round trip (several
+    // microseconds under load) overlaps the drain.  A workgroup then holds one
+    // item beyond the one it has finished computing, and takes items in queue
+    // order, so the lowest unfinished item can always proceed.
+    uint32_t idx = 0;
+    if (wave == 0)
+        idx = __builtin_amdgcn_readfirstlane(__hip_atomic_fetch_add(args.sync + kSyncStride * q, one, __ATOMIC_RELAXED,
+                                                                     __HIP_MEMORY_SCOPE_AGENT));
+    for (;;) {
+        if (wave == 0) {
+            // The previous tile's stores completed before the barrier that
+            // ended it; the add publishes them.
+            if (prev_done) {
+                const uint32_t add = one * prev_tiles;
+                if (args.local_sync)
+                    __hip_atomic_fetch_add(prev_done, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                else
+                    __hip_atomic_fetch_add(prev_done, add, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            uint2 it = {kItemEnd, 0u};
+            if (idx < qlen) {
+                const uint2 raw = args.items[qb + idx];
+                it.x = __builtin_amdgcn_readfirstlane(raw.x);
+                it.y = __builtin_amdgcn_readfirstlane(raw.y);
+                const uint32_t g = it.x & kBlockMask;
+                int pi = 0;
+                for (int i = 1; i < args.n; ++i)
+                    if (g >= args.pr[i].first_blk) pi = i;
+                const PersistProblem& pr = args.pr[pi];
+                const uint32_t t = it.y >> 24, ph = (it.y >> 22) & 3u;
+                const uint32_t need = t * (2 * pr.nsym + pr.nbx) + (ph >= 1 ? pr.nsym : 0u) + (ph >= 2 ? pr.nsym : 0u);
+                uint32_t* const done = pr.done + kSyncStride * (g - pr.first_blk);
+                const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+                for (;;) {
+                    const uint32_t d = __builtin_amdgcn_readfirstlane(
+                        __hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+                    if (d >= need) break;
+                    const uint32_t e = __builtin_amdgcn_readfirstlane(
+                        __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+                    if (e != 0u || __builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) {
+                        __hip_atomic_fetch_or(err, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        it.x = kItemEnd;
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(2);
+                }
+                // Acquire: the CU's L1 may hold lines of this block's
+                // buffers from an earlier iteration.  The device-scope
+                // invalidate drops them (a workgroup-scope one does not, with
+                // all of a workgroup's waves on one CU).
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            }
+            s_item = it;    // every lane of wave 0 writes the same value
+        }
+        __syncthreads();
+        const uint2 raw = s_item;
+        const uint32_t itx = __builtin_amdgcn_readfirstlane(raw.x), ity = __builtin_amdgcn_readfirstlane(raw.y);
+        if (itx == kItemEnd) break;
+        const uint32_t g = itx & kBlockMask;
+        const int ntiles = static_cast<int>(itx >> 28) + 1;
+        int pi = 0;
+        for (int i = 1; i < args.n; ++i)
+            if (g >= args.pr[i].first_blk) pi = i;
+        const PersistProblem& pr = args.pr[pi];
+        const int64_t blk = g - pr.first_blk;
+        const int t = static_cast<int>(ity >> 24), ph = static_cast<int>((ity >> 22) & 3u);
+        const int64_t xs = int64_t(pr.mp) * pr.np, as = int64_t(pr.mp) * pr.mp;
+        for (int c = 0; c < ntiles; ++c) {
+            if (c > 0) __syncthreads();    // the previous tile's epilogue is done with LDS
+            int id = static_cast<int>(ity & 0x3fffffu) + c;
+            TileJob j;
+            j.p[1] = j.q[1] = nullptr;
+            j.out[1] = nullptr;
+            j.scale = nullptr;
+            if (ph < 2) {
+                int r = 0, len = pr.mp / 256;
+                while (id >= len) { id -= len; ++r; --len; }
+                j.ti = r;
+                j.tj = r + id;
+            } else {
+                j.ti = id % (pr.mp / 256);
+                j.tj = id / (pr.mp / 256);
+            }
+            if (ph == 0) {
+                j.p[0] = j.q[0] = pr.x[t & 1] + blk * xs;
+                j.out[0] = pr.a + blk * as;
+                if (t == 0 && pr.scale) j.scale = pr.scale + 2 * blk + 1;
+                j.p_bytes = j.q_bytes = static_cast<uint32_t>(xs * 2);
+                j.K = pr.np;
+                j.ldq = pr.np;
+                j.ldo = pr.mp;
+                gemm_tile<kGram, 256, true>(j, lds, args.ca, args.cb, args.cc);
+            } else if (ph == 1) {
+                j.p[0] = j.q[0] = pr.a + blk * as;
+                j.out[0] = pr.b + blk * as;
+                j.p_bytes = j.q_bytes = static_cast<uint32_t>(as * 2);
+                j.K = pr.mp;
+                j.ldq = pr.mp;
+                j.ldo = pr.mp;
+                gemm_tile<kPoly, 256, true>(j, lds, args.ca, args.cb, args.cc);
+            } else {
+                j.p[0] = pr.b + blk * as;
+                j.q[0] = pr.x[t & 1] + blk * xs;
+                j.out[0] = const_cast<uint16_t*>(pr.x[(t + 1) & 1]) + blk * xs;
+                if (t == 0 && pr.scale) j.scale = pr.scale + 2 * blk;
+                j.p_bytes = static_cast<uint32_t>(as * 2);
+                j.q_bytes = static_cast<uint32_t>(xs * 2);
+                j.K = pr.mp;
+                j.ldq = pr.np;
+                j.ldo = pr.np;
+                gemm_tile<kBx, 256, true>(j, lds, args.ca, args.cb, args.cc);
+            }
+        }
+        if (wave == 0)
+            idx = __builtin_amdgcn_readfirstlane(__hip_atomic_fetch_add(args.sync + kSyncStride * q, one,
+                                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        // Every wave's stores complete before the barrier.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        prev_done = pr.done + kSyncStride * blk;
+        prev_tiles = static_cast<uint32_t>(ntiles);
+    }
+}
+
+// Zeroes the sync regions of a loop launch: region r is [0, n[r]) of p[r].
+struct ZeroArgs {
+    uint32_t* p[kMaxNsLoopProblems];
+    uint32_t n[kMaxNsLoopProblems];
+    int count;
+};
+// Records the XCD of each workgroup (HW_REG_XCC_ID).
+__global__ void k_xcc_probe(uint32_t* out) {
+    if (threadIdx.x == 0) out[blockIdx.x] = __builtin_amdgcn_s_getreg((20) | (0 << 6) | (3 << 11)) & 15u;
+}
+
+__global__ void k_zero_sync(ZeroArgs z) {
+    const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+    for (int r = 0; r < z.count; ++r)
+        if (i < z.n[r]) z.p[r][i] = 0u;
 }
 
 // Every kernel instantiation is named explicitly: with implicit instantiation
@@ -893,6 +1163,431 @@ hipError_t launch_bx(const Plan& p, const uint16_t* b_hi, const uint16_t* b_lo, 
                      hipStream_t s) {
     const BxOp op{&p, b_hi, b_lo, x_hi, x_lo, out_hi, out_lo, scale1};
     return launch_bx(&op, 1, s);
+}
+
+// ---------------------------------------------------------------- persistent NS loop (host)
+namespace {
+
+std::atomic<int> g_ns_mode{0};
+
+struct LoopDims {
+    int mp, np;
+    uint32_t nsym, nbx;
+};
+
+// Estimated cycles of one 256-wide tile of product ph (0 Gram, 1 polynomial,
+// 2 B X): the measured loop time per 32-deep K step plus prologue and
+// epilogue (the symmetric products also store the mirror tile).
+double item_cycles(int ph, const LoopDims& d) {
+    const double K = ph == 0 ? d.np : d.mp;
+    return 1305.0 * (K / 32) + (ph == 0 ? 12000.0 : ph == 1 ? 14000.0 : 9000.0);
+}
+
+// Measured cost of taking one queue item (the queue atomic's round trip under
+// load, the item load and the dependency poll), in cycles: with the counters
+// synchronised within one XCD, and at device scope (an L2 write-back and
+// invalidate per item).
+constexpr double kItemOverheadLocal = 11000.0;
+constexpr double kItemOverheadDevice = 24000.0;
+
+struct SimBlock {
+    int prob;
+    uint32_t g;        // global block index
+};
+
+// Tiles per queue item: symmetric products, B X.
+struct Grouping {
+    uint32_t sym = 1, bx = 1;
+};
+
+// List schedule of the blocks' items over `workers` workgroups.  An item is
+// a run of up to `grp` consecutive tiles of one product of one block.  A
+// free workgroup takes an item of the ready product with the highest
+// priority (Gram products first, then the earliest product, then the lowest
+// block); a block's next product becomes ready when every item of its
+// current one has finished.  Appends the items in the order they start
+// (which respects every dependency) and returns the estimated makespan.
+double list_schedule(const std::vector<SimBlock>& blocks, const std::vector<LoopDims>& dims, int steps, int workers,
+                     const Grouping& grp, double overhead, std::vector<uint2>* out) {
+    const size_t nb = blocks.size();
+    std::vector<int> k(nb, 0);
+    std::vector<uint32_t> issued(nb, 0), running(nb, 0);   // tiles issued / items running
+    auto tiles = [&](size_t i, int kk) { return kk % 3 == 2 ? dims[blocks[i].prob].nbx : dims[blocks[i].prob].nsym; };
+    std::set<std::tuple<int, int, size_t>> ready;
+    for (size_t i = 0; i < nb; ++i) ready.insert({0, 0, i});
+    typedef std::pair<double, size_t> Ev;
+    std::priority_queue<Ev, std::vector<Ev>, std::greater<Ev>> finish;
+    double t = 0.0;
+    int free = workers;
+    for (;;) {
+        while (free > 0 && !ready.empty()) {
+            const auto it = ready.begin();
+            const size_t i = std::get<2>(*it);
+            const int ph = k[i] % 3, iter = k[i] / 3;
+            const uint32_t n = tiles(i, k[i]);
+            const uint32_t cnt = std::min(n - issued[i], ph == 2 ? grp.bx : grp.sym);
+            if (out)
+                out->push_back(uint2{blocks[i].g | ((cnt - 1) << 28),
+                                     issued[i] | (uint32_t(ph) << 22) | (uint32_t(iter) << 24)});
+            finish.push({t + cnt * item_cycles(ph, dims[blocks[i].prob]) + overhead, i});
+            issued[i] += cnt;
+            ++running[i];
+            --free;
+            if (issued[i] == n) ready.erase(it);
+        }
+        if (finish.empty()) break;
+        const Ev e = finish.top();
+        finish.pop();
+        t = e.first;
+        ++free;
+        const size_t i = e.second;
+        --running[i];
+        if (issued[i] == tiles(i, k[i]) && running[i] == 0) {
+            ++k[i];
+            issued[i] = 0;
+            if (k[i] < 3 * steps) ready.insert({k[i] % 3 != 0, k[i], i});
+        }
+    }
+    return t;
+}
+
+struct Schedule {
+    uint2* items = nullptr;   // device
+    uint32_t qbase[9] = {};
+    int nq = 1;
+    bool local_sync = false;
+};
+
+// Whether workgroup w of a launch of `cus` workgroups runs on XCD w % 8 on
+// this device (8 XCDs, as the 8-queue schedule's L2 locality and its
+// XCD-local synchronisation assume): three probe launches, cached per device.
+std::map<int, bool> g_xcd_ok;
+hipError_t xcd_round_robin(int dev, int cus, bool& ok) {
+    auto it = g_xcd_ok.find(dev);
+    if (it != g_xcd_ok.end()) {
+        ok = it->second;
+        return hipSuccess;
+    }
+    ok = false;
+    if (cus % 8 == 0) {
+        uint32_t* d = nullptr;
+        hipError_t e = hipMalloc(&d, size_t(cus) * 4);
+        if (e != hipSuccess) return e;
+        std::vector<uint32_t> h(cus);
+        ok = true;
+        for (int r = 0; r < 3 && ok && e == hipSuccess; ++r) {
+            k_xcc_probe<<<dim3(cus), dim3(64), 0, nullptr>>>(d);
+            e = hipGetLastError();
+            if (e == hipSuccess) e = hipMemcpy(h.data(), d, size_t(cus) * 4, hipMemcpyDeviceToHost);
+            for (int w = 0; w < cus && e == hipSuccess; ++w)
+                if (h[w] != uint32_t(w % 8)) ok = false;
+        }
+        const hipError_t f = hipFree(d);
+        if (e != hipSuccess) return e;
+        if (f != hipSuccess) return f;
+    }
+    g_xcd_ok[dev] = ok;
+    return hipSuccess;
+}
+
+constexpr size_t kMaxSchedules = 64;
+constexpr uint64_t kMaxItems = uint64_t(1) << 22;
+std::mutex g_sched_mu;
+std::map<std::vector<int64_t>, Schedule> g_sched;
+
+// Builds the item lists (host only): with 8 queues each block's tiles stay in
+// one queue (blocks dealt largest first to the least loaded queue), so a
+// block's operands are shared in one XCD's L2; a single queue is used instead
+// when that balances clearly better.
+void schedule_items(const std::vector<LoopDims>& dims, const std::vector<int64_t>& nbs, int steps, int workers,
+                    bool local_ok, std::vector<uint2>& items, uint32_t (&qbase)[9], int& nq) {
+    std::vector<SimBlock> all;
+    std::vector<double> work;
+    uint32_t g = 0;
+    for (size_t p = 0; p < dims.size(); ++p) {
+        const double w = steps * (dims[p].nsym * (item_cycles(0, dims[p]) + item_cycles(1, dims[p])) +
+                                  dims[p].nbx * item_cycles(2, dims[p]));
+        for (int64_t b = 0; b < nbs[p]; ++b) {
+            all.push_back({int(p), g++});
+            work.push_back(w);
+        }
+    }
+    std::vector<std::vector<SimBlock>> qb(8);
+    const bool can8 = workers % 8 == 0 && all.size() >= 8;
+    if (can8) {
+        std::vector<size_t> order(all.size());
+        for (size_t i = 0; i < order.size(); ++i) order[i] = i;
+        std::stable_sort(order.begin(), order.end(), [&](size_t x, size_t y) { return work[x] > work[y]; });
+        double load[8] = {};
+        for (size_t i : order) {
+            const int q = int(std::min_element(load, load + 8) - load);
+            load[q] += work[i];
+            qb[q].push_back(all[i]);
+        }
+        for (auto& v : qb)
+            std::sort(v.begin(), v.end(), [](const SimBlock& x, const SimBlock& y) { return x.g < y.g; });
+    }
+    // Tiles per item and queue count by the estimated makespan (8 queues
+    // preferred within 5%: they keep a block's operands in one L2, and with
+    // local_ok they synchronise within the XCD).
+    const double ov8 = local_ok ? kItemOverheadLocal : kItemOverheadDevice;
+    Grouping best;
+    bool use8 = false;
+    double best_score = 0.0;
+    for (uint32_t gs = 1; gs <= 2; ++gs)
+        for (uint32_t gb = 1; gb <= 4; ++gb) {
+            const Grouping grp{gs, gb};
+            const double m1 = 1.05 * list_schedule(all, dims, steps, workers, grp, kItemOverheadDevice, nullptr);
+            if (best_score == 0.0 || m1 < best_score) {
+                best_score = m1;
+                best = grp;
+                use8 = false;
+            }
+            if (can8) {
+                double m8 = 0.0;
+                for (const auto& v : qb) m8 = std::max(m8, list_schedule(v, dims, steps, workers / 8, grp, ov8, nullptr));
+                if (m8 < best_score) {
+                    best_score = m8;
+                    best = grp;
+                    use8 = true;
+                }
+            }
+        }
+    items.clear();
+    if (use8) {
+        for (int q = 0; q < 8; ++q) {
+            qbase[q] = uint32_t(items.size());
+            list_schedule(qb[q], dims, steps, workers / 8, best, ov8, &items);
+        }
+        nq = 8;
+    } else {
+        list_schedule(all, dims, steps, workers, best, kItemOverheadDevice, &items);
+        for (int q = 0; q < 8; ++q) qbase[q] = 0;
+        nq = 1;
+    }
+    qbase[8] = uint32_t(items.size());
+    if (nq == 1)
+        for (int q = 1; q < 8; ++q) qbase[q] = qbase[8];
+}
+
+hipError_t build_schedule(const std::vector<LoopDims>& dims, const std::vector<int64_t>& nbs, int steps, int workers,
+                          bool local_ok, Schedule& out) {
+    std::vector<uint2> items;
+    schedule_items(dims, nbs, steps, workers, local_ok, items, out.qbase, out.nq);
+    out.local_sync = local_ok && out.nq == 8;
+    hipError_t e = hipMalloc(&out.items, items.size() * sizeof(uint2));
+    if (e != hipSuccess) return e;
+    e = hipMemcpy(out.items, items.data(), items.size() * sizeof(uint2), hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        (void)hipFree(out.items);
+        out.items = nullptr;
+    }
+    return e;
+}
+
+}  // namespace
+
+void set_ns_schedule(int mode) { g_ns_mode.store(mode); }
+
+// Cache key of a schedule: device, steps, workgroups, then (mp, np, nb) per problem.
+std::vector<int64_t> schedule_key(const NsLoopProblem* probs, int n, int ns_steps, int dev, int cus) {
+    std::vector<int64_t> key{dev, ns_steps, cus};
+    for (int i = 0; i < n; ++i) key.insert(key.end(), {probs[i].plan->mp, probs[i].plan->np, probs[i].plan->nb});
+    return key;
+}
+
+bool ns_loop_eligible(const NsLoopProblem* probs, int n, int ns_steps) {
+    if (n < 1 || n > kMaxNsLoopProblems || ns_steps < 1 || ns_steps > 255) return false;
+    {
+        std::lock_guard<std::mutex> lock(g_sched_mu);
+        if (g_sched.size() >= kMaxSchedules) {
+            int dev = 0, cus = 0;
+            if (hipGetDevice(&dev) != hipSuccess ||
+                hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+                return false;
+            if (g_sched.find(schedule_key(probs, n, ns_steps, dev, cus)) == g_sched.end()) return false;
+        }
+    }
+    uint64_t items = 0, blocks = 0;
+    for (int i = 0; i < n; ++i) {
+        const Plan& p = *probs[i].plan;
+        if (p.small || p.precision != MUON_PRECISION_FAST || p.nb < 1 || p.mp % 256 || p.np % 256) return false;
+        const uint64_t T = uint64_t(p.mp / 256), Tn = uint64_t(p.np / 256);
+        if (T * Tn >= (uint64_t(1) << 22)) return false;
+        items += uint64_t(p.nb) * uint64_t(ns_steps) * (T * (T + 1) + T * Tn);
+        blocks += uint64_t(p.nb);
+    }
+    return items <= kMaxItems && blocks < (uint64_t(1) << 27);
+}
+
+namespace {
+
+// Automatic choice (schedule mode 0), per set of shapes: the first
+// kTrialCalls calls alternate the per-product launches (even calls) and the
+// persistent loop (odd calls), each timed with an event pair on the call's
+// stream; once the last trial's events have completed, the schedule with the
+// lower minimum time over the trials after the first of each is kept (the
+// minimum discounts calls slowed by other work).  Both schedules give bitwise
+// the same results.
+constexpr int kTrialCalls = 10;
+constexpr size_t kMaxAutoSets = 256;
+struct AutoState {
+    int calls = 0;
+    int decided = -1;                        // -1 pending, 0 per-product, 1 persistent
+    hipEvent_t ev[kTrialCalls][2] = {};
+    bool recorded[kTrialCalls] = {};
+};
+std::map<std::vector<int64_t>, AutoState> g_auto;    // under g_sched_mu
+
+void release_events(AutoState& st) {
+    for (auto& pair : st.ev)
+        for (hipEvent_t& e : pair)
+            if (e) {
+                (void)hipEventDestroy(e);
+                e = nullptr;
+            }
+}
+
+}  // namespace
+
+NsChoice ns_schedule_begin(const NsLoopProblem* probs, int n, int ns_steps, hipStream_t s) {
+    NsChoice c;
+    const int mode = g_ns_mode.load();
+    if (mode == 1 || !ns_loop_eligible(probs, n, ns_steps)) return c;
+    if (mode == 2) {
+        c.persistent = true;
+        return c;
+    }
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return c;
+    std::lock_guard<std::mutex> lock(g_sched_mu);
+    const std::vector<int64_t> key = schedule_key(probs, n, ns_steps, dev, cus);
+    auto it = g_auto.find(key);
+    if (it == g_auto.end()) {
+        if (g_auto.size() >= kMaxAutoSets) return c;
+        it = g_auto.emplace(key, AutoState()).first;
+    }
+    AutoState& st = it->second;
+    if (st.decided >= 0) {
+        c.persistent = st.decided == 1;
+        return c;
+    }
+    if (st.calls >= kTrialCalls) {
+        // decide once every trial's events have completed
+        bool ready = true;
+        for (int i = 0; i < kTrialCalls && ready; ++i)
+            ready = st.recorded[i] && hipEventQuery(st.ev[i][1]) == hipSuccess;
+        if (ready) {
+            float best[2] = {0.f, 0.f};
+            bool ok = true;
+            for (int i = 2; i < kTrialCalls; ++i) {
+                float ms = 0.f;
+                ok = ok && hipEventElapsedTime(&ms, st.ev[i][0], st.ev[i][1]) == hipSuccess;
+                if (ok && (best[i & 1] == 0.f || ms < best[i & 1])) best[i & 1] = ms;
+            }
+            st.decided = ok && best[1] > 0.f && best[1] < best[0] ? 1 : 0;
+            release_events(st);
+            c.persistent = st.decided == 1;
+            return c;
+        }
+        c.persistent = (st.calls++ & 1) != 0;   // keep alternating, untimed, until then
+        return c;
+    }
+    const int i = st.calls;
+    for (hipEvent_t& e : st.ev[i])
+        if (!e && hipEventCreate(&e) != hipSuccess) return c;
+    if (hipEventRecord(st.ev[i][0], s) != hipSuccess) return c;
+    ++st.calls;
+    c.persistent = (i & 1) != 0;
+    c.trial = i;
+    c.key = &it->first;
+    return c;
+}
+
+void ns_schedule_end(const NsChoice& c, hipStream_t s) {
+    if (c.trial < 0) return;
+    std::lock_guard<std::mutex> lock(g_sched_mu);
+    auto it = g_auto.find(*c.key);
+    if (it == g_auto.end() || it->second.decided >= 0) return;
+    AutoState& st = it->second;
+    if (hipEventRecord(st.ev[c.trial][1], s) == hipSuccess) st.recorded[c.trial] = true;
+}
+
+size_t ns_loop_sync_bytes(int64_t total_blocks) {
+    return (size_t(9 + total_blocks) * kSyncStride * 4 + 255) & ~size_t(255);
+}
+
+hipError_t launch_ns_loop(const NsLoopProblem* probs, int n, int ns_steps, float ca, float cb, float cc,
+                          hipStream_t s) {
+    if (!ns_loop_eligible(probs, n, ns_steps)) return hipErrorInvalidValue;
+    for (int i = 0; i < n; ++i)
+        if (probs[i].sync == nullptr) return hipErrorInvalidValue;
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (cus < 1) return hipErrorInvalidValue;
+    const std::vector<int64_t> key = schedule_key(probs, n, ns_steps, dev, cus);
+    std::vector<LoopDims> dims;
+    std::vector<int64_t> nbs;
+    PersistArgs a{};
+    a.n = n;
+    a.ca = ca;
+    a.cb = cb;
+    a.cc = cc;
+    a.sync = probs[0].sync;
+    ZeroArgs z{};
+    z.count = n;
+    uint32_t zmax = 0;
+    uint32_t first = 0;
+    for (int i = 0; i < n; ++i) {
+        const Plan& p = *probs[i].plan;
+        const uint32_t T = uint32_t(p.mp / 256), Tn = uint32_t(p.np / 256);
+        dims.push_back({int(p.mp), int(p.np), T * (T + 1) / 2, T * Tn});
+        nbs.push_back(p.nb);
+        PersistProblem& pr = a.pr[i];
+        pr.x[0] = probs[i].x[0];
+        pr.x[1] = probs[i].x[1];
+        pr.a = probs[i].a;
+        pr.b = probs[i].b;
+        pr.scale = probs[i].scale;
+        pr.done = probs[i].sync + 9 * kSyncStride;
+        z.p[i] = probs[i].sync;
+        z.n[i] = uint32_t((9 + p.nb) * kSyncStride);
+        zmax = std::max(zmax, z.n[i]);
+        pr.mp = int32_t(p.mp);
+        pr.np = int32_t(p.np);
+        pr.first_blk = first;
+        pr.nsym = dims.back().nsym;
+        pr.nbx = dims.back().nbx;
+        first += uint32_t(p.nb);
+    }
+    {
+        std::lock_guard<std::mutex> lock(g_sched_mu);
+        auto it = g_sched.find(key);
+        if (it == g_sched.end()) {
+            if (g_sched.size() >= kMaxSchedules) return hipErrorOutOfMemory;
+            Schedule sc;
+            bool local_ok = false;
+            e = xcd_round_robin(dev, cus, local_ok);
+            if (e != hipSuccess) return e;
+            e = build_schedule(dims, nbs, ns_steps, cus, local_ok, sc);
+            if (e != hipSuccess) return e;
+            it = g_sched.emplace(key, sc).first;
+        }
+        a.items = it->second.items;
+        a.nq = it->second.nq;
+        a.local_sync = it->second.local_sync ? 1 : 0;
+        for (int q = 0; q < 9; ++q) a.qbase[q] = it->second.qbase[q];
+    }
+    k_zero_sync<<<dim3((zmax + 255) / 256), dim3(256), 0, s>>>(z);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    k_ns_loop<<<dim3(cus), dim3(NTHR), 0, s>>>(a);
+    return hipGetLastError();
 }
 
 }  // namespace muon

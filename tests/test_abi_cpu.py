@@ -60,8 +60,10 @@ def _expected_ws(nb, m, n, split=False):
     xb = up(nb * mp * np_ * 2, 256)
     ab = up(nb * mp * mp * 2, 256)
     tiles = (mp // 64) * (np_ // 64)
-    # iterate ping-pong (and lo planes when split); A; B (+ lo); partials; scales
-    return (4 if split else 2) * xb + (3 if split else 2) * ab + up(nb * tiles * 4, 256) + up(nb * 8, 256)
+    # iterate ping-pong (and lo planes when split); A; B (+ lo); partials; scales;
+    # counters of the persistent NS loop (9 + one per block, each on a 128-byte line)
+    return ((4 if split else 2) * xb + (3 if split else 2) * ab + up(nb * tiles * 4, 256) + up(nb * 8, 256)
+            + up((9 + nb) * 128, 256))
 
 
 def test_workspace_bytes(lib):

@@ -1,0 +1,217 @@
+"""GPU checks of the persistent NS loop (one launch for every iteration of the
+Gram, polynomial and B X products, tiles taken from a precomputed queue).
+
+Its results must be bitwise those of the per-product launches: every 32 x 32
+output block accumulates the same MFMA sequence over k whatever the tiling and
+the order in which tiles run.  The per-product path's parity with the fp64
+oracle is established by the other GPU tests; here the loop's own output is
+also checked against the oracle on sampled blocks.  Cases: one and several
+256-wide tiles per side, tall blocks, the attn view, 1 to 5 iterations (the
+result lands in either iterate), several shape groups in one launch
+(muon_step_multi), a batch that fills more than one round of workgroups, and
+repeated calls that reuse the cached queue and the workspace counters.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from parity import assert_ns_close, bits_to_f64, torch_bf16_to_bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def nsm():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the gpu-marked tests must run on an MI355X")
+    import newton_schulz_muon_amd as m
+    m.load_library()
+    yield m
+    m.muon_set_ns_schedule("auto")
+
+
+def _both(nsm, fn):
+    """fn() under each schedule; returns (persistent, per_product) results and
+    the launch counts of the persistent run."""
+    import torch
+    out = []
+    counts = None
+    for sched in ("persistent", "per_product"):
+        nsm.muon_set_ns_schedule(sched)
+        nsm.muon_timing_collect()
+        nsm.muon_timing_enable(["ns_loop", "gram", "bx"])
+        try:
+            out.append(fn())
+            torch.cuda.synchronize()
+        finally:
+            nsm.muon_timing_enable([])
+            nsm.muon_set_ns_schedule("auto")
+        k = nsm.muon_timing_collect()
+        if sched == "persistent":
+            counts = k
+    return out[0], out[1], counts
+
+
+# (batch, rows, cols, view_blocks, ns_steps)
+NS_CASES = [
+    (3, 256, 512, 1, 5),      # one tile per side of A, two B X tiles
+    (2, 512, 256, 1, 5),      # tall: oriented 256 x 512
+    (5, 768, 768, 1, 5),
+    (4, 768, 3072, 1, 5),
+    (2, 768, 3072, 4, 5),     # attn view: 8 blocks of 768 x 768
+    (2, 1024, 1024, 1, 3),    # odd step count: result in the second iterate
+    (3, 512, 1536, 1, 1),
+    (2, 256, 256, 1, 2),
+]
+
+
+@pytest.mark.parametrize("case", NS_CASES)
+def test_loop_bitwise_equals_per_product(nsm, case):
+    b, r, c, v, steps = case
+    print(f"[ns loop] batch={b} shape={(r, c)} view={v} steps={steps}", flush=True)
+    bits = workloads.gaussian_bits((b, r, c), seed=r * 31 + c + steps)
+    x = workloads.to_device_bf16(bits)
+
+    def run():
+        return torch_bf16_to_bits(nsm.ns_orthogonalize_batched(x, view_blocks=v, ns_steps=steps))
+
+    got, ref, counts = _both(nsm, run)
+    assert counts.get("ns_loop", (0, 0.0))[0] == 1 and "gram" not in counts, counts
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_loop_parity_with_oracle(nsm):
+    print("[ns loop] oracle parity 3 x 512 x 1024", flush=True)
+    bits = workloads.gaussian_bits((3, 512, 1024), seed=4242)
+    x = workloads.to_device_bf16(bits)
+    nsm.muon_set_ns_schedule("persistent")
+    got = bits_to_f64(torch_bf16_to_bits(nsm.ns_orthogonalize_batched(x)))
+    ref = oracle.ns_batched(bits_to_f64(bits), view_blocks=1, steps=5, coeffs=oracle.NS_COEFFS)
+    for i in range(3):
+        assert_ns_close(got[i], ref[i], label=f"loop[{i}]")
+
+
+def test_loop_many_blocks_repeated(nsm):
+    # 40 blocks of 768 x 3072: 240 symmetric and 1440 B X tiles per
+    # iteration, several rounds of the 256 workgroups; three calls in a row
+    # reuse the cached queue and re-zero the counters each time.
+    import torch
+    print("[ns loop] 40 x 768 x 3072, three calls", flush=True)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    x = (torch.randn((40, 768, 3072), generator=gen, device="cuda") * 1e-2).to(torch.bfloat16)
+
+    def run():
+        outs = [nsm.ns_orthogonalize_batched(x) for _ in range(3)]
+        torch.cuda.synchronize()
+        return [o.view(torch.int16).cpu().numpy() for o in outs]
+
+    got, ref, counts = _both(nsm, run)
+    assert counts.get("ns_loop", (0, 0.0))[0] == 3, counts
+    for g in got:
+        np.testing.assert_array_equal(g, ref[0])
+    np.testing.assert_array_equal(ref[1], ref[0])
+
+
+def test_loop_step_batched_bitwise(nsm):
+    import torch
+    print("[ns loop] muon_step_batched 6 x 768 x 1536", flush=True)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    P0 = torch.randn((6, 768, 1536), generator=gen, device="cuda") / 1536 ** 0.5
+    G = (torch.randn((6, 768, 1536), generator=gen, device="cuda") * 1e-2).to(torch.bfloat16)
+    M0 = torch.randn((6, 768, 1536), generator=gen, device="cuda") * 1e-3
+
+    def run():
+        P, M = P0.clone(), M0.clone()
+        O = torch.empty_like(G)
+        nsm.muon_step_batched(P, G, M, lr=0.02, weight_decay=0.01, momentum=0.95, update_out=O)
+        torch.cuda.synchronize()
+        return P.cpu().numpy().view(np.int32), M.cpu().numpy().view(np.int32), O.view(torch.int16).cpu().numpy()
+
+    got, ref, counts = _both(nsm, run)
+    assert counts.get("ns_loop", (0, 0.0))[0] == 1, counts
+    for g, r in zip(got, ref):
+        np.testing.assert_array_equal(g, r)
+
+
+def test_loop_multi_mixed_groups_bitwise(nsm):
+    # One wave of several shape groups sharing the launch: 768 x 768 (attn
+    # view of 768 x 3072), 768 x 3072, tall 1536 x 768, plus gates on the
+    # small-block path.
+    import torch
+    print("[ns loop] muon_step_multi mixed groups", flush=True)
+    shapes = ([(1, 12, 1)] * 3 + [(768, 3072, 4)] * 2 + [(768, 3072, 1)] * 3 + [(1536, 768, 1)] * 2)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    base = []
+    for r, c, v in shapes:
+        base.append(dict(params=torch.randn((r, c), generator=gen, device="cuda") / c ** 0.5,
+                         grads=(torch.randn((r, c), generator=gen, device="cuda") * 1e-2).to(torch.bfloat16),
+                         momentum_buf=torch.randn((r, c), generator=gen, device="cuda") * 1e-3,
+                         view_blocks=v))
+
+    def run():
+        mats = [dict(m, params=m["params"].clone(), momentum_buf=m["momentum_buf"].clone(),
+                     update_out=torch.empty_like(m["grads"])) for m in base]
+        for _ in range(2):
+            nsm.muon_step_multi(mats, lr=0.02, weight_decay=0.01, momentum=0.95)
+        torch.cuda.synchronize()
+        return [(m["params"].cpu().numpy().view(np.int32), m["momentum_buf"].cpu().numpy().view(np.int32),
+                 m["update_out"].view(torch.int16).cpu().numpy()) for m in mats]
+
+    got, ref, counts = _both(nsm, run)
+    assert counts.get("ns_loop", (0, 0.0))[0] >= 2, counts
+    for i, (g, r) in enumerate(zip(got, ref)):
+        for k in range(3):
+            np.testing.assert_array_equal(g[k], r[k], err_msg=f"matrix {i} field {k}")
+
+
+def test_auto_schedule_choice(nsm):
+    # A set of shapes no other test uses: the first ten calls alternate the
+    # per-product launches and the persistent loop (timed), later calls keep
+    # one of them; every call gives the same bits.
+    import torch
+    print("[ns loop] automatic choice 6 x 512 x 1024", flush=True)
+    bits = workloads.gaussian_bits((6, 512, 1024), seed=777)
+    x = workloads.to_device_bf16(bits)
+    nsm.muon_set_ns_schedule("auto")
+    outs, fams = [], []
+    for _ in range(14):
+        nsm.muon_timing_collect()
+        nsm.muon_timing_enable(["ns_loop", "gram"])
+        try:
+            outs.append(torch_bf16_to_bits(nsm.ns_orthogonalize_batched(x)))
+            torch.cuda.synchronize()
+        finally:
+            nsm.muon_timing_enable([])
+        fams.append(nsm.muon_timing_collect())
+    for o in outs[1:]:
+        np.testing.assert_array_equal(o, outs[0])
+    persistent = ["ns_loop" in f for f in fams]
+    assert persistent[:10] == [False, True] * 5, fams
+    assert len(set(persistent[10:])) == 1, fams
+
+
+@pytest.mark.parametrize("shape", [(18, 512, 256), (9, 512, 512), (24, 256, 768)])
+def test_loop_small_blocks_repeated(nsm, shape):
+    # Many small blocks (one or two tiles per product): operands small enough
+    # to stay in a CU's L1 between iterations, so a stale line would be read
+    # if the loop's acquire did not drop it.  Ten calls per schedule, each
+    # bitwise equal to the per-product result.
+    import torch
+    print(f"[ns loop] small blocks {shape}, ten calls", flush=True)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(shape[0] * 1000 + shape[2])
+    x = (torch.randn(shape, generator=gen, device="cuda") * 1e-2).to(torch.bfloat16)
+
+    def run():
+        outs = [nsm.ns_orthogonalize_batched(x) for _ in range(10)]
+        torch.cuda.synchronize()
+        return [o.view(torch.int16).cpu().numpy() for o in outs]
+
+    got, ref, _ = _both(nsm, run)
+    for k, g in enumerate(got):
+        np.testing.assert_array_equal(g, ref[0], err_msg=f"persistent call {k}")
