@@ -827,6 +827,12 @@ __global__ __launch_bounds__(NTHR) void k_ns_loop(PersistArgs args) {
         __hip_atomic_fetch_or(err + 1, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     uint32_t* prev_done = nullptr;    // counter of the item this workgroup finished last ...
     uint32_t prev_tiles = 0;          // ... and its tile count
+    // Lowest NS iteration among the items this workgroup has read operands
+    // for since its CU's L1 was last invalidated (the launch starts with it
+    // invalidated).  Within a launch every buffer version belongs to one
+    // iteration, and a block's versions are read in order, so the L1 can hold
+    // a stale line for an item only if the item's iteration is above this.
+    uint32_t t_low = 0xffffffffu;
     // The queue index of the next item is taken just before each tile's
     // stores are waited for, so that the atomic's round trip (several
     // microseconds under load) overlaps the drain.  A workgroup then holds one
@@ -874,11 +880,18 @@ __global__ __launch_bounds__(NTHR) void k_ns_loop(PersistArgs args) {
                     }
                     __builtin_amdgcn_s_sleep(2);
                 }
-                // Acquire: the CU's L1 may hold lines of this block's
-                // buffers from an earlier iteration.  The device-scope
-                // invalidate drops them (a workgroup-scope one does not, with
-                // all of a workgroup's waves on one CU).
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                // Acquire.  With XCD-local queues the XCD's L2 holds every
+                // write to the block's buffers, so only this CU's L1 can be
+                // stale, and only when t > t_low; the device-scope
+                // invalidate drops its lines (a workgroup-scope one does not,
+                // all of a workgroup's waves sharing one CU).  At device
+                // scope the L2 can be stale too: always invalidate.
+                if (!args.local_sync || t > t_low) {
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                    t_low = t;
+                } else {
+                    t_low = t;    // t <= t_low here
+                }
             }
             s_item = it;    // every lane of wave 0 writes the same value
         }
