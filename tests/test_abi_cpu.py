@@ -290,3 +290,17 @@ def test_workspace_must_not_overlap_data(lib):
     assert lib.muon_step_multi(arr, 2, f(0.02), f(0.01), f(0.95), 1, None, ctypes.c_void_p(base + (1 << 23) - 256),
                                wsb, None) == 1
     assert "workspace overlaps" in nsm.muon_last_error()
+
+
+def test_ns_schedule_modes(lib):
+    # Host-only: the process-wide schedule switch takes modes 0, 1, 2 and
+    # rejects others; the binding maps names to them.
+    for mode in (1, 2, 0):
+        assert lib.muon_set_ns_schedule(mode) == 0
+    assert lib.muon_set_ns_schedule(3) == 1
+    assert "schedule mode" in nsm.muon_last_error()
+    assert lib.muon_set_ns_schedule(-1) == 1
+    for name in ("per_product", "persistent", "auto"):
+        nsm.muon_set_ns_schedule(name)
+    with pytest.raises(ValueError):
+        nsm.muon_set_ns_schedule("fast")
