@@ -9,7 +9,10 @@
 //                     X' = B' X);
 //                     iteration 1 folds the normalisation into its epilogues
 //                     (A = U U^T / s^2, X1 = B' U / s), so X0 = U / s is
-//                     never materialised
+//                     never materialised;
+//                     or, by the NS schedule (muon_set_ns_schedule), one
+//                     k_ns_loop launch running all iterations from a tile
+//                     queue (after a k_zero_sync of its counters)
 //   k_finish          NS output, or the parameter update (+ optional O)
 // Small blocks (m <= 64, m n <= 8192) run the whole step in one k_small launch.
 // adamw_step_multi runs one k_adamw launch per 24 tensors.

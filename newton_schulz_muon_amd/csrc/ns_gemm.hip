@@ -766,9 +766,10 @@ __global__ __launch_bounds__(NTHR) void k_gemm(GemmArgs args) {
 // ---------------------------------------------------------------- persistent NS loop
 // One launch runs every iteration of the Gram, polynomial and B X products of
 // up to kMaxNsLoopProblems block batches, as 256-wide tiles.  Each workgroup
-// (one per CU) takes the next item of its queue (an atomic head), waits until
-// the item's block has completed every tile of the product before it
-// (done[block] reaches the item's count), computes the tile and adds one to
+// (one per CU) takes the next item of its queue (an atomic head): a run of up
+// to 16 consecutive tiles of one product of one block.  It waits until the
+// block has completed every tile of the products before that one (done[block]
+// reaches the item's count), computes the tiles and adds their number to
 // done[block].  Items are listed in an order in which each depends only on
 // items listed before it in the same queue, and an item is taken only by a
 // running workgroup, so the lowest unfinished item can always proceed.  A wait
