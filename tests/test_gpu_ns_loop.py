@@ -215,3 +215,24 @@ def test_loop_small_blocks_repeated(nsm, shape):
     got, ref, _ = _both(nsm, run)
     for k, g in enumerate(got):
         np.testing.assert_array_equal(g, ref[0], err_msg=f"persistent call {k}")
+
+
+@pytest.mark.parametrize("case", [
+    (2, 300, 700, "fast"),        # padded sides 384 x 768: not multiples of 256
+    (3, 512, 1024, "accurate"),   # hi/lo planes: per-product kernels only
+])
+def test_forced_loop_falls_back(nsm, case):
+    # With the persistent schedule forced, calls it does not apply to run the
+    # per-product launches, and give the same bits as under that schedule.
+    import torch
+    b, r, c, precision = case
+    print(f"[ns loop] fallback {case}", flush=True)
+    bits = workloads.gaussian_bits((b, r, c), seed=r + c)
+    x = workloads.to_device_bf16(bits)
+
+    def run():
+        return torch_bf16_to_bits(nsm.ns_orthogonalize_batched(x, precision=precision))
+
+    got, ref, counts = _both(nsm, run)
+    assert "ns_loop" not in counts and counts.get("gram", (0, 0.0))[0] == 5, counts
+    np.testing.assert_array_equal(got, ref)
