@@ -21,7 +21,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libmuon_hip.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["muon_api.hip", "muon_elementwise.hip", "ns_gemm.hip", "small_ns.hip", "adamw.hip"]
+SOURCES = ["muon_api.hip", "muon_elementwise.hip", "ns_gemm.hip", "ns_schedule.cpp", "small_ns.hip", "adamw.hip"]
 
 # -packed-fp32-ops: never emit v_pk_{add,mul,fma}_f32 (the host pass warns that
 # it does not know the feature; that is harmless).
@@ -54,7 +54,7 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     objs = []
     cmds = []
     for src in SOURCES:
-        obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
+        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         cmds.append([cc, *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=jobs) as ex:
