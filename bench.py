@@ -33,6 +33,12 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 WORKLOAD = "gpt124m"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_bx_gpt124m_traffic.json")
 LOOP_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_ns_loop_gpt124m_traffic.json")
+# The NS kernel families (library timing names) and the counter runs of each.
+NS_FAMILIES = {"ns_loop": "k_ns_loop (every NS iteration of a wave: X X^T, aI + bA + cA^2, B' X; nominal flops)",
+               "gram": "k_gemm<kGram> (A = X X^T; nominal flops)",
+               "poly": "k_gemm<kPoly> (B' = aI + bA + cA^2; nominal flops of A A)",
+               "bx": "k_gemm<kBx> (X <- B' X; nominal flops)"}
+TRAFFIC_FILES = {"ns_loop": LOOP_TRAFFIC_FILE, "bx": TRAFFIC_FILE}
 GEMM_SOURCE = os.path.join(ROOT, "newton_schulz_muon_amd", "csrc", "ns_gemm.hip")
 ADAM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_adamw_gpt124m_traffic.json")
 ADAM_SOURCE = os.path.join(ROOT, "newton_schulz_muon_amd", "csrc", "adamw.hip")
@@ -43,12 +49,6 @@ def ns_flops(m: int, n: int, steps: int) -> float:
     """Nominal NS work of one block: steps * (4 m^2 n + 2 m^3), m <= n."""
     m, n = min(m, n), max(m, n)
     return float(steps) * (4.0 * m * m * n + 2.0 * m ** 3)
-
-
-def bx_flops(m: int, n: int, steps: int) -> float:
-    """Work of the B X products of one block: steps * 2 m^2 n."""
-    m, n = min(m, n), max(m, n)
-    return float(steps) * 2.0 * m * m * n
 
 
 def source_digest(path: str) -> str:
@@ -192,12 +192,15 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
 
-    # ---- roofline region: the same K steps again, each NS-loop (or, per
-    # product, B'X) call bracketed by a hipEvent pair on the library's stream.
-    # Every event record costs a short dispatch bubble, which is why `value`
-    # comes from the uninstrumented region above.
+    # ---- roofline region: the same K steps again, each launch of the NS
+    # kernel families bracketed by a hipEvent pair on the library's stream;
+    # the library reports each launch's nominal flops beside its time (with
+    # the automatic schedule one step may run some waves in the persistent
+    # loop and others per product).  Every event record costs a short
+    # dispatch bubble, which is why `value` comes from the uninstrumented
+    # region above.
     nsm.muon_timing_collect()
-    nsm.muon_timing_enable(["bx", "ns_loop"])
+    nsm.muon_timing_enable(list(NS_FAMILIES))
     torch.cuda.synchronize()
     r0 = time.perf_counter()
     for _ in range(args.steps):
@@ -205,7 +208,7 @@ def main():
     torch.cuda.synchronize()
     r1 = time.perf_counter()
     nsm.muon_timing_enable([])
-    kt = nsm.muon_timing_collect()
+    kt = nsm.muon_timing_collect(with_flops=True)
 
     ms_per_step = (t1 - t0) * 1000.0 / args.steps
     flops_step = sum(g.view_blocks * g.count * ns_flops(*g.block_shape, wl.ns_steps) for g in wl.groups)
@@ -216,30 +219,25 @@ def main():
     # path and issue no B'X launch.
     mfma_groups = [g for g in wl.groups
                    if not (min(g.block_shape) <= 64 and g.block_shape[0] * g.block_shape[1] <= 8192)]
-    bx_flops_step = sum(g.n_blocks * bx_flops(*g.block_shape, wl.ns_steps) for g in mfma_groups)
-    bx_launches, bx_ms = kt.get("bx", (0, 0.0))
-    loop_launches, loop_ms = kt.get("ns_loop", (0, 0.0))
+    # Every MFMA-path NS flop of the step is reported by exactly one family.
+    mfma_flops_step = sum(g.n_blocks * ns_flops(*g.block_shape, wl.ns_steps) for g in mfma_groups)
+    reported_step = sum(v[2] for v in kt.values()) / args.steps
     roofline = None
-    if loop_launches:
-        # one launch runs every NS iteration of a wave: nominal NS flops of the
-        # MFMA-path blocks per launch over its duration
-        loop_flops_step = sum(g.n_blocks * ns_flops(*g.block_shape, wl.ns_steps) for g in mfma_groups)
-        achieved = loop_flops_step * args.steps / (loop_ms / 1000.0) / 1e12
+    if kt:
+        # dominant kernel: the NS family with the most time per step
+        fam = max(kt, key=lambda k: kt[k][1])
+        launches, fam_ms, fam_flops = kt[fam]
+        achieved = fam_flops / (fam_ms / 1000.0) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                    "traffic": load_traffic(LOOP_TRAFFIC_FILE),
-                    "kernel": "k_ns_loop (every NS iteration: X X^T, aI + bA + cA^2, B' X; nominal flops)",
-                    "launches": loop_launches, "avg_launch_ms": round(loop_ms / loop_launches, 5),
-                    "flops_per_launch_avg": loop_flops_step * args.steps / loop_launches,
-                    "region_ms_per_step": round((r1 - r0) * 1000.0 / args.steps, 4)}
-    elif bx_launches:
-        achieved = bx_flops_step * args.steps / (bx_ms / 1000.0) / 1e12
-        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                    "traffic": load_traffic(), "kernel": "k_gemm<kBx> (X <- B' X, B' = aI + bA + cA^2)",
-                    "launches": bx_launches, "avg_launch_ms": round(bx_ms / bx_launches, 5),
-                    "flops_per_launch_avg": bx_flops_step * args.steps / bx_launches,
-                    "region_ms_per_step": round((r1 - r0) * 1000.0 / args.steps, 4)}
+                    "traffic": load_traffic(TRAFFIC_FILES.get(fam)) if fam in TRAFFIC_FILES else None,
+                    "kernel": NS_FAMILIES[fam],
+                    "launches": launches, "avg_launch_ms": round(fam_ms / launches, 5),
+                    "flops_per_launch_avg": fam_flops / launches,
+                    "region_ms_per_step": round((r1 - r0) * 1000.0 / args.steps, 4),
+                    "ns_family_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in kt.items()},
+                    "ns_family_tflops": {k: round(v[2] / (v[1] / 1000.0) / 1e12, 2) for k, v in kt.items()},
+                    "flops_accounted": abs(reported_step - mfma_flops_step) <= 1e-9 * mfma_flops_step}
 
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 4
+#define MUON_ABI_VERSION 5
 
 typedef enum muon_status {
     MUON_OK = 0,
@@ -288,10 +288,15 @@ typedef enum muon_kernel_kind {
  * kernel plus a tail kernel, timed together. */
 muon_status muon_timing_enable(uint32_t kernel_mask);
 
-/* Waits for every recorded event, adds launch counts and elapsed milliseconds
- * per family into launches[MUON_KERNEL_COUNT] and total_ms[MUON_KERNEL_COUNT]
- * (either may be NULL), and forgets the recorded launches. */
-muon_status muon_timing_collect(int64_t* launches, double* total_ms);
+/* Waits for every recorded event, adds launch counts, elapsed milliseconds and
+ * nominal flops per family into launches[MUON_KERNEL_COUNT],
+ * total_ms[MUON_KERNEL_COUNT] and nominal_flops[MUON_KERNEL_COUNT] (any of
+ * them may be NULL), and forgets the recorded launches.  Nominal flops count
+ * the NS products a launch computes on the unpadded oriented blocks m x n
+ * (m <= n): 2 m^2 n for X X^T, 2 m^3 for A A, 2 m^2 n for B X, summed over
+ * the launch's blocks and, for MUON_KERNEL_NS_LOOP, its iterations; the
+ * other families report 0. */
+muon_status muon_timing_collect(int64_t* launches, double* total_ms, double* nominal_flops);
 
 /* Text of the last error on the calling thread ("" if none).  Valid until
  * the next call into the library from that thread. */

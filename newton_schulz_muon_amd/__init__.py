@@ -110,7 +110,8 @@ def load_library():
         lib.muon_set_ns_schedule.restype = ctypes.c_int
         lib.muon_timing_enable.argtypes = [ctypes.c_uint32]
         lib.muon_timing_enable.restype = ctypes.c_int
-        lib.muon_timing_collect.argtypes = [ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]
+        lib.muon_timing_collect.argtypes = [ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double),
+                                            ctypes.POINTER(ctypes.c_double)]
         lib.muon_timing_collect.restype = ctypes.c_int
         lib.muon_last_error.argtypes = []
         lib.muon_last_error.restype = ctypes.c_char_p
@@ -160,12 +161,18 @@ def muon_timing_enable(kinds=()) -> None:
     _check(load_library().muon_timing_enable(mask))
 
 
-def muon_timing_collect() -> dict:
-    """{family: (launches, total_ms)} for the launches recorded since the last collect."""
+def muon_timing_collect(with_flops: bool = False) -> dict:
+    """{family: (launches, total_ms)} for the launches recorded since the last
+    collect; with_flops=True adds the nominal flops of those launches as a
+    third element."""
     n = len(KERNEL_KINDS)
     launches = (ctypes.c_int64 * n)()
     total = (ctypes.c_double * n)()
-    _check(load_library().muon_timing_collect(launches, total))
+    flops = (ctypes.c_double * n)()
+    _check(load_library().muon_timing_collect(launches, total, flops))
+    if with_flops:
+        return {k: (int(launches[i]), float(total[i]), float(flops[i]))
+                for i, k in enumerate(KERNEL_KINDS) if launches[i]}
     return {k: (int(launches[i]), float(total[i])) for i, k in enumerate(KERNEL_KINDS) if launches[i]}
 
 

@@ -31,6 +31,9 @@ COMMON_FLAGS = [
     "-Wno-unused-command-line-argument",
     "-I", INCLUDE, "-I", CSRC,
 ]
+# Per-source flags.  ns_gemm.hip: the atomic optimizer would turn the
+# persistent loop's queue claim into an atomic followed by an immediate wait.
+SOURCE_FLAGS = {"ns_gemm.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 
 
 def hipcc() -> str:
@@ -56,7 +59,7 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        cmds.append([cc, *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([cc, *COMMON_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         outs = list(ex.map(_run, cmds))
     if verbose:

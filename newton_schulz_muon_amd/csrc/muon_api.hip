@@ -150,7 +150,7 @@ struct TimingState {
     std::mutex mu;
     std::atomic<uint32_t> mask{0};
     std::map<int, std::vector<hipEvent_t>> pool;   // per device
-    struct Rec { int kind; int dev; hipEvent_t a, b; };
+    struct Rec { int kind; int dev; hipEvent_t a, b; double flops; };
     std::vector<Rec> recs;
 };
 
@@ -173,10 +173,11 @@ hipEvent_t pool_get(TimingState& ts, int dev) {
     return e;
 }
 
-// Records an event pair around one launch when its kernel family is selected.
+// Records an event pair around one launch when its kernel family is selected,
+// with the nominal flops of the products the launch computes.
 class LaunchTimer {
   public:
-    LaunchTimer(int kind, hipStream_t s) : kind_(kind), s_(s) {
+    LaunchTimer(int kind, hipStream_t s, double flops) : kind_(kind), s_(s), flops_(flops) {
         TimingState& ts = timing();
         if (!(ts.mask.load() & (1u << kind))) return;
         std::lock_guard<std::mutex> lk(ts.mu);
@@ -190,24 +191,43 @@ class LaunchTimer {
         on_ = false;
         TimingState& ts = timing();
         std::lock_guard<std::mutex> lk(ts.mu);
-        if (hipEventRecord(b_, s_) == hipSuccess) ts.recs.push_back({kind_, dev_, a_, b_});
+        if (hipEventRecord(b_, s_) == hipSuccess) ts.recs.push_back({kind_, dev_, a_, b_, flops_});
     }
     ~LaunchTimer() { stop(); }
 
   private:
     int kind_;
     hipStream_t s_;
+    double flops_;
     int dev_ = 0;
     hipEvent_t a_ = nullptr, b_ = nullptr;
     bool on_ = false;
 };
 
 template <typename F>
-hipError_t timed(int kind, hipStream_t s, F&& f) {
-    LaunchTimer t(kind, s);
+hipError_t timed(int kind, hipStream_t s, F&& f, double flops = 0.0) {
+    LaunchTimer t(kind, s, flops);
     const hipError_t e = f();
     t.stop();
     return e;
+}
+
+// Nominal flops of one NS product over a plan's blocks, on the unpadded
+// oriented block m x n (m <= n): X X^T 2 m^2 n, A A 2 m^3, B X 2 m^2 n.
+// The polynomial's b A and a X terms and the symmetric products' skipped
+// tiles are not counted, nor the extra products of the hi/lo precision.
+double product_flops(const Plan& p, int kind) {
+    const double m = double(p.m), n = double(p.n), nb = double(p.nb);
+    switch (kind) {
+        case MUON_KERNEL_GRAM: return nb * 2.0 * m * m * n;
+        case MUON_KERNEL_POLY: return nb * 2.0 * m * m * m;
+        case MUON_KERNEL_BX: return nb * 2.0 * m * m * n;
+        default: return 0.0;
+    }
+}
+double ns_flops(const Plan& p, int steps) {
+    return double(steps) * (product_flops(p, MUON_KERNEL_GRAM) + product_flops(p, MUON_KERNEL_POLY) +
+                            product_flops(p, MUON_KERNEL_BX));
 }
 
 bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0; }
@@ -255,7 +275,8 @@ muon_status run_ns(const Plan& p, const muon_ns_config& cfg, const Buffers& b, h
     const NsLoopProblem lp{&p, {b.xh[0], b.xh[1]}, b.a, b.bh, b.scale, b.sync};
     const NsChoice ch = ns_schedule_begin(&lp, 1, cfg.ns_steps, s);
     if (ch.persistent) {
-        e = timed(MUON_KERNEL_NS_LOOP, s, [&] { return launch_ns_loop(&lp, 1, cfg.ns_steps, cfg.a, cfg.b, cfg.c, s); });
+        e = timed(MUON_KERNEL_NS_LOOP, s, [&] { return launch_ns_loop(&lp, 1, cfg.ns_steps, cfg.a, cfg.b, cfg.c, s); },
+                  ns_flops(p, cfg.ns_steps));
         if (e != hipSuccess) return hip_fail(e, "k_ns_loop launch");
         ns_schedule_end(ch, s);
         *final_idx = cfg.ns_steps & 1;
@@ -264,13 +285,15 @@ muon_status run_ns(const Plan& p, const muon_ns_config& cfg, const Buffers& b, h
     int cur = 0;
     for (int it = 0; it < cfg.ns_steps; ++it) {
         const float* sc = it == 0 ? b.scale : nullptr;
-        e = timed(MUON_KERNEL_GRAM, s, [&] { return launch_gram(p, b.xh[cur], b.a, sc, s); });
+        e = timed(MUON_KERNEL_GRAM, s, [&] { return launch_gram(p, b.xh[cur], b.a, sc, s); },
+                  product_flops(p, MUON_KERNEL_GRAM));
         if (e != hipSuccess) return hip_fail(e, "k_gemm<gram> launch");
-        e = timed(MUON_KERNEL_POLY, s, [&] { return launch_poly(p, b.a, b.bh, b.bl, cfg.a, cfg.b, cfg.c, s); });
+        e = timed(MUON_KERNEL_POLY, s, [&] { return launch_poly(p, b.a, b.bh, b.bl, cfg.a, cfg.b, cfg.c, s); },
+                  product_flops(p, MUON_KERNEL_POLY));
         if (e != hipSuccess) return hip_fail(e, "k_gemm<poly> launch");
         e = timed(MUON_KERNEL_BX, s, [&] {
             return launch_bx(p, b.bh, b.bl, b.xh[cur], b.xl[cur], b.xh[cur ^ 1], b.xl[cur ^ 1], sc, s);
-        });
+        }, product_flops(p, MUON_KERNEL_BX));
         if (e != hipSuccess) return hip_fail(e, "k_gemm<bx> launch");
         cur ^= 1;
     }
@@ -712,41 +735,50 @@ muon_status muon_step_multi(const muon_matrix* mats, int32_t count, float lr, fl
         const NsChoice ch = ns_schedule_begin(lps.data(), int(lps.size()), cfg.ns_steps, s);
         const bool loop = ch.persistent;
         if (loop) {
+            double fl = 0.0;
+            for (size_t gi : wave) fl += ns_flops(groups[gi].plan, cfg.ns_steps);
             const hipError_t e = timed(MUON_KERNEL_NS_LOOP, s, [&] {
                 return launch_ns_loop(lps.data(), int(lps.size()), cfg.ns_steps, cfg.a, cfg.b, cfg.c, s);
-            });
+            }, fl);
             if (e != hipSuccess) return hip_fail(e, "k_ns_loop launch");
             cur = cfg.ns_steps & 1;
         }
         for (int it = 0; it < (loop ? 0 : cfg.ns_steps); ++it) {
             for (const auto& bk : by_np) {
                 GramOp ops[kMaxGemmProblems];
+                double fl = 0.0;
                 for (size_t k = 0; k < bk.size(); ++k) {
                     const Buffers& b = bufs[bk[k]];
                     ops[k] = GramOp{&groups[bk[k]].plan, b.xh[cur], b.a, it == 0 ? b.scale : nullptr};
+                    fl += product_flops(groups[bk[k]].plan, MUON_KERNEL_GRAM);
                 }
-                const hipError_t e = timed(MUON_KERNEL_GRAM, s, [&] { return launch_gram(ops, int(bk.size()), s); });
+                const hipError_t e =
+                    timed(MUON_KERNEL_GRAM, s, [&] { return launch_gram(ops, int(bk.size()), s); }, fl);
                 if (e != hipSuccess) return hip_fail(e, "k_gemm<gram> launch");
             }
             for (const auto& bk : by_mp) {
                 PolyOp ops[kMaxGemmProblems];
+                double fl = 0.0;
                 for (size_t k = 0; k < bk.size(); ++k) {
                     const Buffers& b = bufs[bk[k]];
                     ops[k] = PolyOp{&groups[bk[k]].plan, b.a, b.bh, b.bl};
+                    fl += product_flops(groups[bk[k]].plan, MUON_KERNEL_POLY);
                 }
                 const hipError_t e = timed(MUON_KERNEL_POLY, s, [&] {
                     return launch_poly(ops, int(bk.size()), cfg.a, cfg.b, cfg.c, s);
-                });
+                }, fl);
                 if (e != hipSuccess) return hip_fail(e, "k_gemm<poly> launch");
             }
             for (const auto& bk : by_mp) {
                 BxOp ops[kMaxGemmProblems];
+                double fl = 0.0;
                 for (size_t k = 0; k < bk.size(); ++k) {
                     const Buffers& b = bufs[bk[k]];
                     ops[k] = BxOp{&groups[bk[k]].plan, b.bh, b.bl, b.xh[cur], b.xl[cur], b.xh[cur ^ 1],
                                   b.xl[cur ^ 1], it == 0 ? b.scale : nullptr};
+                    fl += product_flops(groups[bk[k]].plan, MUON_KERNEL_BX);
                 }
-                const hipError_t e = timed(MUON_KERNEL_BX, s, [&] { return launch_bx(ops, int(bk.size()), s); });
+                const hipError_t e = timed(MUON_KERNEL_BX, s, [&] { return launch_bx(ops, int(bk.size()), s); }, fl);
                 if (e != hipSuccess) return hip_fail(e, "k_gemm<bx> launch");
             }
             cur ^= 1;
@@ -906,7 +938,7 @@ muon_status muon_timing_enable(uint32_t kernel_mask) {
     return MUON_OK;
 }
 
-muon_status muon_timing_collect(int64_t* launches, double* total_ms) {
+muon_status muon_timing_collect(int64_t* launches, double* total_ms, double* nominal_flops) {
     g_err.clear();
     TimingState& ts = timing();
     std::lock_guard<std::mutex> lk(ts.mu);
@@ -920,6 +952,7 @@ muon_status muon_timing_collect(int64_t* launches, double* total_ms) {
         } else {
             if (launches) launches[r.kind] += 1;
             if (total_ms) total_ms[r.kind] += ms;
+            if (nominal_flops) nominal_flops[r.kind] += r.flops;
         }
         ts.pool[r.dev].push_back(r.a);
         ts.pool[r.dev].push_back(r.b);

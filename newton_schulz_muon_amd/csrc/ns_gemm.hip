@@ -67,7 +67,6 @@
 namespace muon {
 namespace {
 
-constexpr int NTHR = 256;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -106,10 +105,20 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
 //    whole cache lines (a 64-byte row costs the same L1 miss as a full
 //    line), and the other workgroup on the CU covers the first fragment
 //    reads of each step.
+//
+// Waves: a 128-wide tile is computed by 4 waves of 64 x 64, a 256-wide tile
+// by 8 waves of 128 x 64 (two per SIMD, 128 accumulator registers each).
+// With one wave per SIMD, the DMA issue, the vmcnt wait and the barrier of
+// each step leave the matrix core idle for about a quarter of the loop; a
+// second wave on the SIMD issues its MFMAs in those gaps.
 template <int BT, bool RING>
 struct TileCfg {
-    static constexpr int TW = BT / 2;               // wave tile edge
-    static constexpr int F = TW / 32;               // 32x32 blocks per wave side
+    static constexpr int NW = BT == 256 ? 8 : 4;    // waves
+    static constexpr int TWR = BT / 2;              // wave tile rows
+    static constexpr int TWC = 2 * BT / NW;         // wave tile columns
+    static constexpr int FA = TWR / 32;             // 32x32 blocks per wave: rows
+    static constexpr int FB = TWC / 32;             //                        columns
+    static constexpr int WC = BT / TWC;             // waves across the tile's columns
     static constexpr int BK = RING ? 32 : 64;       // K slice per stage
     static constexpr int NS = RING ? 4 : 2;         // LDS stages
     static constexpr int OP_BYTES = BT * BK * 2;    // one operand tile
@@ -136,16 +145,18 @@ __device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t voff, uint32_t
     asm volatile("buffer_load_dwordx4 %1, %2, %3 offen lds" ::"{m0}"(m0), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
 }
 
-// An R x BK slice of a k-contiguous matrix fetched straight into LDS: one
-// instruction of one wave fills 1 KB (lane L writes bytes [16 L, 16 L + 16)),
-// i.e. 512 / BK rows of BK / 8 chunks.  The lane whose LDS slot is (row,
-// physical chunk p) fetches logical chunk p ^ swz(row).
-template <int R, int BK_>
+// An R x BK slice of a k-contiguous matrix fetched straight into LDS by the
+// NW waves of the workgroup: one instruction of one wave fills 1 KB (lane L
+// writes bytes [16 L, 16 L + 16)), i.e. 512 / BK rows of BK / 8 chunks.  The
+// lane whose LDS slot is (row, physical chunk p) fetches logical chunk
+// p ^ swz(row).
+template <int R, int BK_, int NW>
 struct RowDma {
     static constexpr int BK = BK_;
     static constexpr int CPR = BK / 8;               // chunks per row
     static constexpr int RPW = 64 / CPR;             // rows per 1 KB window
-    static constexpr int PW = R / RPW / 4;           // windows per wave
+    static constexpr int PW = R / RPW / NW;          // windows per wave
+    static_assert(PW >= 1 && PW * RPW * NW == R, "slice splits evenly over the waves");
     const void* base;                   // the matrix; its buffer descriptor is built in load()
     uint32_t bytes;
     uint32_t voff[PW];
@@ -178,11 +189,12 @@ __device__ __forceinline__ int col_off(int row, int col) {
     return row * (2 * C) + (((col >> 3) ^ ((row & 3) << 2)) << 4) + (((col >> 2) & 1) << 3);
 }
 
-template <int C, int BK_>
+template <int C, int BK_, int NW>
 struct ColDma {
     static constexpr int BK = BK_;
     static constexpr int ROWS_PER_WIN = 512 / C;
-    static constexpr int PW = BK / ROWS_PER_WIN / 4;   // 1 KB windows per wave
+    static constexpr int PW = BK / ROWS_PER_WIN / NW;  // 1 KB windows per wave
+    static_assert(PW >= 1 && PW * ROWS_PER_WIN * NW == BK, "slice splits evenly over the waves");
     const void* base;
     uint32_t bytes;
     uint32_t ldb;                                      // row pitch in bytes
@@ -260,16 +272,17 @@ __device__ __forceinline__ bf16x8 load_frag(const char* S, int base, int ks, int
 }
 
 // The fragments of one sub-slice, read in the order the MFMAs consume them
-// (a0 with b0 .. b(F-1), then a1, a2, ...), so the reads issued last have the
+// (a0 with b0 .. b(FB-1), then a1, a2, ...), so the reads issued last have the
 // most MFMAs of the next sub-slice to complete behind.  With DMA, the W loads
 // of a stage (into `next`, K offset k1) are issued in between: fragment g of
 // the G fragment reads that carry them (this call's first fragment is number
 // g0) issues the windows w with w G in [g W, (g + 1) W).  The reads are placed
 // one per MFMA, so the DMA instructions are spread over the MFMA stream
 // instead of stalling the wave in a burst when the address queue fills.
-template <int F, bool KMAJOR_A, bool KMAJOR_B, int BT, int BK, bool DMA = false, int G = 1, typename Ops = void>
+template <int FA, int FB, bool KMAJOR_A, bool KMAJOR_B, int BT, int BK, bool DMA = false, int G = 1,
+          typename Ops = void>
 __device__ __forceinline__ void load_frags(const char* As, const char* Bs, int wr0, int wc0, int ks,
-                                           bf16x8 (&a)[F], bf16x8 (&b)[F], int tid, const Ops* ops = nullptr,
+                                           bf16x8 (&a)[FA], bf16x8 (&b)[FB], int tid, const Ops* ops = nullptr,
                                            char* next = nullptr, int k1 = 0, int g0 = 0) {
     auto dma_after = [&](int fi) {
         if constexpr (DMA) {
@@ -283,34 +296,47 @@ __device__ __forceinline__ void load_frags(const char* As, const char* Bs, int w
     a[0] = load_frag<KMAJOR_A, BT, BK>(As, wr0, ks, tid);
     dma_after(0);
 #pragma unroll
-    for (int j = 0; j < F; ++j) {
+    for (int j = 0; j < FB; ++j) {
         b[j] = load_frag<KMAJOR_B, BT, BK>(Bs, wc0 + j * 32, ks, tid);
         dma_after(1 + j);
     }
 #pragma unroll
-    for (int i = 1; i < F; ++i) {
+    for (int i = 1; i < FA; ++i) {
         a[i] = load_frag<KMAJOR_A, BT, BK>(As, wr0 + i * 32, ks, tid);
-        dma_after(F + i);
+        dma_after(FB + i);
     }
 }
 
-template <int F>
-__device__ __forceinline__ void mfma_block(const bf16x8 (&a)[F], const bf16x8 (&b)[F], f32x16 (&acc)[F][F]) {
+template <int FA, int FB>
+__device__ __forceinline__ void mfma_block(const bf16x8 (&a)[FA], const bf16x8 (&b)[FB], f32x16 (&acc)[FA][FB]) {
 #pragma unroll
-    for (int i = 0; i < F; ++i)
+    for (int i = 0; i < FA; ++i)
 #pragma unroll
-        for (int j = 0; j < F; ++j)
+        for (int j = 0; j < FB; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
 }
 
-// Interleaves the F*F MFMAs of one sub-slice with the NREAD LDS reads issued
-// beside them (the fragments of the next sub-slice).
-template <int F, int NREAD>
+// Interleaves the NM MFMAs of one sub-slice with the NREAD LDS reads issued
+// beside them (the fragments of the next sub-slice).  Square 4-wave tiles
+// alternate read and MFMA groups; the 8-wave tiles spread their reads evenly
+// ahead of each MFMA (12 reads over 8 MFMAs for k-major operands).
+template <int NM, int NREAD, int M>
+__device__ __forceinline__ void spread_reads() {
+    constexpr int nr = ((M + 1) * NREAD) / NM - (M * NREAD) / NM;
+    if constexpr (nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, nr, 0);    // LDS reads
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                           // one MFMA
+    if constexpr (M + 1 < NM) spread_reads<NM, NREAD, M + 1>();
+}
+template <int NM, int NREAD, bool SPREAD>
 __device__ __forceinline__ void interleave() {
+    if constexpr (!SPREAD) {
 #pragma unroll
-    for (int t = 0; t < NREAD; ++t) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                   // LDS read
-        __builtin_amdgcn_sched_group_barrier(0x008, (F * F) / NREAD, 0);     // MFMA
+        for (int t = 0; t < NREAD; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);              // LDS read
+            __builtin_amdgcn_sched_group_barrier(0x008, NM / NREAD, 0);     // MFMA
+        }
+    } else {
+        spread_reads<NM, NREAD, 0>();
     }
 }
 
@@ -328,12 +354,12 @@ __device__ __forceinline__ void wait_dma_and_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <int F>
-__device__ __forceinline__ void zero_acc(f32x16 (&acc)[F][F]) {
+template <int FA, int FB>
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[FA][FB]) {
 #pragma unroll
-    for (int i = 0; i < F; ++i)
+    for (int i = 0; i < FA; ++i)
 #pragma unroll
-        for (int j = 0; j < F; ++j)
+        for (int j = 0; j < FB; ++j)
 #pragma unroll
             for (int s = 0; s < 16; ++s) acc[i][j][s] = 0.f;
 }
@@ -353,7 +379,8 @@ __device__ __forceinline__ uint32_t xcd_logical(uint32_t w, uint32_t total) {
     return x * q + (x < r ? x : r) + (w >> 3);
 }
 
-// Epilogue staging, per wave and per 32-row chunk of its TW x TW tile.
+// Epilogue staging, per wave and per 32-row chunk of its wave tile (TW
+// columns).
 // fp32 chunk: rows of TW floats, 16-byte chunk index XOR (row % 16), so the
 // MFMA-layout writes (16 rows, one chunk) and the row-contiguous reads (one
 // row, 16 chunks) are both conflict-free.
@@ -439,19 +466,26 @@ constexpr int tile_lds_bytes() {
     return Cfg::NS * (KIND == kBxSplit ? 4 : 2) * Cfg::OP_BYTES;
 }
 
-// Computes one BT x BT output tile with the 256 threads of the workgroup,
+struct NoHook {
+    __device__ __forceinline__ void operator()() const {}
+};
+
+// Computes one BT x BT output tile with the NW waves of the workgroup,
 // using `lds` (tile_lds_bytes<KIND, BT>() bytes) for the operand stages and
 // the epilogue.  All LDS traffic of the previous use of `lds` must be
-// finished (a barrier) before the call.
-template <int KIND, int BT, bool OPAQUE_TID = false>
-__device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca, float cb, float cc) {
+// finished (a barrier) before the call.  Each wave calls hook() once in its
+// epilogue, after the last global load it waits for (so that a memory
+// operation the hook issues is not waited for by the rest of the tile).
+template <int KIND, int BT, bool OPAQUE_TID = false, typename Hook = NoHook>
+__device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca, float cb, float cc,
+                                          const Hook& hook = Hook()) {
     // In a loop over tiles the thread index is made opaque per tile, so that
     // the compiler does not hoist the lane-dependent address arithmetic of
     // every product out of the loop (and spill it).
     int tid = static_cast<int>(threadIdx.x);
     if constexpr (OPAQUE_TID) asm volatile("" : "+v"(tid));
     using Cfg = TileCfg<BT, BT == 256 || KIND == kBx || KIND == kBxSplit>;
-    constexpr int F = Cfg::F, TW = Cfg::TW;
+    constexpr int FA = Cfg::FA, FB = Cfg::FB, TWR = Cfg::TWR, TWC = Cfg::TWC, NW = Cfg::NW;
     constexpr bool SYM = KIND == kGram || KIND == kPoly || KIND == kPolySplit;
     constexpr bool POLY = KIND == kPoly || KIND == kPolySplit;
     constexpr bool SPLIT_IN = KIND == kBxSplit;                       // hi/lo planes of both operands
@@ -465,8 +499,8 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
     constexpr bool KMAJOR_B = KIND != kGram;
     constexpr int NA = SPLIT_IN ? 2 : 1, NB = SPLIT_IN ? 2 : 1;
     constexpr int BK = Cfg::BK;
-    using ALoader = typename std::conditional<KMAJOR_A, ColDma<BT, BK>, RowDma<BT, BK>>::type;
-    using BLoader = typename std::conditional<KMAJOR_B, ColDma<BT, BK>, RowDma<BT, BK>>::type;
+    using ALoader = typename std::conditional<KMAJOR_A, ColDma<BT, BK, NW>, RowDma<BT, BK, NW>>::type;
+    using BLoader = typename std::conditional<KMAJOR_B, ColDma<BT, BK, NW>, RowDma<BT, BK, NW>>::type;
     using Ops = Operands<BT, NA, NB, ALoader, BLoader>;
     constexpr int STAGE = Ops::STAGE;
     constexpr int LDS_BYTES = Cfg::NS * STAGE;
@@ -474,7 +508,7 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
     const int ti = a.ti, tj = a.tj;
     const int row0 = ti * BT, col0 = tj * BT;
     const int wave = tid >> 6;
-    const int wr0 = (wave >> 1) * TW, wc0 = (wave & 1) * TW;
+    const int wr0 = (wave / Cfg::WC) * TWR, wc0 = (wave % Cfg::WC) * TWC;
 
     Ops ops;
 #pragma unroll
@@ -482,8 +516,11 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
 #pragma unroll
     for (int j = 0; j < NB; ++j) ops.b[j].init(a.q[j], a.q_bytes, KMAJOR_B ? a.ldq : a.K, col0, tid);
 
-    f32x16 acc[F][F];
-    zero_acc<F>(acc);
+    f32x16 acc[FA][FB];
+    zero_acc<FA, FB>(acc);
+    // The epilogue's factor, loaded with the operand prologue, so that the
+    // epilogue waits for no global load of its own.
+    const float sc = a.scale ? *a.scale : 1.0f;
 
     // A K step is U sub-slices (16 deep, and for the split B X three products
     // each); the fragments of sub-slice u + 1 are read from LDS while the
@@ -493,13 +530,15 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
     constexpr int P = SPLIT_IN ? 3 : 1;
     constexpr int U = P * KS;
     static_assert(U % 2 == 0, "fragment ping-pong restarts at 0 each step");
-    constexpr int NREAD = (KMAJOR_A ? 2 * F : F) + (KMAJOR_B ? 2 * F : F);
+    constexpr int NREAD = (KMAJOR_A ? 2 * FA : FA) + (KMAJOR_B ? 2 * FB : FB);
+    constexpr int NM = FA * FB;
+    constexpr bool SPREAD = NW == 8;
     constexpr int W = Ops::WINDOWS;
     const int nk = static_cast<int>(a.K / BK);
-    bf16x8 fa[2][F], fb[2][F];
-    auto frags = [&](const char* st, int u, bf16x8 (&xa)[F], bf16x8 (&xb)[F]) {
+    bf16x8 fa[2][FA], fb[2][FB];
+    auto frags = [&](const char* st, int u, bf16x8 (&xa)[FA], bf16x8 (&xb)[FB]) {
         const int pn = u / KS, ks = u % KS;
-        load_frags<F, KMAJOR_A, KMAJOR_B, BT, BK>(Ops::a_tile(const_cast<char*>(st), pn == 2 ? 1 : 0),
+        load_frags<FA, FB, KMAJOR_A, KMAJOR_B, BT, BK>(Ops::a_tile(const_cast<char*>(st), pn == 2 ? 1 : 0),
                                               Ops::b_tile(const_cast<char*>(st), pn == 1 ? 1 : 0), wr0, wc0, ks,
                                               xa, xb, tid);
     };
@@ -528,12 +567,12 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
                 } else {
                     wait_dma_and_barrier<(NS - 3) * W>();
                     const int kn = kt + NS - 1;
-                    load_frags<F, KMAJOR_A, KMAJOR_B, BT, BK, true, 2 * F>(
+                    load_frags<FA, FB, KMAJOR_A, KMAJOR_B, BT, BK, true, FA + FB>(
                         Ops::a_tile(nxt, 0), Ops::b_tile(nxt, 0), wr0, wc0, 0, fa[c ^ 1], fb[c ^ 1], tid, &ops,
                         lds + (kn % NS) * STAGE, (kn < nk ? kn : kt) * BK, 0);
                 }
-                mfma_block<F>(fa[c], fb[c], acc);
-                interleave<F, NREAD>();
+                mfma_block<FA, FB>(fa[c], fb[c], acc);
+                interleave<NM, NREAD, SPREAD>();
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -554,12 +593,12 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
                 const int c = u & 1;
                 if (u + 1 < U) {
                     const int pn = (u + 1) / KS, ks = (u + 1) % KS;
-                    load_frags<F, KMAJOR_A, KMAJOR_B, BT, BK, true, (U - 1) * 2 * F>(
+                    load_frags<FA, FB, KMAJOR_A, KMAJOR_B, BT, BK, true, (U - 1) * (FA + FB)>(
                         Ops::a_tile(cur, pn == 2 ? 1 : 0), Ops::b_tile(cur, pn == 1 ? 1 : 0), wr0, wc0, ks,
-                        fa[c ^ 1], fb[c ^ 1], tid, &ops, nxt, k1, u * 2 * F);
+                        fa[c ^ 1], fb[c ^ 1], tid, &ops, nxt, k1, u * (FA + FB));
                 }
-                mfma_block<F>(fa[c], fb[c], acc);
-                if (u + 1 < U) interleave<F, NREAD>();
+                mfma_block<FA, FB>(fa[c], fb[c], acc);
+                if (u + 1 < U) interleave<NM, NREAD, SPREAD>();
                 __builtin_amdgcn_sched_barrier(0);
             }
             wait_dma_and_barrier<0>();
@@ -575,19 +614,18 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
     // of one wave complete in order, so no barrier is needed.
     const int lane = tid & 63;
     const int lr = lane & 31, lk = lane >> 5;
-    const float sc = a.scale ? *a.scale : 1.0f;
     const uint16_t* amat = POLY ? a.p[0] : nullptr;
     uint16_t* out0 = a.out[0];
     uint16_t* out1 = SPLIT_OUT ? a.out[1] : nullptr;
-    constexpr int ST_F32 = 32 * TW * 4;
-    constexpr int ST_BF = SYM ? 32 * TW * 2 : 0;
+    constexpr int ST_F32 = 32 * TWC * 4;
+    constexpr int ST_BF = SYM ? 32 * TWC * 2 : 0;
     constexpr int WAVE_LDS = ST_F32 + ST_BF * (SPLIT_OUT ? 2 : 1);
-    static_assert(4 * WAVE_LDS <= LDS_BYTES, "epilogue staging must fit in LDS");
+    static_assert(NW * WAVE_LDS <= LDS_BYTES, "epilogue staging must fit in LDS");
     char* sf = lds + wave * WAVE_LDS;
     char* sb = sf + ST_F32;
     char* sb_lo = sb + ST_BF;
     const bool mirror = SYM && ti != tj;
-    constexpr int LPR = TW / 4;       // lanes per row on read-back (4 values each)
+    constexpr int LPR = TWC / 4;      // lanes per row on read-back (4 values each)
     constexpr int RPI = 64 / LPR;     // rows per read-back instruction
     const int rrow = lane / LPR, rcol = (lane % LPR) * 4;
     const int64_t gcol = col0 + wc0 + rcol;
@@ -601,29 +639,32 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
             dst[t] = *reinterpret_cast<const u32x2*>(amat + (int64_t)(row0 + wr0 + i * 32 + t * RPI + rrow) * a.ldo +
                                                      gcol);
     };
-    if constexpr (POLY) load_a(0, abuf[0]);
+    if constexpr (POLY)
+        load_a(0, abuf[0]);
+    else
+        hook();
 #pragma unroll
-    for (int i = 0; i < F; ++i) {
+    for (int i = 0; i < FA; ++i) {
         if constexpr (KIND == kBx) {
             // B X: the rounded bf16 values go through LDS (half the bytes of
             // fp32 staging) and leave as 16-byte pieces of rows.
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int j = 0; j < F; ++j)
+            for (int j = 0; j < FB; ++j)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     uint16_t hb[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) hb[e] = f32_to_bf16(acc[i][j][g * 4 + e] * sc);
-                    *reinterpret_cast<u32x2*>(sf + bst_off<TW>(lr, j * 32 + g * 8 + lk * 4)) = pack4(hb);
+                    *reinterpret_cast<u32x2*>(sf + bst_off<TWC>(lr, j * 32 + g * 8 + lk * 4)) = pack4(hb);
                 }
             __builtin_amdgcn_sched_barrier(0);
-            constexpr int CH = TW / 8, RPB = 64 / CH;
+            constexpr int CH = TWC / 8, RPB = 64 / CH;
             const int brow = lane / CH, bch = lane % CH;
 #pragma unroll
             for (int t = 0; t < 32 / RPB; ++t) {
                 const int rr = t * RPB + brow;
-                u32x4 v = *reinterpret_cast<const u32x4*>(sf + rr * (TW * 2) + ((bch ^ (rr & (CH - 1))) << 4));
+                u32x4 v = *reinterpret_cast<const u32x4*>(sf + rr * (TWC * 2) + ((bch ^ (rr & (CH - 1))) << 4));
                 if ((rr / CH) & 1) v = u32x4{v[2], v[3], v[0], v[1]};
                 *reinterpret_cast<u32x4*>(out0 + (int64_t)(row0 + wr0 + i * 32 + rr) * a.ldo + col0 + wc0 + 8 * bch) = v;
             }
@@ -631,15 +672,15 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < F; ++j)
+        for (int j = 0; j < FB; ++j)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const f32x4 v = {acc[i][j][g * 4 + 0], acc[i][j][g * 4 + 1], acc[i][j][g * 4 + 2],
                                  acc[i][j][g * 4 + 3]};
-                *reinterpret_cast<f32x4*>(sf + f32_off<TW>(lr, j * 32 + g * 8 + lk * 4)) = v;
+                *reinterpret_cast<f32x4*>(sf + f32_off<TWC>(lr, j * 32 + g * 8 + lk * 4)) = v;
             }
         if constexpr (POLY) {
-            if (i + 1 < F) load_a(i + 1, abuf[(i + 1) & 1]);
+            if (i + 1 < FA) load_a(i + 1, abuf[(i + 1) & 1]);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -647,7 +688,7 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
             const int rr = t * RPI + rrow;
             const int64_t grow = row0 + wr0 + i * 32 + rr;
             const int64_t o = grow * a.ldo + gcol;
-            const f32x4 x = *reinterpret_cast<const f32x4*>(sf + f32_off<TW>(rr, rcol));
+            const f32x4 x = *reinterpret_cast<const f32x4*>(sf + f32_off<TWC>(rr, rcol));
             float am[4] = {0.f, 0.f, 0.f, 0.f};
             if constexpr (POLY) {
                 const u32x2 av = abuf[i & 1][t];
@@ -673,10 +714,14 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
             if constexpr (SPLIT_OUT) *reinterpret_cast<u32x2*>(out1 + o) = pack4(lb);
             if constexpr (SYM) {
                 if (mirror) {
-                    *reinterpret_cast<u32x2*>(sb + mir_off<TW>(rr, rcol)) = pack4(hb);
-                    if constexpr (SPLIT_OUT) *reinterpret_cast<u32x2*>(sb_lo + mir_off<TW>(rr, rcol)) = pack4(lb);
+                    *reinterpret_cast<u32x2*>(sb + mir_off<TWC>(rr, rcol)) = pack4(hb);
+                    if constexpr (SPLIT_OUT) *reinterpret_cast<u32x2*>(sb_lo + mir_off<TWC>(rr, rcol)) = pack4(lb);
                 }
             }
+        }
+        // The polynomial's last wait for A values is above.
+        if constexpr (POLY) {
+            if (i + 1 == FA) hook();
         }
         if constexpr (SYM) {
             // Mirror: output row (col0 + wc0 + c) gets this chunk's 32 values of
@@ -686,19 +731,19 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
                 const int L = lane & 15, g4 = lane >> 4;
                 const int srow = 8 * g4 + (L >> 2);
 #pragma unroll
-                for (int cb = 0; cb < TW; cb += 16) {
+                for (int cb = 0; cb < TWC; cb += 16) {
                     const int scol = cb + 4 * (L & 3);
                     const int64_t o = (int64_t)(col0 + wc0 + cb + L) * a.ldo + row0 + wr0 + i * 32 + 8 * g4;
                     const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) i16x4*)(sb + mir_off<TW>(srow, scol)));
+                        (__attribute__((address_space(3))) i16x4*)(sb + mir_off<TWC>(srow, scol)));
                     const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) i16x4*)(sb + mir_off<TW>(srow + 4, scol)));
+                        (__attribute__((address_space(3))) i16x4*)(sb + mir_off<TWC>(srow + 4, scol)));
                     *reinterpret_cast<i16x8*>(out0 + o) = i16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
                     if constexpr (SPLIT_OUT) {
                         const i16x4 w0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) i16x4*)(sb_lo + mir_off<TW>(srow, scol)));
+                            (__attribute__((address_space(3))) i16x4*)(sb_lo + mir_off<TWC>(srow, scol)));
                         const i16x4 w1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) i16x4*)(sb_lo + mir_off<TW>(srow + 4, scol)));
+                            (__attribute__((address_space(3))) i16x4*)(sb_lo + mir_off<TWC>(srow + 4, scol)));
                         *reinterpret_cast<i16x8*>(out1 + o) =
                             i16x8{w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
                     }
@@ -708,8 +753,14 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
     }
 }
 
+// Threads of a tile's workgroup.
+template <int BT>
+constexpr int tile_threads() {
+    return 64 * TileCfg<BT, true>::NW;
+}
+
 template <int KIND, int BT>
-__global__ __launch_bounds__(NTHR) void k_gemm(GemmArgs args) {
+__global__ __launch_bounds__(tile_threads<BT>()) void k_gemm(GemmArgs args) {
     constexpr bool SYM = KIND == kGram || KIND == kPoly || KIND == kPolySplit;
     constexpr bool SPLIT_IN = KIND == kBxSplit;
     constexpr bool SPLIT_OUT = KIND == kPolySplit || KIND == kBxSplit;
@@ -803,20 +854,28 @@ constexpr uint32_t kSyncStride = 32;
 constexpr uint64_t kSpinTicks = 100000000;   // 1 s of the 100 MHz real-time counter
 constexpr uint32_t kItemEnd = 0xffffffffu;
 constexpr uint32_t kBlockMask = 0x0fffffffu;   // item.x: block; the top 4 bits: tiles in the item - 1
+// Items of the workgroup's queue held in LDS (a window from the queue index
+// win0; wave 0 reloads it when an index passes its end).
+constexpr uint32_t kLdsItems = 2048;
 
-__global__ __launch_bounds__(NTHR) void k_ns_loop(PersistArgs args) {
+__global__ __launch_bounds__(tile_threads<256>()) void k_ns_loop(PersistArgs args) {
     constexpr int LDS = tile_lds_bytes<kBx, 256>();
     static_assert(tile_lds_bytes<kGram, 256>() <= LDS && tile_lds_bytes<kPoly, 256>() <= LDS, "LDS size");
+    static_assert(LDS + 8 * kLdsItems + 8 <= 160 * 1024, "LDS of a gfx950 workgroup");
     __shared__ __attribute__((aligned(16))) char lds[LDS];
+    __shared__ uint2 s_items[kLdsItems];
     __shared__ uint2 s_item;
     // The loop's control flow is uniform across the workgroup: wave 0 does the
-    // queue and counter work with all its lanes (lane 0 alone adds 1 in each
-    // atomic, the others add 0) and every value that steers the loop is read
-    // with readfirstlane.  (Lane-divergent code at the head and the end of
-    // this loop let the compiler split it into separate loops for lane 0 and
-    // the other lanes, which never meet at the barriers again.)
+    // queue and counter work, lane 0 alone issuing each atomic (in a branch
+    // that holds nothing else), and every value that steers the loop is read
+    // with readfirstlane.  (Lane-divergent loop conditions at the head and
+    // the end of this loop let the compiler split it into separate loops for
+    // lane 0 and the other lanes, which never meet at the barriers again.)
+    // The compiler's atomic optimizer is off for this source: it rewrites a
+    // returning atomic into a one-lane atomic followed by an immediate wait
+    // and broadcast of the result, which would stall the claim below.
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-    const uint32_t one = (threadIdx.x & 63) == 0 ? 1u : 0u;
+    const bool lane0 = (threadIdx.x & 63) == 0;
     // With 8 queues, workgroup w serves queue w % 8, which gives every queue
     // the same number of workgroups; the launcher enables local_sync only
     // where workgroup w runs on XCD w % 8 (checked once per device), so a
@@ -825,8 +884,8 @@ __global__ __launch_bounds__(NTHR) void k_ns_loop(PersistArgs args) {
     const int q = args.nq == 8 ? static_cast<int>(blockIdx.x & 7) : 0;
     const uint32_t qb = args.qbase[q], qlen = args.qbase[q + 1] - qb;
     uint32_t* const err = args.sync + kSyncStride * 8;
-    if (args.local_sync && wave == 0 && xcc != (blockIdx.x & 7))
-        __hip_atomic_fetch_or(err + 1, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (args.local_sync && wave == 0 && xcc != (blockIdx.x & 7) && lane0)
+        __hip_atomic_fetch_or(err + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     uint32_t* prev_done = nullptr;    // counter of the item this workgroup finished last ...
     uint32_t prev_tiles = 0;          // ... and its tile count
     // Lowest NS iteration among the items this workgroup has read operands
@@ -835,29 +894,43 @@ __global__ __launch_bounds__(NTHR) void k_ns_loop(PersistArgs args) {
     // iteration, and a block's versions are read in order, so the L1 can hold
     // a stale line for an item only if the item's iteration is above this.
     uint32_t t_low = 0xffffffffu;
-    // The queue index of the next item is taken just before each tile's
-    // stores are waited for, so that the atomic's round trip (several
-    // microseconds under load) overlaps the drain.  A workgroup then holds one
-    // item beyond the one it has finished computing, and takes items in queue
-    // order, so the lowest unfinished item can always proceed.
-    uint32_t idx = 0;
-    if (wave == 0)
-        idx = __builtin_amdgcn_readfirstlane(__hip_atomic_fetch_add(args.sync + kSyncStride * q, one, __ATOMIC_RELAXED,
-                                                                     __HIP_MEMORY_SCOPE_AGENT));
+    // The queue index of the next item is taken in the epilogue of an item's
+    // last tile (by wave 0, once it has no load left to wait for), so that
+    // the atomic's round trip (several microseconds under load) overlaps the
+    // epilogue's stores; vector memory operations retire in order, so taken
+    // any earlier it would stall the K loop's DMA waits.  A workgroup then
+    // holds one item beyond the one it has finished computing, and takes
+    // items in queue order, so the lowest unfinished item can always proceed.
+    // The item descriptors are read from the LDS copy of the queue.
+    uint32_t win0 = 0;
+    {
+        const uint32_t n0 = qlen < kLdsItems ? qlen : kLdsItems;
+        for (uint32_t i = threadIdx.x; i < n0; i += blockDim.x) s_items[i] = args.items[qb + i];
+    }
+    uint32_t* const head = args.sync + kSyncStride * q;
+    uint32_t idx_v = 0;      // the claimed index (lane 0 of wave 0), read once the stores have drained
+    if (wave == 0 && lane0) idx_v = __hip_atomic_fetch_add(head, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
     for (;;) {
         if (wave == 0) {
             // The previous tile's stores completed before the barrier that
             // ended it; the add publishes them.
-            if (prev_done) {
-                const uint32_t add = one * prev_tiles;
+            if (prev_done && lane0) {
                 if (args.local_sync)
-                    __hip_atomic_fetch_add(prev_done, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_fetch_add(prev_done, prev_tiles, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 else
-                    __hip_atomic_fetch_add(prev_done, add, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_fetch_add(prev_done, prev_tiles, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
             }
             uint2 it = {kItemEnd, 0u};
+            const uint32_t idx = __builtin_amdgcn_readfirstlane(idx_v);
             if (idx < qlen) {
-                const uint2 raw = args.items[qb + idx];
+                if (idx - win0 >= kLdsItems) {
+                    // Only wave 0 reads the window; its LDS accesses complete in order.
+                    win0 = idx;
+                    const uint32_t n = qlen - win0 < kLdsItems ? qlen - win0 : kLdsItems;
+                    for (uint32_t i = threadIdx.x; i < n; i += 64) s_items[i] = args.items[qb + win0 + i];
+                }
+                const uint2 raw = s_items[idx - win0];
                 it.x = __builtin_amdgcn_readfirstlane(raw.x);
                 it.y = __builtin_amdgcn_readfirstlane(raw.y);
                 const uint32_t g = it.x & kBlockMask;
@@ -876,7 +949,7 @@ __global__ __launch_bounds__(NTHR) void k_ns_loop(PersistArgs args) {
                     const uint32_t e = __builtin_amdgcn_readfirstlane(
                         __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
                     if (e != 0u || __builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) {
-                        __hip_atomic_fetch_or(err, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        if (lane0) __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                         it.x = kItemEnd;
                         break;
                     }
@@ -912,6 +985,11 @@ __global__ __launch_bounds__(NTHR) void k_ns_loop(PersistArgs args) {
         const int64_t xs = int64_t(pr.mp) * pr.np, as = int64_t(pr.mp) * pr.mp;
         for (int c = 0; c < ntiles; ++c) {
             if (c > 0) __syncthreads();    // the previous tile's epilogue is done with LDS
+            const bool last = c + 1 == ntiles;
+            const auto claim = [&]() {
+                if (wave == 0 && last && lane0)
+                    idx_v = __hip_atomic_fetch_add(head, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            };
             int id = static_cast<int>(ity & 0x3fffffu) + c;
             TileJob j;
             j.p[1] = j.q[1] = nullptr;
@@ -934,7 +1012,7 @@ __global__ __launch_bounds__(NTHR) void k_ns_loop(PersistArgs args) {
                 j.K = pr.np;
                 j.ldq = pr.np;
                 j.ldo = pr.mp;
-                gemm_tile<kGram, 256, true>(j, lds, args.ca, args.cb, args.cc);
+                gemm_tile<kGram, 256, true>(j, lds, args.ca, args.cb, args.cc, claim);
             } else if (ph == 1) {
                 j.p[0] = j.q[0] = pr.a + blk * as;
                 j.out[0] = pr.b + blk * as;
@@ -942,7 +1020,7 @@ __global__ __launch_bounds__(NTHR) void k_ns_loop(PersistArgs args) {
                 j.K = pr.mp;
                 j.ldq = pr.mp;
                 j.ldo = pr.mp;
-                gemm_tile<kPoly, 256, true>(j, lds, args.ca, args.cb, args.cc);
+                gemm_tile<kPoly, 256, true>(j, lds, args.ca, args.cb, args.cc, claim);
             } else {
                 j.p[0] = pr.b + blk * as;
                 j.q[0] = pr.x[t & 1] + blk * xs;
@@ -953,13 +1031,10 @@ __global__ __launch_bounds__(NTHR) void k_ns_loop(PersistArgs args) {
                 j.K = pr.mp;
                 j.ldq = pr.np;
                 j.ldo = pr.np;
-                gemm_tile<kBx, 256, true>(j, lds, args.ca, args.cb, args.cc);
+                gemm_tile<kBx, 256, true>(j, lds, args.ca, args.cb, args.cc, claim);
             }
         }
-        if (wave == 0)
-            idx = __builtin_amdgcn_readfirstlane(__hip_atomic_fetch_add(args.sync + kSyncStride * q, one,
-                                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        // Every wave's stores complete before the barrier.
+        // Every wave's stores (and wave 0's claim) complete before the barrier.
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         prev_done = pr.done + kSyncStride * blk;
@@ -1045,9 +1120,9 @@ hipError_t run(const Plan* const* plans, GemmArgs a, hipStream_t s) {
         a.big_base = base;
         a.total = static_cast<uint32_t>(total);
         if (bt == 256) {
-            if constexpr (HAS_BIG) k_gemm<KIND, 256><<<dim3(a.total), dim3(NTHR), 0, s>>>(a);
+            if constexpr (HAS_BIG) k_gemm<KIND, 256><<<dim3(a.total), dim3(tile_threads<256>()), 0, s>>>(a);
         } else {
-            k_gemm<KIND, 128><<<dim3(a.total), dim3(NTHR), 0, s>>>(a);
+            k_gemm<KIND, 128><<<dim3(a.total), dim3(tile_threads<128>()), 0, s>>>(a);
         }
         return hipGetLastError();
     };
@@ -1446,7 +1521,7 @@ hipError_t launch_ns_loop(const NsLoopProblem* probs, int n, int ns_steps, float
     k_zero_sync<<<dim3((zmax + 255) / 256), dim3(256), 0, s>>>(z);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    k_ns_loop<<<dim3(cus), dim3(NTHR), 0, s>>>(a);
+    k_ns_loop<<<dim3(cus), dim3(tile_threads<256>()), 0, s>>>(a);
     return hipGetLastError();
 }
 
