@@ -12,19 +12,21 @@ namespace muon {
 namespace {
 
 // Estimated cycles of one 256-wide tile of product ph (0 Gram, 1 polynomial,
-// 2 B X): the measured loop time per 32-deep K step plus prologue and
-// epilogue (the symmetric products also store the mirror tile).
+// 2 B X): the measured loop time per 32-deep K step (the Gram's k-contiguous
+// operand rows cost more) plus prologue, epilogue (the symmetric products
+// also store the mirror tile, the polynomial reads A) and the barrier between
+// tiles.
 double item_cycles(int ph, const LoopDims& d) {
     const double K = ph == 0 ? d.np : d.mp;
-    return 1305.0 * (K / 32) + (ph == 0 ? 12000.0 : ph == 1 ? 14000.0 : 9000.0);
+    return (ph == 0 ? 1424.0 : 1216.0) * (K / 32) + (ph == 0 ? 12700.0 : ph == 1 ? 16300.0 : 7500.0);
 }
 
-// Measured cost of taking one queue item (the queue atomic's round trip under
-// load, the item load and the dependency poll), in cycles: with the counters
-// synchronised within one XCD, and at device scope (an L2 write-back and
-// invalidate per item).
-constexpr double kItemOverheadLocal = 11000.0;
-constexpr double kItemOverheadDevice = 24000.0;
+// Measured cost of one item boundary beyond a tile boundary (store drain,
+// counter release, item read and a satisfied dependency poll), in cycles:
+// with the counters synchronised within one XCD, and at device scope (an L2
+// write-back and invalidate per item).
+constexpr double kItemOverheadLocal = 2000.0;
+constexpr double kItemOverheadDevice = 15000.0;
 
 struct SimBlock {
     int prob;
@@ -39,12 +41,14 @@ struct Grouping {
 // List schedule of the blocks' items over `workers` workgroups.  An item is
 // a run of up to `grp` consecutive tiles of one product of one block.  A
 // free workgroup takes an item of the ready product with the highest
-// priority (Gram products first, then the earliest product, then the lowest
-// block); a block's next product becomes ready when every item of its
+// priority: with gram_first, Gram products first (they are the longest, and
+// every later product of the block waits for them), then the earliest
+// product, then the lowest block; otherwise the earliest product, then the
+// lowest block.  A block's next product becomes ready when every item of its
 // current one has finished.  Appends the items in the order they start
 // (which respects every dependency) and returns the estimated makespan.
 double list_schedule(const std::vector<SimBlock>& blocks, const std::vector<LoopDims>& dims, int steps, int workers,
-                     const Grouping& grp, double overhead, std::vector<ScheduleItem>* out) {
+                     const Grouping& grp, bool gram_first, double overhead, std::vector<ScheduleItem>* out) {
     const size_t nb = blocks.size();
     std::vector<int> k(nb, 0);
     std::vector<uint32_t> issued(nb, 0), running(nb, 0);   // tiles issued / items running
@@ -81,7 +85,7 @@ double list_schedule(const std::vector<SimBlock>& blocks, const std::vector<Loop
         if (issued[i] == tiles(i, k[i]) && running[i] == 0) {
             ++k[i];
             issued[i] = 0;
-            if (k[i] < 3 * steps) ready.insert({k[i] % 3 != 0, k[i], i});
+            if (k[i] < 3 * steps) ready.insert({gram_first && k[i] % 3 != 0, k[i], i});
         }
     }
     return t;
@@ -121,41 +125,47 @@ void schedule_items(const std::vector<LoopDims>& dims, const std::vector<int64_t
         for (auto& v : qb)
             std::sort(v.begin(), v.end(), [](const SimBlock& x, const SimBlock& y) { return x.g < y.g; });
     }
-    // Tiles per item and queue count by the estimated makespan (8 queues
-    // preferred within 5%: they keep a block's operands in one L2, and with
-    // local_ok they synchronise within the XCD).
+    // Tiles per item, priority rule and queue count by the estimated makespan
+    // (8 queues preferred within 5%: they keep a block's operands in one L2,
+    // and with local_ok they synchronise within the XCD).
     const double ov8 = local_ok ? kItemOverheadLocal : kItemOverheadDevice;
     Grouping best;
+    bool best_gram_first = true;
     bool use8 = false;
     double best_score = 0.0;
-    for (uint32_t gs = 1; gs <= 2; ++gs)
-        for (uint32_t gb = 1; gb <= 4; ++gb) {
-            const Grouping grp{gs, gb};
-            const double m1 = 1.05 * list_schedule(all, dims, steps, workers, grp, kItemOverheadDevice, nullptr);
-            if (best_score == 0.0 || m1 < best_score) {
-                best_score = m1;
-                best = grp;
-                use8 = false;
-            }
-            if (can8) {
-                double m8 = 0.0;
-                for (const auto& v : qb) m8 = std::max(m8, list_schedule(v, dims, steps, workers / 8, grp, ov8, nullptr));
-                if (m8 < best_score) {
-                    best_score = m8;
+    for (int gf = 1; gf >= 0; --gf)
+        for (uint32_t gs = 1; gs <= 2; ++gs)
+            for (uint32_t gb = 1; gb <= 4; ++gb) {
+                const Grouping grp{gs, gb};
+                const double m1 =
+                    1.05 * list_schedule(all, dims, steps, workers, grp, gf != 0, kItemOverheadDevice, nullptr);
+                if (best_score == 0.0 || m1 < best_score) {
+                    best_score = m1;
                     best = grp;
-                    use8 = true;
+                    best_gram_first = gf != 0;
+                    use8 = false;
+                }
+                if (can8) {
+                    double m8 = 0.0;
+                    for (const auto& v : qb)
+                        m8 = std::max(m8, list_schedule(v, dims, steps, workers / 8, grp, gf != 0, ov8, nullptr));
+                    if (m8 < best_score) {
+                        best_score = m8;
+                        best = grp;
+                        best_gram_first = gf != 0;
+                        use8 = true;
+                    }
                 }
             }
-        }
     items.clear();
     if (use8) {
         for (int q = 0; q < 8; ++q) {
             qbase[q] = uint32_t(items.size());
-            list_schedule(qb[q], dims, steps, workers / 8, best, ov8, &items);
+            list_schedule(qb[q], dims, steps, workers / 8, best, best_gram_first, ov8, &items);
         }
         nq = 8;
     } else {
-        list_schedule(all, dims, steps, workers, best, kItemOverheadDevice, &items);
+        list_schedule(all, dims, steps, workers, best, best_gram_first, kItemOverheadDevice, &items);
         for (int q = 0; q < 8; ++q) qbase[q] = 0;
         nq = 1;
     }

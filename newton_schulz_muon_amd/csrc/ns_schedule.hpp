@@ -32,8 +32,9 @@ struct ScheduleItem {
 // `workers` workgroups: either 8 queues (qbase[q]..qbase[q + 1], a block's
 // items all in one queue; preferred, and with local_ok modelled with the
 // cheaper XCD-local synchronisation) or 1 queue (qbase[0] = 0, qbase[1..8] =
-// items.size()).  The run lengths and the queue count are those with the
-// lowest simulated makespan.
+// items.size()).  The run lengths, the priority rule (Gram products first, or
+// the earliest product first) and the queue count are those with the lowest
+// simulated makespan.
 void schedule_items(const std::vector<LoopDims>& dims, const std::vector<int64_t>& nbs, int steps, int workers,
                     bool local_ok, std::vector<ScheduleItem>& items, uint32_t (&qbase)[9], int& nq);
 
