@@ -8,6 +8,7 @@ newton_schulz_muon_amd/libmuon_hip.so (replaced atomically).
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -32,8 +33,31 @@ COMMON_FLAGS = [
     "-I", INCLUDE, "-I", CSRC,
 ]
 # Per-source flags.  ns_gemm.hip: the atomic optimizer would turn the
-# persistent loop's queue claim into an atomic followed by an immediate wait.
-SOURCE_FLAGS = {"ns_gemm.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
+# persistent loop's queue claim into an atomic followed by an immediate wait;
+# its kernels' resource usage is reported so that the build can reject
+# scratch use (its hand-counted vmcnt waits assume no compiler-placed vector
+# memory operation, and scratch accesses are such operations).
+SOURCE_FLAGS = {"ns_gemm.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
+                                "-Rpass-analysis=kernel-resource-usage"]}
+NO_SCRATCH_SOURCES = ("ns_gemm.hip",)
+
+
+def _check_no_scratch(src: str, out: str) -> None:
+    """Raises if the resource remarks in `out` show a kernel using scratch."""
+    name = None
+    seen = 0
+    for line in out.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m:
+            seen += 1
+            if int(m.group(1)) != 0:
+                raise RuntimeError(f"{src}: kernel {name} uses {m.group(1)} bytes of scratch per lane")
+    if seen == 0:
+        raise RuntimeError(f"{src}: no kernel resource report in the compiler output")
 
 
 def hipcc() -> str:
@@ -62,6 +86,9 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
         cmds.append([cc, *COMMON_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         outs = list(ex.map(_run, cmds))
+    for src, out in zip(SOURCES, outs):
+        if src in NO_SCRATCH_SOURCES:
+            _check_no_scratch(src, out)
     if verbose:
         for o in outs:
             if o.strip():
