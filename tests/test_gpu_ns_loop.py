@@ -236,3 +236,36 @@ def test_forced_loop_falls_back(nsm, case):
     got, ref, counts = _both(nsm, run)
     assert "ns_loop" not in counts and counts.get("gram", (0, 0.0))[0] == 5, counts
     np.testing.assert_array_equal(got, ref)
+
+
+@pytest.mark.parametrize("sched", ["persistent", "per_product"])
+@pytest.mark.parametrize("shape", [(3, 512, 1024, 1), (2, 768, 3072, 4), (2, 300, 700, 1)])
+def test_timing_reports_nominal_flops(nsm, sched, shape):
+    # The nominal flops muon_timing_collect reports per kernel family add up,
+    # over the families, to 5 (4 m^2 n + 2 m^3) per NS block (m <= n, the
+    # unpadded block), whichever kernels ran: the persistent loop reports them
+    # all, the per-product launches 2 m^2 n (X X^T, B X) and 2 m^3 (A A) each
+    # per iteration.  300 x 700 blocks (padded sides not multiples of 256)
+    # always run per product.
+    import torch
+    b, r, c, v = shape
+    print(f"[timing flops] {sched} {shape}", flush=True)
+    x = workloads.to_device_bf16(workloads.gaussian_bits((b, r, c), seed=r + c + v))
+    nsm.muon_set_ns_schedule(sched)
+    nsm.muon_timing_collect()
+    nsm.muon_timing_enable(["ns_loop", "gram", "poly", "bx"])
+    try:
+        nsm.ns_orthogonalize_batched(x, view_blocks=v)
+        torch.cuda.synchronize()
+    finally:
+        nsm.muon_timing_enable([])
+        nsm.muon_set_ns_schedule("auto")
+    k = nsm.muon_timing_collect(with_flops=True)
+    m, n = min(r, c // v), max(r, c // v)
+    expect = b * v * 5 * (4.0 * m * m * n + 2.0 * m ** 3)
+    assert sum(f for _, _, f in k.values()) == pytest.approx(expect, rel=1e-12), k
+    loop = sched == "persistent" and r % 256 == 0 and (c // v) % 256 == 0
+    assert set(k) == ({"ns_loop"} if loop else {"gram", "poly", "bx"}), k
+    if not loop:
+        assert k["gram"][2] == pytest.approx(b * v * 5 * 2.0 * m * m * n, rel=1e-12)
+        assert k["poly"][2] == pytest.approx(b * v * 5 * 2.0 * m ** 3, rel=1e-12)
