@@ -18,9 +18,11 @@
 // their column panels, and poly and bx read every operand as a k-major panel
 // (k rows of 2 BT contiguous bytes: whole cache lines), like X in B X.
 //
-// Tiling: a 256-thread workgroup (2 x 2 waves) computes a BT x BT output tile
-// (BT = 256 or 128), each wave (BT/2)^2 as a grid of v_mfma_f32_32x32x16_bf16
-// accumulators.  K steps by 32 through a ring of four LDS stages, operand
+// Tiling: a workgroup computes a BT x BT output tile, BT = 256 with 8 waves of
+// 128 x 64 (two per SIMD) or BT = 128 with 4 waves of 64 x 64, each wave's
+// part a grid of v_mfma_f32_32x32x16_bf16 accumulators.  K steps by 32
+// through a ring of four LDS stages (256-wide tiles and every B X tile; the
+// 128-wide Gram and polynomial tiles use two stages of 64, below), operand
 // slices fetched straight into LDS with buffer_load_dwordx4 ... lds (no
 // staging registers).  Once per step, just before its last 16-deep
 // sub-slice, every wave waits for its own loads of the next slice and then at
@@ -35,8 +37,8 @@
 // global side of the DMA.
 //
 // Epilogue: 32 rows of a wave's accumulators at a time are staged in LDS as
-// fp32 and read back row by row, so global stores write 256- (or 128-) byte
-// row segments.  The mirror tile of a symmetric output is staged as bf16 and
+// fp32 and read back row by row, so global stores write 128-byte row segments
+// (a wave tile's 64 columns).  The mirror tile of a symmetric output is staged as bf16 and
 // read back with ds_read_b64_tr_b16, two reads handing each lane 8
 // consecutive rows of one column for a 16-byte store.
 //
