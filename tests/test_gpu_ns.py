@@ -232,19 +232,25 @@ def test_ns_parity_large_dense(nsm, group, index):
 
 
 @pytest.mark.timeout(300)
-def test_ns_parity_metric_batch(nsm):
+@pytest.mark.parametrize("schedule", ["per_product", "persistent"])
+def test_ns_parity_metric_batch(nsm, schedule):
     # The batch the throughput metric is quoted on, in the call the benchmark
     # times for it: 32 x 768x3072 bf16, N(0, 0.01^2), one ns_orthogonalize_batched
-    # over the whole batch (256-wide Gram round at K = 3072, 128-wide polynomial,
-    # four 256-wide B X rounds plus a quadrant tail); the first, a middle and the
-    # last block are checked against the fp64 oracle.
+    # over the whole batch, per product (256-wide Gram round at K = 3072,
+    # 128-wide polynomial, four 256-wide B X rounds plus a quadrant tail) and
+    # in the persistent loop the automatic schedule settles on for it; the
+    # first, a middle and the last block are checked against the fp64 oracle.
     import torch
     wl = workloads.get_workload("metric32")
     g = wl.groups[0]
-    print(f"[ns metric batch] {g.count}x{g.rows}x{g.cols}", flush=True)
+    print(f"[ns metric batch] {schedule} {g.count}x{g.rows}x{g.cols}", flush=True)
     x = workloads.grads_device(wl, g, 0, torch.device("cuda:0"))
-    out = nsm.ns_orthogonalize_batched(x)
-    torch.cuda.synchronize()
+    nsm.muon_set_ns_schedule(schedule)
+    try:
+        out = nsm.ns_orthogonalize_batched(x)
+        torch.cuda.synchronize()
+    finally:
+        nsm.muon_set_ns_schedule("auto")
     for i in (0, 17, g.count - 1):
         bits = torch_bf16_to_bits(x[i:i + 1])
         got = bits_to_f64(torch_bf16_to_bits(out[i:i + 1]))
