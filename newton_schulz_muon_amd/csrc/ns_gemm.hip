@@ -567,6 +567,12 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
                 if (u + 1 < U) {
                     frags(cur, u + 1, fa[c ^ 1], fb[c ^ 1]);
                 } else {
+                    // The sub-slice that waits, passes the barrier and issues
+                    // the next stage's DMA runs at raised wave priority, so
+                    // the SIMD's other wave does not delay the loads
+                    // (measured 0.7% faster; raising it around the MFMAs
+                    // instead was 3.7% slower).
+                    __builtin_amdgcn_s_setprio(1);
                     wait_dma_and_barrier<(NS - 3) * W>();
                     const int kn = kt + NS - 1;
                     load_frags<FA, FB, KMAJOR_A, KMAJOR_B, BT, BK, true, FA + FB>(
@@ -576,6 +582,7 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
                 mfma_block<FA, FB>(fa[c], fb[c], acc);
                 interleave<NM, NREAD, SPREAD>();
                 __builtin_amdgcn_sched_barrier(0);
+                if (u + 1 == U) __builtin_amdgcn_s_setprio(0);
             }
         }
     } else {
