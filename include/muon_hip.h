@@ -30,12 +30,18 @@
  *   - Matrices are row-major and contiguous: a batch is [batch, rows, cols].
  *   - bf16 data is passed as `void*` holding IEEE bfloat16 bit patterns.
  *   - All pointers are device pointers owned by the caller, 16-byte aligned.
- *     The library never allocates or frees device memory; scratch memory is
- *     the caller's `workspace` (size from muon_workspace_bytes, 256-byte
- *     aligned, contents undefined before and after a call).
- *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
- *     and the call returns without synchronising.  Faults inside kernels
- *     surface at the caller's next synchronisation.
+ *     The library never allocates or frees device memory and keeps no device
+ *     state between calls; scratch memory is the caller's `workspace` (size
+ *     from the *_workspace_bytes queries, 256-byte aligned).  Its first 256
+ *     bytes hold the status words of the last call that used it (see
+ *     muon_workspace_status); the rest is undefined before and after a call.
+ *     The only host state is a cache of persistent-loop queues per set of
+ *     block shapes, kept in pinned host memory and copied into the workspace
+ *     by every call that runs the loop.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every kernel and
+ *     copy of a call is enqueued on it and the call returns without
+ *     synchronising.  Faults inside kernels surface at the caller's next
+ *     synchronisation.
  *   - Arguments are validated before anything is enqueued: on any error the
  *     call has no side effects.  batch == 0 is a valid no-op.
  *   - Non-finite inputs propagate; they are not checked.
@@ -60,7 +66,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 5
+#define MUON_ABI_VERSION 6
 
 typedef enum muon_status {
     MUON_OK = 0,
@@ -243,6 +249,35 @@ muon_status adamw_step_multi(const muon_adam_tensor* tensors, int32_t count,
 muon_status muon_merge_small_dims(const int64_t* shape, int32_t ndim, int64_t threshold,
                                   int32_t target_ndim, int64_t* merged, int32_t* merged_ndim);
 
+/*
+ * Status of the last call that used `workspace` (any entry point that needed
+ * a workspace), copied into status_out[0..1] on `stream` after that call's
+ * work:
+ *   status_out[0]  number of NS blocks whose persistent-loop iterations did
+ *                  not all complete; their outputs (NS output, update_out,
+ *                  and the updated params) are NaN
+ *   status_out[1]  flags: 1 a dependency wait of the loop ran out of time (or
+ *                  was forced to, muon_debug_set_loop_fault), 2 blocks were
+ *                  left incomplete, 4 a workgroup ran on an XCD that serves no
+ *                  queue
+ * Both are 0 after a call that completed.  The persistent loop bounds each
+ * wait for a dependency (1 s) so that a stalled run ends; such a run never
+ * returns unmarked results.  The call's first kernel clears the words.
+ *   workspace   the workspace the call used (non-null, 256-byte aligned)
+ *   status_out  2 uint32: device memory or pinned host memory (the copy is
+ *               then asynchronous), or pageable host memory (the call then
+ *               waits for the stream)
+ */
+muon_status muon_workspace_status(const void* workspace, uint32_t* status_out, void* stream);
+
+/* Diagnostics for tests of the failure path (process-wide): mode 0 normal;
+ * mode 1 every persistent-loop launch sets its error word at its start, so
+ * every workgroup leaves at its first item; mode 2 every dependency wait that
+ * is not met at once counts as timed out.  Every kernel still exits normally;
+ * results are then NaN where blocks were left incomplete, as reported by
+ * muon_workspace_status.  Returns MUON_ERR_INVALID_ARG for any other mode. */
+muon_status muon_debug_set_loop_fault(int32_t mode);
+
 /* Schedule of the Newton-Schulz iterations of large blocks (process-wide).
  * Two schedules give bitwise the same results:
  *   per-product: each iteration launches the Gram, polynomial and B X
@@ -258,10 +293,12 @@ muon_status muon_merge_small_dims(const int64_t* shape, int32_t ndim, int64_t th
  *   (recorded on the call's stream) and, once those events have completed,
  *   later calls use the one with the lower best time;
  * mode 1: per-product always;  mode 2: persistent wherever it applies.
- * The persistent schedule keeps one device copy of the queue of each distinct
- * set (built with hipMalloc and hipMemcpy by the first call that needs it)
- * until the process ends; beyond 64 such sets (256 for the automatic
- * choice), calls with a new set use the per-product schedule.
+ * The persistent schedule's queue for each distinct set of shapes is built on
+ * the host by the first call that needs it and kept in pinned host memory
+ * (hipHostMalloc) until the process ends; each call copies it into its
+ * workspace on its stream.  Beyond 64 such sets (256 for the automatic
+ * choice), calls with a new set use the per-product schedule.  With 8 queues
+ * a workgroup serves the queue of the XCD it runs on.
  * Returns MUON_ERR_INVALID_ARG for any other mode. */
 muon_status muon_set_ns_schedule(int32_t mode);
 

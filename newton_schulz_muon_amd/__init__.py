@@ -14,6 +14,8 @@ Entry points (same names as the C ABI):
     muon_merge_small_dims(shape, threshold, target_ndim=2)
     muon_workspace_bytes(batch, rows, cols, view_blocks=1, cfg=None)
     muon_step_multi_workspace_bytes(matrices, cfg=None)
+    muon_workspace_status(workspace, stream=None), last_call_status(device=None)
+    muon_debug_set_loop_fault(mode)
     muon_ns_config_default(), muon_last_error(), muon_abi_version()
 """
 from __future__ import annotations
@@ -29,14 +31,16 @@ __all__ = [
     "muon_step_batched", "muon_step_multi", "muon_step_multi_workspace_bytes", "MuonMatrix",
     "adamw_step_multi", "MuonAdamTensor", "muon_merge_small_dims",
     "muon_timing_enable", "muon_timing_collect", "muon_last_error", "muon_abi_version", "make_config",
-    "muon_set_ns_schedule", "KERNEL_KINDS", "NS_SCHEDULES",
+    "muon_set_ns_schedule", "KERNEL_KINDS", "NS_SCHEDULES", "muon_workspace_status", "last_call_status",
+    "muon_debug_set_loop_fault",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmuon_hip.so")
 EXPORTED_SYMBOLS = ("muon_ns_config_default", "muon_workspace_bytes", "ns_orthogonalize_batched",
                     "muon_step_batched", "muon_step_multi_workspace_bytes", "muon_step_multi",
                     "adamw_step_multi", "muon_merge_small_dims", "muon_set_ns_schedule", "muon_timing_enable",
-                    "muon_timing_collect", "muon_last_error", "muon_abi_version")
+                    "muon_timing_collect", "muon_workspace_status", "muon_debug_set_loop_fault",
+                    "muon_last_error", "muon_abi_version")
 KERNEL_KINDS = ("prep", "norm_finalize", "gram", "poly", "bx", "finish", "small", "adamw", "ns_loop")
 NS_SCHEDULES = {"auto": 0, "per_product": 1, "persistent": 2}
 
@@ -113,6 +117,10 @@ def load_library():
         lib.muon_timing_collect.argtypes = [ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double),
                                             ctypes.POINTER(ctypes.c_double)]
         lib.muon_timing_collect.restype = ctypes.c_int
+        lib.muon_workspace_status.argtypes = [vp, vp, vp]
+        lib.muon_workspace_status.restype = ctypes.c_int
+        lib.muon_debug_set_loop_fault.argtypes = [i32]
+        lib.muon_debug_set_loop_fault.restype = ctypes.c_int
         lib.muon_last_error.argtypes = []
         lib.muon_last_error.restype = ctypes.c_char_p
         lib.muon_abi_version.argtypes = []
@@ -174,6 +182,38 @@ def muon_timing_collect(with_flops: bool = False) -> dict:
         return {k: (int(launches[i]), float(total[i]), float(flops[i]))
                 for i, k in enumerate(KERNEL_KINDS) if launches[i]}
     return {k: (int(launches[i]), float(total[i])) for i, k in enumerate(KERNEL_KINDS) if launches[i]}
+
+
+def muon_workspace_status(workspace, stream=None):
+    """(blocks left incomplete, error flags) of the last call that used the
+    workspace tensor (see the C ABI's muon_workspace_status); waits for it."""
+    import torch
+    with torch.cuda.device(workspace.device):
+        st = stream if stream is not None else torch.cuda.current_stream(workspace.device).cuda_stream
+        out = torch.empty(2, dtype=torch.int32, device=workspace.device)
+        _check(load_library().muon_workspace_status(workspace.data_ptr(), out.data_ptr(), st))
+        v = out.cpu().tolist()
+    return int(v[0]) & 0xffffffff, int(v[1]) & 0xffffffff
+
+
+def last_call_status(device=None):
+    """Status of the last call on `device` (default: current) and its current
+    stream that used the binding's cached workspace: (blocks left incomplete,
+    error flags); (0, 0) when no call there needed a workspace."""
+    import torch
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    with _ws_lock:
+        buf = _ws_cache.get((dev.index, stream))
+    if buf is None:
+        return 0, 0
+    return muon_workspace_status(buf, stream)
+
+
+def muon_debug_set_loop_fault(mode: int) -> None:
+    """Diagnostics: 0 normal, 1 every persistent-loop launch stops at its
+    first item, 2 every dependency wait not met at once times out."""
+    _check(load_library().muon_debug_set_loop_fault(int(mode)))
 
 
 def muon_last_error() -> str:

@@ -12,8 +12,14 @@
 //                     never materialised;
 //                     or, by the NS schedule (muon_set_ns_schedule), one
 //                     k_ns_loop launch running all iterations from a tile
-//                     queue (after a k_zero_sync of its counters)
+//                     queue (after k_loop_setup zeroes its counters and copies
+//                     the queue into the workspace from pinned host memory)
 //   k_finish          NS output, or the parameter update (+ optional O)
+// An NS-only call on wide blocks whose sides are tile multiples reads x in
+// place (k_prep only sums squares) and its last iteration writes out directly
+// (no k_finish).  The schedule and the queue are settled on the host before
+// the first launch; the library allocates no device memory, and every launch
+// and copy of a call goes to the caller's stream.
 // Small blocks (m <= 64, m n <= 8192) run the whole step in one k_small launch.
 // adamw_step_multi runs one k_adamw launch per 24 tensors.
 #include <algorithm>
@@ -238,6 +244,12 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
     return a0 < b0 + bn && b0 < a0 + an;
 }
 
+// Every workspace starts with a 256-byte header: word 0 counts the NS blocks
+// whose persistent-loop iteration did not complete in the last call that used
+// the workspace (their outputs are NaN), word 1 holds that call's error flags.
+// The call's first kernel clears both.  The plan regions follow the header.
+constexpr size_t kHeaderBytes = 256;
+
 struct Buffers {
     uint16_t* xh[2];
     uint16_t* xl[2];
@@ -266,47 +278,103 @@ Buffers carve(const Plan& p, void* ws) {
     return b;
 }
 
-// Runs finalize + the NS loop on an iterate already written by k_prep into
-// xh[0] (and xl[0]).  Returns the buffer holding the result.
-muon_status run_ns(const Plan& p, const muon_ns_config& cfg, const Buffers& b, hipStream_t s,
+// Queue region of the persistent loop for these block batches: bytes (0 when
+// the loop does not take them) and entries.
+size_t loop_items_bytes(const Plan* const* plans, int n, int ns_steps, uint64_t* cap = nullptr) {
+    const uint64_t c = ns_loop_items_cap(plans, n, ns_steps);
+    if (cap) *cap = c;
+    return align256(size_t(c) * 8);
+}
+
+// Layout of a single-batch call's workspace: header, plan regions, queue.
+struct BatchedLayout {
+    size_t items_off = 0;
+    uint64_t items_cap = 0;
+    size_t total = 0;
+};
+BatchedLayout batched_layout(const Plan& p, int ns_steps) {
+    BatchedLayout l;
+    if (p.small || p.nb == 0) return l;
+    const Plan* pp = &p;
+    const size_t ib = loop_items_bytes(&pp, 1, ns_steps, &l.items_cap);
+    l.items_off = kHeaderBytes + p.total;
+    l.total = kHeaderBytes + p.total + ib;
+    return l;
+}
+
+// The iterate a call starts from and the buffer its last iteration writes.
+// A wide block whose sides are already multiples of the tile (r = mp,
+// c / v = np) is laid out in the caller's bf16 buffer exactly as the
+// oriented padded iterate, so NS-only calls in FAST precision read x in
+// place (the prep pass then only sums squares) and the last iteration writes
+// the caller's output directly (no write-back pass).  With one iteration and
+// out == x the output would overwrite operands still being read, so that
+// case writes the workspace and copies back.
+struct NsEnds {
+    const uint16_t* x0;
+    uint16_t* xlast;
+    bool direct_in = false, direct_out = false;
+};
+NsEnds ns_ends(const Plan& p, const muon_ns_config& cfg, const Buffers& b, const void* x, void* out) {
+    NsEnds e;
+    e.x0 = b.xh[0];
+    e.xlast = b.xh[cfg.ns_steps & 1];
+    const bool exact = !p.small && !p.tall && p.precision == MUON_PRECISION_FAST && p.r == p.mp && p.c == p.np;
+    if (x != nullptr && exact && cfg.ns_steps >= 1) {
+        e.direct_in = true;
+        e.x0 = static_cast<const uint16_t*>(x);
+        if (out != nullptr && (cfg.ns_steps >= 2 || out != x)) {
+            e.direct_out = true;
+            e.xlast = static_cast<uint16_t*>(out);
+        }
+    }
+    return e;
+}
+
+// Runs finalize + the NS loop on an iterate already prepared by k_prep
+// (e.x0: in xh[0] and xl[0], or the caller's x in place) with the schedule
+// resolved before the call enqueued anything.  Returns the buffer index of
+// the result (when it is not e.xlast outside the workspace).
+muon_status run_ns(const Plan& p, const muon_ns_config& cfg, const Buffers& b, const NsEnds& ends,
+                   const NsChoice& ch, uint2* items, uint64_t items_cap, uint32_t* status, hipStream_t s,
                    int* final_idx) {
     hipError_t e = timed(MUON_KERNEL_NORM_FINALIZE, s, [&] { return launch_norm_finalize(p, b.part, b.scale, cfg.eps, s); });
     if (e != hipSuccess) return hip_fail(e, "k_norm_finalize launch");
-    const NsLoopProblem lp{&p, {b.xh[0], b.xh[1]}, b.a, b.bh, b.scale, b.sync};
-    const NsChoice ch = ns_schedule_begin(&lp, 1, cfg.ns_steps, s);
+    *final_idx = cfg.ns_steps & 1;
+    ns_schedule_start(ch, s);
     if (ch.persistent) {
-        e = timed(MUON_KERNEL_NS_LOOP, s, [&] { return launch_ns_loop(&lp, 1, cfg.ns_steps, cfg.a, cfg.b, cfg.c, s); },
-                  ns_flops(p, cfg.ns_steps));
+        const NsLoopProblem lp{&p, ends.x0, {b.xh[0], b.xh[1]}, ends.xlast, b.a, b.bh, b.scale, b.sync};
+        e = timed(MUON_KERNEL_NS_LOOP, s, [&] {
+            return launch_ns_loop(&lp, 1, cfg.ns_steps, cfg.a, cfg.b, cfg.c, ch, items, items_cap, status, s);
+        }, ns_flops(p, cfg.ns_steps));
         if (e != hipSuccess) return hip_fail(e, "k_ns_loop launch");
         ns_schedule_end(ch, s);
-        *final_idx = cfg.ns_steps & 1;
         return MUON_OK;
     }
-    int cur = 0;
     for (int it = 0; it < cfg.ns_steps; ++it) {
+        const int cur = it & 1;
         const float* sc = it == 0 ? b.scale : nullptr;
-        e = timed(MUON_KERNEL_GRAM, s, [&] { return launch_gram(p, b.xh[cur], b.a, sc, s); },
+        const uint16_t* xin = it == 0 ? ends.x0 : b.xh[cur];
+        uint16_t* xout = it + 1 == cfg.ns_steps ? ends.xlast : b.xh[cur ^ 1];
+        e = timed(MUON_KERNEL_GRAM, s, [&] { return launch_gram(p, xin, b.a, sc, s); },
                   product_flops(p, MUON_KERNEL_GRAM));
         if (e != hipSuccess) return hip_fail(e, "k_gemm<gram> launch");
         e = timed(MUON_KERNEL_POLY, s, [&] { return launch_poly(p, b.a, b.bh, b.bl, cfg.a, cfg.b, cfg.c, s); },
                   product_flops(p, MUON_KERNEL_POLY));
         if (e != hipSuccess) return hip_fail(e, "k_gemm<poly> launch");
         e = timed(MUON_KERNEL_BX, s, [&] {
-            return launch_bx(p, b.bh, b.bl, b.xh[cur], b.xl[cur], b.xh[cur ^ 1], b.xl[cur ^ 1], sc, s);
+            return launch_bx(p, b.bh, b.bl, xin, b.xl[cur], xout, b.xl[cur ^ 1], sc, s);
         }, product_flops(p, MUON_KERNEL_BX));
         if (e != hipSuccess) return hip_fail(e, "k_gemm<bx> launch");
-        cur ^= 1;
     }
     ns_schedule_end(ch, s);
-    *final_idx = cur;
     return MUON_OK;
 }
 
-muon_status common_checks(const Plan& p, void* ws, size_t ws_bytes) {
-    if (p.total > 0) {
-        if (ws == nullptr || ws_bytes < p.total)
-            return fail(MUON_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws ? ws_bytes : 0,
-                        p.total);
+muon_status common_checks(size_t need, void* ws, size_t ws_bytes) {
+    if (need > 0) {
+        if (ws == nullptr || ws_bytes < need)
+            return fail(MUON_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws ? ws_bytes : 0, need);
         if (!aligned(ws, 256)) return fail(MUON_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
     }
     return MUON_OK;
@@ -330,9 +398,20 @@ struct ShapeGroup {
 // slower than running them one after the other).
 constexpr size_t kWaveBudget = size_t(160) << 20;
 
+// One wave of a multi-matrix call: its groups' plan regions follow the
+// workspace header, then the persistent loop's queue for all of them.
+struct WavePlan {
+    int64_t mp = 0;
+    size_t bytes = 0;        // plan regions
+    int n = 0;               // groups
+    size_t items_off = 0;    // queue region (from the workspace start)
+    uint64_t items_cap = 0;  // its entries (0: the loop does not take this wave)
+};
+
 muon_status plan_multi(const muon_matrix* mats, int32_t count, const muon_ns_config& cfg,
-                       std::vector<ShapeGroup>& groups, size_t& total) {
+                       std::vector<ShapeGroup>& groups, std::vector<WavePlan>& waves, size_t& total) {
     groups.clear();
+    waves.clear();
     total = 0;
     if (count < 0) return fail(MUON_ERR_INVALID_ARG, "count %d < 0", count);
     if (count > 0 && mats == nullptr) return fail(MUON_ERR_INVALID_ARG, "matrices must be non-null");
@@ -362,8 +441,6 @@ muon_status plan_multi(const muon_matrix* mats, int32_t count, const muon_ns_con
     // products share launches by m) whose workspace stays within the budget
     // and which has room for it; else it opens a new wave.  Waves run one
     // after the other and reuse one workspace region.
-    struct WaveInfo { int64_t mp; size_t bytes; int n; };
-    std::vector<WaveInfo> waves;
     for (ShapeGroup& g : groups) {
         if (g.plan.small) continue;
         const size_t need = align256(g.plan.total);
@@ -373,14 +450,24 @@ muon_status plan_multi(const muon_matrix* mats, int32_t count, const muon_ns_con
                 w = int(k);
         if (w < 0) {
             w = int(waves.size());
-            waves.push_back({g.plan.mp, 0, 0});
+            waves.push_back(WavePlan());
+            waves.back().mp = g.plan.mp;
         }
         g.wave = w;
-        g.ws_off = waves[w].bytes;
+        g.ws_off = kHeaderBytes + waves[w].bytes;
         waves[w].bytes += need;
         waves[w].n += 1;
     }
-    for (const WaveInfo& w : waves) total = std::max(total, w.bytes);
+    for (size_t w = 0; w < waves.size(); ++w) {
+        const Plan* plans[kMaxGemmProblems];
+        int n = 0;
+        for (const ShapeGroup& g : groups)
+            if (!g.plan.small && g.wave == int(w)) plans[n++] = &g.plan;
+        WavePlan& wp = waves[w];
+        const size_t ib = loop_items_bytes(plans, n, cfg.ns_steps, &wp.items_cap);
+        wp.items_off = kHeaderBytes + wp.bytes;
+        total = std::max(total, kHeaderBytes + wp.bytes + ib);
+    }
     return MUON_OK;
 }
 
@@ -487,7 +574,7 @@ size_t muon_workspace_bytes(int64_t batch, int64_t rows, int64_t cols, int32_t v
     Plan p;
     if (make_plan(batch, rows, cols, view_blocks, cfg, p) != MUON_OK) return size_t(-1);
     if (batch == 0) return 0;
-    return p.total;
+    return batched_layout(p, cfg.ns_steps).total;
 }
 
 muon_status ns_orthogonalize_batched(const void* x, void* out, int64_t batch, int64_t rows,
@@ -506,9 +593,10 @@ muon_status ns_orthogonalize_batched(const void* x, void* out, int64_t batch, in
     const size_t bytes = size_t(batch) * size_t(rows) * size_t(cols) * 2;
     if (x != out && overlaps(x, bytes, out, bytes))
         return fail(MUON_ERR_INVALID_ARG, "out overlaps x without being x");
-    st = common_checks(p, workspace, workspace_bytes);
+    const BatchedLayout lay = batched_layout(p, cfg.ns_steps);
+    st = common_checks(lay.total, workspace, workspace_bytes);
     if (st != MUON_OK) return st;
-    if (p.total > 0 && (overlaps(workspace, p.total, x, bytes) || overlaps(workspace, p.total, out, bytes)))
+    if (lay.total > 0 && (overlaps(workspace, lay.total, x, bytes) || overlaps(workspace, lay.total, out, bytes)))
         return fail(MUON_ERR_INVALID_ARG, "workspace overlaps x or out");
     st = check_device();
     if (st != MUON_OK) return st;
@@ -527,14 +615,22 @@ muon_status ns_orthogonalize_batched(const void* x, void* out, int64_t batch, in
         const hipError_t e = timed(MUON_KERNEL_SMALL, s, [&] { return launch_small(p, ss, s); });
         return e == hipSuccess ? MUON_OK : hip_fail(e, "k_small launch");
     }
-    const Buffers b = carve(p, workspace);
+    char* ws = static_cast<char*>(workspace);
+    uint32_t* status = reinterpret_cast<uint32_t*>(ws);
+    const Buffers b = carve(p, ws + kHeaderBytes);
+    const NsEnds ends = ns_ends(p, cfg, b, x, out);
+    // The schedule (and on first use its queue) is settled before anything is enqueued.
+    const NsLoopProblem lp{&p, ends.x0, {b.xh[0], b.xh[1]}, ends.xlast, b.a, b.bh, b.scale, b.sync};
+    const NsChoice ch = ns_schedule_begin(&lp, 1, cfg.ns_steps, s);
     hipError_t e = timed(MUON_KERNEL_PREP, s, [&] {
-        return launch_prep(p, kPrepCast, static_cast<const uint16_t*>(x), nullptr, 0.f, b.xh[0], b.xl[0], b.part, s);
+        return launch_prep(p, kPrepCast, static_cast<const uint16_t*>(x), nullptr, 0.f,
+                           ends.direct_in ? nullptr : b.xh[0], b.xl[0], b.part, status, s);
     });
     if (e != hipSuccess) return hip_fail(e, "k_prep launch");
     int fin = 0;
-    st = run_ns(p, cfg, b, s, &fin);
+    st = run_ns(p, cfg, b, ends, ch, reinterpret_cast<uint2*>(ws + lay.items_off), lay.items_cap, status, s, &fin);
     if (st != MUON_OK) return st;
+    if (ends.direct_out) return MUON_OK;
     e = timed(MUON_KERNEL_FINISH, s, [&] {
         return launch_finish(p, b.xh[fin], b.xl[fin], cfg.ns_steps == 0 ? b.scale : nullptr, nullptr, 1.f, 0.f,
                              static_cast<uint16_t*>(out), s);
@@ -568,11 +664,12 @@ muon_status muon_step_batched(float* params, const void* grads, float* momentum_
         overlaps(grads, 2 * n, momentum_buf, 4 * n) || overlaps(update_out, 2 * n, params, 4 * n) ||
         overlaps(update_out, 2 * n, grads, 2 * n) || overlaps(update_out, 2 * n, momentum_buf, 4 * n))
         return fail(MUON_ERR_INVALID_ARG, "params, grads, momentum_buf and update_out must not overlap");
-    st = common_checks(p, workspace, workspace_bytes);
+    const BatchedLayout lay = batched_layout(p, cfg.ns_steps);
+    st = common_checks(lay.total, workspace, workspace_bytes);
     if (st != MUON_OK) return st;
-    if (p.total > 0 &&
-        (overlaps(workspace, p.total, params, 4 * n) || overlaps(workspace, p.total, grads, 2 * n) ||
-         overlaps(workspace, p.total, momentum_buf, 4 * n) || overlaps(workspace, p.total, update_out, 2 * n)))
+    if (lay.total > 0 &&
+        (overlaps(workspace, lay.total, params, 4 * n) || overlaps(workspace, lay.total, grads, 2 * n) ||
+         overlaps(workspace, lay.total, momentum_buf, 4 * n) || overlaps(workspace, lay.total, update_out, 2 * n)))
         return fail(MUON_ERR_INVALID_ARG, "workspace overlaps a data buffer");
     st = check_device();
     if (st != MUON_OK) return st;
@@ -601,14 +698,19 @@ muon_status muon_step_batched(float* params, const void* grads, float* momentum_
         const hipError_t e = timed(MUON_KERNEL_SMALL, s, [&] { return launch_small(p, ss, s); });
         return e == hipSuccess ? MUON_OK : hip_fail(e, "k_small launch");
     }
-    const Buffers b = carve(p, workspace);
+    char* ws = static_cast<char*>(workspace);
+    uint32_t* status = reinterpret_cast<uint32_t*>(ws);
+    const Buffers b = carve(p, ws + kHeaderBytes);
+    const NsEnds ends = ns_ends(p, cfg, b, nullptr, nullptr);
+    const NsLoopProblem lp{&p, ends.x0, {b.xh[0], b.xh[1]}, ends.xlast, b.a, b.bh, b.scale, b.sync};
+    const NsChoice ch = ns_schedule_begin(&lp, 1, cfg.ns_steps, s);
     hipError_t e = timed(MUON_KERNEL_PREP, s, [&] {
         return launch_prep(p, mode, static_cast<const uint16_t*>(grads), momentum_buf, momentum, b.xh[0], b.xl[0],
-                           b.part, s);
+                           b.part, status, s);
     });
     if (e != hipSuccess) return hip_fail(e, "k_prep launch");
     int fin = 0;
-    st = run_ns(p, cfg, b, s, &fin);
+    st = run_ns(p, cfg, b, ends, ch, reinterpret_cast<uint2*>(ws + lay.items_off), lay.items_cap, status, s, &fin);
     if (st != MUON_OK) return st;
     e = timed(MUON_KERNEL_FINISH, s, [&] {
         return launch_finish(p, b.xh[fin], b.xl[fin], cfg.ns_steps == 0 ? b.scale : nullptr, params, decay, step,
@@ -622,8 +724,9 @@ size_t muon_step_multi_workspace_bytes(const muon_matrix* mats, int32_t count, c
     const muon_ns_config cfg = cfg_in ? *cfg_in : default_config();
     if (validate_config(cfg) != MUON_OK) return size_t(-1);
     std::vector<ShapeGroup> groups;
+    std::vector<WavePlan> waves;
     size_t total = 0;
-    if (plan_multi(mats, count, cfg, groups, total) != MUON_OK) return size_t(-1);
+    if (plan_multi(mats, count, cfg, groups, waves, total) != MUON_OK) return size_t(-1);
     return total;
 }
 
@@ -638,22 +741,39 @@ muon_status muon_step_multi(const muon_matrix* mats, int32_t count, float lr, fl
         return fail(MUON_ERR_INVALID_ARG, "lr and weight_decay must be finite");
     if (!(momentum >= 0.f && momentum <= 1.f)) return fail(MUON_ERR_INVALID_ARG, "momentum must be in [0, 1]");
     std::vector<ShapeGroup> groups;
+    std::vector<WavePlan> waves;
     size_t total = 0;
-    st = plan_multi(mats, count, cfg, groups, total);
+    st = plan_multi(mats, count, cfg, groups, waves, total);
     if (st != MUON_OK) return st;
     if (count == 0) return MUON_OK;
     st = check_multi_buffers(mats, count, groups, total > 0 ? workspace : nullptr, total);
     if (st != MUON_OK) return st;
-    if (total > 0) {
-        if (workspace == nullptr || workspace_bytes < total)
-            return fail(MUON_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : 0,
-                        total);
-        if (!aligned(workspace, 256)) return fail(MUON_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
-    }
+    st = common_checks(total, workspace, workspace_bytes);
+    if (st != MUON_OK) return st;
     st = check_device();
     if (st != MUON_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const PrepMode mode = nesterov ? kPrepNesterov : kPrepPlain;
+    char* ws = static_cast<char*>(workspace);
+    uint32_t* status = total > 0 ? reinterpret_cast<uint32_t*>(ws) : nullptr;
+
+    // Every wave's buffers and NS schedule, settled before anything is enqueued.
+    const int nwaves = int(waves.size());
+    std::vector<Buffers> bufs(groups.size());
+    std::vector<std::vector<size_t>> wave_groups(nwaves);
+    std::vector<std::vector<NsLoopProblem>> wave_lps(nwaves);
+    std::vector<NsChoice> choices(nwaves);
+    for (size_t gi = 0; gi < groups.size(); ++gi) {
+        const ShapeGroup& g = groups[gi];
+        if (g.plan.small) continue;
+        bufs[gi] = carve(g.plan, ws + g.ws_off);
+        const Buffers& bb = bufs[gi];
+        wave_groups[g.wave].push_back(gi);
+        wave_lps[g.wave].push_back(
+            NsLoopProblem{&g.plan, bb.xh[0], {bb.xh[0], bb.xh[1]}, bb.xh[cfg.ns_steps & 1], bb.a, bb.bh, bb.scale, bb.sync});
+    }
+    for (int w = 0; w < nwaves; ++w)
+        choices[w] = ns_schedule_begin(wave_lps[w].data(), int(wave_lps[w].size()), cfg.ns_steps, s);
 
     // Small groups: the whole step in one launch per pointer table.
     for (const ShapeGroup& g : groups) {
@@ -677,28 +797,26 @@ muon_status muon_step_multi(const muon_matrix* mats, int32_t count, float lr, fl
     }
 
     // Large groups, one wave after the other.
-    int nwaves = 0;
-    for (const ShapeGroup& g : groups)
-        if (!g.plan.small) nwaves = std::max(nwaves, g.wave + 1);
-    std::vector<Buffers> bufs(groups.size());
+    bool first_prep = true;
+    const int fin = cfg.ns_steps & 1;
     for (int w = 0; w < nwaves; ++w) {
-        std::vector<size_t> wave;
-        for (size_t gi = 0; gi < groups.size(); ++gi)
-            if (!groups[gi].plan.small && groups[gi].wave == w) wave.push_back(gi);
+        const std::vector<size_t>& wave = wave_groups[w];
 
         // Momentum + cast to the iterate, per group in chunks of pointer tables.
         for (size_t gi : wave) {
             const ShapeGroup& g = groups[gi];
             const Plan& p = g.plan;
             const double aspect = std::sqrt(std::fmax(1.0, double(g.R) / double(g.C)));
-            bufs[gi] = carve(p, static_cast<char*>(workspace) + g.ws_off);
             for (size_t m0 = 0; m0 < g.mats.size(); m0 += kTabMax) {
                 const size_t cnt = std::min<size_t>(kTabMax, g.mats.size() - m0);
                 const MatTable tab = make_table(mats, g, m0, cnt, lr, weight_decay, aspect);
                 const Plan pc = chunk_plan(p, int64_t(cnt));
                 const Buffers bc = chunk_buffers(p, bufs[gi], int64_t(m0));
+                uint32_t* reset = first_prep ? status : nullptr;
+                first_prep = false;
                 const hipError_t e = timed(MUON_KERNEL_PREP, s, [&] {
-                    return launch_prep(pc, mode, nullptr, nullptr, momentum, bc.xh[0], bc.xl[0], bc.part, s, &tab);
+                    return launch_prep(pc, mode, nullptr, nullptr, momentum, bc.xh[0], bc.xl[0], bc.part, reset, s,
+                                       &tab);
                 });
                 if (e != hipSuccess) return hip_fail(e, "k_prep launch");
             }
@@ -726,24 +844,20 @@ muon_status muon_step_multi(const muon_matrix* mats, int32_t count, float lr, fl
         };
         const auto by_np = buckets([](const Plan& p) { return p.np; });
         const auto by_mp = buckets([](const Plan& p) { return p.mp; });
-        int cur = 0;
-        std::vector<NsLoopProblem> lps;
-        for (size_t gi : wave) {
-            const Buffers& b = bufs[gi];
-            lps.push_back(NsLoopProblem{&groups[gi].plan, {b.xh[0], b.xh[1]}, b.a, b.bh, b.scale, b.sync});
-        }
-        const NsChoice ch = ns_schedule_begin(lps.data(), int(lps.size()), cfg.ns_steps, s);
-        const bool loop = ch.persistent;
-        if (loop) {
+        const NsChoice& ch = choices[w];
+        ns_schedule_start(ch, s);
+        if (ch.persistent) {
             double fl = 0.0;
             for (size_t gi : wave) fl += ns_flops(groups[gi].plan, cfg.ns_steps);
+            const std::vector<NsLoopProblem>& lps = wave_lps[w];
             const hipError_t e = timed(MUON_KERNEL_NS_LOOP, s, [&] {
-                return launch_ns_loop(lps.data(), int(lps.size()), cfg.ns_steps, cfg.a, cfg.b, cfg.c, s);
+                return launch_ns_loop(lps.data(), int(lps.size()), cfg.ns_steps, cfg.a, cfg.b, cfg.c, ch,
+                                      reinterpret_cast<uint2*>(ws + waves[w].items_off), waves[w].items_cap, status, s);
             }, fl);
             if (e != hipSuccess) return hip_fail(e, "k_ns_loop launch");
-            cur = cfg.ns_steps & 1;
         }
-        for (int it = 0; it < (loop ? 0 : cfg.ns_steps); ++it) {
+        for (int it = 0; it < (ch.persistent ? 0 : cfg.ns_steps); ++it) {
+            const int cur = it & 1;
             for (const auto& bk : by_np) {
                 GramOp ops[kMaxGemmProblems];
                 double fl = 0.0;
@@ -781,7 +895,6 @@ muon_status muon_step_multi(const muon_matrix* mats, int32_t count, float lr, fl
                 const hipError_t e = timed(MUON_KERNEL_BX, s, [&] { return launch_bx(ops, int(bk.size()), s); }, fl);
                 if (e != hipSuccess) return hip_fail(e, "k_gemm<bx> launch");
             }
-            cur ^= 1;
         }
         ns_schedule_end(ch, s);
 
@@ -796,7 +909,7 @@ muon_status muon_step_multi(const muon_matrix* mats, int32_t count, float lr, fl
                 const Plan pc = chunk_plan(p, int64_t(cnt));
                 const Buffers bc = chunk_buffers(p, bufs[gi], int64_t(m0));
                 const hipError_t e = timed(MUON_KERNEL_FINISH, s, [&] {
-                    return launch_finish(pc, bc.xh[cur], bc.xl[cur], cfg.ns_steps == 0 ? bc.scale : nullptr, nullptr,
+                    return launch_finish(pc, bc.xh[fin], bc.xl[fin], cfg.ns_steps == 0 ? bc.scale : nullptr, nullptr,
                                          1.f, 0.f, nullptr, s, &tab);
                 });
                 if (e != hipSuccess) return hip_fail(e, "k_finish launch");
@@ -959,6 +1072,24 @@ muon_status muon_timing_collect(int64_t* launches, double* total_ms, double* nom
     }
     ts.recs.clear();
     return st;
+}
+
+muon_status muon_workspace_status(const void* workspace, uint32_t* status_out, void* stream) {
+    g_err.clear();
+    if (status_out == nullptr || workspace == nullptr)
+        return fail(MUON_ERR_INVALID_ARG, "workspace and status_out must be non-null");
+    if (!aligned(workspace, 256)) return fail(MUON_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
+    if (!aligned(status_out, 4)) return fail(MUON_ERR_ALIGNMENT, "status_out must be 4-byte aligned");
+    const hipError_t e = hipMemcpyAsync(status_out, workspace, 2 * sizeof(uint32_t), hipMemcpyDefault,
+                                        static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MUON_OK : hip_fail(e, "muon_workspace_status copy");
+}
+
+muon_status muon_debug_set_loop_fault(int32_t mode) {
+    g_err.clear();
+    if (mode < 0 || mode > 2) return fail(MUON_ERR_INVALID_ARG, "loop fault mode %d is not 0, 1 or 2", mode);
+    set_loop_fault(mode);
+    return MUON_OK;
 }
 
 const char* muon_last_error(void) { return g_err.c_str(); }

@@ -31,6 +31,8 @@ constexpr int T = kEwTile;
 
 struct PrepArgs {
     MatTable tab;          // per-matrix buffers (tab.n > 0) or strided (src, mom)
+    int64_t b0;            // first NS block of this launch (launches are split at kMaxGridY blocks)
+    uint32_t* status;      // when non-null: the call's status words, cleared by workgroup (0, 0)
     const uint16_t* src;   // stored bf16 (gradients or x), this launch's first block
     float* mom;            // stored fp32 momentum buffer
     uint16_t* dh;          // padded copy in stored orientation [rp][cp] (hi, lo)
@@ -152,10 +154,12 @@ __global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
     const int64_t blk = blockIdx.y;
     const int tile = blockIdx.x;
     const int si = tile / a.tiles_j, sj = tile % a.tiles_j;
+    if (a.status != nullptr && blk == 0 && tile == 0 && t < 2) a.status[t] = 0u;
     const uint16_t* src;
     float* mom = nullptr;
     if (a.tab.n > 0) {
-        const int64_t mi = blk / a.tab.v, sub = blk % a.tab.v;
+        const int64_t tb = a.b0 + blk;      // block index within the table
+        const int64_t mi = tb / a.tab.v, sub = tb % a.tab.v;
         src = a.tab.src[mi] + sub * a.be;
         if constexpr (MODE != kPrepCast) mom = a.tab.mom[mi] + sub * a.be;
     } else {
@@ -163,7 +167,7 @@ __global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
         if constexpr (MODE != kPrepCast) mom = a.mom + blk * a.be;
     }
     const int64_t pad = a.rp * a.cp;
-    uint16_t* dh = TALL ? nullptr : a.dh + blk * pad;
+    uint16_t* dh = (TALL || a.dh == nullptr) ? nullptr : a.dh + blk * pad;
     uint16_t* dl = (!TALL && SPLIT) ? a.dl + blk * pad : nullptr;
     uint16_t* th = TALL ? a.th + blk * pad : nullptr;
     uint16_t* tl = (TALL && SPLIT) ? a.tl + blk * pad : nullptr;
@@ -199,6 +203,7 @@ __global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
             }
         }
         if constexpr (!TALL) {
+            if (dh == nullptr) continue;         // sums of squares only: X0 is the caller's buffer
             const int64_t o = bi * a.cp + bj0;   // inside the padded block
             u32x4 w;
 #pragma unroll
@@ -259,6 +264,7 @@ __global__ __launch_bounds__(256) void k_norm_finalize(const float* part, float*
 
 struct FinArgs {
     MatTable tab;          // per-matrix buffers and scalars (tab.n > 0) or strided (P, out)
+    int64_t b0;            // first NS block of this launch (launches are split at kMaxGridY blocks)
     const uint16_t* xhi;   // oriented padded final iterate
     const uint16_t* xlo;
     const float* scale;    // [nb][2] or null
@@ -345,7 +351,8 @@ __global__ __launch_bounds__(256) void k_finish(FinArgs a) {
     uint16_t* out = nullptr;
     float decay = a.decay, step = a.step;
     if (a.tab.n > 0) {
-        const int64_t mi = blk / a.tab.v, sub = blk % a.tab.v;
+        const int64_t tb = a.b0 + blk;      // block index within the table
+        const int64_t mi = tb / a.tab.v, sub = tb % a.tab.v;
         if constexpr (UPDATE) P = a.tab.P[mi] + sub * a.be;
         out = a.tab.out[mi] ? a.tab.out[mi] + sub * a.be : nullptr;
         decay = a.tab.decay[mi];
@@ -439,6 +446,8 @@ hipError_t run_prep(const Plan& p, const PrepArgs& a, hipStream_t s) {
     const int64_t pad = p.mp * p.np;
     return for_block_chunks(p.nb, [&](int64_t b0, unsigned cnt) {
         PrepArgs c = a;
+        c.b0 = b0;
+        c.status = b0 == 0 ? a.status : nullptr;
         c.src = a.src ? a.src + b0 * be : nullptr;
         c.mom = a.mom ? a.mom + b0 * be : nullptr;
         c.dh = a.dh ? a.dh + b0 * pad : nullptr;
@@ -471,6 +480,7 @@ hipError_t run_finish(const Plan& p, const FinArgs& a, hipStream_t s) {
     const int64_t tiles = ti * a.tiles_j;
     return for_block_chunks(p.nb, [&](int64_t b0, unsigned cnt) {
         FinArgs c = a;
+        c.b0 = b0;
         c.xhi = a.xhi + b0 * pad;
         c.xlo = a.xlo ? a.xlo + b0 * pad : nullptr;
         c.scale = a.scale ? a.scale + 2 * b0 : nullptr;
@@ -495,8 +505,12 @@ hipError_t finish_mode(const Plan& p, const FinArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_prep(const Plan& p, PrepMode mode, const uint16_t* src, float* mom, float mu,
-                       uint16_t* x_hi, uint16_t* x_lo, float* partials, hipStream_t s, const MatTable* tab) {
+                       uint16_t* x_hi, uint16_t* x_lo, float* partials, uint32_t* status, hipStream_t s,
+                       const MatTable* tab) {
+    if (x_hi == nullptr && (p.tall || x_lo != nullptr)) return hipErrorInvalidValue;
     PrepArgs a;
+    a.b0 = 0;
+    a.status = status;
     if (tab != nullptr) {
         if (tab->n < 1 || tab->n > kTabMax || tab->v != p.v || p.nb != int64_t(tab->n) * tab->v)
             return hipErrorInvalidValue;
@@ -538,6 +552,7 @@ hipError_t launch_finish(const Plan& p, const uint16_t* x_hi, const uint16_t* x_
                          const float* scale, float* params, float decay, float step,
                          uint16_t* out, hipStream_t s, const MatTable* tab) {
     FinArgs a;
+    a.b0 = 0;
     if (tab != nullptr) {
         if (tab->n < 1 || tab->n > kTabMax || tab->v != p.v || p.nb != int64_t(tab->n) * tab->v)
             return hipErrorInvalidValue;

@@ -92,9 +92,11 @@ enum PrepMode { kPrepCast = 0, kPrepNesterov = 1, kPrepPlain = 2 };
 
 // Reads the stored batch (bf16 x or gradients), updates the momentum buffer
 // (momentum modes), writes the oriented padded iterate X0 (bf16 hi plane; lo
-// plane too when x_lo != nullptr) and per-tile sums of squares.
+// plane too when x_lo != nullptr; nothing when x_hi is null, for a wide block
+// read in place) and per-tile sums of squares.  When status is non-null the
+// launch also clears the call's two status words.
 hipError_t launch_prep(const Plan& p, PrepMode mode, const uint16_t* src, float* mom, float mu,
-                       uint16_t* x_hi, uint16_t* x_lo, float* partials, hipStream_t s,
+                       uint16_t* x_hi, uint16_t* x_lo, float* partials, uint32_t* status, hipStream_t s,
                        const MatTable* tab = nullptr);
 // scales[2k] = 1/(sqrt(sum_k) + eps), scales[2k+1] = scales[2k]^2.
 hipError_t launch_norm_finalize(const Plan& p, const float* partials, float* scales, float eps,
@@ -152,36 +154,57 @@ hipError_t launch_bx(const Plan& p, const uint16_t* b_hi, const uint16_t* b_lo, 
 // of up to kMaxNsLoopProblems block batches in one launch of one workgroup
 // per CU, which take tiles from a precomputed queue and wait on per-block
 // completion counters.  Each problem brings a sync region of
-// ns_loop_sync_bytes(nb) (the launcher zeroes it first).  Iteration t reads
-// x[t % 2] and writes x[(t + 1) % 2]; the first one applies `scale` as the
-// per-product launches do.
+// ns_loop_sync_bytes(nb) (the launch zeroes it first).  Iteration 0 reads x0,
+// iteration t > 0 reads x[t % 2]; every iteration but the last writes
+// x[(t + 1) % 2] and the last writes xlast; the first one applies `scale` as
+// the per-product launches do.
 struct NsLoopProblem {
     const Plan* plan;
+    const uint16_t* x0;
     uint16_t* x[2];
+    uint16_t* xlast;
     uint16_t* a;
     uint16_t* b;
     const float* scale;
     uint32_t* sync;
 };
 constexpr int kMaxNsLoopProblems = 8;
-// Whether launch_ns_loop takes these problems: FAST precision, both padded
-// sides multiples of 256, 1 <= ns_steps, at most kMaxNsLoopProblems.
+// Queue entries the loop needs in the workspace for these block batches and
+// step count: 0 when the loop does not take them (it needs FAST precision,
+// both padded sides multiples of 256, 1 <= ns_steps <= 255, at most
+// kMaxNsLoopProblems batches and at most 2^22 entries).
+uint64_t ns_loop_items_cap(const Plan* const* plans, int n, int ns_steps);
 bool ns_loop_eligible(const NsLoopProblem* probs, int n, int ns_steps);
 // Which schedule runs the NS iterations of these problems on stream s (see
-// set_ns_schedule); the caller launches it between begin and end.
+// set_ns_schedule), resolved before anything of the call is enqueued (it may
+// build and cache the queues on the host); the caller launches it between
+// begin and end.
 struct NsChoice {
     bool persistent = false;
     int trial = -1;                            // timed trial call of the automatic choice
     const std::vector<int64_t>* key = nullptr;
+    const void* sched = nullptr;               // the loop's queues (host)
+    int cus = 0;                               // workgroups of the loop launch
 };
 NsChoice ns_schedule_begin(const NsLoopProblem* probs, int n, int ns_steps, hipStream_t s);
+// Marks where the call's NS iterations start and end on stream s (the timed
+// trials of the automatic choice record events there).
+void ns_schedule_start(const NsChoice& c, hipStream_t s);
 void ns_schedule_end(const NsChoice& c, hipStream_t s);
 size_t ns_loop_sync_bytes(int64_t total_blocks);
+// Enqueues the loop's setup (counters zeroed, queue copied from the pinned
+// host copy into items_ws, which holds items_cap entries) and the loop.  An
+// interrupted run NaN-fills the final iterates of the blocks it left
+// incomplete and adds their count and its error flags to status[0], status[1].
 hipError_t launch_ns_loop(const NsLoopProblem* probs, int n, int ns_steps, float ca, float cb, float cc,
+                          const NsChoice& choice, uint2* items_ws, uint64_t items_cap, uint32_t* status,
                           hipStream_t s);
 // 0: automatic per set of shapes (default); 1: per-product launches only;
 // 2: the persistent loop wherever eligible.
 void set_ns_schedule(int mode);
+// Diagnostics: 0 normal; 1 every loop launch sets its error word at its start;
+// 2 every dependency wait of the loop that is not met at once times out.
+void set_loop_fault(int mode);
 
 // AdamW for the non-matrix parameters (adamw.hip): one launch over up to
 // kAdamTab tensors.  decay = 1 - lr lr_mul wd wd_mul (exactly 1 when wd = 0),

@@ -54,6 +54,7 @@
 // row-major tile, lane i gets rows rb .. rb + 3 of column cb + i.
 #include <algorithm>
 #include <atomic>
+#include <cstring>
 #include <functional>
 #include <map>
 #include <mutex>
@@ -833,44 +834,115 @@ __global__ __launch_bounds__(tile_threads<BT>()) void k_gemm(GemmArgs args) {
 // reaches the item's count), computes the tiles and adds their number to
 // done[block].  Items are listed in an order in which each depends only on
 // items listed before it in the same queue, and an item is taken only by a
-// running workgroup, so the lowest unfinished item can always proceed.  A wait
-// longer than kSpinTicks sets the error word and every workgroup leaves.
+// running workgroup, so the lowest unfinished item can always proceed.
+//
+// Failure is loud.  A wait longer than spin_ticks sets the error word, and a
+// workgroup that finds the error word set takes no further item.  The last
+// workgroup to leave checks every block's counter: the final iterate of each
+// block that did not complete all of its tiles is overwritten with NaN, and
+// the number of such blocks and the error flags are added to the call's
+// status words (which the caller can read back), so no result of an
+// interrupted run passes for a valid one.
 struct PersistProblem {
-    const uint16_t* x[2];
+    const uint16_t* x0;       // iteration 0's input (oriented, padded)
+    uint16_t* xb[2];          // ping-pong iterates: iteration t > 0 reads xb[t % 2] and
+    uint16_t* xlast;          // writes xb[(t + 1) % 2]; the last iteration writes xlast
     uint16_t* a;
     uint16_t* b;
     const float* scale;
     uint32_t* done;           // [nb] completion counters, kSyncStride words apart
     int32_t mp, np;
     uint32_t first_blk;       // global index of its first block
+    uint32_t nb;              // blocks
     uint32_t nsym, nbx;       // tiles per block: symmetric products, B X
 };
 
 struct PersistArgs {
     PersistProblem pr[kMaxNsLoopProblems];
     int n;
-    int nq;                   // queues: 1, or 8 (workgroup w serves queue w % 8)
+    int nq;                   // queues: 1, or 8 (a workgroup serves the queue of the XCD it runs on)
+    int steps;                // iterations
+    int inject;               // diagnostics: every workgroup sets the error word at its start
     const uint2* items;       // x = global block | (tiles - 1) << 28, y = first tile | product << 22 | iteration << 24
     uint32_t qbase[9];        // queue q is items[qbase[q], qbase[q + 1])
-    uint32_t* sync;           // queue heads 0..7, then the error word and an XCD mismatch flag
-    int local_sync;           // 8 queues served by the workgroups of one XCD each
+    uint32_t* sync;           // queue heads 0..7, then the error word and the exit counter
+    uint32_t* status;         // the call's status words: [0] blocks left incomplete, [1] error flags
+    uint64_t spin_ticks;      // longest dependency wait (ticks of the 100 MHz real-time counter)
     float ca, cb, cc;
 };
 
 // Counters of the loop each sit on their own 128-byte line (kSyncStride
-// words apart): queue heads 0..7, then the error word, then per block.
+// words apart): queue heads 0..7, then the error word (word 0 of line 8) and
+// the exit counter (word 1 of line 8), then one line per block.
 constexpr uint32_t kSyncStride = 32;
-constexpr uint64_t kSpinTicks = 100000000;   // 1 s of the 100 MHz real-time counter
+constexpr uint32_t kSyncLines = 9;
 constexpr uint32_t kItemEnd = 0xffffffffu;
 constexpr uint32_t kBlockMask = 0x0fffffffu;   // item.x: block; the top 4 bits: tiles in the item - 1
 // Items of the workgroup's queue held in LDS (a window from the queue index
 // win0; wave 0 reloads it when an index passes its end).
 constexpr uint32_t kLdsItems = 2048;
 
+__device__ __forceinline__ uint32_t hw_xcc_id() {
+    return __builtin_amdgcn_s_getreg((20) | (0 << 6) | (3 << 11)) & 15u;   // HW_REG_XCC_ID
+}
+
+// Run by the last workgroup to leave, with all its threads, once every other
+// workgroup has left (so nothing else writes the iterates any more): each
+// block whose counter shows fewer than all of its tiles gets NaN in its final
+// iterate; the count and the error word go to the call's status words.
+__device__ void ns_loop_verify(const PersistArgs& args, uint32_t* err, char* lds) {
+    uint32_t* const s_bad = reinterpret_cast<uint32_t*>(lds);          // incomplete blocks of one round
+    uint32_t* const s_cnt = reinterpret_cast<uint32_t*>(lds) + 512;    // their count
+    const uint32_t tid = threadIdx.x;
+    const PersistProblem& lastp = args.pr[args.n - 1];
+    const uint32_t total = lastp.first_blk + lastp.nb;
+    // Every other workgroup's completion counts were released by its exit
+    // increment, which this workgroup's exit increment acquired.
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    uint32_t bad = 0;
+    for (uint32_t base = 0; base < total; base += 512) {
+        if (tid == 0) *s_cnt = 0;
+        __syncthreads();
+        const uint32_t g = base + tid;
+        if (g < total) {
+            int pi = 0;
+            for (int i = 1; i < args.n; ++i)
+                if (g >= args.pr[i].first_blk) pi = i;
+            const PersistProblem& pr = args.pr[pi];
+            const uint32_t expect = uint32_t(args.steps) * (2 * pr.nsym + pr.nbx);
+            const uint32_t d =
+                __hip_atomic_load(pr.done + kSyncStride * (g - pr.first_blk), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (d != expect) s_bad[atomicAdd(s_cnt, 1u)] = g;
+        }
+        __syncthreads();
+        const uint32_t nbad = *s_cnt;
+        for (uint32_t k = 0; k < nbad; ++k) {
+            const uint32_t g2 = s_bad[k];
+            int pi = 0;
+            for (int i = 1; i < args.n; ++i)
+                if (g2 >= args.pr[i].first_blk) pi = i;
+            const PersistProblem& pr = args.pr[pi];
+            const int64_t elems = int64_t(pr.mp) * pr.np;
+            u32x4* dst = reinterpret_cast<u32x4*>(pr.xlast + int64_t(g2 - pr.first_blk) * elems);
+            const u32x4 nan4 = {0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};   // bf16 quiet NaN
+            for (int64_t e = tid; e < elems / 8; e += blockDim.x) dst[e] = nan4;
+        }
+        bad += nbad;
+        __syncthreads();
+    }
+    if (tid == 0) {
+        const uint32_t e = __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (bad) __hip_atomic_fetch_add(args.status, bad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (bad || e)
+            __hip_atomic_fetch_or(args.status + 1, e | (bad ? 2u : 0u), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
 __global__ __launch_bounds__(tile_threads<256>()) void k_ns_loop(PersistArgs args) {
     constexpr int LDS = tile_lds_bytes<kBx, 256>();
     static_assert(tile_lds_bytes<kGram, 256>() <= LDS && tile_lds_bytes<kPoly, 256>() <= LDS, "LDS size");
     static_assert(LDS + 8 * kLdsItems + 8 <= 160 * 1024, "LDS of a gfx950 workgroup");
+    static_assert(LDS >= 513 * 4, "verification list fits in the tile LDS");
     __shared__ __attribute__((aligned(16))) char lds[LDS];
     __shared__ uint2 s_items[kLdsItems];
     __shared__ uint2 s_item;
@@ -885,16 +957,20 @@ __global__ __launch_bounds__(tile_threads<256>()) void k_ns_loop(PersistArgs arg
     // and broadcast of the result, which would stall the claim below.
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
     const bool lane0 = (threadIdx.x & 63) == 0;
-    // With 8 queues, workgroup w serves queue w % 8, which gives every queue
-    // the same number of workgroups; the launcher enables local_sync only
-    // where workgroup w runs on XCD w % 8 (checked once per device), so a
-    // queue's tiles, and hence its blocks' buffers, stay in one XCD's L2.
-    const uint32_t xcc = __builtin_amdgcn_s_getreg((20) | (0 << 6) | (3 << 11)) & 7u;   // HW_REG_XCC_ID
-    const int q = args.nq == 8 ? static_cast<int>(blockIdx.x & 7) : 0;
-    const uint32_t qb = args.qbase[q], qlen = args.qbase[q + 1] - qb;
     uint32_t* const err = args.sync + kSyncStride * 8;
-    if (args.local_sync && wave == 0 && xcc != (blockIdx.x & 7) && lane0)
-        __hip_atomic_fetch_or(err + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t* const exits = err + 1;
+    // With 8 queues a workgroup serves the queue of the XCD it runs on, so
+    // that a queue's tiles, and hence its blocks' buffers, stay in one XCD's
+    // L2 whatever the placement of workgroups on XCDs; the synchronisation
+    // below relies on that.  A workgroup on an XCD beyond the eighth (none on
+    // this part) serves no queue and stops the launch.
+    const uint32_t xcc = __builtin_amdgcn_readfirstlane(hw_xcc_id());
+    const bool serve = args.nq != 8 || xcc < 8;
+    const int q = args.nq == 8 ? static_cast<int>(xcc & 7u) : 0;
+    const bool local_sync = args.nq == 8;
+    if (wave == 0 && lane0 && (args.inject || !serve))
+        __hip_atomic_fetch_or(err, serve ? 1u : 4u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t qb = args.qbase[q], qlen = serve ? args.qbase[q + 1] - qb : 0u;
     uint32_t* prev_done = nullptr;    // counter of the item this workgroup finished last ...
     uint32_t prev_tiles = 0;          // ... and its tile count
     // Lowest NS iteration among the items this workgroup has read operands
@@ -918,14 +994,15 @@ __global__ __launch_bounds__(tile_threads<256>()) void k_ns_loop(PersistArgs arg
     }
     uint32_t* const head = args.sync + kSyncStride * q;
     uint32_t idx_v = 0;      // the claimed index (lane 0 of wave 0), read once the stores have drained
-    if (wave == 0 && lane0) idx_v = __hip_atomic_fetch_add(head, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (wave == 0 && lane0 && serve)
+        idx_v = __hip_atomic_fetch_add(head, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     for (;;) {
         if (wave == 0) {
             // The previous tile's stores completed before the barrier that
             // ended it; the add publishes them.
             if (prev_done && lane0) {
-                if (args.local_sync)
+                if (local_sync)
                     __hip_atomic_fetch_add(prev_done, prev_tiles, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 else
                     __hip_atomic_fetch_add(prev_done, prev_tiles, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
@@ -951,13 +1028,20 @@ __global__ __launch_bounds__(tile_threads<256>()) void k_ns_loop(PersistArgs arg
                 const uint32_t need = t * (2 * pr.nsym + pr.nbx) + (ph >= 1 ? pr.nsym : 0u) + (ph >= 2 ? pr.nsym : 0u);
                 uint32_t* const done = pr.done + kSyncStride * (g - pr.first_blk);
                 const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+                // The error word is read with every poll, so a set word stops
+                // the workgroup at its next item even when that item's
+                // dependencies are met.
                 for (;;) {
                     const uint32_t d = __builtin_amdgcn_readfirstlane(
                         __hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-                    if (d >= need) break;
                     const uint32_t e = __builtin_amdgcn_readfirstlane(
                         __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-                    if (e != 0u || __builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) {
+                    if (e != 0u) {
+                        it.x = kItemEnd;
+                        break;
+                    }
+                    if (d >= need) break;
+                    if (__builtin_amdgcn_s_memrealtime() - t0 > args.spin_ticks) {
                         if (lane0) __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                         it.x = kItemEnd;
                         break;
@@ -970,7 +1054,7 @@ __global__ __launch_bounds__(tile_threads<256>()) void k_ns_loop(PersistArgs arg
                 // invalidate drops its lines (a workgroup-scope one does not,
                 // all of a workgroup's waves sharing one CU).  At device
                 // scope the L2 can be stale too: always invalidate.
-                if (!args.local_sync || t > t_low) {
+                if (!local_sync || t > t_low) {
                     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
                     t_low = t;
                 } else {
@@ -992,6 +1076,7 @@ __global__ __launch_bounds__(tile_threads<256>()) void k_ns_loop(PersistArgs arg
         const int64_t blk = g - pr.first_blk;
         const int t = static_cast<int>(ity >> 24), ph = static_cast<int>((ity >> 22) & 3u);
         const int64_t xs = int64_t(pr.mp) * pr.np, as = int64_t(pr.mp) * pr.mp;
+        const uint16_t* const xin = (t == 0 ? pr.x0 : pr.xb[t & 1]) + blk * xs;
         for (int c = 0; c < ntiles; ++c) {
             if (c > 0) __syncthreads();    // the previous tile's epilogue is done with LDS
             const bool last = c + 1 == ntiles;
@@ -1014,7 +1099,7 @@ __global__ __launch_bounds__(tile_threads<256>()) void k_ns_loop(PersistArgs arg
                 j.tj = id / (pr.mp / 256);
             }
             if (ph == 0) {
-                j.p[0] = j.q[0] = pr.x[t & 1] + blk * xs;
+                j.p[0] = j.q[0] = xin;
                 j.out[0] = pr.a + blk * as;
                 if (t == 0 && pr.scale) j.scale = pr.scale + 2 * blk + 1;
                 j.p_bytes = j.q_bytes = static_cast<uint32_t>(xs * 2);
@@ -1032,8 +1117,8 @@ __global__ __launch_bounds__(tile_threads<256>()) void k_ns_loop(PersistArgs arg
                 gemm_tile<kPoly, 256, true>(j, lds, args.ca, args.cb, args.cc, claim);
             } else {
                 j.p[0] = pr.b + blk * as;
-                j.q[0] = pr.x[t & 1] + blk * xs;
-                j.out[0] = const_cast<uint16_t*>(pr.x[(t + 1) & 1]) + blk * xs;
+                j.q[0] = xin;
+                j.out[0] = (t + 1 == args.steps ? pr.xlast : pr.xb[(t + 1) & 1]) + blk * xs;
                 if (t == 0 && pr.scale) j.scale = pr.scale + 2 * blk;
                 j.p_bytes = static_cast<uint32_t>(as * 2);
                 j.q_bytes = static_cast<uint32_t>(xs * 2);
@@ -1049,23 +1134,37 @@ __global__ __launch_bounds__(tile_threads<256>()) void k_ns_loop(PersistArgs arg
         prev_done = pr.done + kSyncStride * blk;
         prev_tiles = static_cast<uint32_t>(ntiles);
     }
+    // Leave: the exit count tells the last workgroup out, which verifies the
+    // run.  Every completion of this workgroup was published above, before
+    // the item it found at the end.
+    __shared__ uint32_t s_last;
+    if (wave == 0) {
+        uint32_t old = 0;
+        if (lane0) old = __hip_atomic_fetch_add(exits, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        old = __builtin_amdgcn_readfirstlane(old);
+        s_last = old + 1 == gridDim.x ? 1u : 0u;
+    }
+    __syncthreads();
+    if (s_last) ns_loop_verify(args, err, lds);
 }
 
-// Zeroes the sync regions of a loop launch: region r is [0, n[r]) of p[r].
-struct ZeroArgs {
+// Prepares a loop launch: zeroes the counter regions (region r is [0, n[r])
+// of p[r]) and copies the item list into the workspace from the library's
+// pinned host copy.
+struct SetupArgs {
     uint32_t* p[kMaxNsLoopProblems];
     uint32_t n[kMaxNsLoopProblems];
     int count;
+    const uint2* src;         // host (pinned, device-readable)
+    uint2* dst;               // workspace
+    uint32_t items;
 };
-// Records the XCD of each workgroup (HW_REG_XCC_ID).
-__global__ void k_xcc_probe(uint32_t* out) {
-    if (threadIdx.x == 0) out[blockIdx.x] = __builtin_amdgcn_s_getreg((20) | (0 << 6) | (3 << 11)) & 15u;
-}
 
-__global__ void k_zero_sync(ZeroArgs z) {
+__global__ void k_loop_setup(SetupArgs z) {
     const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
     for (int r = 0; r < z.count; ++r)
         if (i < z.n[r]) z.p[r][i] = 0u;
+    if (i < z.items) z.dst[i] = z.src[i];
 }
 
 // Every kernel instantiation is named explicitly: with implicit instantiation
@@ -1080,7 +1179,14 @@ template __global__ void k_gemm<kBx, 128>(GemmArgs);
 template __global__ void k_gemm<kBx, 256>(GemmArgs);
 template __global__ void k_gemm<kBxSplit, 128>(GemmArgs);
 
-constexpr int64_t kCUs = 256;
+// Compute units of the current device (the rounds of the cost model below).
+int64_t device_cus() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        return 256;
+    return cus;
+}
 
 // Estimated cycles of one round of workgroups at reduction length K, from the
 // measured per-K-step loop time and the prologue + epilogue of each tiling:
@@ -1136,6 +1242,7 @@ hipError_t run(const Plan* const* plans, GemmArgs a, hipStream_t s) {
         return hipGetLastError();
     };
     const int64_t K = a.pr[0].K;
+    const int64_t kCUs = device_cus();
     bool big_ok = HAS_BIG;
     for (int i = 0; i < a.n; ++i) {
         if (a.pr[i].K != K) return hipErrorInvalidValue;
@@ -1268,70 +1375,46 @@ hipError_t launch_bx(const Plan& p, const uint16_t* b_hi, const uint16_t* b_lo, 
 namespace {
 
 std::atomic<int> g_ns_mode{0};
+std::atomic<int> g_loop_fault{0};
 
+// One distinct set of block shapes: its queues, built once by the host list
+// scheduler and kept in pinned host memory (never device memory), from which
+// every launch copies them into the caller's workspace on the caller's stream.
 struct Schedule {
-    uint2* items = nullptr;   // device
+    uint2* host_items = nullptr;   // hipHostMalloc, device-readable, kept until the process ends
+    uint32_t count = 0;
     uint32_t qbase[9] = {};
     int nq = 1;
-    bool local_sync = false;
 };
-
-// Whether workgroup w of a launch of `cus` workgroups runs on XCD w % 8 on
-// this device (8 XCDs, as the 8-queue schedule's L2 locality and its
-// XCD-local synchronisation assume): three probe launches, cached per device.
-std::map<int, bool> g_xcd_ok;
-hipError_t xcd_round_robin(int dev, int cus, bool& ok) {
-    auto it = g_xcd_ok.find(dev);
-    if (it != g_xcd_ok.end()) {
-        ok = it->second;
-        return hipSuccess;
-    }
-    ok = false;
-    if (cus % 8 == 0) {
-        uint32_t* d = nullptr;
-        hipError_t e = hipMalloc(&d, size_t(cus) * 4);
-        if (e != hipSuccess) return e;
-        std::vector<uint32_t> h(cus);
-        ok = true;
-        for (int r = 0; r < 3 && ok && e == hipSuccess; ++r) {
-            k_xcc_probe<<<dim3(cus), dim3(64), 0, nullptr>>>(d);
-            e = hipGetLastError();
-            if (e == hipSuccess) e = hipMemcpy(h.data(), d, size_t(cus) * 4, hipMemcpyDeviceToHost);
-            for (int w = 0; w < cus && e == hipSuccess; ++w)
-                if (h[w] != uint32_t(w % 8)) ok = false;
-        }
-        const hipError_t f = hipFree(d);
-        if (e != hipSuccess) return e;
-        if (f != hipSuccess) return f;
-    }
-    g_xcd_ok[dev] = ok;
-    return hipSuccess;
-}
 
 constexpr size_t kMaxSchedules = 64;
 constexpr uint64_t kMaxItems = uint64_t(1) << 22;
 std::mutex g_sched_mu;
 std::map<std::vector<int64_t>, Schedule> g_sched;
 
+// The queues of one set of shapes (host only).  With 8 queues every
+// workgroup serves the queue of the XCD it runs on, so the cost model prices
+// the XCD-local synchronisation.
 hipError_t build_schedule(const std::vector<LoopDims>& dims, const std::vector<int64_t>& nbs, int steps, int workers,
-                          bool local_ok, Schedule& out) {
+                          Schedule& out) {
     std::vector<ScheduleItem> items;
-    schedule_items(dims, nbs, steps, workers, local_ok, items, out.qbase, out.nq);
+    schedule_items(dims, nbs, steps, workers, true, items, out.qbase, out.nq);
     static_assert(sizeof(ScheduleItem) == sizeof(uint2), "item layout");
-    out.local_sync = local_ok && out.nq == 8;
-    hipError_t e = hipMalloc(&out.items, items.size() * sizeof(uint2));
-    if (e != hipSuccess) return e;
-    e = hipMemcpy(out.items, items.data(), items.size() * sizeof(uint2), hipMemcpyHostToDevice);
+    out.count = static_cast<uint32_t>(items.size());
+    hipError_t e = hipHostMalloc(reinterpret_cast<void**>(&out.host_items), std::max<size_t>(1, items.size()) * sizeof(uint2),
+                                 hipHostMallocDefault);
     if (e != hipSuccess) {
-        (void)hipFree(out.items);
-        out.items = nullptr;
+        out.host_items = nullptr;
+        return e;
     }
-    return e;
+    if (!items.empty()) std::memcpy(out.host_items, items.data(), items.size() * sizeof(uint2));
+    return hipSuccess;
 }
 
 }  // namespace
 
 void set_ns_schedule(int mode) { g_ns_mode.store(mode); }
+void set_loop_fault(int mode) { g_loop_fault.store(mode); }
 
 // Cache key of a schedule: device, steps, workgroups, then (mp, np, nb) per problem.
 std::vector<int64_t> schedule_key(const NsLoopProblem* probs, int n, int ns_steps, int dev, int cus) {
@@ -1340,28 +1423,26 @@ std::vector<int64_t> schedule_key(const NsLoopProblem* probs, int n, int ns_step
     return key;
 }
 
-bool ns_loop_eligible(const NsLoopProblem* probs, int n, int ns_steps) {
-    if (n < 1 || n > kMaxNsLoopProblems || ns_steps < 1 || ns_steps > 255) return false;
-    {
-        std::lock_guard<std::mutex> lock(g_sched_mu);
-        if (g_sched.size() >= kMaxSchedules) {
-            int dev = 0, cus = 0;
-            if (hipGetDevice(&dev) != hipSuccess ||
-                hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-                return false;
-            if (g_sched.find(schedule_key(probs, n, ns_steps, dev, cus)) == g_sched.end()) return false;
-        }
-    }
+uint64_t ns_loop_items_cap(const Plan* const* plans, int n, int ns_steps) {
+    if (n < 1 || n > kMaxNsLoopProblems || ns_steps < 1 || ns_steps > 255) return 0;
     uint64_t items = 0, blocks = 0;
     for (int i = 0; i < n; ++i) {
-        const Plan& p = *probs[i].plan;
-        if (p.small || p.precision != MUON_PRECISION_FAST || p.nb < 1 || p.mp % 256 || p.np % 256) return false;
+        const Plan& p = *plans[i];
+        if (p.small || p.precision != MUON_PRECISION_FAST || p.nb < 1 || p.mp % 256 || p.np % 256) return 0;
         const uint64_t T = uint64_t(p.mp / 256), Tn = uint64_t(p.np / 256);
-        if (T * Tn >= (uint64_t(1) << 22)) return false;
+        if (T * Tn >= (uint64_t(1) << 22)) return 0;
+        // at most one item per tile: T (T + 1) / 2 tiles per symmetric product, T Tn for B X
         items += uint64_t(p.nb) * uint64_t(ns_steps) * (T * (T + 1) + T * Tn);
         blocks += uint64_t(p.nb);
     }
-    return items <= kMaxItems && blocks < (uint64_t(1) << 27);
+    return items <= kMaxItems && blocks < (uint64_t(1) << 27) ? items : 0;
+}
+
+bool ns_loop_eligible(const NsLoopProblem* probs, int n, int ns_steps) {
+    if (n < 1 || n > kMaxNsLoopProblems) return false;
+    const Plan* plans[kMaxNsLoopProblems];
+    for (int i = 0; i < n; ++i) plans[i] = probs[i].plan;
+    return ns_loop_items_cap(plans, n, ns_steps) > 0;
 }
 
 namespace {
@@ -1379,6 +1460,7 @@ struct AutoState {
     int calls = 0;
     int decided = -1;                        // -1 pending, 0 per-product, 1 persistent
     hipEvent_t ev[kTrialCalls][2] = {};
+    bool started[kTrialCalls] = {};
     bool recorded[kTrialCalls] = {};
 };
 std::map<std::vector<int64_t>, AutoState> g_auto;    // under g_sched_mu
@@ -1392,21 +1474,47 @@ void release_events(AutoState& st) {
             }
 }
 
+// The cached schedule of this set of shapes, built on first use; null when
+// the cache is full or building failed (the caller then runs per product).
+const Schedule* find_schedule(const NsLoopProblem* probs, int n, int ns_steps, int dev, int cus) {
+    const std::vector<int64_t> key = schedule_key(probs, n, ns_steps, dev, cus);
+    auto it = g_sched.find(key);
+    if (it != g_sched.end()) return &it->second;
+    if (g_sched.size() >= kMaxSchedules) return nullptr;
+    std::vector<LoopDims> dims;
+    std::vector<int64_t> nbs;
+    for (int i = 0; i < n; ++i) {
+        const Plan& p = *probs[i].plan;
+        const uint32_t T = uint32_t(p.mp / 256), Tn = uint32_t(p.np / 256);
+        dims.push_back({int(p.mp), int(p.np), T * (T + 1) / 2, T * Tn});
+        nbs.push_back(p.nb);
+    }
+    Schedule sc;
+    if (build_schedule(dims, nbs, ns_steps, cus, sc) != hipSuccess) return nullptr;
+    return &g_sched.emplace(key, sc).first->second;
+}
+
 }  // namespace
 
 NsChoice ns_schedule_begin(const NsLoopProblem* probs, int n, int ns_steps, hipStream_t s) {
     NsChoice c;
     const int mode = g_ns_mode.load();
     if (mode == 1 || !ns_loop_eligible(probs, n, ns_steps)) return c;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        return c;
+    std::lock_guard<std::mutex> lock(g_sched_mu);
+    // The loop needs its queue: without one (cache full, or no pinned host
+    // memory) the call runs per product, which gives the same results.
+    const Schedule* sched = find_schedule(probs, n, ns_steps, dev, cus);
+    if (sched == nullptr) return c;
+    c.sched = sched;
+    c.cus = cus;
     if (mode == 2) {
         c.persistent = true;
         return c;
     }
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        return c;
-    std::lock_guard<std::mutex> lock(g_sched_mu);
     const std::vector<int64_t> key = schedule_key(probs, n, ns_steps, dev, cus);
     auto it = g_auto.find(key);
     if (it == g_auto.end()) {
@@ -1420,9 +1528,17 @@ NsChoice ns_schedule_begin(const NsLoopProblem* probs, int n, int ns_steps, hipS
     }
     if (st.calls >= kTrialCalls) {
         // decide once every trial's events have completed
-        bool ready = true;
-        for (int i = 0; i < kTrialCalls && ready; ++i)
-            ready = st.recorded[i] && hipEventQuery(st.ev[i][1]) == hipSuccess;
+        bool ready = true, failed = false;
+        for (int i = 0; i < kTrialCalls && ready; ++i) {
+            failed = failed || !st.recorded[i];
+            ready = !st.recorded[i] || hipEventQuery(st.ev[i][1]) == hipSuccess;
+        }
+        if (ready && failed) {
+            // a trial was not timed (event record failed): keep per-product
+            st.decided = 0;
+            release_events(st);
+            return c;
+        }
         if (ready) {
             float best[2] = {0.f, 0.f};
             bool ok = true;
@@ -1442,12 +1558,20 @@ NsChoice ns_schedule_begin(const NsLoopProblem* probs, int n, int ns_steps, hipS
     const int i = st.calls;
     for (hipEvent_t& e : st.ev[i])
         if (!e && hipEventCreate(&e) != hipSuccess) return c;
-    if (hipEventRecord(st.ev[i][0], s) != hipSuccess) return c;
     ++st.calls;
     c.persistent = (i & 1) != 0;
     c.trial = i;
     c.key = &it->first;
     return c;
+}
+
+void ns_schedule_start(const NsChoice& c, hipStream_t s) {
+    if (c.trial < 0) return;
+    std::lock_guard<std::mutex> lock(g_sched_mu);
+    auto it = g_auto.find(*c.key);
+    if (it == g_auto.end() || it->second.decided >= 0) return;
+    AutoState& st = it->second;
+    st.started[c.trial] = hipEventRecord(st.ev[c.trial][0], s) == hipSuccess;
 }
 
 void ns_schedule_end(const NsChoice& c, hipStream_t s) {
@@ -1456,81 +1580,71 @@ void ns_schedule_end(const NsChoice& c, hipStream_t s) {
     auto it = g_auto.find(*c.key);
     if (it == g_auto.end() || it->second.decided >= 0) return;
     AutoState& st = it->second;
-    if (hipEventRecord(st.ev[c.trial][1], s) == hipSuccess) st.recorded[c.trial] = true;
+    if (st.started[c.trial] && hipEventRecord(st.ev[c.trial][1], s) == hipSuccess) st.recorded[c.trial] = true;
 }
 
 size_t ns_loop_sync_bytes(int64_t total_blocks) {
-    return (size_t(9 + total_blocks) * kSyncStride * 4 + 255) & ~size_t(255);
+    return (size_t(kSyncLines + total_blocks) * kSyncStride * 4 + 255) & ~size_t(255);
 }
 
 hipError_t launch_ns_loop(const NsLoopProblem* probs, int n, int ns_steps, float ca, float cb, float cc,
+                          const NsChoice& choice, uint2* items_ws, uint64_t items_cap, uint32_t* status,
                           hipStream_t s) {
-    if (!ns_loop_eligible(probs, n, ns_steps)) return hipErrorInvalidValue;
+    if (!choice.persistent || choice.sched == nullptr || !ns_loop_eligible(probs, n, ns_steps) || status == nullptr)
+        return hipErrorInvalidValue;
+    const Schedule& sc = *static_cast<const Schedule*>(choice.sched);
+    if (items_ws == nullptr || sc.count > items_cap) return hipErrorInvalidValue;
     for (int i = 0; i < n; ++i)
         if (probs[i].sync == nullptr) return hipErrorInvalidValue;
-    int dev = 0, cus = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    if (cus < 1) return hipErrorInvalidValue;
-    const std::vector<int64_t> key = schedule_key(probs, n, ns_steps, dev, cus);
-    std::vector<LoopDims> dims;
-    std::vector<int64_t> nbs;
     PersistArgs a{};
     a.n = n;
+    a.steps = ns_steps;
     a.ca = ca;
     a.cb = cb;
     a.cc = cc;
     a.sync = probs[0].sync;
-    ZeroArgs z{};
+    a.status = status;
+    const int fault = g_loop_fault.load();
+    a.inject = fault == 1 ? 1 : 0;
+    a.spin_ticks = fault == 2 ? 0 : 100000000ull;   // 1 s of the 100 MHz real-time counter
+    SetupArgs z{};
     z.count = n;
     uint32_t zmax = 0;
     uint32_t first = 0;
     for (int i = 0; i < n; ++i) {
         const Plan& p = *probs[i].plan;
         const uint32_t T = uint32_t(p.mp / 256), Tn = uint32_t(p.np / 256);
-        dims.push_back({int(p.mp), int(p.np), T * (T + 1) / 2, T * Tn});
-        nbs.push_back(p.nb);
         PersistProblem& pr = a.pr[i];
-        pr.x[0] = probs[i].x[0];
-        pr.x[1] = probs[i].x[1];
+        pr.x0 = probs[i].x0;
+        pr.xb[0] = probs[i].x[0];
+        pr.xb[1] = probs[i].x[1];
+        pr.xlast = probs[i].xlast;
         pr.a = probs[i].a;
         pr.b = probs[i].b;
         pr.scale = probs[i].scale;
-        pr.done = probs[i].sync + 9 * kSyncStride;
+        pr.done = probs[i].sync + kSyncLines * kSyncStride;
         z.p[i] = probs[i].sync;
-        z.n[i] = uint32_t((9 + p.nb) * kSyncStride);
+        z.n[i] = uint32_t((kSyncLines + p.nb) * kSyncStride);
         zmax = std::max(zmax, z.n[i]);
         pr.mp = int32_t(p.mp);
         pr.np = int32_t(p.np);
         pr.first_blk = first;
-        pr.nsym = dims.back().nsym;
-        pr.nbx = dims.back().nbx;
+        pr.nb = uint32_t(p.nb);
+        pr.nsym = T * (T + 1) / 2;
+        pr.nbx = T * Tn;
         first += uint32_t(p.nb);
     }
-    {
-        std::lock_guard<std::mutex> lock(g_sched_mu);
-        auto it = g_sched.find(key);
-        if (it == g_sched.end()) {
-            if (g_sched.size() >= kMaxSchedules) return hipErrorOutOfMemory;
-            Schedule sc;
-            bool local_ok = false;
-            e = xcd_round_robin(dev, cus, local_ok);
-            if (e != hipSuccess) return e;
-            e = build_schedule(dims, nbs, ns_steps, cus, local_ok, sc);
-            if (e != hipSuccess) return e;
-            it = g_sched.emplace(key, sc).first;
-        }
-        a.items = it->second.items;
-        a.nq = it->second.nq;
-        a.local_sync = it->second.local_sync ? 1 : 0;
-        for (int q = 0; q < 9; ++q) a.qbase[q] = it->second.qbase[q];
-    }
-    k_zero_sync<<<dim3((zmax + 255) / 256), dim3(256), 0, s>>>(z);
-    e = hipGetLastError();
+    a.items = items_ws;
+    a.nq = sc.nq;
+    for (int q = 0; q < 9; ++q) a.qbase[q] = sc.qbase[q];
+    z.src = sc.host_items;
+    z.dst = items_ws;
+    z.items = sc.count;
+    const uint32_t work = std::max(zmax, sc.count);
+    k_loop_setup<<<dim3((work + 255) / 256), dim3(256), 0, s>>>(z);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    k_ns_loop<<<dim3(cus), dim3(tile_threads<256>()), 0, s>>>(a);
+    k_ns_loop<<<dim3(choice.cus), dim3(tile_threads<256>()), 0, s>>>(a);
     return hipGetLastError();
 }
 

@@ -53,17 +53,34 @@ def test_default_config(lib):
     assert cfg.precision == 0
 
 
-def _expected_ws(nb, m, n, split=False):
-    def up(x, a):
-        return (x + a - 1) // a * a
-    mp, np_ = up(m, 128), up(n, 128)
-    xb = up(nb * mp * np_ * 2, 256)
-    ab = up(nb * mp * mp * 2, 256)
+def _up(x, a):
+    return (x + a - 1) // a * a
+
+
+def _regions(nb, m, n, split=False):
+    """Bytes of one block batch's plan regions (no header, no loop queue)."""
+    mp, np_ = _up(m, 128), _up(n, 128)
+    xb = _up(nb * mp * np_ * 2, 256)
+    ab = _up(nb * mp * mp * 2, 256)
     tiles = (mp // 64) * (np_ // 64)
     # iterate ping-pong (and lo planes when split); A; B (+ lo); partials; scales;
     # counters of the persistent NS loop (9 + one per block, each on a 128-byte line)
-    return ((4 if split else 2) * xb + (3 if split else 2) * ab + up(nb * tiles * 4, 256) + up(nb * 8, 256)
-            + up((9 + nb) * 128, 256))
+    return ((4 if split else 2) * xb + (3 if split else 2) * ab + _up(nb * tiles * 4, 256) + _up(nb * 8, 256)
+            + _up((9 + nb) * 128, 256))
+
+
+def _queue_entries(nb, m, n, steps=5, split=False):
+    """Entries of the persistent loop's queue region (one per 256-wide tile at most)."""
+    mp, np_ = _up(m, 128), _up(n, 128)
+    if split or mp % 256 or np_ % 256:
+        return 0
+    t, tn = mp // 256, np_ // 256
+    return nb * steps * (t * (t + 1) + t * tn)
+
+
+def _expected_ws(nb, m, n, split=False, steps=5):
+    # a 256-byte status header, the plan regions, the loop queue (8 bytes per entry)
+    return 256 + _regions(nb, m, n, split) + _up(8 * _queue_entries(nb, m, n, steps, split), 256)
 
 
 def test_workspace_bytes(lib):
@@ -170,7 +187,9 @@ def test_multi_workspace_bytes(lib):
     es += [_mat(base + 6 * (1 << 26), base + 6 * (1 << 26) + 4096, base + 6 * (1 << 26) + 8192, 1, 12)]
     arr = _mats(*es)
     got = lib.muon_step_multi_workspace_bytes(arr, len(es), None)
-    assert got == _expected_ws(3, 768, 3072) + _expected_ws(8, 768, 768)
+    # one wave (equal padded side): header, both groups' regions, one queue for both
+    q = _queue_entries(3, 768, 3072) + _queue_entries(8, 768, 768)
+    assert got == 256 + _regions(3, 768, 3072) + _regions(8, 768, 768) + _up(8 * q, 256)
     assert lib.muon_step_multi_workspace_bytes(arr, 0, None) == 0
     bad = _mats(_mat(base, base + 4096, base + 8192, 8, 10, 4))
     assert lib.muon_step_multi_workspace_bytes(bad, 1, None) == ctypes.c_size_t(-1).value
@@ -304,3 +323,19 @@ def test_ns_schedule_modes(lib):
         nsm.muon_set_ns_schedule(name)
     with pytest.raises(ValueError):
         nsm.muon_set_ns_schedule("fast")
+
+
+def test_workspace_status_validation(lib):
+    # host-side checks only (no copy is enqueued)
+    assert lib.muon_workspace_status(None, ctypes.c_void_p(1 << 30), None) == 1
+    assert lib.muon_workspace_status(ctypes.c_void_p(1 << 30), None, None) == 1
+    assert lib.muon_workspace_status(ctypes.c_void_p((1 << 30) + 16), ctypes.c_void_p(1 << 30), None) == 3
+    assert lib.muon_workspace_status(ctypes.c_void_p(1 << 30), ctypes.c_void_p((1 << 30) + 2), None) == 3
+
+
+def test_loop_fault_modes(lib):
+    for mode in (1, 2, 0):
+        assert lib.muon_debug_set_loop_fault(mode) == 0
+    assert lib.muon_debug_set_loop_fault(3) == 1
+    assert lib.muon_debug_set_loop_fault(-1) == 1
+    assert "loop fault mode" in nsm.muon_last_error()
