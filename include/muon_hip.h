@@ -120,6 +120,30 @@ muon_status ns_orthogonalize_batched(const void* x, void* out,
                                      void* workspace, size_t workspace_bytes,
                                      void* stream);
 
+/* Largest scratch ns_orthogonalize_batched_noalloc uses (bytes): the 256-byte
+ * status header plus the plan regions muon_workspace_bytes describes (without
+ * the persistent loop's queue). */
+#define MUON_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * ns_orthogonalize_batched for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same arguments without a workspace and the same results,
+ * bit for bit.  Its scratch is one library-owned static device array per GPU
+ * of MUON_NOALLOC_SCRATCH_BYTES, held until the process ends; the call makes
+ * no allocation (device or host), records no timing events, and always runs
+ * the per-product NS schedule.
+ *   Returns MUON_ERR_WORKSPACE when the batch needs more scratch than that
+ *   (muon_workspace_bytes minus the loop queue); nothing is enqueued then.
+ *   Every call on one GPU shares its scratch, so calls that overlap on one
+ *   GPU (different streams or host threads without ordering) race; calls on
+ *   one stream are ordered and safe.
+ */
+muon_status ns_orthogonalize_batched_noalloc(const void* x, void* out,
+                                             int64_t batch, int64_t rows, int64_t cols,
+                                             int32_t view_blocks, const muon_ns_config* cfg,
+                                             void* stream);
+
 /*
  * One Muon step for a [batch, rows, cols] batch of parameters ([CS] sections
  * 1 and 4, [PG] Part 1), in place:

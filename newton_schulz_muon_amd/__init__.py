@@ -8,6 +8,7 @@ calls raise.
 
 Entry points (same names as the C ABI):
     ns_orthogonalize_batched(x, out=None, *, view_blocks=1, ...)
+    ns_orthogonalize_batched_noalloc(x, out=None, *, view_blocks=1, ...)
     muon_step_batched(params, grads, momentum_buf, *, lr, weight_decay, momentum, ...)
     muon_step_multi(matrices, *, lr, weight_decay, momentum, ...)
     adamw_step_multi(tensors, *, lr, betas, eps, weight_decay)
@@ -28,7 +29,7 @@ from typing import Optional, Tuple
 __all__ = [
     "MuonNSConfig", "MuonError", "LIB_PATH", "EXPORTED_SYMBOLS", "load_library",
     "muon_ns_config_default", "muon_workspace_bytes", "ns_orthogonalize_batched",
-    "muon_step_batched", "muon_step_multi", "muon_step_multi_workspace_bytes", "MuonMatrix",
+    "ns_orthogonalize_batched_noalloc", "NOALLOC_SCRATCH_BYTES", "muon_step_batched", "muon_step_multi", "muon_step_multi_workspace_bytes", "MuonMatrix",
     "adamw_step_multi", "MuonAdamTensor", "muon_merge_small_dims",
     "muon_timing_enable", "muon_timing_collect", "muon_last_error", "muon_abi_version", "make_config",
     "muon_set_ns_schedule", "KERNEL_KINDS", "NS_SCHEDULES", "muon_workspace_status", "last_call_status",
@@ -37,10 +38,12 @@ __all__ = [
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmuon_hip.so")
 EXPORTED_SYMBOLS = ("muon_ns_config_default", "muon_workspace_bytes", "ns_orthogonalize_batched",
+                    "ns_orthogonalize_batched_noalloc",
                     "muon_step_batched", "muon_step_multi_workspace_bytes", "muon_step_multi",
                     "adamw_step_multi", "muon_merge_small_dims", "muon_set_ns_schedule", "muon_timing_enable",
                     "muon_timing_collect", "muon_workspace_status", "muon_debug_set_loop_fault",
                     "muon_last_error", "muon_abi_version")
+NOALLOC_SCRATCH_BYTES = 64 << 20   # MUON_NOALLOC_SCRATCH_BYTES of the header
 KERNEL_KINDS = ("prep", "norm_finalize", "gram", "poly", "bx", "finish", "small", "adamw", "ns_loop")
 NS_SCHEDULES = {"auto": 0, "per_product": 1, "persistent": 2}
 
@@ -96,6 +99,8 @@ def load_library():
         lib.muon_workspace_bytes.restype = ctypes.c_size_t
         lib.ns_orthogonalize_batched.argtypes = [vp, vp, i64, i64, i64, i32, cfgp, vp, ctypes.c_size_t, vp]
         lib.ns_orthogonalize_batched.restype = ctypes.c_int
+        lib.ns_orthogonalize_batched_noalloc.argtypes = [vp, vp, i64, i64, i64, i32, cfgp, vp]
+        lib.ns_orthogonalize_batched_noalloc.restype = ctypes.c_int
         lib.muon_step_batched.argtypes = [vp, vp, vp, i64, i64, i64, i32, f32, f32, f32, i32, f32, f32,
                                           cfgp, vp, vp, ctypes.c_size_t, vp]
         lib.muon_step_batched.restype = ctypes.c_int
@@ -303,6 +308,30 @@ def ns_orthogonalize_batched(x, out=None, *, view_blocks: int = 1, ns_steps: int
         _check(lib.ns_orthogonalize_batched(
             x3.data_ptr(), o3.data_ptr(), B, R, C, int(view_blocks), ctypes.byref(cfg),
             ws.data_ptr() if ws is not None else None, nbytes, stream))
+    return out
+
+
+def ns_orthogonalize_batched_noalloc(x, out=None, *, view_blocks: int = 1, ns_steps: int = 5,
+                                     coeffs: Optional[Tuple[float, float, float]] = None,
+                                     eps: Optional[float] = None, precision: str = "fast",
+                                     cfg: Optional[MuonNSConfig] = None):
+    """ns_orthogonalize_batched without a workspace: the library's static
+    per-GPU scratch (NOALLOC_SCRATCH_BYTES) serves instead, and the C call
+    allocates nothing (pass `out` to keep the binding from allocating it)."""
+    import torch
+    _require(x, "x", torch.bfloat16)
+    if out is None:
+        out = torch.empty_like(x)
+    _require(out, "out", torch.bfloat16, x.device)
+    if out.shape != x.shape:
+        raise ValueError("out must have the shape of x")
+    x3, o3 = _as3d(x, "x"), _as3d(out, "out")
+    cfg = cfg if cfg is not None else make_config(ns_steps, coeffs, eps, precision)
+    B, R, C = x3.shape
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        _check(load_library().ns_orthogonalize_batched_noalloc(
+            x3.data_ptr(), o3.data_ptr(), B, R, C, int(view_blocks), ctypes.byref(cfg), stream))
     return out
 
 

@@ -181,11 +181,15 @@ hipEvent_t pool_get(TimingState& ts, int dev) {
 
 // Records an event pair around one launch when its kernel family is selected,
 // with the nominal flops of the products the launch computes.
+// Set for the duration of a call that must not create timing events (the
+// no-allocation entry point).
+thread_local bool g_timing_off = false;
+
 class LaunchTimer {
   public:
     LaunchTimer(int kind, hipStream_t s, double flops) : kind_(kind), s_(s), flops_(flops) {
         TimingState& ts = timing();
-        if (!(ts.mask.load() & (1u << kind))) return;
+        if (g_timing_off || !(ts.mask.load() & (1u << kind))) return;
         std::lock_guard<std::mutex> lk(ts.mu);
         if (hipGetDevice(&dev_) != hipSuccess) return;
         a_ = pool_get(ts, dev_);
@@ -555,32 +559,41 @@ MatTable make_table(const muon_matrix* mats, const ShapeGroup& g, size_t m0, siz
     return t;
 }
 
-}  // namespace
-}  // namespace muon
+// ---------------------------------------------------------------- no-allocation scratch
+// Scratch memory of ns_orthogonalize_batched_noalloc, for callers that cannot
+// allocate (code under graph capture, tight serving loops): one copy per GPU,
+// held until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory; the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kScratchBytes = size_t(MUON_NOALLOC_SCRATCH_BYTES);
+static __device__ __align__(256) char scratch[kScratchBytes];
 
-using namespace muon;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
 
-extern "C" {
-
-void muon_ns_config_default(muon_ns_config* cfg) {
-    if (cfg) *cfg = default_config();
+muon_status scratch_of_current_device(void** out) {
+    int dev = 0;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(MUON_ERR_UNSUPPORTED, "device index %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        const hipError_t e2 = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e2 != hipSuccess) return hip_fail(e2, "hipGetSymbolAddress(scratch)");
+        if (ptr == nullptr || !aligned(ptr, 256)) return fail(MUON_ERR_HIP, "scratch symbol has no usable address");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return MUON_OK;
 }
 
-size_t muon_workspace_bytes(int64_t batch, int64_t rows, int64_t cols, int32_t view_blocks,
-                            const muon_ns_config* cfg_in) {
-    g_err.clear();
-    const muon_ns_config cfg = cfg_in ? *cfg_in : default_config();
-    if (validate_config(cfg) != MUON_OK) return size_t(-1);
-    Plan p;
-    if (make_plan(batch, rows, cols, view_blocks, cfg, p) != MUON_OK) return size_t(-1);
-    if (batch == 0) return 0;
-    return batched_layout(p, cfg.ns_steps).total;
-}
-
-muon_status ns_orthogonalize_batched(const void* x, void* out, int64_t batch, int64_t rows,
-                                     int64_t cols, int32_t view_blocks, const muon_ns_config* cfg_in,
-                                     void* workspace, size_t workspace_bytes, void* stream) {
-    g_err.clear();
+// ns_orthogonalize_batched; with per_product_only the persistent loop (whose
+// queue lives in pinned host memory the first call allocates) is not used.
+muon_status ns_batched_impl(const void* x, void* out, int64_t batch, int64_t rows, int64_t cols, int32_t view_blocks,
+                            const muon_ns_config* cfg_in, void* workspace, size_t workspace_bytes, void* stream,
+                            bool per_product_only) {
     const muon_ns_config cfg = cfg_in ? *cfg_in : default_config();
     muon_status st = validate_config(cfg);
     if (st != MUON_OK) return st;
@@ -593,7 +606,11 @@ muon_status ns_orthogonalize_batched(const void* x, void* out, int64_t batch, in
     const size_t bytes = size_t(batch) * size_t(rows) * size_t(cols) * 2;
     if (x != out && overlaps(x, bytes, out, bytes))
         return fail(MUON_ERR_INVALID_ARG, "out overlaps x without being x");
-    const BatchedLayout lay = batched_layout(p, cfg.ns_steps);
+    BatchedLayout lay = batched_layout(p, cfg.ns_steps);
+    if (per_product_only && lay.total > 0) {
+        lay.total = kHeaderBytes + p.total;
+        lay.items_cap = 0;
+    }
     st = common_checks(lay.total, workspace, workspace_bytes);
     if (st != MUON_OK) return st;
     if (lay.total > 0 && (overlaps(workspace, lay.total, x, bytes) || overlaps(workspace, lay.total, out, bytes)))
@@ -621,7 +638,7 @@ muon_status ns_orthogonalize_batched(const void* x, void* out, int64_t batch, in
     const NsEnds ends = ns_ends(p, cfg, b, x, out);
     // The schedule (and on first use its queue) is settled before anything is enqueued.
     const NsLoopProblem lp{&p, ends.x0, {b.xh[0], b.xh[1]}, ends.xlast, b.a, b.bh, b.scale, b.sync};
-    const NsChoice ch = ns_schedule_begin(&lp, 1, cfg.ns_steps, s);
+    const NsChoice ch = per_product_only ? NsChoice() : ns_schedule_begin(&lp, 1, cfg.ns_steps, s);
     hipError_t e = timed(MUON_KERNEL_PREP, s, [&] {
         return launch_prep(p, kPrepCast, static_cast<const uint16_t*>(x), nullptr, 0.f,
                            ends.direct_in ? nullptr : b.xh[0], b.xl[0], b.part, status, s);
@@ -636,6 +653,67 @@ muon_status ns_orthogonalize_batched(const void* x, void* out, int64_t batch, in
                              static_cast<uint16_t*>(out), s);
     });
     return e == hipSuccess ? MUON_OK : hip_fail(e, "k_finish launch");
+}
+
+}  // namespace
+}  // namespace muon
+
+using namespace muon;
+
+extern "C" {
+
+void muon_ns_config_default(muon_ns_config* cfg) {
+    if (cfg) *cfg = default_config();
+}
+
+size_t muon_workspace_bytes(int64_t batch, int64_t rows, int64_t cols, int32_t view_blocks,
+                            const muon_ns_config* cfg_in) {
+    g_err.clear();
+    const muon_ns_config cfg = cfg_in ? *cfg_in : default_config();
+    if (validate_config(cfg) != MUON_OK) return size_t(-1);
+    Plan p;
+    if (make_plan(batch, rows, cols, view_blocks, cfg, p) != MUON_OK) return size_t(-1);
+    if (batch == 0) return 0;
+    return batched_layout(p, cfg.ns_steps).total;
+}
+
+muon_status ns_orthogonalize_batched(const void* x, void* out, int64_t batch, int64_t rows,
+                                     int64_t cols, int32_t view_blocks, const muon_ns_config* cfg_in,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+    g_err.clear();
+    return ns_batched_impl(x, out, batch, rows, cols, view_blocks, cfg_in, workspace, workspace_bytes, stream,
+                           false);
+}
+
+muon_status ns_orthogonalize_batched_noalloc(const void* x, void* out, int64_t batch, int64_t rows, int64_t cols,
+                                             int32_t view_blocks, const muon_ns_config* cfg_in, void* stream) {
+    g_err.clear();
+    const muon_ns_config cfg = cfg_in ? *cfg_in : default_config();
+    muon_status st = validate_config(cfg);
+    if (st != MUON_OK) return st;
+    Plan p;
+    st = make_plan(batch, rows, cols, view_blocks, cfg, p);
+    if (st != MUON_OK) return st;
+    if (batch == 0) return MUON_OK;
+    // This entry point runs the per-product schedule only, which needs no
+    // queue region.
+    const size_t need = p.small ? 0 : kHeaderBytes + p.total;
+    if (need > kScratchBytes)
+        return fail(MUON_ERR_WORKSPACE,
+                    "this batch needs %zu bytes of scratch; the no-allocation entry point has %zu (use "
+                    "ns_orthogonalize_batched with a workspace)", need, kScratchBytes);
+    st = check_device();
+    if (st != MUON_OK) return st;
+    void* ws = nullptr;
+    if (need > 0) {
+        st = scratch_of_current_device(&ws);
+        if (st != MUON_OK) return st;
+    }
+    struct TimingOff {
+        TimingOff() { g_timing_off = true; }
+        ~TimingOff() { g_timing_off = false; }
+    } no_events;
+    return ns_batched_impl(x, out, batch, rows, cols, view_blocks, cfg_in, ws, need, stream, true);
 }
 
 muon_status muon_step_batched(float* params, const void* grads, float* momentum_buf, int64_t batch,
