@@ -1,16 +1,28 @@
 #!/usr/bin/env python3
-"""Benchmark of the batched Muon step on one MI355X.
+"""Benchmark of the batched Newton-Schulz / Muon step on one MI355X.
 
-A step is one pass of the whole hot path over one batch: momentum, per-block
-Frobenius normalisation, 5 quintic Newton-Schulz iterations, aspect-scaled
-decoupled-decay update, for the 124M GPT custom-sizing set: 11 gate matrices
-1x12 (first), 10 attention matrices stored 768x3072 and viewed as 4 x 768x768,
-and 22 MLP matrices 768x3072 (seeded synthetic bf16 gradients ~N(0, 1e-2),
-fp32 parameters and momentum buffers resident in HBM).
+Headline (the metric's own configuration): one `ns_orthogonalize_batched`
+call over 32 matrices 768x3072 (bf16, seeded N(0, 0.01^2), resident in HBM),
+FAST precision, 5 quintic iterations.  `value` is nominal NS TFLOP/s:
+32 * 5 * (4 m^2 n + 2 m^3) flops (m = 768, n = 3072) divided by the
+wall-clock time of one call; matrices/s is 32 per call.
 
-Prints one JSON line.  `value` is nominal Newton-Schulz TFLOP/s of the whole
-step (5 (4 m^2 n + 2 m^3) flops per NS block, m <= n, divided by the wall-clock
-step time); matrices/s and NS blocks/s are reported beside it.
+Beside it the JSON line carries
+  * roofline: the dominant kernel of the call (the NS kernel family with the
+    most time; with the automatic schedule the persistent loop k_ns_loop),
+    timed with hipEvents the library records around each launch, at three
+    flop counts: nominal (the metric's), executed (the 256-wide tiles the
+    kernel computes: symmetric products skip lower tiles) and algorithmic
+    (the method's symmetric work 5 (3 m^2 n + m^3)); plus the MFMA-busy
+    fraction and the HBM traffic from committed rocprofv3 counter runs
+    (profiles/, null once the kernel source changed);
+  * percentiles of the call time (per-call events) with a warm and a cold
+    (1 GiB written between calls) Infinity Cache;
+  * extras: the full 124M custom-sizing Muon step (muon_step_multi over 43
+    matrices) with its element-wise kernels' HBM rates, one GPU's share of it
+    under 8-way sharding by whole matrices, the AdamW step of the same model;
+  * cpu_baseline: the fp64 NumPy oracle on a bounded sample of the same
+    workload on the host cores.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -20,6 +32,7 @@ import argparse
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -30,25 +43,40 @@ if ROOT not in sys.path:
 METRIC = "Newton-Schulz TFLOP/s and matrices/s at 32x768x3072 bf16; % of MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
-WORKLOAD = "gpt124m"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_bx_gpt124m_traffic.json")
-LOOP_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_ns_loop_gpt124m_traffic.json")
-# The NS kernel families (library timing names) and the counter runs of each.
-NS_FAMILIES = {"ns_loop": "k_ns_loop (every NS iteration of a wave: X X^T, aI + bA + cA^2, B' X; nominal flops)",
-               "gram": "k_gemm<kGram> (A = X X^T; nominal flops)",
-               "poly": "k_gemm<kPoly> (B' = aI + bA + cA^2; nominal flops of A A)",
-               "bx": "k_gemm<kBx> (X <- B' X; nominal flops)"}
-TRAFFIC_FILES = {"ns_loop": LOOP_TRAFFIC_FILE, "bx": TRAFFIC_FILE}
+PROFILES = os.path.join(ROOT, "profiles")
 GEMM_SOURCE = os.path.join(ROOT, "newton_schulz_muon_amd", "csrc", "ns_gemm.hip")
-ADAM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_adamw_gpt124m_traffic.json")
+EW_SOURCE = os.path.join(ROOT, "newton_schulz_muon_amd", "csrc", "muon_elementwise.hip")
 ADAM_SOURCE = os.path.join(ROOT, "newton_schulz_muon_amd", "csrc", "adamw.hip")
+NS_FAMILIES = ("ns_loop", "gram", "poly", "bx")
+FAMILY_NAMES = {"ns_loop": "k_ns_loop (all NS iterations of a call in one launch: X X^T, aI + bA + cA^2, B' X)",
+                "gram": "k_gemm<kGram> (A = X X^T)",
+                "poly": "k_gemm<kPoly> (B' = aI + bA + cA^2)",
+                "bx": "k_gemm<kBx> (X <- B' X)"}
 SETTLE_CALLS = 12              # calls before warm-up that let the automatic NS schedule choose
+NS_STEPS = 5
 
 
-def ns_flops(m: int, n: int, steps: int) -> float:
-    """Nominal NS work of one block: steps * (4 m^2 n + 2 m^3), m <= n."""
+def ns_flops(m: int, n: int, steps: int = NS_STEPS) -> float:
+    """Nominal NS work of one block (the metric's count): steps (4 m^2 n + 2 m^3), m <= n."""
     m, n = min(m, n), max(m, n)
     return float(steps) * (4.0 * m * m * n + 2.0 * m ** 3)
+
+
+def ns_flops_symmetric(m: int, n: int, steps: int = NS_STEPS) -> float:
+    """The method's own work with A and B' symmetric: steps (3 m^2 n + m^3)."""
+    m, n = min(m, n), max(m, n)
+    return float(steps) * (3.0 * m * m * n + float(m) ** 3)
+
+
+def loop_executed_flops(m: int, n: int, steps: int = NS_STEPS) -> float:
+    """MFMA flops the persistent loop executes for one block: 256-wide tiles of
+    the padded oriented block (mp x np), upper-triangle tiles of the symmetric
+    products (T (T + 1) / 2 of them), every tile of B' X."""
+    m, n = min(m, n), max(m, n)
+    mp, np_ = -(-m // 128) * 128, -(-n // 128) * 128
+    t, tn = mp // 256, np_ // 256
+    nsym, nbx = t * (t + 1) // 2, t * tn
+    return float(steps) * 2.0 * 256 * 256 * (nsym * np_ + nsym * mp + nbx * mp)
 
 
 def source_digest(path: str) -> str:
@@ -56,55 +84,327 @@ def source_digest(path: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def load_traffic(path: str = TRAFFIC_FILE, source: str = GEMM_SOURCE):
-    """HBM bytes per launch of a kernel from the committed rocprofv3 counter
-    runs, or None when they are missing or the kernel source changed since."""
+def load_profile(name: str, source: str, key: str):
+    """A figure from a committed rocprofv3 summary (profiles/<name>.json), or
+    None when it is missing or the kernel source changed since it was taken."""
     try:
-        with open(path) as f:
+        with open(os.path.join(PROFILES, name + ".json")) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
     if t.get("source_sha256_16") != source_digest(source):
         return None
-    return t.get("bytes_per_launch")
+    return t.get(key)
 
 
-def cpu_baseline(wl, seconds: float):
-    """The fp64 oracle on a bounded sample of the workload (host cores)."""
+def percentiles(xs):
+    xs = sorted(xs)
+
+    def q(p):
+        k = (len(xs) - 1) * p
+        lo, hi = int(k), min(int(k) + 1, len(xs) - 1)
+        return xs[lo] + (xs[hi] - xs[lo]) * (k - lo)
+    return {"p10": round(q(0.1), 4), "p50": round(q(0.5), 4), "p90": round(q(0.9), 4)}
+
+
+# ----------------------------------------------------------------------------- host description
+def host_info():
+    import numpy as np
+    info = {"os_cpu_count": os.cpu_count()}
+    try:
+        info["affinity_cpus"] = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        info["affinity_cpus"] = None
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    info["cpu_model"] = model or platform.processor() or None
+    blas, threads = None, None
+    try:
+        from threadpoolctl import threadpool_info
+        pools = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if pools:
+            blas = f"{pools[0].get('internal_api')} {pools[0].get('version')}"
+            threads = max(int(p.get("num_threads", 1)) for p in pools)
+    except Exception:
+        pass
+    if blas is None:
+        try:
+            cfg = np.show_config(mode="dicts")
+            blas = cfg.get("Build Dependencies", {}).get("blas", {}).get("name")
+        except Exception:
+            blas = None
+    info["blas"] = blas
+    info["blas_threads"] = threads
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS"):
+        info[var] = os.environ.get(var)
+    return info
+
+
+def cpu_baseline(seconds: float):
+    """The fp64 oracle (as it stands) on 768x3072 blocks of the headline
+    workload, one after another, until about `seconds` of work."""
     import numpy as np
     import oracle
     import workloads
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    except Exception:
-        threads = os.cpu_count() or 1
-    groups = {g.name: g for g in wl.groups}
-    plan = [("gate", i) for i in range(groups["gate"].count)]
-    for i in range(max(groups["mlp"].count, groups["attn"].count)):
-        if i < groups["mlp"].count:
-            plan.append(("mlp", i))
-        if i < groups["attn"].count:
-            plan.append(("attn", i))
-    done_flops, done_mats, used = 0.0, 0, []
-    t0 = time.perf_counter()
-    for name, i in plan:
-        g = groups[name]
-        G = workloads.bf16_bits_to_f32(workloads.grad_bits_host(wl, g, 0, [i])).astype(np.float64)
-        P = workloads.param_init_host(wl, g, [i]).astype(np.float64)
-        M = np.zeros_like(G)
-        oracle.muon_step(P, G, M, lr=wl.lr, weight_decay=wl.weight_decay, momentum=wl.momentum,
-                         view_blocks=g.view_blocks, ns_steps=wl.ns_steps)
-        r, c = g.block_shape
-        done_flops += g.view_blocks * ns_flops(r, c, wl.ns_steps)
-        done_mats += 1
-        used.append(f"{name}[{i}]")
+    wl = workloads.get_workload("metric32")
+    g = wl.groups[0]
+    done, t0 = 0, time.perf_counter()
+    while True:
+        bits = workloads.grad_bits_host(wl, g, 0, [done % g.count])
+        oracle.ns_batched(workloads.bf16_bits_to_f32(bits).astype(np.float64), steps=NS_STEPS)
+        done += 1
         if time.perf_counter() - t0 > seconds:
             break
     dt = time.perf_counter() - t0
-    return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"fp64 numpy oracle, one full Muon step of {done_mats} matrices "
-                      f"({', '.join(used)}) in {dt:.1f} s; {done_mats / dt:.3f} matrices/s"}
+    info = host_info()
+    cores = info["blas_threads"] or info["affinity_cpus"] or info["os_cpu_count"] or 1
+    return {"value": round(done * ns_flops(768, 3072) / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"fp64 numpy oracle NS (5 iterations) of {done} of the 32 matrices 768x3072, one at a time, "
+                      f"in {dt:.1f} s: {done / dt:.3f} matrices/s, nominal flops",
+            "host": info}
+
+
+# ----------------------------------------------------------------------------- GPU parts
+class Timer:
+    """Library-recorded hipEvent timing of selected kernel families."""
+
+    def __init__(self, nsm, families):
+        self.nsm, self.families = nsm, list(families)
+
+    def __enter__(self):
+        self.nsm.muon_timing_collect()
+        self.nsm.muon_timing_enable(self.families)
+        return self
+
+    def __exit__(self, *exc):
+        import torch
+        torch.cuda.synchronize()
+        self.nsm.muon_timing_enable([])
+        self.result = self.nsm.muon_timing_collect(with_flops=True)
+        return False
+
+
+def timed_region(fn, steps):
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1000.0 / steps
+
+
+def per_call_ms(fn, steps, flush=None):
+    """Per-call event times on torch's current stream (the library launches
+    there); with `flush`, a 1 GiB write runs between calls (outside the events)."""
+    import torch
+    out = []
+    for _ in range(steps):
+        if flush is not None:
+            flush.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        e1.synchronize()
+        out.append(e0.elapsed_time(e1))
+    return out
+
+
+def headline(nsm, args, dev):
+    import torch
+    import workloads
+    wl = workloads.get_workload("metric32")
+    g = wl.groups[0]
+    x = workloads.grads_device(wl, g, 0, dev)
+    out = torch.empty_like(x)
+    call = lambda: nsm.ns_orthogonalize_batched(x, out, precision="fast")     # noqa: E731
+    # The automatic NS schedule times its first ten calls per set of shapes
+    # (alternating the per-product launches and the persistent loop) and keeps
+    # the faster once those calls' events have completed: let it settle.
+    for _ in range(SETTLE_CALLS):
+        call()
+        torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    ms = timed_region(call, args.steps)                       # uninstrumented: `value`
+    m, n, nb = g.rows, g.cols, g.count
+    nominal = nb * ns_flops(m, n)
+    res = {"ms": ms, "nominal": nominal, "nb": nb}
+    # per-call distribution, warm and with the Infinity Cache flushed between calls
+    res["warm"] = percentiles(per_call_ms(call, args.steps))
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    res["cold"] = percentiles(per_call_ms(call, args.steps, flush))
+    del flush
+    # the call's kernels, each launch bracketed by events (a region of its own)
+    with Timer(nsm, nsm.KERNEL_KINDS) as t:
+        for _ in range(args.steps):
+            call()
+    res["families"] = t.result
+    res["status"] = nsm.last_call_status(dev)
+    del x, out
+    return res
+
+
+def roofline_of(res, steps):
+    fam = res["families"]
+    ns = {k: v for k, v in fam.items() if k in NS_FAMILIES}
+    if not ns:
+        return None
+    k = max(ns, key=lambda f: ns[f][1])
+    launches, tot_ms, nominal = ns[k]
+    avg_ms = tot_ms / launches
+    nom = nominal / launches
+    r = {"bound": "mfma", "kernel": FAMILY_NAMES[k], "flops_basis": "nominal 5 (4 m^2 n + 2 m^3) per block",
+         "achieved": round(nom / (avg_ms / 1e3) / 1e12, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    r["frac"] = round(r["achieved"] / PEAK_BF16_TFLOPS, 4)
+    if k == "ns_loop":
+        per_block = nom / res["nb"]
+        assert abs(per_block - ns_flops(768, 3072)) < 1e-6 * per_block
+        ex = res["nb"] * loop_executed_flops(768, 3072)
+        alg = res["nb"] * ns_flops_symmetric(768, 3072)
+        r["achieved_executed"] = round(ex / (avg_ms / 1e3) / 1e12, 2)
+        r["frac_executed"] = round(r["achieved_executed"] / PEAK_BF16_TFLOPS, 4)
+        r["achieved_algorithmic"] = round(alg / (avg_ms / 1e3) / 1e12, 2)
+        r["frac_algorithmic"] = round(r["achieved_algorithmic"] / PEAK_BF16_TFLOPS, 4)
+        r["executed_flops_per_launch"] = ex
+        r["algorithmic_flops_per_launch"] = alg
+        r["mfma_busy_frac"] = load_profile("k_ns_loop_metric32_sq", GEMM_SOURCE, "mfma_busy_frac")
+        r["traffic"] = load_profile("k_ns_loop_metric32_traffic", GEMM_SOURCE, "bytes_per_launch")
+    else:
+        r["traffic"] = None
+    r.update({"launches": launches, "avg_launch_ms": round(avg_ms, 5), "flops_per_launch": nom,
+              "ns_family_ms_per_call": {f: round(v[1] / steps, 4) for f, v in ns.items()}})
+    total_reported = sum(v[2] for v in ns.values()) / steps
+    r["flops_accounted"] = abs(total_reported - res["nominal"]) <= 1e-9 * res["nominal"]
+    return r
+
+
+def gpt124m_step(nsm, args, dev):
+    """The full Muon step of the 124M custom-sizing set (muon_step_multi)."""
+    import torch
+    import workloads
+    wl = workloads.get_workload("gpt124m")
+    state = []
+    for g in wl.groups:
+        P = workloads.params_device(wl, g, dev)
+        state.append((g, P, workloads.grads_device(wl, g, 0, dev), torch.zeros_like(P)))
+    mats = [dict(params=P[i], grads=G[i], momentum_buf=M[i], view_blocks=g.view_blocks)
+            for g, P, G, M in state for i in range(g.count)]
+    step = lambda: nsm.muon_step_multi(mats, lr=wl.lr, weight_decay=wl.weight_decay,   # noqa: E731
+                                       momentum=wl.momentum, ns_steps=wl.ns_steps, precision="fast")
+    for _ in range(SETTLE_CALLS):
+        step()
+        torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step()
+    ms = timed_region(step, args.steps)
+    with Timer(nsm, nsm.KERNEL_KINDS) as t:
+        for _ in range(args.steps):
+            step()
+    fam = t.result
+    flops = sum(g.n_blocks * ns_flops(*g.block_shape) for g in wl.groups)
+    n_blocks = sum(g.n_blocks for g in wl.groups)
+    # the element-wise kernels (blocks on the matrix-core path): 12 B per
+    # element before NS (g 2, M 8, U 2), 10 B after (P 8, O 2)
+    mfma_elems = sum(g.count * g.rows * g.cols for g in wl.groups if min(g.block_shape) > 64)
+    out = {"workload": "124M GPT custom sizing: 11 gates 1x12 (fp32 small-block path) + 10 attn 768x3072 viewed "
+                       "as 4x768x768 + 22 mlp 768x3072; muon_step_multi, momentum 0.95 Nesterov, 5 NS steps, "
+                       "lr 0.05, wd 0, FAST",
+           "ms": round(ms, 4), "tflops_nominal": round(flops / (ms / 1e3) / 1e12, 2),
+           "mfma_peak_frac_nominal": round(flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "matrices_per_s": round(wl.n_matrices / (ms / 1e3), 1),
+           "matrices_per_s_excluding_gates": round(32 / (ms / 1e3), 1),
+           "ns_blocks_per_s": round(n_blocks / (ms / 1e3), 1),
+           "kernel_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in fam.items()}}
+    for kind, bpe, name in (("prep", 12, "k_prep"), ("finish", 10, "k_finish")):
+        if kind in fam:
+            n_l, tot = fam[kind][0], fam[kind][1]
+            gbs = bpe * mfma_elems / (tot / args.steps / 1e3) / 1e9
+            out[kind] = {"kernel": name, "bound": "hbm", "bytes_per_element": bpe, "elements": mfma_elems,
+                         "launches_per_step": n_l // args.steps, "ms_per_step": round(tot / args.steps, 4),
+                         "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": load_profile(f"{name}_gpt124m_traffic", EW_SOURCE, "bytes_per_step")}
+    out["status"] = nsm.last_call_status(dev)
+    del state, mats
+    return out
+
+
+def rank_shares(nsm, args, dev):
+    """One GPU's share of the 124M set under 8-way sharding by whole matrices:
+    2 attn matrices (8 blocks of 768x768) or 2 mlp matrices 768x3072, each a
+    muon_step_batched call."""
+    import torch
+    import workloads
+    wl = workloads.get_workload("gpt124m")
+    groups = {g.name: g for g in wl.groups}
+    out = {}
+    for name, gname in (("c3_share_attn", "attn"), ("c3_share_mlp", "mlp")):
+        g = groups[gname]
+        P = workloads.params_device(wl, g, dev)[:2].contiguous()
+        G = workloads.grads_device(wl, g, 0, dev)[:2].contiguous()
+        M = torch.zeros_like(P)
+        step = lambda: nsm.muon_step_batched(P, G, M, lr=wl.lr, weight_decay=wl.weight_decay,  # noqa: E731
+                                             momentum=wl.momentum, view_blocks=g.view_blocks,
+                                             ns_steps=wl.ns_steps, precision="fast")
+        for _ in range(SETTLE_CALLS):
+            step()
+            torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            step()
+        ms = timed_region(step, args.steps)
+        with Timer(nsm, nsm.KERNEL_KINDS) as t:
+            for _ in range(args.steps):
+                step()
+        flops = 2 * g.view_blocks * ns_flops(*g.block_shape)
+        out[name] = {"blocks": f"{2 * g.view_blocks} x {g.block_shape[0]}x{g.block_shape[1]}",
+                     "ms": round(ms, 4), "tflops_nominal": round(flops / (ms / 1e3) / 1e12, 2),
+                     "mfma_peak_frac_nominal": round(flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "kernel_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in t.result.items()}}
+        del P, G, M
+    return out
+
+
+def adamw_gpt124m(nsm, args, dev):
+    import torch
+    import workloads
+    awl = workloads.ADAM_WORKLOADS["gpt124m_adam"]
+    tens = []
+    for i in range(len(awl.tensors)):
+        P = workloads.adam_params_device(awl, i, dev)
+        tens.append(dict(params=P, grads=workloads.adam_grads_device(awl, i, 0, dev),
+                         exp_avg=torch.zeros_like(P), exp_avg_sq=torch.zeros_like(P), step=1))
+
+    def adam_step():
+        nsm.adamw_step_multi(tens, lr=awl.lr, betas=awl.betas, eps=awl.eps, weight_decay=awl.weight_decay)
+        for t in tens:
+            t["step"] += 1
+    for _ in range(3):
+        adam_step()
+    torch.cuda.synchronize()
+    with Timer(nsm, ["adamw"]) as t:
+        for _ in range(args.steps):
+            adam_step()
+    n_l, a_ms = t.result.get("adamw", (0, 0.0, 0.0))[:2]
+    del tens
+    if not n_l:
+        return None
+    ms = a_ms / n_l
+    gbs = 26.0 * awl.numel / (ms / 1e3) / 1e9
+    return {"kernel": "k_adamw", "elements": awl.numel, "launches": n_l, "avg_launch_ms": round(ms, 5),
+            "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_element": 26,
+            "traffic": load_profile("k_adamw_gpt124m_traffic", ADAM_SOURCE, "bytes_per_launch")}
 
 
 def main():
@@ -114,13 +414,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extras", action="store_true", help="skip the kernel breakdown and NS-only passes")
-    ap.add_argument("--api", choices=("multi", "batched"), default="multi",
-                    help="multi: one muon_step_multi call per step over all matrices (default); "
-                         "batched: one muon_step_batched call per shape group")
+    ap.add_argument("--no-extras", action="store_true", help="the headline call only")
+    ap.add_argument("--extras", default="step,shares,adamw",
+                    help="comma-separated extras: step (124M Muon step), shares (one GPU's 8-way share), adamw")
     ap.add_argument("--ns-schedule", choices=("auto", "persistent", "per_product"), default="auto",
                     help="auto: the library's per-shape choice (default); persistent: all NS iterations of "
-                         "a wave in one launch; per_product: three launches per iteration")
+                         "a call in one launch; per_product: three launches per iteration")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run a plain device copy of MIB MiB first (HBM counter calibration)")
     args = ap.parse_args()
@@ -132,7 +431,6 @@ def main():
 
     import torch
     import newton_schulz_muon_amd as nsm
-    import workloads
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -141,7 +439,6 @@ def main():
     nsm.muon_set_ns_schedule(args.ns_schedule)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    wl = workloads.get_workload(WORKLOAD)
 
     if args.copy_calibration > 0:
         n = args.copy_calibration * (1 << 20) // 4
@@ -152,199 +449,37 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    state = []
-    for g in wl.groups:
-        P = workloads.params_device(wl, g, dev)
-        G = workloads.grads_device(wl, g, 0, dev)
-        M = torch.zeros_like(P)
-        state.append((g, P, G, M))
-    torch.cuda.synchronize()
-
-    # every matrix of the workload, each a [rows, cols] slice of its group's stack
-    matrices = [dict(params=P[i], grads=G[i], momentum_buf=M[i], view_blocks=g.view_blocks)
-                for g, P, G, M in state for i in range(g.count)]
-
-    def step():
-        if args.api == "multi":
-            nsm.muon_step_multi(matrices, lr=wl.lr, weight_decay=wl.weight_decay, momentum=wl.momentum,
-                                ns_steps=wl.ns_steps, precision="fast")
-            return
-        for g, P, G, M in state:
-            nsm.muon_step_batched(P, G, M, lr=wl.lr, weight_decay=wl.weight_decay, momentum=wl.momentum,
-                                  view_blocks=g.view_blocks, ns_steps=wl.ns_steps, precision=g.precision)
-
-    # The library's automatic NS schedule times its first ten calls per set of
-    # shapes (alternating the per-product launches and the persistent loop)
-    # and keeps the faster one once those calls' events have completed: let it
-    # settle, synchronising after each call, before the warm-up proper.
-    for _ in range(SETTLE_CALLS):
-        step()
-        torch.cuda.synchronize()
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # ---- timed region: K steps, no instrumentation
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-
-    # ---- roofline region: the same K steps again, each launch of the NS
-    # kernel families bracketed by a hipEvent pair on the library's stream;
-    # the library reports each launch's nominal flops beside its time (with
-    # the automatic schedule one step may run some waves in the persistent
-    # loop and others per product).  Every event record costs a short
-    # dispatch bubble, which is why `value` comes from the uninstrumented
-    # region above.
-    nsm.muon_timing_collect()
-    nsm.muon_timing_enable(list(NS_FAMILIES))
-    torch.cuda.synchronize()
-    r0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    r1 = time.perf_counter()
-    nsm.muon_timing_enable([])
-    kt = nsm.muon_timing_collect(with_flops=True)
-
-    ms_per_step = (t1 - t0) * 1000.0 / args.steps
-    flops_step = sum(g.view_blocks * g.count * ns_flops(*g.block_shape, wl.ns_steps) for g in wl.groups)
-    n_blocks = sum(g.n_blocks for g in wl.groups)
-    value = flops_step / (ms_per_step / 1000.0) / 1e12
-
-    # Blocks with m <= 64 and m n <= 8192 take the one-launch fp32 small-block
-    # path and issue no B'X launch.
-    mfma_groups = [g for g in wl.groups
-                   if not (min(g.block_shape) <= 64 and g.block_shape[0] * g.block_shape[1] <= 8192)]
-    # Every MFMA-path NS flop of the step is reported by exactly one family.
-    mfma_flops_step = sum(g.n_blocks * ns_flops(*g.block_shape, wl.ns_steps) for g in mfma_groups)
-    reported_step = sum(v[2] for v in kt.values()) / args.steps
-    roofline = None
-    if kt:
-        # dominant kernel: the NS family with the most time per step
-        fam = max(kt, key=lambda k: kt[k][1])
-        launches, fam_ms, fam_flops = kt[fam]
-        achieved = fam_flops / (fam_ms / 1000.0) / 1e12
-        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                    "traffic": load_traffic(TRAFFIC_FILES.get(fam)) if fam in TRAFFIC_FILES else None,
-                    "kernel": NS_FAMILIES[fam],
-                    "launches": launches, "avg_launch_ms": round(fam_ms / launches, 5),
-                    "flops_per_launch_avg": fam_flops / launches,
-                    "region_ms_per_step": round((r1 - r0) * 1000.0 / args.steps, 4),
-                    "ns_family_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in kt.items()},
-                    "ns_family_tflops": {k: round(v[2] / (v[1] / 1000.0) / 1e12, 2) for k, v in kt.items()},
-                    "flops_accounted": abs(reported_step - mfma_flops_step) <= 1e-9 * mfma_flops_step}
-
+    h = headline(nsm, args, dev)
+    value = h["nominal"] / (h["ms"] / 1e3) / 1e12
+    fams = h["families"]
+    used = "persistent" if "ns_loop" in fams else "per_product"
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(h["ms"], 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "124M GPT custom sizing: 11 gates 1x12 + 10 attn 768x3072 viewed as "
-                               "4x768x768 + 22 mlp 768x3072; full Muon step (momentum 0.95 Nesterov, "
-                               "5 NS steps, lr 0.05, wd 0)",
-                   "matrices": wl.n_matrices, "ns_blocks": n_blocks, "ns_steps": wl.ns_steps,
-                   "precision": "fast (bf16 MFMA, fp32 accumulate); gates on the fp32 small-block path",
-                   "nominal_ns_gflop_per_step": round(flops_step / 1e9, 2)},
-        "ns_schedule": args.ns_schedule, "settle_calls": SETTLE_CALLS,
-        "matrices_per_s": round(wl.n_matrices / (ms_per_step / 1000.0), 1),
-        "ns_blocks_per_s": round(n_blocks / (ms_per_step / 1000.0), 1),
+        "config": {"workload": "32 matrices 768x3072 bf16 ~N(0, 0.01^2), one ns_orthogonalize_batched call, "
+                               "FAST (bf16 MFMA, fp32 accumulate), 5 quintic NS iterations",
+                   "matrices": h["nb"], "ns_steps": NS_STEPS, "precision": "fast",
+                   "nominal_ns_gflop_per_call": round(h["nominal"] / 1e9, 2), "ns_schedule": args.ns_schedule,
+                   "ns_schedule_used": used},
+        "matrices_per_s": round(h["nb"] / (h["ms"] / 1e3), 1),
         "mfma_peak_frac_nominal": round(value / PEAK_BF16_TFLOPS, 4),
-        "roofline": roofline,
+        "call_ms_percentiles": {"warm": h["warm"], "cold_infinity_cache": h["cold"]},
+        "kernel_ms_per_call": {k: round(v[1] / args.steps, 4) for k, v in fams.items()},
+        "status": list(h["status"]),
+        "roofline": roofline_of(h, args.steps),
     }
-
     if not args.no_extras:
-        # ---- attribution pass (separate from the timed region): every kernel family timed
-        nsm.muon_timing_enable(list(nsm.KERNEL_KINDS))
-        for _ in range(args.steps):
-            step()
-        torch.cuda.synchronize()
-        nsm.muon_timing_enable([])
-        allk = nsm.muon_timing_collect()
-        result["kernel_ms_per_step"] = {k: round(v[1] / args.steps, 4) for k, v in allk.items()}
-        ew_bytes = sum(g.count * g.rows * g.cols for g in mfma_groups)
-        if "prep" in allk:
-            prep_ms = allk["prep"][1] / args.steps
-            result["prep_hbm_gbs"] = round(12.0 * ew_bytes / (prep_ms / 1000.0) / 1e9, 1)
-        if "finish" in allk:
-            fin_ms = allk["finish"][1] / args.steps
-            result["finish_hbm_gbs"] = round(10.0 * ew_bytes / (fin_ms / 1000.0) / 1e9, 1)
-        # ---- NS only on the metric's exact batch: 32 x 768 x 3072, no view
-        x = workloads.grads_device(workloads.get_workload("metric32"), workloads.get_workload("metric32").groups[0], 0, dev)
-        out = torch.empty_like(x)
-        for _ in range(SETTLE_CALLS):
-            nsm.ns_orthogonalize_batched(x, out)
-            torch.cuda.synchronize()
-        for _ in range(3):
-            nsm.ns_orthogonalize_batched(x, out)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(args.steps):
-            nsm.ns_orthogonalize_batched(x, out)
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / args.steps
-        # a second pass with every kernel family bracketed by hipEvents (its
-        # own region: the events add dispatch bubbles)
-        nsm.muon_timing_collect()
-        nsm.muon_timing_enable(list(nsm.KERNEL_KINDS))
-        for _ in range(args.steps):
-            nsm.ns_orthogonalize_batched(x, out)
-        torch.cuda.synchronize()
-        nsm.muon_timing_enable([])
-        fam = nsm.muon_timing_collect()
-        used = "persistent" if "ns_loop" in fam else "per_product"
-        f = 32 * ns_flops(768, 3072, 5)
-        ns_kernels = [k for k in ("ns_loop", "gram", "poly", "bx") if k in fam]
-        ns_ms = sum(fam[k][1] for k in ns_kernels) / args.steps
-        result["ns_only_32x768x3072"] = {"ms": round(ms, 4), "tflops": round(f / (ms / 1000) / 1e12, 2),
-                                         "schedule": used,
-                                         "kernel_ms_per_call": {k: round(v[1] / args.steps, 4) for k, v in fam.items()},
-                                         "ns_kernels_tflops": round(f / (ns_ms / 1000) / 1e12, 2),
-                                         "ns_kernels_frac": round(f / (ns_ms / 1000) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                                         "matrices_per_s": round(32 / (ms / 1000), 1),
-                                         "mfma_peak_frac_nominal": round(f / (ms / 1000) / 1e12 / PEAK_BF16_TFLOPS, 4)}
-        del x, out
-        # ---- AdamW for the same model's embedding, head and scalars (the other
-        # optimizer of the step): 26 bytes of HBM traffic per element.
-        awl = workloads.ADAM_WORKLOADS["gpt124m_adam"]
-        tens = []
-        for i in range(len(awl.tensors)):
-            P = workloads.adam_params_device(awl, i, dev)
-            tens.append(dict(params=P, grads=workloads.adam_grads_device(awl, i, 0, dev),
-                             exp_avg=torch.zeros_like(P), exp_avg_sq=torch.zeros_like(P), step=1))
-
-        def adam_step():
-            nsm.adamw_step_multi(tens, lr=awl.lr, betas=awl.betas, eps=awl.eps, weight_decay=awl.weight_decay)
-            for t in tens:
-                t["step"] += 1
-        for _ in range(3):
-            adam_step()
-        torch.cuda.synchronize()
-        nsm.muon_timing_enable(["adamw"])
-        for _ in range(args.steps):
-            adam_step()
-        torch.cuda.synchronize()
-        nsm.muon_timing_enable([])
-        n_l, a_ms = nsm.muon_timing_collect().get("adamw", (0, 0.0))
-        if n_l:
-            ms = a_ms / n_l
-            gbs = 26.0 * awl.numel / (ms / 1000.0) / 1e9
-            result["adamw_gpt124m"] = {"kernel": "k_adamw", "elements": awl.numel, "launches": n_l,
-                                       "avg_launch_ms": round(ms, 5), "bound": "hbm", "achieved": round(gbs, 1),
-                                       "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                                       "traffic": load_traffic(ADAM_TRAFFIC_FILE, ADAM_SOURCE),
-                                       "bytes_per_element": 26}
-        del tens
-
+        want = set(x.strip() for x in args.extras.split(",") if x.strip())
+        if "step" in want:
+            result["gpt124m_step"] = gpt124m_step(nsm, args, dev)
+        if "shares" in want:
+            result["rank_share_8way"] = rank_shares(nsm, args, dev)
+        if "adamw" in want:
+            result["adamw_gpt124m"] = adamw_gpt124m(nsm, args, dev)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
-
+        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

@@ -837,7 +837,7 @@ __global__ __launch_bounds__(tile_threads<BT>()) void k_gemm(GemmArgs args) {
 // running workgroup, so the lowest unfinished item can always proceed.
 //
 // Failure is loud.  A wait longer than spin_ticks sets the error word, and a
-// workgroup that finds the error word set takes no further item.  The last
+// workgroup that finds it set while waiting takes no further item.  The last
 // workgroup to leave checks every block's counter: the final iterate of each
 // block that did not complete all of its tiles is overwritten with NaN, and
 // the number of such blocks and the error flags are added to the call's
@@ -1028,19 +1028,24 @@ __global__ __launch_bounds__(tile_threads<256>()) void k_ns_loop(PersistArgs arg
                 const uint32_t need = t * (2 * pr.nsym + pr.nbx) + (ph >= 1 ? pr.nsym : 0u) + (ph >= 2 ? pr.nsym : 0u);
                 uint32_t* const done = pr.done + kSyncStride * (g - pr.first_blk);
                 const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-                // The error word is read with every poll, so a set word stops
-                // the workgroup at its next item even when that item's
-                // dependencies are met.
+                // The error word is read only while waiting: a workgroup whose
+                // dependencies are met keeps going (the final check marks
+                // every block left incomplete); with `inject` every workgroup
+                // stops at its first item.
                 for (;;) {
+                    if (args.inject) {
+                        it.x = kItemEnd;
+                        break;
+                    }
                     const uint32_t d = __builtin_amdgcn_readfirstlane(
                         __hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+                    if (d >= need) break;
                     const uint32_t e = __builtin_amdgcn_readfirstlane(
                         __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
                     if (e != 0u) {
                         it.x = kItemEnd;
                         break;
                     }
-                    if (d >= need) break;
                     if (__builtin_amdgcn_s_memrealtime() - t0 > args.spin_ticks) {
                         if (lane0) __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                         it.x = kItemEnd;
