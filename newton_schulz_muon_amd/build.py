@@ -96,7 +96,22 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     tmp = LIB_PATH + ".tmp"
     _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB_PATH)
+    build_test_kernels(cc)
     return LIB_PATH
+
+
+def build_test_kernels(cc: str) -> None:
+    """Test-only HIP kernels (tests/kernels/*.hip), each its own shared library
+    beside the tests; the library above does not contain them."""
+    src_dir = os.path.join(ROOT, "tests", "kernels")
+    if not os.path.isdir(src_dir):
+        return
+    for src in sorted(os.listdir(src_dir)):
+        if not src.endswith(".hip"):
+            continue
+        out = os.path.join(ROOT, "tests", "lib" + os.path.splitext(src)[0] + ".so")
+        _run([cc, *COMMON_FLAGS, "-shared", os.path.join(src_dir, src), "-o", out + ".tmp"])
+        os.replace(out + ".tmp", out)
 
 
 if __name__ == "__main__":

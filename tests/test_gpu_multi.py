@@ -5,7 +5,9 @@ oracle the other GPU tests establish), whatever the grouping and launch
 sharing.  Cases: the 124M custom-sizing set (gates, attn view, mlp: B'X and
 the polynomial of attn and mlp share launches), mixed shapes with per-matrix
 lr_mul / wd_mul and tall blocks, ACCURATE precision, and a shape group larger
-than one pointer table."""
+than one pointer table.  The 124M set, in the call the benchmark times (one
+muon_step_multi over all 43 matrices), is also checked against the fp64
+oracle directly."""
 import pytest
 
 import workloads
@@ -140,3 +142,54 @@ def test_multi_merged_conv_kernels_match_oracle(nsm):
     with pytest.raises(ValueError):
         nsm.muon_step_multi([dict(params=bad, grads=bad.to(torch.bfloat16), momentum_buf=bad.clone())],
                             lr=0.02, weight_decay=0.0, momentum=0.95)
+
+
+@pytest.mark.timeout(600)
+def test_multi_gpt124m_set_matches_oracle(nsm):
+    """One muon_step_multi over the 43 matrices of the 124M custom-sizing set
+    (11 gates 1x12, 10 attn 768x3072 with view 4, 22 mlp 768x3072), 3 steps of
+    the workload's settings, every matrix against the fp64 oracle after every
+    step: NS output (update_out), momentum buffer and parameters."""
+    import numpy as np
+    import torch
+    import oracle
+    from parity import MOMENTUM_TOL, NS_REL_TOL, assert_ns_close, bits_to_f64, rel_fro, torch_bf16_to_bits
+    wl = workloads.get_workload("gpt124m")
+    mats, refs = [], []
+    for grp in wl.groups:
+        P_host = workloads.param_init_host(wl, grp)
+        for i in range(grp.count):
+            P = torch.from_numpy(P_host[i].copy()).cuda()
+            mats.append(dict(params=P, grads=None, momentum_buf=torch.zeros_like(P),
+                             update_out=torch.empty(P.shape, dtype=torch.bfloat16, device="cuda"),
+                             view_blocks=grp.view_blocks))
+            refs.append(dict(grp=grp, i=i, P=P_host[i].astype(np.float64), M=np.zeros(P.shape), bound=0.0))
+    worst = 0.0
+    for t in range(wl.steps):
+        print(f"[multi oracle] 124M set step {t}", flush=True)
+        bits = {}
+        for grp in wl.groups:
+            bits[grp.name] = workloads.grad_bits_host(wl, grp, t)
+        for m, r in zip(mats, refs):
+            m["grads"] = workloads.to_device_bf16(bits[r["grp"].name][r["i"]])
+        nsm.muon_step_multi(mats, lr=wl.lr, weight_decay=wl.weight_decay, momentum=wl.momentum,
+                            ns_steps=wl.ns_steps, precision="fast")
+        torch.cuda.synchronize()
+        for m, r in zip(mats, refs):
+            grp = r["grp"]
+            g = bits_to_f64(bits[grp.name][r["i"]])
+            P_new, M_new, O_ref = oracle.muon_step(r["P"][None], g[None], r["M"][None], lr=wl.lr,
+                                                   weight_decay=wl.weight_decay, momentum=wl.momentum,
+                                                   view_blocks=grp.view_blocks, ns_steps=wl.ns_steps)
+            label = f"{grp.name}[{r['i']}] step {t}"
+            rel, _ = assert_ns_close(bits_to_f64(torch_bf16_to_bits(m["update_out"])), O_ref[0], grp.view_blocks,
+                                     sigma=(t == 0), label=label)
+            worst = max(worst, rel)
+            em = rel_fro(m["momentum_buf"].cpu().numpy(), M_new[0])
+            assert em <= MOMENTUM_TOL, f"momentum {label}: {em:.3e}"
+            lr_eff = float(np.float32(wl.lr)) * oracle.aspect_factor(grp.rows, grp.cols)
+            r["bound"] += NS_REL_TOL * lr_eff * np.linalg.norm(O_ref) + 4 * 2.0 ** -24 * np.linalg.norm(P_new)
+            ep = np.linalg.norm(m["params"].cpu().numpy() - P_new[0])
+            assert ep <= r["bound"], f"params {label}: {ep:.3e} > {r['bound']:.3e}"
+            r["P"], r["M"] = P_new[0], M_new[0]
+    print(f"[multi oracle] worst NS relative error over 43 matrices x {wl.steps} steps: {worst:.3e}", flush=True)

@@ -105,43 +105,103 @@ def test_step_gpt124m(nsm):
     _run_host_workload(nsm, workloads.get_workload("gpt124m"), sigma_every=False)
 
 
+@pytest.mark.timeout(900)
 def test_step_gpt2_medium_sampled(nsm):
     """96 matrices (48 wide 1024x4096, 48 stored tall 4096x1024), heavy-tailed
-    rows, 20 steps on the GPU; the oracle follows one wide and one tall matrix
-    through all 20 steps (momentum and parameters every step, NS output at the
-    first and the last step)."""
+    rows, 20 steps on the GPU.  The oracle follows 8 of the 96 (4 wide, 4 tall)
+    through all 20 steps (parameters every step, NS output at the first and the
+    last step) and checks the momentum buffer of all 96 matrices after every
+    step."""
     import torch
     wl = workloads.get_workload("gpt2_medium")
-    sample = {0: [17], 1: [30]}
+    sample = {0: [0, 17, 33, 47], 1: [5, 30, 41, 47]}
     for gi, grp in enumerate(wl.groups):
         P = workloads.params_device(wl, grp)
         M = torch.zeros_like(P)
         O = torch.empty(P.shape, dtype=torch.bfloat16, device="cuda")
         idx = sample[gi]
         P_ref = P[idx].cpu().numpy().astype(np.float64)
-        M_ref = np.zeros_like(P_ref)
+        M_all = np.zeros((grp.count, grp.rows, grp.cols), np.float64)   # the oracle's buffers of every matrix
         bound = 0.0
+        worst_m = 0.0
         for t in range(wl.steps):
             print(f"[step parity] gpt2_medium/{grp.name} step={t}", flush=True)
             G = workloads.grads_device(wl, grp, t)
-            g_host = bits_to_f64(torch_bf16_to_bits(G[idx]))
+            g_bits = torch_bf16_to_bits(G)
             nsm.muon_step_batched(P, G, M, lr=wl.lr, weight_decay=wl.weight_decay,
                                   momentum=wl.momentum, update_out=O)
             torch.cuda.synchronize()
             need_ns = t in (0, wl.steps - 1)
-            M_new, U = oracle.nesterov_momentum(g_host, M_ref, wl.momentum)
-            O_ref = np.stack([oracle.newton_schulz(u) for u in U])
+            M_gpu = M.cpu().numpy()
+            U_s = {}
+            for i in range(grp.count):
+                M_all[i], U = oracle.nesterov_momentum(bits_to_f64(g_bits[i]), M_all[i], wl.momentum)
+                em = rel_fro(M_gpu[i], M_all[i])
+                assert em <= MOMENTUM_TOL, f"momentum {grp.name}[{i}] step {t}: {em:.3e}"
+                worst_m = max(worst_m, em)
+                if i in idx:
+                    U_s[i] = U
+            O_ref = np.stack([oracle.newton_schulz(U_s[i]) for i in idx])
             P_new = np.stack([oracle.muon_update(P_ref[k], O_ref[k], wl.lr, wl.weight_decay)
                               for k in range(len(idx))])
-            M_got = M[idx].cpu().numpy()
-            for k in range(len(idx)):
-                assert rel_fro(M_got[k], M_new[k]) <= MOMENTUM_TOL
-                if need_ns:
-                    assert_ns_close(bits_to_f64(torch_bf16_to_bits(O[idx[k]])), O_ref[k],
-                                    label=f"{grp.name}[{idx[k]}] step {t}")
+            if need_ns:
+                O_bits = torch_bf16_to_bits(O[idx])
+                for k in range(len(idx)):
+                    assert_ns_close(bits_to_f64(O_bits[k]), O_ref[k], label=f"{grp.name}[{idx[k]}] step {t}")
             lr_eff = float(np.float32(wl.lr)) * oracle.aspect_factor(grp.rows, grp.cols)
             bound += NS_REL_TOL * lr_eff * np.linalg.norm(O_ref) + 4 * 2.0 ** -24 * np.linalg.norm(P_new)
             ep = np.linalg.norm(P[idx].cpu().numpy() - P_new)
             assert ep <= bound, (t, ep, bound)
-            P_ref, M_ref = P_new, M_new
+            P_ref = P_new
             del G
+        print(f"[step parity] gpt2_medium/{grp.name}: worst momentum {worst_m:.3e} over {grp.count} matrices",
+              flush=True)
+
+
+@pytest.mark.timeout(900)
+def test_step_large_dense_accurate(nsm):
+    """The large dense batch (8 x 4096^2 and 8 x 4096x14336, spectra 1/i) as
+    full Muon steps in ACCURATE precision, 2 steps: the momentum buffers of all
+    16 matrices against the oracle after each step, and one matrix per group
+    (2 of 16) followed through both steps by the oracle (NS output, params)."""
+    import torch
+    wl = workloads.get_workload("large_dense")
+    sample = {"sq": 3, "wide": 6}
+    for grp in wl.groups:
+        P = workloads.params_device(wl, grp)
+        M = torch.zeros_like(P)
+        O = torch.empty(P.shape, dtype=torch.bfloat16, device="cuda")
+        k = sample[grp.name]
+        P_ref = P[k].cpu().numpy().astype(np.float64)
+        M_all = np.zeros((grp.count, grp.rows, grp.cols), np.float64)
+        bound = 0.0
+        for t in range(wl.steps):
+            print(f"[step parity] large_dense/{grp.name} {grp.count}x{grp.rows}x{grp.cols} {grp.precision} "
+                  f"step={t}", flush=True)
+            G = workloads.grads_device(wl, grp, t)
+            g_bits = torch_bf16_to_bits(G)
+            nsm.muon_step_batched(P, G, M, lr=wl.lr, weight_decay=wl.weight_decay, momentum=wl.momentum,
+                                  precision=grp.precision, update_out=O)
+            torch.cuda.synchronize()
+            M_gpu = M.cpu().numpy()
+            U_k = None
+            for i in range(grp.count):
+                M_all[i], U = oracle.nesterov_momentum(bits_to_f64(g_bits[i]), M_all[i], wl.momentum)
+                em = rel_fro(M_gpu[i], M_all[i])
+                assert em <= MOMENTUM_TOL, f"momentum {grp.name}[{i}] step {t}: {em:.3e}"
+                if i == k:
+                    U_k = U
+            del M_gpu, g_bits
+            O_ref = oracle.newton_schulz(U_k)
+            print(f"[step parity] large_dense/{grp.name}[{k}] step {t}: oracle done", flush=True)
+            rel, sig = assert_ns_close(bits_to_f64(torch_bf16_to_bits(O[k])), O_ref,
+                                       label=f"large_dense {grp.name}[{k}] step {t}")
+            print(f"[step parity] large_dense/{grp.name}[{k}] step {t}: rel {rel:.3e} sigma {sig:.3e}", flush=True)
+            P_new = oracle.muon_update(P_ref, O_ref, wl.lr, wl.weight_decay)
+            lr_eff = float(np.float32(wl.lr)) * oracle.aspect_factor(grp.rows, grp.cols)
+            bound += NS_REL_TOL * lr_eff * np.linalg.norm(O_ref) + 4 * 2.0 ** -24 * np.linalg.norm(P_new)
+            ep = np.linalg.norm(P[k].cpu().numpy() - P_new)
+            assert ep <= bound, (grp.name, t, ep, bound)
+            P_ref = P_new
+            del G
+        del P, M, O
