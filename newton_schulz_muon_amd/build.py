@@ -42,10 +42,11 @@ SOURCE_FLAGS = {"ns_gemm.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=Non
 NO_SCRATCH_SOURCES = ("ns_gemm.hip",)
 
 
-def _check_no_scratch(src: str, out: str) -> None:
-    """Raises if the resource remarks in `out` show a kernel using scratch."""
+def _kernels_with_scratch(out: str):
+    """Kernels whose resource remarks in `out` report a private segment."""
     name = None
     seen = 0
+    found = []
     for line in out.splitlines():
         m = re.search(r"Function Name: (\S+)", line)
         if m:
@@ -55,9 +56,31 @@ def _check_no_scratch(src: str, out: str) -> None:
         if m:
             seen += 1
             if int(m.group(1)) != 0:
-                raise RuntimeError(f"{src}: kernel {name} uses {m.group(1)} bytes of scratch per lane")
+                found.append(name)
     if seen == 0:
-        raise RuntimeError(f"{src}: no kernel resource report in the compiler output")
+        raise RuntimeError("no kernel resource report in the compiler output")
+    return found
+
+
+def _check_no_scratch(src: str, out: str, cc: str, flags) -> None:
+    """Raises if a kernel of `src` accesses scratch memory.  A kernel may
+    reserve a private segment that its code never touches (the register
+    allocator's emergency slot beside SGPR spills to VGPR lanes); such a
+    kernel is accepted only when its generated code holds no scratch access."""
+    found = _kernels_with_scratch(out)
+    if not found:
+        return
+    asm = subprocess.run([cc, *flags, "--cuda-device-only", "-S", "-o", "-", os.path.join(CSRC, src)],
+                         stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
+    if asm.returncode != 0:
+        raise RuntimeError(f"{src}: device assembly failed")
+    for name in found:
+        body = asm.stdout.split(f"\n{name}:", 1)
+        if len(body) < 2:
+            raise RuntimeError(f"{src}: kernel {name} not found in the device assembly")
+        code = body[1].split("s_endpgm", 1)[0]
+        if re.search(r"\bscratch_|\bbuffer_\w+ [^\n]*s\[0:3\]|flat_\w+", code):
+            raise RuntimeError(f"{src}: kernel {name} accesses scratch memory")
 
 
 def hipcc() -> str:
@@ -88,7 +111,8 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
         outs = list(ex.map(_run, cmds))
     for src, out in zip(SOURCES, outs):
         if src in NO_SCRATCH_SOURCES:
-            _check_no_scratch(src, out)
+            _check_no_scratch(src, out, cc, [f for f in COMMON_FLAGS + SOURCE_FLAGS.get(src, [])
+                                             if not f.startswith("-Rpass")])
     if verbose:
         for o in outs:
             if o.strip():

@@ -347,7 +347,7 @@ muon_status run_ns(const Plan& p, const muon_ns_config& cfg, const Buffers& b, c
     *final_idx = cfg.ns_steps & 1;
     ns_schedule_start(ch, s);
     if (ch.persistent) {
-        const NsLoopProblem lp{&p, ends.x0, {b.xh[0], b.xh[1]}, ends.xlast, b.a, b.bh, b.scale, b.sync};
+        const NsLoopProblem lp{&p, ends.x0, {b.xh[0], b.xh[1]}, ends.xlast, b.a, b.bh, b.scale, b.sync, {b.xl[0], b.xl[1]}, b.bl};
         e = timed(MUON_KERNEL_NS_LOOP, s, [&] {
             return launch_ns_loop(&lp, 1, cfg.ns_steps, cfg.a, cfg.b, cfg.c, ch, items, items_cap, status, s);
         }, ns_flops(p, cfg.ns_steps));
@@ -637,7 +637,7 @@ muon_status ns_batched_impl(const void* x, void* out, int64_t batch, int64_t row
     const Buffers b = carve(p, ws + kHeaderBytes);
     const NsEnds ends = ns_ends(p, cfg, b, x, out);
     // The schedule (and on first use its queue) is settled before anything is enqueued.
-    const NsLoopProblem lp{&p, ends.x0, {b.xh[0], b.xh[1]}, ends.xlast, b.a, b.bh, b.scale, b.sync};
+    const NsLoopProblem lp{&p, ends.x0, {b.xh[0], b.xh[1]}, ends.xlast, b.a, b.bh, b.scale, b.sync, {b.xl[0], b.xl[1]}, b.bl};
     const NsChoice ch = per_product_only ? NsChoice() : ns_schedule_begin(&lp, 1, cfg.ns_steps, s);
     hipError_t e = timed(MUON_KERNEL_PREP, s, [&] {
         return launch_prep(p, kPrepCast, static_cast<const uint16_t*>(x), nullptr, 0.f,
@@ -780,7 +780,7 @@ muon_status muon_step_batched(float* params, const void* grads, float* momentum_
     uint32_t* status = reinterpret_cast<uint32_t*>(ws);
     const Buffers b = carve(p, ws + kHeaderBytes);
     const NsEnds ends = ns_ends(p, cfg, b, nullptr, nullptr);
-    const NsLoopProblem lp{&p, ends.x0, {b.xh[0], b.xh[1]}, ends.xlast, b.a, b.bh, b.scale, b.sync};
+    const NsLoopProblem lp{&p, ends.x0, {b.xh[0], b.xh[1]}, ends.xlast, b.a, b.bh, b.scale, b.sync, {b.xl[0], b.xl[1]}, b.bl};
     const NsChoice ch = ns_schedule_begin(&lp, 1, cfg.ns_steps, s);
     hipError_t e = timed(MUON_KERNEL_PREP, s, [&] {
         return launch_prep(p, mode, static_cast<const uint16_t*>(grads), momentum_buf, momentum, b.xh[0], b.xl[0],
@@ -848,7 +848,8 @@ muon_status muon_step_multi(const muon_matrix* mats, int32_t count, float lr, fl
         const Buffers& bb = bufs[gi];
         wave_groups[g.wave].push_back(gi);
         wave_lps[g.wave].push_back(
-            NsLoopProblem{&g.plan, bb.xh[0], {bb.xh[0], bb.xh[1]}, bb.xh[cfg.ns_steps & 1], bb.a, bb.bh, bb.scale, bb.sync});
+            NsLoopProblem{&g.plan, bb.xh[0], {bb.xh[0], bb.xh[1]}, bb.xh[cfg.ns_steps & 1], bb.a, bb.bh, bb.scale, bb.sync,
+                          {bb.xl[0], bb.xl[1]}, bb.bl});
     }
     for (int w = 0; w < nwaves; ++w)
         choices[w] = ns_schedule_begin(wave_lps[w].data(), int(wave_lps[w].size()), cfg.ns_steps, s);

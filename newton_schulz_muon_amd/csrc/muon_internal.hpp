@@ -157,7 +157,9 @@ hipError_t launch_bx(const Plan& p, const uint16_t* b_hi, const uint16_t* b_lo, 
 // ns_loop_sync_bytes(nb) (the launch zeroes it first).  Iteration 0 reads x0,
 // iteration t > 0 reads x[t % 2]; every iteration but the last writes
 // x[(t + 1) % 2] and the last writes xlast; the first one applies `scale` as
-// the per-product launches do.
+// the per-product launches do.  ACCURATE adds the lo planes: iteration t
+// reads xlo[t % 2] and writes xlo[(t + 1) % 2] (so x0 = x[0], xlast =
+// x[ns_steps % 2] there), and B' is stored as b + blo.
 struct NsLoopProblem {
     const Plan* plan;
     const uint16_t* x0;
@@ -167,12 +169,14 @@ struct NsLoopProblem {
     uint16_t* b;
     const float* scale;
     uint32_t* sync;
+    uint16_t* xlo[2];       // ACCURATE: lo planes of the iterates (null for FAST)
+    uint16_t* blo;          // ACCURATE: lo plane of B' (null for FAST)
 };
 constexpr int kMaxNsLoopProblems = 8;
 // Queue entries the loop needs in the workspace for these block batches and
-// step count: 0 when the loop does not take them (it needs FAST precision,
-// both padded sides multiples of 256, 1 <= ns_steps <= 255, at most
-// kMaxNsLoopProblems batches and at most 2^22 entries).
+// step count: 0 when the loop does not take them (it needs one precision for
+// all of them, both padded sides multiples of 256, 1 <= ns_steps <= 255, at
+// most kMaxNsLoopProblems batches and at most 2^22 entries).
 uint64_t ns_loop_items_cap(const Plan* const* plans, int n, int ns_steps);
 bool ns_loop_eligible(const NsLoopProblem* probs, int n, int ns_steps);
 // Which schedule runs the NS iterations of these problems on stream s (see

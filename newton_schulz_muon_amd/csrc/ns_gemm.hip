@@ -18,6 +18,12 @@
 // their column panels, and poly and bx read every operand as a k-major panel
 // (k rows of 2 BT contiguous bytes: whole cache lines), like X in B X.
 //
+// ACCURATE precision keeps B' and X as bf16 hi + lo pairs; its B X product
+// Bh Xh + Bh Xl + Bl Xh is one product over a reduction three times as long,
+// [Bh | Bh | Bl] [Xh; Xl; Xh], whose segments are read from the three pairs
+// of planes in turn (so every tiling accumulates a 32 x 32 output block in
+// the same order, and a stage holds two operand tiles, as for FAST).
+//
 // Tiling: a workgroup computes a BT x BT output tile, BT = 256 with 8 waves of
 // 128 x 64 (two per SIMD) or BT = 128 with 4 waves of 64 x 64, each wave's
 // part a grid of v_mfma_f32_32x32x16_bf16 accumulators.  K steps by 32
@@ -192,21 +198,29 @@ __device__ __forceinline__ int col_off(int row, int col) {
     return row * (2 * C) + (((col >> 3) ^ ((row & 3) << 2)) << 4) + (((col >> 2) & 1) << 3);
 }
 
-template <int C, int BK_, int NW>
+template <int C, int BK_, int NW, int LO_SEG = -1>
 struct ColDma {
     static constexpr int BK = BK_;
     static constexpr int ROWS_PER_WIN = 512 / C;
     static constexpr int PW = BK / ROWS_PER_WIN / NW;  // 1 KB windows per wave
     static_assert(PW >= 1 && PW * ROWS_PER_WIN * NW == BK, "slice splits evenly over the waves");
+    // LO_SEG >= 0: the reduction runs over three segments of seg_k rows each,
+    // segment LO_SEG read from `lo` and the other two from `base` (same
+    // layout); k0 counts over all of them.
     const void* base;
+    const void* lo;
     uint32_t bytes;
     uint32_t ldb;                                      // row pitch in bytes
+    int seg_k;
     uint32_t voff[PW];
 
-    __device__ __forceinline__ void init(const void* base_, uint32_t bytes_, int64_t ld, int col0, int tid) {
+    __device__ __forceinline__ void init(const void* base_, uint32_t bytes_, int64_t ld, int col0, int tid,
+                                         const void* lo_ = nullptr, int seg_k_ = 0) {
         base = base_;
+        lo = lo_;
         bytes = bytes_;
         ldb = static_cast<uint32_t>(ld * 2);
+        seg_k = seg_k_;
         const int w = tid >> 6, l = tid & 63;
 #pragma unroll
         for (int q = 0; q < PW; ++q) {
@@ -217,13 +231,26 @@ struct ColDma {
     }
     __device__ __forceinline__ void load_q(char* lds, int k0, int q, int tid) const {
         const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-        dma16(make_rsrc(base, bytes), voff[q], static_cast<uint32_t>(k0) * ldb, lds + (w * PW + q) * 1024);
+        if constexpr (LO_SEG >= 0) {
+            // k0 is uniform: the segment and its base are kept in scalar registers
+            const int s = (k0 >= seg_k) + (k0 >= 2 * seg_k);
+            const uint64_t bp = reinterpret_cast<uint64_t>(s == LO_SEG ? lo : base);
+            // readfirstlane returns int: widen through uint32_t (a sign extension
+            // would set the high address word whenever bit 31 is set)
+            const uint32_t b_lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(bp)));
+            const uint32_t b_hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(bp >> 32)));
+            const uint64_t bs = uint64_t(b_lo) | (uint64_t(b_hi) << 32);
+            const uint32_t soff = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(k0 - s * seg_k) * ldb);
+            dma16(make_rsrc(reinterpret_cast<const void*>(bs), bytes), voff[q], soff, lds + (w * PW + q) * 1024);
+        } else {
+            dma16(make_rsrc(base, bytes), voff[q], static_cast<uint32_t>(k0) * ldb, lds + (w * PW + q) * 1024);
+        }
     }
 };
 
 // The operands of one kernel: NA tiles for the output rows and NB tiles for
-// the output columns (1 + 1, or 2 + 2 hi/lo planes for the split B X).  Each
-// is either k-contiguous rows (RowDma) or k-major columns (ColDma).
+// the output columns, each either k-contiguous rows (RowDma) or k-major
+// columns (ColDma).
 template <int BT, int NA, int NB, typename ALoader, typename BLoader>
 struct Operands {
     ALoader a[NA];
@@ -466,7 +493,7 @@ struct TileJob {
 template <int KIND, int BT>
 constexpr int tile_lds_bytes() {
     using Cfg = TileCfg<BT, BT == 256 || KIND == kBx || KIND == kBxSplit>;
-    return Cfg::NS * (KIND == kBxSplit ? 4 : 2) * Cfg::OP_BYTES;
+    return Cfg::NS * 2 * Cfg::OP_BYTES;
 }
 
 struct NoHook {
@@ -500,10 +527,12 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
     // full cache lines, where a k-contiguous slice row is only 2 BK bytes.
     constexpr bool KMAJOR_A = KIND != kGram;
     constexpr bool KMAJOR_B = KIND != kGram;
-    constexpr int NA = SPLIT_IN ? 2 : 1, NB = SPLIT_IN ? 2 : 1;
+    constexpr int NA = 1, NB = 1;
+    constexpr int NSEG = SPLIT_IN ? 3 : 1;            // reduction segments (split B X: Bh Xh, Bh Xl, Bl Xh)
     constexpr int BK = Cfg::BK;
-    using ALoader = typename std::conditional<KMAJOR_A, ColDma<BT, BK, NW>, RowDma<BT, BK, NW>>::type;
-    using BLoader = typename std::conditional<KMAJOR_B, ColDma<BT, BK, NW>, RowDma<BT, BK, NW>>::type;
+    // split B X: the row operand reads its lo plane in segment 2, the column operand in segment 1
+    using ALoader = typename std::conditional<KMAJOR_A, ColDma<BT, BK, NW, SPLIT_IN ? 2 : -1>, RowDma<BT, BK, NW>>::type;
+    using BLoader = typename std::conditional<KMAJOR_B, ColDma<BT, BK, NW, SPLIT_IN ? 1 : -1>, RowDma<BT, BK, NW>>::type;
     using Ops = Operands<BT, NA, NB, ALoader, BLoader>;
     constexpr int STAGE = Ops::STAGE;
     constexpr int LDS_BYTES = Cfg::NS * STAGE;
@@ -514,10 +543,14 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
     const int wr0 = (wave / Cfg::WC) * TWR, wc0 = (wave % Cfg::WC) * TWC;
 
     Ops ops;
-#pragma unroll
-    for (int i = 0; i < NA; ++i) ops.a[i].init(a.p[i], a.p_bytes, a.K, row0, tid);   // K = ld (square when k-major)
-#pragma unroll
-    for (int j = 0; j < NB; ++j) ops.b[j].init(a.q[j], a.q_bytes, KMAJOR_B ? a.ldq : a.K, col0, tid);
+    if constexpr (SPLIT_IN) {
+        // segments: Bh Xh, Bh Xl, Bl Xh
+        ops.a[0].init(a.p[0], a.p_bytes, a.K, row0, tid, a.p[1], static_cast<int>(a.K));
+        ops.b[0].init(a.q[0], a.q_bytes, a.ldq, col0, tid, a.q[1], static_cast<int>(a.K));
+    } else {
+        ops.a[0].init(a.p[0], a.p_bytes, a.K, row0, tid);   // K = ld (square when k-major)
+        ops.b[0].init(a.q[0], a.q_bytes, KMAJOR_B ? a.ldq : a.K, col0, tid);
+    }
 
     f32x16 acc[FA][FB];
     zero_acc<FA, FB>(acc);
@@ -525,25 +558,21 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
     // epilogue waits for no global load of its own.
     const float sc = a.scale ? *a.scale : 1.0f;
 
-    // A K step is U sub-slices (16 deep, and for the split B X three products
-    // each); the fragments of sub-slice u + 1 are read from LDS while the
-    // MFMAs of u run.  products: 0 = (A hi, B hi), 1 = (A hi, B lo), 2 = (A lo, B hi)
+    // A K step is U sub-slices (16 deep); the fragments of sub-slice u + 1 are
+    // read from LDS while the MFMAs of u run.
     constexpr int NS = Cfg::NS;
     constexpr int KS = BK / 16;
-    constexpr int P = SPLIT_IN ? 3 : 1;
-    constexpr int U = P * KS;
+    constexpr int U = KS;
     static_assert(U % 2 == 0, "fragment ping-pong restarts at 0 each step");
     constexpr int NREAD = (KMAJOR_A ? 2 * FA : FA) + (KMAJOR_B ? 2 * FB : FB);
     constexpr int NM = FA * FB;
     constexpr bool SPREAD = NW == 8;
     constexpr int W = Ops::WINDOWS;
-    const int nk = static_cast<int>(a.K / BK);
+    const int nk = static_cast<int>(NSEG * a.K / BK);
     bf16x8 fa[2][FA], fb[2][FB];
     auto frags = [&](const char* st, int u, bf16x8 (&xa)[FA], bf16x8 (&xb)[FB]) {
-        const int pn = u / KS, ks = u % KS;
-        load_frags<FA, FB, KMAJOR_A, KMAJOR_B, BT, BK>(Ops::a_tile(const_cast<char*>(st), pn == 2 ? 1 : 0),
-                                              Ops::b_tile(const_cast<char*>(st), pn == 1 ? 1 : 0), wr0, wc0, ks,
-                                              xa, xb, tid);
+        load_frags<FA, FB, KMAJOR_A, KMAJOR_B, BT, BK>(Ops::a_tile(const_cast<char*>(st), 0),
+                                              Ops::b_tile(const_cast<char*>(st), 0), wr0, wc0, u, xa, xb, tid);
     };
 
     if constexpr (NS >= 3) {
@@ -602,9 +631,8 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
             for (int u = 0; u < U; ++u) {
                 const int c = u & 1;
                 if (u + 1 < U) {
-                    const int pn = (u + 1) / KS, ks = (u + 1) % KS;
                     load_frags<FA, FB, KMAJOR_A, KMAJOR_B, BT, BK, true, (U - 1) * (FA + FB)>(
-                        Ops::a_tile(cur, pn == 2 ? 1 : 0), Ops::b_tile(cur, pn == 1 ? 1 : 0), wr0, wc0, ks,
+                        Ops::a_tile(cur, 0), Ops::b_tile(cur, 0), wr0, wc0, u + 1,
                         fa[c ^ 1], fb[c ^ 1], tid, &ops, nxt, k1, u * (FA + FB));
                 }
                 mfma_block<FA, FB>(fa[c], fb[c], acc);
@@ -847,8 +875,10 @@ struct PersistProblem {
     const uint16_t* x0;       // iteration 0's input (oriented, padded)
     uint16_t* xb[2];          // ping-pong iterates: iteration t > 0 reads xb[t % 2] and
     uint16_t* xlast;          // writes xb[(t + 1) % 2]; the last iteration writes xlast
+    uint16_t* xlo[2];         // ACCURATE: lo planes of the iterates (iteration t reads xlo[t % 2])
     uint16_t* a;
     uint16_t* b;
+    uint16_t* blo;            // ACCURATE: lo plane of B'
     const float* scale;
     uint32_t* done;           // [nb] completion counters, kSyncStride words apart
     int32_t mp, np;
@@ -938,9 +968,12 @@ __device__ void ns_loop_verify(const PersistArgs& args, uint32_t* err, char* lds
     }
 }
 
+// SPLIT: ACCURATE precision (B' and X as hi + lo planes).
+template <bool SPLIT>
 __global__ __launch_bounds__(tile_threads<256>()) void k_ns_loop(PersistArgs args) {
     constexpr int LDS = tile_lds_bytes<kBx, 256>();
-    static_assert(tile_lds_bytes<kGram, 256>() <= LDS && tile_lds_bytes<kPoly, 256>() <= LDS, "LDS size");
+    static_assert(tile_lds_bytes<kGram, 256>() <= LDS && tile_lds_bytes<kPoly, 256>() <= LDS &&
+                  tile_lds_bytes<kPolySplit, 256>() <= LDS && tile_lds_bytes<kBxSplit, 256>() <= LDS, "LDS size");
     static_assert(LDS + 8 * kLdsItems + 8 <= 160 * 1024, "LDS of a gfx950 workgroup");
     static_assert(LDS >= 513 * 4, "verification list fits in the tile LDS");
     __shared__ __attribute__((aligned(16))) char lds[LDS];
@@ -1082,6 +1115,7 @@ __global__ __launch_bounds__(tile_threads<256>()) void k_ns_loop(PersistArgs arg
         const int t = static_cast<int>(ity >> 24), ph = static_cast<int>((ity >> 22) & 3u);
         const int64_t xs = int64_t(pr.mp) * pr.np, as = int64_t(pr.mp) * pr.mp;
         const uint16_t* const xin = (t == 0 ? pr.x0 : pr.xb[t & 1]) + blk * xs;
+        const uint16_t* const xin_lo = SPLIT ? pr.xlo[t & 1] + blk * xs : nullptr;
         for (int c = 0; c < ntiles; ++c) {
             if (c > 0) __syncthreads();    // the previous tile's epilogue is done with LDS
             const bool last = c + 1 == ntiles;
@@ -1119,7 +1153,12 @@ __global__ __launch_bounds__(tile_threads<256>()) void k_ns_loop(PersistArgs arg
                 j.K = pr.mp;
                 j.ldq = pr.mp;
                 j.ldo = pr.mp;
-                gemm_tile<kPoly, 256, true>(j, lds, args.ca, args.cb, args.cc, claim);
+                if constexpr (SPLIT) {
+                    j.out[1] = pr.blo + blk * as;
+                    gemm_tile<kPolySplit, 256, true>(j, lds, args.ca, args.cb, args.cc, claim);
+                } else {
+                    gemm_tile<kPoly, 256, true>(j, lds, args.ca, args.cb, args.cc, claim);
+                }
             } else {
                 j.p[0] = pr.b + blk * as;
                 j.q[0] = xin;
@@ -1130,7 +1169,14 @@ __global__ __launch_bounds__(tile_threads<256>()) void k_ns_loop(PersistArgs arg
                 j.K = pr.mp;
                 j.ldq = pr.np;
                 j.ldo = pr.np;
-                gemm_tile<kBx, 256, true>(j, lds, args.ca, args.cb, args.cc, claim);
+                if constexpr (SPLIT) {
+                    j.p[1] = pr.blo + blk * as;
+                    j.q[1] = xin_lo;
+                    j.out[1] = pr.xlo[(t + 1) & 1] + blk * xs;
+                    gemm_tile<kBxSplit, 256, true>(j, lds, args.ca, args.cb, args.cc, claim);
+                } else {
+                    gemm_tile<kBx, 256, true>(j, lds, args.ca, args.cb, args.cc, claim);
+                }
             }
         }
         // Every wave's stores (and wave 0's claim) complete before the barrier.
@@ -1180,9 +1226,13 @@ template __global__ void k_gemm<kGram, 256>(GemmArgs);
 template __global__ void k_gemm<kPoly, 128>(GemmArgs);
 template __global__ void k_gemm<kPoly, 256>(GemmArgs);
 template __global__ void k_gemm<kPolySplit, 128>(GemmArgs);
+template __global__ void k_gemm<kPolySplit, 256>(GemmArgs);
 template __global__ void k_gemm<kBx, 128>(GemmArgs);
 template __global__ void k_gemm<kBx, 256>(GemmArgs);
 template __global__ void k_gemm<kBxSplit, 128>(GemmArgs);
+template __global__ void k_gemm<kBxSplit, 256>(GemmArgs);
+template __global__ void k_ns_loop<false>(PersistArgs);
+template __global__ void k_ns_loop<true>(PersistArgs);
 
 // Compute units of the current device (the rounds of the cost model below).
 int64_t device_cus() {
@@ -1216,7 +1266,6 @@ double round_cycles_small(int64_t K) { return 812.0 * double(K / 32) + 8500.0; }
 template <int KIND>
 hipError_t run(const Plan* const* plans, GemmArgs a, hipStream_t s) {
     constexpr bool SYM = KIND == kGram || KIND == kPoly || KIND == kPolySplit;
-    constexpr bool HAS_BIG = KIND == kGram || KIND == kPoly || KIND == kBx;
     auto geometry = [&](int bt) {
         int64_t first = 0;
         for (int i = 0; i < a.n; ++i) {
@@ -1240,7 +1289,7 @@ hipError_t run(const Plan* const* plans, GemmArgs a, hipStream_t s) {
         a.big_base = base;
         a.total = static_cast<uint32_t>(total);
         if (bt == 256) {
-            if constexpr (HAS_BIG) k_gemm<KIND, 256><<<dim3(a.total), dim3(tile_threads<256>()), 0, s>>>(a);
+            k_gemm<KIND, 256><<<dim3(a.total), dim3(tile_threads<256>()), 0, s>>>(a);
         } else {
             k_gemm<KIND, 128><<<dim3(a.total), dim3(tile_threads<128>()), 0, s>>>(a);
         }
@@ -1248,20 +1297,22 @@ hipError_t run(const Plan* const* plans, GemmArgs a, hipStream_t s) {
     };
     const int64_t K = a.pr[0].K;
     const int64_t kCUs = device_cus();
-    bool big_ok = HAS_BIG;
+    bool big_ok = true;
     for (int i = 0; i < a.n; ++i) {
         if (a.pr[i].K != K) return hipErrorInvalidValue;
         big_ok = big_ok && plans[i]->mp % 256 == 0 && (SYM || plans[i]->np % 256 == 0);
     }
+    // the split B X runs a reduction three times as long (Bh Xh, Bh Xl, Bl Xh)
+    const int64_t Kc = KIND == kBxSplit ? 3 * K : K;
     const int64_t small = geometry(128);
     if (small < 0) return hipErrorInvalidValue;
-    const double t_small = double((small + 2 * kCUs - 1) / (2 * kCUs)) * round_cycles_small(K);
+    const double t_small = double((small + 2 * kCUs - 1) / (2 * kCUs)) * round_cycles_small(Kc);
     if (big_ok) {
         const int64_t big = geometry(256);
         const int64_t full = big / kCUs, tail = big % kCUs;
-        const double rb = round_cycles_big(K, SYM);
+        const double rb = round_cycles_big(Kc, SYM);
         const double t_split = double(full) * rb +
-                               double((4 * tail + 2 * kCUs - 1) / (2 * kCUs)) * round_cycles_small(K);
+                               double((4 * tail + 2 * kCUs - 1) / (2 * kCUs)) * round_cycles_small(Kc);
         const double t_big = double(full + (tail ? 1 : 0)) * rb;
         if (t_big <= t_split && t_big < t_small) return launch(256, big, 0, 0);
         if (t_split < t_small) {
@@ -1433,7 +1484,7 @@ uint64_t ns_loop_items_cap(const Plan* const* plans, int n, int ns_steps) {
     uint64_t items = 0, blocks = 0;
     for (int i = 0; i < n; ++i) {
         const Plan& p = *plans[i];
-        if (p.small || p.precision != MUON_PRECISION_FAST || p.nb < 1 || p.mp % 256 || p.np % 256) return 0;
+        if (p.small || p.precision != plans[0]->precision || p.nb < 1 || p.mp % 256 || p.np % 256) return 0;
         const uint64_t T = uint64_t(p.mp / 256), Tn = uint64_t(p.np / 256);
         if (T * Tn >= (uint64_t(1) << 22)) return 0;
         // at most one item per tile: T (T + 1) / 2 tiles per symmetric product, T Tn for B X
@@ -1491,7 +1542,7 @@ const Schedule* find_schedule(const NsLoopProblem* probs, int n, int ns_steps, i
     for (int i = 0; i < n; ++i) {
         const Plan& p = *probs[i].plan;
         const uint32_t T = uint32_t(p.mp / 256), Tn = uint32_t(p.np / 256);
-        dims.push_back({int(p.mp), int(p.np), T * (T + 1) / 2, T * Tn});
+        dims.push_back({int(p.mp), int(p.np), T * (T + 1) / 2, T * Tn, p.precision == MUON_PRECISION_ACCURATE});
         nbs.push_back(p.nb);
     }
     Schedule sc;
@@ -1616,6 +1667,7 @@ hipError_t launch_ns_loop(const NsLoopProblem* probs, int n, int ns_steps, float
     z.count = n;
     uint32_t zmax = 0;
     uint32_t first = 0;
+    const bool split = probs[0].plan->precision == MUON_PRECISION_ACCURATE;
     for (int i = 0; i < n; ++i) {
         const Plan& p = *probs[i].plan;
         const uint32_t T = uint32_t(p.mp / 256), Tn = uint32_t(p.np / 256);
@@ -1624,8 +1676,13 @@ hipError_t launch_ns_loop(const NsLoopProblem* probs, int n, int ns_steps, float
         pr.xb[0] = probs[i].x[0];
         pr.xb[1] = probs[i].x[1];
         pr.xlast = probs[i].xlast;
+        pr.xlo[0] = probs[i].xlo[0];
+        pr.xlo[1] = probs[i].xlo[1];
         pr.a = probs[i].a;
         pr.b = probs[i].b;
+        pr.blo = probs[i].blo;
+        if (split != (probs[i].blo != nullptr && probs[i].xlo[0] != nullptr && probs[i].xlo[1] != nullptr))
+            return hipErrorInvalidValue;
         pr.scale = probs[i].scale;
         pr.done = probs[i].sync + kSyncLines * kSyncStride;
         z.p[i] = probs[i].sync;
@@ -1649,7 +1706,10 @@ hipError_t launch_ns_loop(const NsLoopProblem* probs, int n, int ns_steps, float
     k_loop_setup<<<dim3((work + 255) / 256), dim3(256), 0, s>>>(z);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    k_ns_loop<<<dim3(choice.cus), dim3(tile_threads<256>()), 0, s>>>(a);
+    if (split)
+        k_ns_loop<true><<<dim3(choice.cus), dim3(tile_threads<256>()), 0, s>>>(a);
+    else
+        k_ns_loop<false><<<dim3(choice.cus), dim3(tile_threads<256>()), 0, s>>>(a);
     return hipGetLastError();
 }
 

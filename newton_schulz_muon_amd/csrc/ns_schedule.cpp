@@ -17,8 +17,10 @@ namespace {
 // also store the mirror tile, the polynomial reads A) and the barrier between
 // tiles.
 double item_cycles(int ph, const LoopDims& d) {
-    const double K = ph == 0 ? d.np : d.mp;
-    return (ph == 0 ? 1424.0 : 1216.0) * (K / 32) + (ph == 0 ? 12700.0 : ph == 1 ? 16300.0 : 7500.0);
+    const double K = ph == 0 ? d.np : (ph == 2 && d.split ? 3.0 * d.mp : d.mp);
+    // the split products store a second plane (B': and its mirror; X': through the fp32 epilogue)
+    const double epi = ph == 0 ? 12700.0 : ph == 1 ? (d.split ? 24000.0 : 16300.0) : (d.split ? 12000.0 : 7500.0);
+    return (ph == 0 ? 1424.0 : 1216.0) * (K / 32) + epi;
 }
 
 // Measured cost of one item boundary beyond a tile boundary (store drain,

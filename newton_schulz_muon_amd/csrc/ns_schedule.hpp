@@ -22,6 +22,7 @@ namespace muon {
 struct LoopDims {
     int mp, np;
     uint32_t nsym, nbx;    // symmetric products' upper tiles; B X tiles
+    bool split = false;    // ACCURATE: B X reduces over 3 mp (Bh Xh, Bh Xl, Bl Xh), B' has two planes
 };
 
 struct ScheduleItem {

@@ -82,6 +82,60 @@ def test_loop_bitwise_equals_per_product(nsm, case):
     np.testing.assert_array_equal(got, ref)
 
 
+# ACCURATE precision: B' and X as hi + lo planes, B' X over the three segments
+# Bh Xh, Bh Xl, Bl Xh (batch, rows, cols, view_blocks, ns_steps)
+ACC_CASES = [
+    (3, 512, 1024, 1, 5),
+    (2, 1024, 512, 1, 5),     # tall
+    (4, 768, 768, 1, 2),
+    (2, 256, 256, 1, 3),
+]
+
+
+@pytest.mark.parametrize("case", ACC_CASES)
+def test_loop_accurate_bitwise_equals_per_product(nsm, case):
+    b, r, c, v, steps = case
+    print(f"[ns loop] accurate batch={b} shape={(r, c)} steps={steps}", flush=True)
+    bits = workloads.gaussian_bits((b, r, c), seed=r * 17 + c + steps)
+    x = workloads.to_device_bf16(bits)
+
+    def run():
+        return torch_bf16_to_bits(nsm.ns_orthogonalize_batched(x, view_blocks=v, ns_steps=steps,
+                                                                precision="accurate"))
+
+    got, ref, counts = _both(nsm, run)
+    assert counts.get("ns_loop", (0, 0.0))[0] == 1 and "gram" not in counts, counts
+    np.testing.assert_array_equal(got, ref)
+    if steps == 5:
+        want = oracle.ns_batched(bits_to_f64(bits), view_blocks=v)
+        for i in range(b):
+            assert_ns_close(bits_to_f64(got[i]), want[i], tol=1e-2, label=f"accurate loop[{i}]")
+
+
+def test_loop_accurate_step_bitwise(nsm):
+    # a full ACCURATE Muon step in the loop equals the per-product step bit for bit
+    import torch
+    print("[ns loop] accurate muon_step_batched 4 x 512 x 1536", flush=True)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(12)
+    P0 = torch.randn((4, 512, 1536), generator=gen, device="cuda") / 1536 ** 0.5
+    G = (torch.randn((4, 512, 1536), generator=gen, device="cuda") * 1e-2).to(torch.bfloat16)
+    M0 = torch.randn((4, 512, 1536), generator=gen, device="cuda") * 1e-3
+
+    def run():
+        P, M = P0.clone(), M0.clone()
+        O = torch.empty_like(G)
+        nsm.muon_step_batched(P, G, M, lr=0.02, weight_decay=0.01, momentum=0.95, update_out=O,
+                              precision="accurate")
+        torch.cuda.synchronize()
+        return P.cpu().numpy().view(np.int32), M.cpu().numpy().view(np.int32), O.view(torch.int16).cpu().numpy()
+
+    got, ref, counts = _both(nsm, run)
+    assert counts.get("ns_loop", (0, 0.0))[0] == 1, counts
+    for a, b in zip(got, ref):
+        np.testing.assert_array_equal(a, b)
+
+
 def test_loop_parity_with_oracle(nsm):
     print("[ns loop] oracle parity 3 x 512 x 1024", flush=True)
     bits = workloads.gaussian_bits((3, 512, 1024), seed=4242)
@@ -219,7 +273,7 @@ def test_loop_small_blocks_repeated(nsm, shape):
 
 @pytest.mark.parametrize("case", [
     (2, 300, 700, "fast"),        # padded sides 384 x 768: not multiples of 256
-    (3, 512, 1024, "accurate"),   # hi/lo planes: per-product kernels only
+    (2, 300, 700, "accurate"),
 ])
 def test_forced_loop_falls_back(nsm, case):
     # With the persistent schedule forced, calls it does not apply to run the
@@ -269,3 +323,43 @@ def test_timing_reports_nominal_flops(nsm, sched, shape):
     if not loop:
         assert k["gram"][2] == pytest.approx(b * v * 5 * 2.0 * m * m * n, rel=1e-12)
         assert k["poly"][2] == pytest.approx(b * v * 5 * 2.0 * m ** 3, rel=1e-12)
+
+
+@pytest.mark.parametrize("sched,shape", [("per_product", (2, 256, 640)), ("persistent", (2, 256, 512)),
+                                         ("per_product", (2, 512, 1024))])
+def test_accurate_workspace_at_high_addresses(nsm, sched, shape):
+    # The split B X kernels rebuild their buffer descriptors from 64-bit plane
+    # addresses in scalar registers.  A workspace whose planes sit at
+    # addresses with bit 31 set (the low word >= 2^31) must give the same
+    # bits as one elsewhere (a sign-extended low word once corrupted the
+    # descriptor's high address bits there).
+    import ctypes
+    import torch
+    b, r, c = shape
+    print(f"[ns loop] accurate, workspace at high address bits, {sched} {shape}", flush=True)
+    lib = nsm.load_library()
+    cfg = nsm.make_config(precision="accurate")
+    need = nsm.muon_workspace_bytes(b, r, c, 1, cfg)
+    assert need < (1 << 30)
+    big = torch.empty(need + (1 << 32), dtype=torch.uint8, device="cuda")
+    base = big.data_ptr()
+    d = ((0x80000000 - (base & 0xFFFFFFFF)) % (1 << 32) + 255) // 256 * 256
+    ws_hi = base + d
+    assert (ws_hi & 0xFFFFFFFF) >= 0x80000000 and ((ws_hi + need) & 0xFFFFFFFF) >= 0x80000000
+    assert d + need <= big.numel()
+    x = workloads.to_device_bf16(workloads.gaussian_bits(shape, seed=r + c + 99))
+    ref_ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    outs = []
+    nsm.muon_set_ns_schedule(sched)
+    try:
+        for ws in (ref_ws.data_ptr(), ws_hi):
+            out = torch.empty_like(x)
+            st = lib.ns_orthogonalize_batched(x.data_ptr(), out.data_ptr(), b, r, c, 1, ctypes.byref(cfg),
+                                              ctypes.c_void_p(ws), need, torch.cuda.current_stream().cuda_stream)
+            assert st == 0, nsm.muon_last_error()
+            torch.cuda.synchronize()
+            outs.append(torch_bf16_to_bits(out))
+    finally:
+        nsm.muon_set_ns_schedule("auto")
+    np.testing.assert_array_equal(outs[0], outs[1])
+    del big
