@@ -20,7 +20,9 @@ Beside it the JSON line carries
     (1 GiB written between calls) Infinity Cache;
   * extras: the full 124M custom-sizing Muon step (muon_step_multi over 43
     matrices) with its element-wise kernels' HBM rates, one GPU's share of it
-    under 8-way sharding by whole matrices, the AdamW step of the same model;
+    under 8-way sharding by whole matrices, full steps of the GPT-2-medium-like
+    96 x 1024x4096 batch and of the large dense ACCURATE batch (nominal and
+    executed MFMA rates), the AdamW step of the 124M model;
   * cpu_baseline: the fp64 NumPy oracle on a bounded sample of the same
     workload on the host cores.
 
@@ -261,7 +263,7 @@ def roofline_of(res, steps):
     if not ns:
         return None
     k = max(ns, key=lambda f: ns[f][1])
-    launches, tot_ms, nominal = ns[k]
+    launches, tot_ms, nominal, executed = ns[k]
     avg_ms = tot_ms / launches
     nom = nominal / launches
     r = {"bound": "mfma", "kernel": FAMILY_NAMES[k], "flops_basis": "nominal 5 (4 m^2 n + 2 m^3) per block",
@@ -270,7 +272,8 @@ def roofline_of(res, steps):
     if k == "ns_loop":
         per_block = nom / res["nb"]
         assert abs(per_block - ns_flops(768, 3072)) < 1e-6 * per_block
-        ex = res["nb"] * loop_executed_flops(768, 3072)
+        ex = executed / launches          # the library's count of the tiles the launch ran
+        assert abs(ex - res["nb"] * loop_executed_flops(768, 3072)) <= 1e-9 * ex
         alg = res["nb"] * ns_flops_symmetric(768, 3072)
         r["achieved_executed"] = round(ex / (avg_ms / 1e3) / 1e12, 2)
         r["frac_executed"] = round(r["achieved_executed"] / PEAK_BF16_TFLOPS, 4)
@@ -314,6 +317,9 @@ def gpt124m_step(nsm, args, dev):
     fam = t.result
     flops = sum(g.n_blocks * ns_flops(*g.block_shape) for g in wl.groups)
     n_blocks = sum(g.n_blocks for g in wl.groups)
+    ns = {k: v for k, v in fam.items() if k in NS_FAMILIES}
+    ns_ms = sum(v[1] for v in ns.values()) / args.steps
+    executed = sum(v[3] for v in ns.values()) / args.steps
     # the element-wise kernels (blocks on the matrix-core path): 12 B per
     # element before NS (g 2, M 8, U 2), 10 B after (P 8, O 2)
     mfma_elems = sum(g.count * g.rows * g.cols for g in wl.groups if min(g.block_shape) > 64)
@@ -325,6 +331,9 @@ def gpt124m_step(nsm, args, dev):
            "matrices_per_s": round(wl.n_matrices / (ms / 1e3), 1),
            "matrices_per_s_excluding_gates": round(32 / (ms / 1e3), 1),
            "ns_blocks_per_s": round(n_blocks / (ms / 1e3), 1),
+           "ns_kernels": {"ms_per_step": round(ns_ms, 4),
+                          "tflops_executed": round(executed / (ns_ms / 1e3) / 1e12, 2),
+                          "frac_executed": round(executed / (ns_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
            "kernel_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in fam.items()}}
     for kind, bpe, name in (("prep", 12, "k_prep"), ("finish", 10, "k_finish")):
         if kind in fam:
@@ -375,6 +384,55 @@ def rank_shares(nsm, args, dev):
     return out
 
 
+def large_step(nsm, args, dev, name):
+    """A full Muon step of a large workload (each shape group one
+    muon_step_batched call in the group's precision): the GPT-2-medium-like
+    96 x 1024x4096 batch (48 stored tall) or the large dense batch
+    8 x 4096^2 + 8 x 4096x14336 (ACCURATE)."""
+    import torch
+    import workloads
+    wl = workloads.get_workload(name)
+    state = []
+    for g in wl.groups:
+        P = workloads.params_device(wl, g, dev)
+        state.append((g, P, workloads.grads_device(wl, g, 0, dev), torch.zeros_like(P)))
+
+    def step():
+        for g, P, G, M in state:
+            nsm.muon_step_batched(P, G, M, lr=wl.lr, weight_decay=wl.weight_decay, momentum=wl.momentum,
+                                  view_blocks=g.view_blocks, ns_steps=wl.ns_steps, precision=g.precision)
+    steps = max(1, min(args.steps, 10))
+    for _ in range(SETTLE_CALLS):
+        step()
+        torch.cuda.synchronize()
+    for _ in range(min(args.warmup, 3)):
+        step()
+    ms = timed_region(step, steps)
+    with Timer(nsm, nsm.KERNEL_KINDS) as t:
+        for _ in range(steps):
+            step()
+    fam = t.result
+    nominal = sum(g.n_blocks * ns_flops(*g.block_shape) for g in wl.groups)
+    ns = {k: v for k, v in fam.items() if k in NS_FAMILIES}
+    ns_ms = sum(v[1] for v in ns.values()) / steps
+    executed = sum(v[3] for v in ns.values()) / steps
+    out = {"workload": wl.description, "precision": sorted({g.precision for g in wl.groups}),
+           "steps": steps, "ms": round(ms, 4), "nominal_ns_gflop_per_step": round(nominal / 1e9, 1),
+           "tflops_nominal": round(nominal / (ms / 1e3) / 1e12, 2),
+           "mfma_peak_frac_nominal": round(nominal / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "executed_gflop_per_step": round(executed / 1e9, 1),
+           "ns_kernels": {"ms_per_step": round(ns_ms, 4),
+                          "tflops_executed": round(executed / (ns_ms / 1e3) / 1e12, 2),
+                          "frac_executed": round(executed / (ns_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                          "tflops_nominal": round(nominal / (ns_ms / 1e3) / 1e12, 2)},
+           "matrices_per_s": round(wl.n_matrices / (ms / 1e3), 1),
+           "kernel_ms_per_step": {k: round(v[1] / steps, 4) for k, v in fam.items()},
+           "status": list(nsm.last_call_status(dev))}
+    del state
+    torch.cuda.empty_cache()
+    return out
+
+
 def adamw_gpt124m(nsm, args, dev):
     import torch
     import workloads
@@ -415,8 +473,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="the headline call only")
-    ap.add_argument("--extras", default="step,shares,adamw",
-                    help="comma-separated extras: step (124M Muon step), shares (one GPU's 8-way share), adamw")
+    ap.add_argument("--extras", default="step,shares,c4,c5,adamw",
+                    help="comma-separated extras: step (124M Muon step), shares (one GPU's 8-way share), "
+                         "c4 (96 x 1024x4096 step), c5 (large dense ACCURATE step), adamw")
     ap.add_argument("--ns-schedule", choices=("auto", "persistent", "per_product"), default="auto",
                     help="auto: the library's per-shape choice (default); persistent: all NS iterations of "
                          "a call in one launch; per_product: three launches per iteration")
@@ -476,6 +535,10 @@ def main():
             result["gpt124m_step"] = gpt124m_step(nsm, args, dev)
         if "shares" in want:
             result["rank_share_8way"] = rank_shares(nsm, args, dev)
+        if "c4" in want:
+            result["gpt2_medium_step"] = large_step(nsm, args, dev, "gpt2_medium")
+        if "c5" in want:
+            result["large_dense_step"] = large_step(nsm, args, dev, "large_dense")
         if "adamw" in want:
             result["adamw_gpt124m"] = adamw_gpt124m(nsm, args, dev)
     if not args.no_cpu_baseline:

@@ -349,15 +349,19 @@ typedef enum muon_kernel_kind {
  * kernel plus a tail kernel, timed together. */
 muon_status muon_timing_enable(uint32_t kernel_mask);
 
-/* Waits for every recorded event, adds launch counts, elapsed milliseconds and
- * nominal flops per family into launches[MUON_KERNEL_COUNT],
- * total_ms[MUON_KERNEL_COUNT] and nominal_flops[MUON_KERNEL_COUNT] (any of
- * them may be NULL), and forgets the recorded launches.  Nominal flops count
- * the NS products a launch computes on the unpadded oriented blocks m x n
- * (m <= n): 2 m^2 n for X X^T, 2 m^3 for A A, 2 m^2 n for B X, summed over
- * the launch's blocks and, for MUON_KERNEL_NS_LOOP, its iterations; the
- * other families report 0. */
-muon_status muon_timing_collect(int64_t* launches, double* total_ms, double* nominal_flops);
+/* Waits for every recorded event, adds launch counts, elapsed milliseconds,
+ * nominal and executed flops per family into launches[MUON_KERNEL_COUNT],
+ * total_ms[MUON_KERNEL_COUNT], nominal_flops[MUON_KERNEL_COUNT] and
+ * executed_flops[MUON_KERNEL_COUNT] (any of them may be NULL), and forgets
+ * the recorded launches.  Nominal flops count the NS products a launch
+ * computes on the unpadded oriented blocks m x n (m <= n): 2 m^2 n for
+ * X X^T, 2 m^3 for A A, 2 m^2 n for B X, summed over the launch's blocks and,
+ * for MUON_KERNEL_NS_LOOP, its iterations.  Executed flops count the matrix
+ * core work of the tiles the launch ran: 2 t^2 K per t x t tile over its
+ * reduction K (padding, the diagonal tiles of the symmetric products and
+ * ACCURATE's three-segment B X included).  The other families report 0. */
+muon_status muon_timing_collect(int64_t* launches, double* total_ms, double* nominal_flops,
+                                double* executed_flops);
 
 /* Text of the last error on the calling thread ("" if none).  Valid until
  * the next call into the library from that thread. */

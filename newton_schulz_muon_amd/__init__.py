@@ -120,7 +120,7 @@ def load_library():
         lib.muon_timing_enable.argtypes = [ctypes.c_uint32]
         lib.muon_timing_enable.restype = ctypes.c_int
         lib.muon_timing_collect.argtypes = [ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double),
-                                            ctypes.POINTER(ctypes.c_double)]
+                                            ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
         lib.muon_timing_collect.restype = ctypes.c_int
         lib.muon_workspace_status.argtypes = [vp, vp, vp]
         lib.muon_workspace_status.restype = ctypes.c_int
@@ -176,15 +176,16 @@ def muon_timing_enable(kinds=()) -> None:
 
 def muon_timing_collect(with_flops: bool = False) -> dict:
     """{family: (launches, total_ms)} for the launches recorded since the last
-    collect; with_flops=True adds the nominal flops of those launches as a
-    third element."""
+    collect; with_flops=True adds the nominal and the executed flops of those
+    launches as third and fourth elements."""
     n = len(KERNEL_KINDS)
     launches = (ctypes.c_int64 * n)()
     total = (ctypes.c_double * n)()
     flops = (ctypes.c_double * n)()
-    _check(load_library().muon_timing_collect(launches, total, flops))
+    executed = (ctypes.c_double * n)()
+    _check(load_library().muon_timing_collect(launches, total, flops, executed))
     if with_flops:
-        return {k: (int(launches[i]), float(total[i]), float(flops[i]))
+        return {k: (int(launches[i]), float(total[i]), float(flops[i]), float(executed[i]))
                 for i, k in enumerate(KERNEL_KINDS) if launches[i]}
     return {k: (int(launches[i]), float(total[i])) for i, k in enumerate(KERNEL_KINDS) if launches[i]}
 

@@ -156,7 +156,7 @@ struct TimingState {
     std::mutex mu;
     std::atomic<uint32_t> mask{0};
     std::map<int, std::vector<hipEvent_t>> pool;   // per device
-    struct Rec { int kind; int dev; hipEvent_t a, b; double flops; };
+    struct Rec { int kind; int dev; hipEvent_t a, b; double flops, exec; };
     std::vector<Rec> recs;
 };
 
@@ -188,6 +188,7 @@ thread_local bool g_timing_off = false;
 class LaunchTimer {
   public:
     LaunchTimer(int kind, hipStream_t s, double flops) : kind_(kind), s_(s), flops_(flops) {
+        last_exec_flops() = 0.0;
         TimingState& ts = timing();
         if (g_timing_off || !(ts.mask.load() & (1u << kind))) return;
         std::lock_guard<std::mutex> lk(ts.mu);
@@ -201,7 +202,7 @@ class LaunchTimer {
         on_ = false;
         TimingState& ts = timing();
         std::lock_guard<std::mutex> lk(ts.mu);
-        if (hipEventRecord(b_, s_) == hipSuccess) ts.recs.push_back({kind_, dev_, a_, b_, flops_});
+        if (hipEventRecord(b_, s_) == hipSuccess) ts.recs.push_back({kind_, dev_, a_, b_, flops_, last_exec_flops()});
     }
     ~LaunchTimer() { stop(); }
 
@@ -1130,7 +1131,8 @@ muon_status muon_timing_enable(uint32_t kernel_mask) {
     return MUON_OK;
 }
 
-muon_status muon_timing_collect(int64_t* launches, double* total_ms, double* nominal_flops) {
+muon_status muon_timing_collect(int64_t* launches, double* total_ms, double* nominal_flops,
+                                double* executed_flops) {
     g_err.clear();
     TimingState& ts = timing();
     std::lock_guard<std::mutex> lk(ts.mu);
@@ -1145,6 +1147,7 @@ muon_status muon_timing_collect(int64_t* launches, double* total_ms, double* nom
             if (launches) launches[r.kind] += 1;
             if (total_ms) total_ms[r.kind] += ms;
             if (nominal_flops) nominal_flops[r.kind] += r.flops;
+            if (executed_flops) executed_flops[r.kind] += r.exec;
         }
         ts.pool[r.dev].push_back(r.a);
         ts.pool[r.dev].push_back(r.b);

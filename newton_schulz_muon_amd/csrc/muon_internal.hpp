@@ -134,6 +134,9 @@ struct BxOp {
     const float* scale1;
 };
 constexpr int kMaxGemmProblems = 4;
+// MFMA flops the GEMM launchers below (and the persistent loop) enqueue,
+// added up on the calling thread (timing diagnostics reset and read it).
+double& last_exec_flops();
 hipError_t launch_gram(const GramOp* ops, int n, hipStream_t s);
 hipError_t launch_poly(const PolyOp* ops, int n, float ca, float cb, float cc, hipStream_t s);
 hipError_t launch_bx(const BxOp* ops, int n, hipStream_t s);

@@ -1234,6 +1234,15 @@ template __global__ void k_gemm<kBxSplit, 256>(GemmArgs);
 template __global__ void k_ns_loop<false>(PersistArgs);
 template __global__ void k_ns_loop<true>(PersistArgs);
 
+}  // namespace
+
+double& last_exec_flops() {
+    thread_local double v = 0.0;
+    return v;
+}
+
+namespace {
+
 // Compute units of the current device (the rounds of the cost model below).
 int64_t device_cus() {
     int dev = 0, cus = 0;
@@ -1266,6 +1275,9 @@ double round_cycles_small(int64_t K) { return 812.0 * double(K / 32) + 8500.0; }
 template <int KIND>
 hipError_t run(const Plan* const* plans, GemmArgs a, hipStream_t s) {
     constexpr bool SYM = KIND == kGram || KIND == kPoly || KIND == kPolySplit;
+    const int64_t K = a.pr[0].K;
+    // the split B X runs a reduction three times as long (Bh Xh, Bh Xl, Bl Xh)
+    const int64_t Kc = KIND == kBxSplit ? 3 * K : K;
     auto geometry = [&](int bt) {
         int64_t first = 0;
         for (int i = 0; i < a.n; ++i) {
@@ -1284,10 +1296,26 @@ hipError_t run(const Plan* const* plans, GemmArgs a, hipStream_t s) {
         }
         return first;
     };
+    // Executed MFMA flops of the launches (for the timing diagnostics): every
+    // workgroup computes a bt x bt tile over the reduction, except the lower
+    // quadrants of diagonal 256-wide tiles in quadrant mode, which return.
     auto launch = [&](int bt, int64_t total, uint32_t quad, uint32_t base) {
         a.quad = quad;
         a.big_base = base;
         a.total = static_cast<uint32_t>(total);
+        int64_t tiles = total;
+        if (quad && SYM) {
+            tiles = 0;
+            for (int64_t t = base; t < int64_t(base) + total / 4; ++t) {
+                int pi = 0;
+                for (int i = 1; i < a.n; ++i)
+                    if (t >= int64_t(a.pr[i].first)) pi = i;
+                int id = static_cast<int>((t - a.pr[pi].first) % a.pr[pi].tiles), len = a.pr[pi].T, r = 0;
+                while (id >= len) { id -= len; ++r; --len; }
+                tiles += id == 0 ? 3 : 4;     // id == 0: the row's diagonal tile
+            }
+        }
+        last_exec_flops() += double(tiles) * 2.0 * double(bt) * double(bt) * double(Kc);
         if (bt == 256) {
             k_gemm<KIND, 256><<<dim3(a.total), dim3(tile_threads<256>()), 0, s>>>(a);
         } else {
@@ -1295,15 +1323,12 @@ hipError_t run(const Plan* const* plans, GemmArgs a, hipStream_t s) {
         }
         return hipGetLastError();
     };
-    const int64_t K = a.pr[0].K;
     const int64_t kCUs = device_cus();
     bool big_ok = true;
     for (int i = 0; i < a.n; ++i) {
         if (a.pr[i].K != K) return hipErrorInvalidValue;
         big_ok = big_ok && plans[i]->mp % 256 == 0 && (SYM || plans[i]->np % 256 == 0);
     }
-    // the split B X runs a reduction three times as long (Bh Xh, Bh Xl, Bl Xh)
-    const int64_t Kc = KIND == kBxSplit ? 3 * K : K;
     const int64_t small = geometry(128);
     if (small < 0) return hipErrorInvalidValue;
     const double t_small = double((small + 2 * kCUs - 1) / (2 * kCUs)) * round_cycles_small(Kc);
@@ -1706,6 +1731,13 @@ hipError_t launch_ns_loop(const NsLoopProblem* probs, int n, int ns_steps, float
     k_loop_setup<<<dim3((work + 255) / 256), dim3(256), 0, s>>>(z);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    double ex = 0.0;
+    for (int i = 0; i < n; ++i) {
+        const PersistProblem& pr = a.pr[i];
+        ex += double(pr.nb) * double(ns_steps) * 2.0 * 256.0 * 256.0 *
+              (double(pr.nsym) * pr.np + double(pr.nsym) * pr.mp + double(pr.nbx) * pr.mp * (split ? 3.0 : 1.0));
+    }
+    last_exec_flops() += ex;
     if (split)
         k_ns_loop<true><<<dim3(choice.cus), dim3(tile_threads<256>()), 0, s>>>(a);
     else

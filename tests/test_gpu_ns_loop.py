@@ -317,12 +317,22 @@ def test_timing_reports_nominal_flops(nsm, sched, shape):
     k = nsm.muon_timing_collect(with_flops=True)
     m, n = min(r, c // v), max(r, c // v)
     expect = b * v * 5 * (4.0 * m * m * n + 2.0 * m ** 3)
-    assert sum(f for _, _, f in k.values()) == pytest.approx(expect, rel=1e-12), k
+    assert sum(f for _, _, f, _ in k.values()) == pytest.approx(expect, rel=1e-12), k
     loop = sched == "persistent" and r % 256 == 0 and (c // v) % 256 == 0
     assert set(k) == ({"ns_loop"} if loop else {"gram", "poly", "bx"}), k
     if not loop:
         assert k["gram"][2] == pytest.approx(b * v * 5 * 2.0 * m * m * n, rel=1e-12)
         assert k["poly"][2] == pytest.approx(b * v * 5 * 2.0 * m ** 3, rel=1e-12)
+    # executed flops: the tiles that ran, on the padded block; never below the
+    # symmetric work 5 (3 m^2 n + m^3) nor above the padded dense work
+    mp, np_ = -(-m // 128) * 128, -(-n // 128) * 128
+    executed = sum(e for _, _, _, e in k.values())
+    assert b * v * 5 * (3.0 * m * m * n + m ** 3) <= executed <= b * v * 5 * (4.0 * mp * mp * np_ + 2.0 * mp ** 3)
+    if loop:
+        t, tn = mp // 256, np_ // 256
+        sym = t * (t + 1) // 2
+        assert executed == pytest.approx(b * v * 5 * 2.0 * 256 * 256 * (sym * np_ + sym * mp + t * tn * mp),
+                                         rel=1e-12)
 
 
 @pytest.mark.parametrize("sched,shape", [("per_product", (2, 256, 640)), ("persistent", (2, 256, 512)),

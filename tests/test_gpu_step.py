@@ -205,3 +205,35 @@ def test_step_large_dense_accurate(nsm):
             P_ref = P_new
             del G
         del P, M, O
+
+
+@pytest.mark.parametrize("group", ["attn", "mlp"])
+def test_step_rank_share(nsm, group):
+    """One GPU's share of the 124M set under 8-way sharding by whole matrices,
+    as the benchmark runs it: 2 stored 768x3072 matrices per muon_step_batched
+    call (attn: viewed as 8 blocks of 768x768), 3 steps against the oracle."""
+    import torch
+    wl = workloads.get_workload("gpt124m")
+    grp = {g.name: g for g in wl.groups}[group]
+    P_host = workloads.param_init_host(wl, grp, [0, 1])
+    P = torch.from_numpy(P_host).cuda()
+    M = torch.zeros_like(P)
+    O = torch.empty(P.shape, dtype=torch.bfloat16, device="cuda")
+    P_ref, M_ref = P_host.astype(np.float64), np.zeros(P_host.shape)
+    bound = 0.0
+    for t in range(wl.steps):
+        print(f"[step parity] rank share {group} step={t}", flush=True)
+        gbits = workloads.grad_bits_host(wl, grp, t, [0, 1])
+        nsm.muon_step_batched(P, workloads.to_device_bf16(gbits), M, lr=wl.lr, weight_decay=wl.weight_decay,
+                              momentum=wl.momentum, view_blocks=grp.view_blocks, update_out=O)
+        torch.cuda.synchronize()
+        P_ref, M_ref, O_ref = oracle.muon_step(P_ref, bits_to_f64(gbits), M_ref, lr=wl.lr,
+                                               weight_decay=wl.weight_decay, momentum=wl.momentum,
+                                               view_blocks=grp.view_blocks)
+        O_got = bits_to_f64(torch_bf16_to_bits(O))
+        for i in range(2):
+            assert_ns_close(O_got[i], O_ref[i], grp.view_blocks, label=f"share {group}[{i}] step {t}")
+            assert rel_fro(M.cpu().numpy()[i], M_ref[i]) <= MOMENTUM_TOL
+        lr_eff = float(np.float32(wl.lr)) * oracle.aspect_factor(grp.rows, grp.cols)
+        bound += NS_REL_TOL * lr_eff * np.linalg.norm(O_ref) + 4 * 2.0 ** -24 * np.linalg.norm(P_ref)
+        assert np.linalg.norm(P.cpu().numpy() - P_ref) <= bound
