@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define MUON_ABI_VERSION 6
+#define MUON_ABI_VERSION 7
 
 typedef enum muon_status {
     MUON_OK = 0,
@@ -325,6 +325,27 @@ muon_status muon_debug_set_loop_fault(int32_t mode);
  * a workgroup serves the queue of the XCD it runs on.
  * Returns MUON_ERR_INVALID_ARG for any other mode. */
 muon_status muon_set_ns_schedule(int32_t mode);
+
+/* Tile width of the per-product Gram, polynomial and B X launches
+ * (process-wide).  Every width accumulates each 32 x 32 output block with the
+ * same MFMA sequence in the same order, so results are bitwise the same:
+ *   0 (default): automatic, per launch signature (product kind, reduction
+ *     length, device, every block batch's padded sides and block count),
+ *     among 64-wide tiles (up to five per CU; for launches of few tiles,
+ *     where the chain of dependent products is the time), 128-wide,
+ *     256-wide, and 256-wide with the last partial round as 128-wide
+ *     quadrants.  The plans estimated within 2x of the best estimate each
+ *     run 3 launches timed with an event pair on the launch's stream; once
+ *     those events have completed the plan with the lowest time is kept for
+ *     the signature.  Until then, under stream capture, in
+ *     ns_orthogonalize_batched_noalloc (which creates no events) and beyond
+ *     1024 signatures, the best estimate is used;
+ *   64, 128: that width;
+ *   256: that width where both padded sides of every block batch of the
+ *     launch are multiples of 256, else 128.
+ * The persistent loop always uses 256-wide tiles.  Returns
+ * MUON_ERR_INVALID_ARG for any other width. */
+muon_status muon_set_gemm_tiling(int32_t width);
 
 /* Kernel timing (diagnostics).  Kernel families of the library: */
 typedef enum muon_kernel_kind {

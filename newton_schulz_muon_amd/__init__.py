@@ -16,7 +16,7 @@ Entry points (same names as the C ABI):
     muon_workspace_bytes(batch, rows, cols, view_blocks=1, cfg=None)
     muon_step_multi_workspace_bytes(matrices, cfg=None)
     muon_workspace_status(workspace, stream=None), last_call_status(device=None)
-    muon_debug_set_loop_fault(mode)
+    muon_debug_set_loop_fault(mode), muon_set_ns_schedule(schedule), muon_set_gemm_tiling(width)
     muon_ns_config_default(), muon_last_error(), muon_abi_version()
 """
 from __future__ import annotations
@@ -33,19 +33,20 @@ __all__ = [
     "adamw_step_multi", "MuonAdamTensor", "muon_merge_small_dims",
     "muon_timing_enable", "muon_timing_collect", "muon_last_error", "muon_abi_version", "make_config",
     "muon_set_ns_schedule", "KERNEL_KINDS", "NS_SCHEDULES", "muon_workspace_status", "last_call_status",
-    "muon_debug_set_loop_fault",
+    "muon_debug_set_loop_fault", "muon_set_gemm_tiling", "GEMM_TILINGS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmuon_hip.so")
 EXPORTED_SYMBOLS = ("muon_ns_config_default", "muon_workspace_bytes", "ns_orthogonalize_batched",
                     "ns_orthogonalize_batched_noalloc",
                     "muon_step_batched", "muon_step_multi_workspace_bytes", "muon_step_multi",
-                    "adamw_step_multi", "muon_merge_small_dims", "muon_set_ns_schedule", "muon_timing_enable",
+                    "adamw_step_multi", "muon_merge_small_dims", "muon_set_ns_schedule", "muon_set_gemm_tiling", "muon_timing_enable",
                     "muon_timing_collect", "muon_workspace_status", "muon_debug_set_loop_fault",
                     "muon_last_error", "muon_abi_version")
 NOALLOC_SCRATCH_BYTES = 64 << 20   # MUON_NOALLOC_SCRATCH_BYTES of the header
 KERNEL_KINDS = ("prep", "norm_finalize", "gram", "poly", "bx", "finish", "small", "adamw", "ns_loop")
 NS_SCHEDULES = {"auto": 0, "per_product": 1, "persistent": 2}
+GEMM_TILINGS = (0, 64, 128, 256)
 
 MUON_OK = 0
 _STATUS_NAMES = {0: "MUON_OK", 1: "MUON_ERR_INVALID_ARG", 2: "MUON_ERR_SHAPE", 3: "MUON_ERR_ALIGNMENT",
@@ -126,6 +127,8 @@ def load_library():
         lib.muon_workspace_status.restype = ctypes.c_int
         lib.muon_debug_set_loop_fault.argtypes = [i32]
         lib.muon_debug_set_loop_fault.restype = ctypes.c_int
+        lib.muon_set_gemm_tiling.argtypes = [i32]
+        lib.muon_set_gemm_tiling.restype = ctypes.c_int
         lib.muon_last_error.argtypes = []
         lib.muon_last_error.restype = ctypes.c_char_p
         lib.muon_abi_version.argtypes = []
@@ -163,6 +166,16 @@ def muon_set_ns_schedule(schedule: str) -> None:
     if schedule not in NS_SCHEDULES:
         raise ValueError(f"schedule must be one of {sorted(NS_SCHEDULES)}")
     _check(load_library().muon_set_ns_schedule(NS_SCHEDULES[schedule]))
+
+
+def muon_set_gemm_tiling(width: int = 0) -> None:
+    """Process-wide tile width of the per-product launches: 0 (the default:
+    per launch, the lowest estimated time), 64, 128 or 256 (256 where both
+    padded block sides are multiples of 256, else 128).  Results are bitwise
+    equal."""
+    if width not in GEMM_TILINGS:
+        raise ValueError(f"tile width must be one of {GEMM_TILINGS}")
+    _check(load_library().muon_set_gemm_tiling(int(width)))
 
 
 def muon_timing_enable(kinds=()) -> None:

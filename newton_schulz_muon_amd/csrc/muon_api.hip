@@ -714,6 +714,7 @@ muon_status ns_orthogonalize_batched_noalloc(const void* x, void* out, int64_t b
         TimingOff() { g_timing_off = true; }
         ~TimingOff() { g_timing_off = false; }
     } no_events;
+    const TileTrialsOff no_tile_events;
     return ns_batched_impl(x, out, batch, rows, cols, view_blocks, cfg_in, ws, need, stream, true);
 }
 
@@ -1165,6 +1166,14 @@ muon_status muon_workspace_status(const void* workspace, uint32_t* status_out, v
     const hipError_t e = hipMemcpyAsync(status_out, workspace, 2 * sizeof(uint32_t), hipMemcpyDefault,
                                         static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MUON_OK : hip_fail(e, "muon_workspace_status copy");
+}
+
+muon_status muon_set_gemm_tiling(int32_t width) {
+    g_err.clear();
+    if (width != 0 && width != 64 && width != 128 && width != 256)
+        return fail(MUON_ERR_INVALID_ARG, "tile width %d is not 0, 64, 128 or 256", width);
+    set_gemm_tiling(width);
+    return MUON_OK;
 }
 
 muon_status muon_debug_set_loop_fault(int32_t mode) {

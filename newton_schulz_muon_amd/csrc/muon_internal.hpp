@@ -212,6 +212,22 @@ void set_ns_schedule(int mode);
 // Diagnostics: 0 normal; 1 every loop launch sets its error word at its start;
 // 2 every dependency wait of the loop that is not met at once times out.
 void set_loop_fault(int mode);
+// Tile width of the per-product launches: 0 by the cost model (default); 64,
+// 128 or 256 where the block shapes allow it (256: padded sides multiples of
+// 256; otherwise 128).
+void set_gemm_tiling(int width);
+// While one exists on a thread, per-product launches of that thread create,
+// record and query no events for the automatic tiling choice (they use a
+// settled choice or the estimate): for callers that may not allocate.
+class TileTrialsOff {
+public:
+    TileTrialsOff();
+    ~TileTrialsOff();
+    TileTrialsOff(const TileTrialsOff&) = delete;
+    TileTrialsOff& operator=(const TileTrialsOff&) = delete;
+private:
+    bool prev_;
+};
 
 // AdamW for the non-matrix parameters (adamw.hip): one launch over up to
 // kAdamTab tensors.  decay = 1 - lr lr_mul wd wd_mul (exactly 1 when wd = 0),

@@ -115,8 +115,11 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
 //    line), and the other workgroup on the CU covers the first fragment
 //    reads of each step.
 //
-// Waves: a 128-wide tile is computed by 4 waves of 64 x 64, a 256-wide tile
-// by 8 waves of 128 x 64 (two per SIMD, 128 accumulator registers each).
+// Waves: a 64-wide tile is computed by 4 waves of 32 x 32, a 128-wide tile by
+// 4 waves of 64 x 64, a 256-wide tile by 8 waves of 128 x 64 (two per SIMD,
+// 128 accumulator registers each).  The 64-wide tiles are for batches too
+// small to fill the CUs, whose time is the chain of dependent products: a
+// shorter tile shortens every link.
 // With one wave per SIMD, the DMA issue, the vmcnt wait and the barrier of
 // each step leave the matrix core idle for about a quarter of the loop; a
 // second wave on the SIMD issues its MFMAs in those gaps.
@@ -194,8 +197,14 @@ struct RowDma {
 // read touch land in 4 distinct 64-byte bank groups.
 // One DMA instruction of one wave fills 1 KB = 512 / C rows.
 template <int C>
+__device__ __forceinline__ int col_swz(int row) {
+    // C >= 128: 16 or more chunks per row, XOR 4 (row % 4); C = 64 (8 chunks):
+    // XOR 4 ((row / 2) % 2), so rows r and r + 2, which share banks, differ
+    return C >= 128 ? (row & 3) << 2 : ((row >> 1) & 1) << 2;
+}
+template <int C>
 __device__ __forceinline__ int col_off(int row, int col) {
-    return row * (2 * C) + (((col >> 3) ^ ((row & 3) << 2)) << 4) + (((col >> 2) & 1) << 3);
+    return row * (2 * C) + (((col >> 3) ^ col_swz<C>(row)) << 4) + (((col >> 2) & 1) << 3);
 }
 
 template <int C, int BK_, int NW, int LO_SEG = -1>
@@ -225,7 +234,7 @@ struct ColDma {
 #pragma unroll
         for (int q = 0; q < PW; ++q) {
             const int row = ROWS_PER_WIN * (w * PW + q) + l / (C / 8);
-            const int chunk = (l % (C / 8)) ^ ((row & 3) << 2);
+            const int chunk = (l % (C / 8)) ^ col_swz<C>(row);
             voff[q] = static_cast<uint32_t>(((int64_t)row * ld + col0 + chunk * 8) * 2);
         }
     }
@@ -416,7 +425,7 @@ __device__ __forceinline__ uint32_t xcd_logical(uint32_t w, uint32_t total) {
 // row, 16 chunks) are both conflict-free.
 template <int TW>
 __device__ __forceinline__ int f32_off(int row, int col) {
-    return row * (TW * 4) + (((col >> 2) ^ (row & 15)) << 4);
+    return row * (TW * 4) + (((col >> 2) ^ (row & (TW >= 64 ? 15 : TW / 4 - 1))) << 4);
 }
 // bf16 chunk for the mirror store: rows of TW bf16, 16-byte chunk index XOR
 // an even row function chosen so that the transposing reads (rows 0-3 and
@@ -424,7 +433,8 @@ __device__ __forceinline__ int f32_off(int row, int col) {
 template <int TW>
 __device__ __forceinline__ int mir_off(int row, int col) {
     const int f = TW == 128 ? 2 * ((row & 3) | (((row >> 3) & 1) << 2))
-                            : 2 * (((row >> 1) & 1) | (((row >> 3) & 1) << 1));
+                : TW == 64  ? 2 * (((row >> 1) & 1) | (((row >> 3) & 1) << 1))
+                            : 2 * ((row >> 1) & 1);
     return row * (TW * 2) + (((col >> 3) ^ f) << 4) + (((col >> 2) & 1) << 3);
 }
 
@@ -490,9 +500,13 @@ struct TileJob {
 
 // LDS bytes of one tile of KIND at width BT (the operand stages; the
 // epilogue staging reuses them).
+template <int BT, int KIND>
+constexpr bool ring_pipeline() {
+    return BT != 128 || KIND == kBx || KIND == kBxSplit;
+}
 template <int KIND, int BT>
 constexpr int tile_lds_bytes() {
-    using Cfg = TileCfg<BT, BT == 256 || KIND == kBx || KIND == kBxSplit>;
+    using Cfg = TileCfg<BT, ring_pipeline<BT, KIND>()>;
     return Cfg::NS * 2 * Cfg::OP_BYTES;
 }
 
@@ -514,7 +528,7 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
     // every product out of the loop (and spill it).
     int tid = static_cast<int>(threadIdx.x);
     if constexpr (OPAQUE_TID) asm volatile("" : "+v"(tid));
-    using Cfg = TileCfg<BT, BT == 256 || KIND == kBx || KIND == kBxSplit>;
+    using Cfg = TileCfg<BT, ring_pipeline<BT, KIND>()>;
     constexpr int FA = Cfg::FA, FB = Cfg::FB, TWR = Cfg::TWR, TWC = Cfg::TWC, NW = Cfg::NW;
     constexpr bool SYM = KIND == kGram || KIND == kPoly || KIND == kPolySplit;
     constexpr bool POLY = KIND == kPoly || KIND == kPolySplit;
@@ -566,7 +580,7 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
     static_assert(U % 2 == 0, "fragment ping-pong restarts at 0 each step");
     constexpr int NREAD = (KMAJOR_A ? 2 * FA : FA) + (KMAJOR_B ? 2 * FB : FB);
     constexpr int NM = FA * FB;
-    constexpr bool SPREAD = NW == 8;
+    constexpr bool SPREAD = NW == 8 || NM < NREAD;
     constexpr int W = Ops::WINDOWS;
     const int nk = static_cast<int>(NSEG * a.K / BK);
     bf16x8 fa[2][FA], fb[2][FB];
@@ -1221,6 +1235,11 @@ __global__ void k_loop_setup(SetupArgs z) {
 // Every kernel instantiation is named explicitly: with implicit instantiation
 // from the launchers below, hipcc emitted host launch stubs for only some of
 // them, leaving undefined symbols in the shared library.
+template __global__ void k_gemm<kGram, 64>(GemmArgs);
+template __global__ void k_gemm<kPoly, 64>(GemmArgs);
+template __global__ void k_gemm<kPolySplit, 64>(GemmArgs);
+template __global__ void k_gemm<kBx, 64>(GemmArgs);
+template __global__ void k_gemm<kBxSplit, 64>(GemmArgs);
 template __global__ void k_gemm<kGram, 128>(GemmArgs);
 template __global__ void k_gemm<kGram, 256>(GemmArgs);
 template __global__ void k_gemm<kPoly, 128>(GemmArgs);
@@ -1264,9 +1283,155 @@ int64_t device_cus() {
 // step as 128-wide tiles).
 double round_cycles_big(int64_t K, bool sym) { return 1305.0 * double(K / 32) + (sym ? 25000.0 : 12000.0); }
 double round_cycles_small(int64_t K) { return 812.0 * double(K / 32) + 8500.0; }
+// 64-wide tiles: up to kTinyPerCU workgroups share a CU (32 KB of LDS each).
+// A K step costs more per resident tile as the CU fills (LDS bandwidth: 4
+// waves of 32 x 32 read twice the operand bytes per MFMA of the 64 x 64 wave
+// tiles); measured per kind, cycles per K step with 1..5 tiles per CU.
+constexpr int64_t kTinyPerCU = 5;
+template <int KIND>
+double tiny_step_cycles(int64_t per_cu) {
+    static constexpr double gram[5] = {381, 510, 851, 1414, 1816};
+    static constexpr double poly[5] = {373, 496, 664, 1218, 1419};
+    static constexpr double poly_split[5] = {274, 371, 599, 911, 1477};
+    static constexpr double bx[5] = {378, 552, 735, 1126, 1493};
+    static constexpr double bx_split[5] = {585, 740, 835, 1162, 1494};    // per K step of the 3 K reduction
+    const double* t = KIND == kGram ? gram : KIND == kPoly ? poly : KIND == kPolySplit ? poly_split
+                    : KIND == kBx ? bx : bx_split;
+    return t[per_cu - 1];
+}
+template <int KIND>
+double tiny_cycles(int64_t tiles, int64_t K, int64_t cus) {
+    const int64_t per_cu = (tiles + cus - 1) / cus;                 // tiles each CU runs in total
+    const int64_t rounds = (per_cu + kTinyPerCU - 1) / kTinyPerCU;
+    const int64_t last = per_cu - (rounds - 1) * kTinyPerCU;
+    return 6500.0 + double(K / 32) * (double(rounds - 1) * tiny_step_cycles<KIND>(kTinyPerCU) +
+                                      tiny_step_cycles<KIND>(last));
+}
 
-// Tiling of one launch (n products of one kind), by the estimated duration
-// of three plans over all their tiles together:
+std::atomic<int> g_gemm_tiling{0};
+
+// ---- automatic tiling
+// The tilings give bitwise the same results but none of the estimates above
+// ranks them reliably across shapes (the per-K-step cost depends on how many
+// tiles share a CU, on L2 reuse and on the store traffic), so the choice is
+// measured: per launch signature (kind, reduction length, device and every
+// problem's padded sides and block count), the plans estimated within 2x of
+// the best estimate each run kTileTrials launches timed with an event pair
+// on the launch's stream, and once all those events have completed the plan
+// with the lowest minimum time is kept.  Until then, and for launches that
+// may not time (stream capture, the allocation-free entry point, more than
+// kMaxTileKeys signatures), the best estimate is used.
+constexpr int kTilePlans = 4;        // 64-wide, 128-wide, 256-wide, 256-wide with 128-wide quadrant tail
+constexpr int kTileTrials = 3;
+constexpr size_t kMaxTileKeys = 1024;
+struct TileTune {
+    int ncand = 0;
+    int cand[kTilePlans] = {};
+    int issued = 0;                                  // trial launches handed out
+    int decided = -1;                                // the plan, or -1 while trials run
+    hipEvent_t ev[kTilePlans * kTileTrials][2] = {};
+    bool recorded[kTilePlans * kTileTrials] = {};
+};
+std::mutex g_tile_mu;
+std::map<std::vector<int64_t>, TileTune> g_tile;     // under g_tile_mu (entries are never erased)
+thread_local bool t_tile_no_trials = false;
+
+struct TileChoice {
+    int plan;
+    TileTune* tune = nullptr;                        // set for a timed trial launch
+    int trial = -1;
+    bool started = false;
+};
+
+// Under g_tile_mu: decides once every trial's events have completed; false
+// while some are pending.
+bool tile_decide(TileTune& t, int fallback) {
+    const int ntr = t.ncand * kTileTrials;
+    for (int i = 0; i < ntr; ++i) {
+        if (!t.recorded[i]) continue;
+        const hipError_t q = hipEventQuery(t.ev[i][1]);
+        if (q == hipErrorNotReady) return false;
+        if (q != hipSuccess) t.recorded[i] = false;
+    }
+    float best[kTilePlans];
+    for (float& b : best) b = -1.f;
+    for (int i = 0; i < ntr; ++i) {
+        float ms = 0.f;
+        if (!t.recorded[i] || hipEventElapsedTime(&ms, t.ev[i][0], t.ev[i][1]) != hipSuccess) continue;
+        float& b = best[i % t.ncand];
+        if (b < 0.f || ms < b) b = ms;
+    }
+    t.decided = fallback;
+    float win = -1.f;
+    for (int c = 0; c < t.ncand; ++c)
+        if (best[c] >= 0.f && (win < 0.f || best[c] < win)) {
+            win = best[c];
+            t.decided = t.cand[c];
+        }
+    for (auto& pair : t.ev)
+        for (hipEvent_t& e : pair)
+            if (e) {
+                (void)hipEventDestroy(e);
+                e = nullptr;
+            }
+    return true;
+}
+
+// est[p]: the plan's estimated cycles (kNever where it does not apply).
+TileChoice tile_choose(const std::vector<int64_t>& key, const double (&est)[kTilePlans], hipStream_t s) {
+    int model = 1;
+    for (int p = 0; p < kTilePlans; ++p)
+        if (est[p] < est[model]) model = p;
+    TileChoice c{model};
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    const bool can_time = !t_tile_no_trials && hipStreamIsCapturing(s, &cs) == hipSuccess &&
+                          cs == hipStreamCaptureStatusNone;
+    std::lock_guard<std::mutex> lock(g_tile_mu);
+    auto it = g_tile.find(key);
+    if (it == g_tile.end()) {
+        if (!can_time || g_tile.size() >= kMaxTileKeys) return c;
+        TileTune t;
+        for (int p = 0; p < kTilePlans; ++p)
+            if (est[p] <= 2.0 * est[model]) t.cand[t.ncand++] = p;
+        if (t.ncand < 2) t.decided = model;
+        it = g_tile.emplace(key, t).first;
+    }
+    TileTune& t = it->second;
+    if (t.decided >= 0) {
+        c.plan = t.decided;
+        return c;
+    }
+    if (!can_time) return c;
+    if (t.issued >= t.ncand * kTileTrials) {
+        if (tile_decide(t, model)) c.plan = t.decided;
+        return c;
+    }
+    const int i = t.issued;
+    for (hipEvent_t& e : t.ev[i])
+        if (!e && hipEventCreate(&e) != hipSuccess) return c;
+    ++t.issued;
+    c.plan = t.cand[i % t.ncand];
+    c.tune = &t;
+    c.trial = i;
+    return c;
+}
+
+void tile_trial_start(TileChoice& c, hipStream_t s) {
+    if (c.trial < 0) return;
+    std::lock_guard<std::mutex> lock(g_tile_mu);
+    c.started = hipEventRecord(c.tune->ev[c.trial][0], s) == hipSuccess;
+}
+
+void tile_trial_end(const TileChoice& c, hipStream_t s) {
+    if (c.trial < 0 || !c.started) return;
+    std::lock_guard<std::mutex> lock(g_tile_mu);
+    if (hipEventRecord(c.tune->ev[c.trial][1], s) == hipSuccess) c.tune->recorded[c.trial] = true;
+}
+
+// Tiling of one launch (n products of one kind): the width set with
+// set_gemm_tiling where the shapes allow it, else by the automatic choice
+// above among four plans, estimated over all their tiles together:
+//  * 64-wide tiles throughout (up to 1024 per round);
 //  * 128-wide tiles throughout (512 per round);
 //  * 256-wide tiles (256 per round) with the last partial round split into
 //    128-wide quadrants in a second launch;
@@ -1318,8 +1483,10 @@ hipError_t run(const Plan* const* plans, GemmArgs a, hipStream_t s) {
         last_exec_flops() += double(tiles) * 2.0 * double(bt) * double(bt) * double(Kc);
         if (bt == 256) {
             k_gemm<KIND, 256><<<dim3(a.total), dim3(tile_threads<256>()), 0, s>>>(a);
-        } else {
+        } else if (bt == 128) {
             k_gemm<KIND, 128><<<dim3(a.total), dim3(tile_threads<128>()), 0, s>>>(a);
+        } else {
+            k_gemm<KIND, 64><<<dim3(a.total), dim3(tile_threads<64>()), 0, s>>>(a);
         }
         return hipGetLastError();
     };
@@ -1329,27 +1496,67 @@ hipError_t run(const Plan* const* plans, GemmArgs a, hipStream_t s) {
         if (a.pr[i].K != K) return hipErrorInvalidValue;
         big_ok = big_ok && plans[i]->mp % 256 == 0 && (SYM || plans[i]->np % 256 == 0);
     }
+    constexpr double kNever = 1e300;
     const int64_t small = geometry(128);
     if (small < 0) return hipErrorInvalidValue;
     const double t_small = double((small + 2 * kCUs - 1) / (2 * kCUs)) * round_cycles_small(Kc);
+    const int64_t tiny = geometry(64);      // negative past the tile index range
+    const double t_tiny = tiny < 0 ? kNever : tiny_cycles<KIND>(tiny, Kc, kCUs);
+    int64_t big = 0, full = 0, tail = 0;
+    double t_big = kNever, t_split = kNever;
     if (big_ok) {
-        const int64_t big = geometry(256);
-        const int64_t full = big / kCUs, tail = big % kCUs;
+        big = geometry(256);
+        full = big / kCUs;
+        tail = big % kCUs;
         const double rb = round_cycles_big(Kc, SYM);
-        const double t_split = double(full) * rb +
-                               double((4 * tail + 2 * kCUs - 1) / (2 * kCUs)) * round_cycles_small(Kc);
-        const double t_big = double(full + (tail ? 1 : 0)) * rb;
-        if (t_big <= t_split && t_big < t_small) return launch(256, big, 0, 0);
-        if (t_split < t_small) {
-            if (full > 0) {
-                const hipError_t e = launch(256, full * kCUs, 0, 0);
-                if (e != hipSuccess || tail == 0) return e;
-            }
-            return launch(128, 4 * tail, 1, static_cast<uint32_t>(full * kCUs));
-        }
-        geometry(128);
+        t_split = double(full) * rb + double((4 * tail + 2 * kCUs - 1) / (2 * kCUs)) * round_cycles_small(Kc);
+        t_big = double(full + (tail ? 1 : 0)) * rb;
     }
-    return launch(128, small, 0, 0);
+    // plan: 0 = 64-wide, 1 = 128-wide, 2 = 256-wide, 3 = 256-wide with 128-wide quadrants for the tail
+    TileChoice ch{1};
+    const int force = g_gemm_tiling.load();
+    if (force == 64 && tiny >= 0) {
+        ch.plan = 0;
+    } else if (force == 128 || (force == 256 && !big_ok)) {
+        ch.plan = 1;
+    } else if (force == 256) {
+        ch.plan = 2;
+    } else {
+        // the split plan is distinct only with both full rounds and a tail
+        const double est[kTilePlans] = {t_tiny, t_small, t_big, full > 0 && tail > 0 ? t_split : kNever};
+        std::vector<int64_t> key = {KIND, Kc, device_cus(), a.n};
+        for (int i = 0; i < a.n; ++i) {
+            key.push_back(plans[i]->mp);
+            key.push_back(plans[i]->np);
+            key.push_back(plans[i]->nb);
+        }
+        int dev = 0;
+        if (hipGetDevice(&dev) == hipSuccess) key.push_back(dev);
+        ch = tile_choose(key, est, s);
+    }
+    tile_trial_start(ch, s);
+    hipError_t e = hipSuccess;
+    switch (ch.plan) {
+        case 0:
+            geometry(64);
+            e = launch(64, tiny, 0, 0);
+            break;
+        case 2:
+            geometry(256);
+            e = launch(256, big, 0, 0);
+            break;
+        case 3:
+            geometry(256);
+            if (full > 0) e = launch(256, full * kCUs, 0, 0);
+            if (e == hipSuccess && tail > 0) e = launch(128, 4 * tail, 1, static_cast<uint32_t>(full * kCUs));
+            break;
+        default:
+            geometry(128);
+            e = launch(128, small, 0, 0);
+            break;
+    }
+    tile_trial_end(ch, s);
+    return e;
 }
 
 }  // namespace
@@ -1496,6 +1703,9 @@ hipError_t build_schedule(const std::vector<LoopDims>& dims, const std::vector<i
 
 void set_ns_schedule(int mode) { g_ns_mode.store(mode); }
 void set_loop_fault(int mode) { g_loop_fault.store(mode); }
+void set_gemm_tiling(int width) { g_gemm_tiling.store(width); }
+TileTrialsOff::TileTrialsOff() : prev_(t_tile_no_trials) { t_tile_no_trials = true; }
+TileTrialsOff::~TileTrialsOff() { t_tile_no_trials = prev_; }
 
 // Cache key of a schedule: device, steps, workgroups, then (mp, np, nb) per problem.
 std::vector<int64_t> schedule_key(const NsLoopProblem* probs, int n, int ns_steps, int dev, int cus) {

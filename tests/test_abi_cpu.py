@@ -325,6 +325,18 @@ def test_ns_schedule_modes(lib):
         nsm.muon_set_ns_schedule("fast")
 
 
+def test_gemm_tiling_widths(lib):
+    # Host-only: the process-wide tile width takes 0, 64, 128, 256
+    for w in (64, 128, 256, 0):
+        assert lib.muon_set_gemm_tiling(w) == 0
+    for bad in (-1, 1, 32, 96, 512):
+        assert lib.muon_set_gemm_tiling(bad) == 1
+        assert "tile width" in nsm.muon_last_error()
+        with pytest.raises(ValueError):
+            nsm.muon_set_gemm_tiling(bad)
+    nsm.muon_set_gemm_tiling(0)
+
+
 def test_workspace_status_validation(lib):
     # host-side checks only (no copy is enqueued)
     assert lib.muon_workspace_status(None, ctypes.c_void_p(1 << 30), None) == 1
