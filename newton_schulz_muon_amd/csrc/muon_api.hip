@@ -126,6 +126,8 @@ muon_status make_plan(int64_t batch, int64_t rows, int64_t cols, int32_t v,
     if (split) { p.off_blo = off; off = align256(off + abytes); }
     p.off_part = off; off = align256(off + size_t(p.nb) * size_t(p.ew_tiles) * 4);
     p.off_scale = off; off = align256(off + size_t(p.nb) * 2 * 4);
+    p.trace_stride = round_up(p.mp / 32, 32);
+    p.off_trace = off; off = align256(off + size_t(p.nb) * size_t(p.trace_stride) * 4);
     p.off_sync = off; off += ns_loop_sync_bytes(p.nb);
     p.total = off;
     return MUON_OK;
@@ -263,6 +265,7 @@ struct Buffers {
     uint16_t* bl;
     float* part;
     float* scale;
+    float* trace;
     uint32_t* sync;
 };
 
@@ -279,6 +282,7 @@ Buffers carve(const Plan& p, void* ws) {
     b.bl = split ? reinterpret_cast<uint16_t*>(base + p.off_blo) : nullptr;
     b.part = reinterpret_cast<float*>(base + p.off_part);
     b.scale = reinterpret_cast<float*>(base + p.off_scale);
+    b.trace = reinterpret_cast<float*>(base + p.off_trace);
     b.sync = reinterpret_cast<uint32_t*>(base + p.off_sync);
     return b;
 }
@@ -336,21 +340,29 @@ NsEnds ns_ends(const Plan& p, const muon_ns_config& cfg, const Buffers& b, const
     return e;
 }
 
-// Runs finalize + the NS loop on an iterate already prepared by k_prep
-// (e.x0: in xh[0] and xl[0], or the caller's x in place) with the schedule
-// resolved before the call enqueued anything.  Returns the buffer index of
-// the result (when it is not e.xlast outside the workspace).
+// Runs the NS iterations on an iterate already prepared by k_prep (e.x0: in
+// xh[0] and xl[0], or the caller's x in place) with the schedule resolved
+// before the call enqueued anything.  The first iteration's Gram also yields
+// the norm |X|_F^2 = trace(X X^T) (partials in b.trace); with no iteration
+// the prep's sums of squares are finalized instead (for k_finish).
+// clear_status: the first kernel enqueued here clears the call's status
+// words (no prep did).  Returns the buffer index of the result (when it is
+// not e.xlast outside the workspace).
 muon_status run_ns(const Plan& p, const muon_ns_config& cfg, const Buffers& b, const NsEnds& ends,
-                   const NsChoice& ch, uint2* items, uint64_t items_cap, uint32_t* status, hipStream_t s,
-                   int* final_idx) {
-    hipError_t e = timed(MUON_KERNEL_NORM_FINALIZE, s, [&] { return launch_norm_finalize(p, b.part, b.scale, cfg.eps, s); });
-    if (e != hipSuccess) return hip_fail(e, "k_norm_finalize launch");
+                   const NsChoice& ch, uint2* items, uint64_t items_cap, uint32_t* status, bool clear_status,
+                   hipStream_t s, int* final_idx) {
+    hipError_t e = hipSuccess;
     *final_idx = cfg.ns_steps & 1;
+    if (cfg.ns_steps == 0) {
+        e = timed(MUON_KERNEL_NORM_FINALIZE, s, [&] { return launch_norm_finalize(p, b.part, b.scale, cfg.eps, s); });
+        return e == hipSuccess ? MUON_OK : hip_fail(e, "k_norm_finalize launch");
+    }
     ns_schedule_start(ch, s);
     if (ch.persistent) {
-        const NsLoopProblem lp{&p, ends.x0, {b.xh[0], b.xh[1]}, ends.xlast, b.a, b.bh, b.scale, b.sync, {b.xl[0], b.xl[1]}, b.bl};
+        const NsLoopProblem lp{&p, ends.x0, {b.xh[0], b.xh[1]}, ends.xlast, b.a, b.bh, b.trace, b.sync, {b.xl[0], b.xl[1]}, b.bl};
         e = timed(MUON_KERNEL_NS_LOOP, s, [&] {
-            return launch_ns_loop(&lp, 1, cfg.ns_steps, cfg.a, cfg.b, cfg.c, ch, items, items_cap, status, s);
+            return launch_ns_loop(&lp, 1, cfg.ns_steps, cfg.a, cfg.b, cfg.c, cfg.eps, ch, items, items_cap, status,
+                                  clear_status, s);
         }, ns_flops(p, cfg.ns_steps));
         if (e != hipSuccess) return hip_fail(e, "k_ns_loop launch");
         ns_schedule_end(ch, s);
@@ -358,17 +370,19 @@ muon_status run_ns(const Plan& p, const muon_ns_config& cfg, const Buffers& b, c
     }
     for (int it = 0; it < cfg.ns_steps; ++it) {
         const int cur = it & 1;
-        const float* sc = it == 0 ? b.scale : nullptr;
+        float* tr = it == 0 ? b.trace : nullptr;
         const uint16_t* xin = it == 0 ? ends.x0 : b.xh[cur];
         uint16_t* xout = it + 1 == cfg.ns_steps ? ends.xlast : b.xh[cur ^ 1];
-        e = timed(MUON_KERNEL_GRAM, s, [&] { return launch_gram(p, xin, b.a, sc, s); },
+        uint32_t* clr = it == 0 && clear_status ? status : nullptr;
+        e = timed(MUON_KERNEL_GRAM, s, [&] { return launch_gram(p, xin, b.a, tr, clr, s); },
                   product_flops(p, MUON_KERNEL_GRAM));
         if (e != hipSuccess) return hip_fail(e, "k_gemm<gram> launch");
-        e = timed(MUON_KERNEL_POLY, s, [&] { return launch_poly(p, b.a, b.bh, b.bl, cfg.a, cfg.b, cfg.c, s); },
-                  product_flops(p, MUON_KERNEL_POLY));
+        e = timed(MUON_KERNEL_POLY, s, [&] {
+            return launch_poly(p, b.a, b.bh, b.bl, cfg.a, cfg.b, cfg.c, tr, cfg.eps, s);
+        }, product_flops(p, MUON_KERNEL_POLY));
         if (e != hipSuccess) return hip_fail(e, "k_gemm<poly> launch");
         e = timed(MUON_KERNEL_BX, s, [&] {
-            return launch_bx(p, b.bh, b.bl, xin, b.xl[cur], xout, b.xl[cur ^ 1], sc, s);
+            return launch_bx(p, b.bh, b.bl, xin, b.xl[cur], xout, b.xl[cur ^ 1], tr, cfg.eps, s);
         }, product_flops(p, MUON_KERNEL_BX));
         if (e != hipSuccess) return hip_fail(e, "k_gemm<bx> launch");
     }
@@ -533,6 +547,7 @@ Buffers chunk_buffers(const Plan& p, const Buffers& b, int64_t m0) {
     }
     c.part = b.part + blk0 * p.ew_tiles;
     c.scale = b.scale + 2 * blk0;
+    c.trace = b.trace + blk0 * p.trace_stride;
     return c;
 }
 
@@ -638,15 +653,21 @@ muon_status ns_batched_impl(const void* x, void* out, int64_t batch, int64_t row
     const Buffers b = carve(p, ws + kHeaderBytes);
     const NsEnds ends = ns_ends(p, cfg, b, x, out);
     // The schedule (and on first use its queue) is settled before anything is enqueued.
-    const NsLoopProblem lp{&p, ends.x0, {b.xh[0], b.xh[1]}, ends.xlast, b.a, b.bh, b.scale, b.sync, {b.xl[0], b.xl[1]}, b.bl};
+    const NsLoopProblem lp{&p, ends.x0, {b.xh[0], b.xh[1]}, ends.xlast, b.a, b.bh, b.trace, b.sync, {b.xl[0], b.xl[1]}, b.bl};
     const NsChoice ch = per_product_only ? NsChoice() : ns_schedule_begin(&lp, 1, cfg.ns_steps, s);
-    hipError_t e = timed(MUON_KERNEL_PREP, s, [&] {
-        return launch_prep(p, kPrepCast, static_cast<const uint16_t*>(x), nullptr, 0.f,
-                           ends.direct_in ? nullptr : b.xh[0], b.xl[0], b.part, status, s);
-    });
-    if (e != hipSuccess) return hip_fail(e, "k_prep launch");
+    hipError_t e = hipSuccess;
+    // With x read in place there is nothing to prepare: the first Gram also
+    // yields the norm.
+    if (!ends.direct_in) {
+        e = timed(MUON_KERNEL_PREP, s, [&] {
+            return launch_prep(p, kPrepCast, static_cast<const uint16_t*>(x), nullptr, 0.f, b.xh[0], b.xl[0],
+                               cfg.ns_steps == 0 ? b.part : nullptr, status, s);
+        });
+        if (e != hipSuccess) return hip_fail(e, "k_prep launch");
+    }
     int fin = 0;
-    st = run_ns(p, cfg, b, ends, ch, reinterpret_cast<uint2*>(ws + lay.items_off), lay.items_cap, status, s, &fin);
+    st = run_ns(p, cfg, b, ends, ch, reinterpret_cast<uint2*>(ws + lay.items_off), lay.items_cap, status,
+                ends.direct_in, s, &fin);
     if (st != MUON_OK) return st;
     if (ends.direct_out) return MUON_OK;
     e = timed(MUON_KERNEL_FINISH, s, [&] {
@@ -782,15 +803,16 @@ muon_status muon_step_batched(float* params, const void* grads, float* momentum_
     uint32_t* status = reinterpret_cast<uint32_t*>(ws);
     const Buffers b = carve(p, ws + kHeaderBytes);
     const NsEnds ends = ns_ends(p, cfg, b, nullptr, nullptr);
-    const NsLoopProblem lp{&p, ends.x0, {b.xh[0], b.xh[1]}, ends.xlast, b.a, b.bh, b.scale, b.sync, {b.xl[0], b.xl[1]}, b.bl};
+    const NsLoopProblem lp{&p, ends.x0, {b.xh[0], b.xh[1]}, ends.xlast, b.a, b.bh, b.trace, b.sync, {b.xl[0], b.xl[1]}, b.bl};
     const NsChoice ch = ns_schedule_begin(&lp, 1, cfg.ns_steps, s);
     hipError_t e = timed(MUON_KERNEL_PREP, s, [&] {
         return launch_prep(p, mode, static_cast<const uint16_t*>(grads), momentum_buf, momentum, b.xh[0], b.xl[0],
-                           b.part, status, s);
+                           cfg.ns_steps == 0 ? b.part : nullptr, status, s);
     });
     if (e != hipSuccess) return hip_fail(e, "k_prep launch");
     int fin = 0;
-    st = run_ns(p, cfg, b, ends, ch, reinterpret_cast<uint2*>(ws + lay.items_off), lay.items_cap, status, s, &fin);
+    st = run_ns(p, cfg, b, ends, ch, reinterpret_cast<uint2*>(ws + lay.items_off), lay.items_cap, status, false, s,
+                &fin);
     if (st != MUON_OK) return st;
     e = timed(MUON_KERNEL_FINISH, s, [&] {
         return launch_finish(p, b.xh[fin], b.xl[fin], cfg.ns_steps == 0 ? b.scale : nullptr, params, decay, step,
@@ -850,7 +872,7 @@ muon_status muon_step_multi(const muon_matrix* mats, int32_t count, float lr, fl
         const Buffers& bb = bufs[gi];
         wave_groups[g.wave].push_back(gi);
         wave_lps[g.wave].push_back(
-            NsLoopProblem{&g.plan, bb.xh[0], {bb.xh[0], bb.xh[1]}, bb.xh[cfg.ns_steps & 1], bb.a, bb.bh, bb.scale, bb.sync,
+            NsLoopProblem{&g.plan, bb.xh[0], {bb.xh[0], bb.xh[1]}, bb.xh[cfg.ns_steps & 1], bb.a, bb.bh, bb.trace, bb.sync,
                           {bb.xl[0], bb.xl[1]}, bb.bl});
     }
     for (int w = 0; w < nwaves; ++w)
@@ -896,15 +918,19 @@ muon_status muon_step_multi(const muon_matrix* mats, int32_t count, float lr, fl
                 uint32_t* reset = first_prep ? status : nullptr;
                 first_prep = false;
                 const hipError_t e = timed(MUON_KERNEL_PREP, s, [&] {
-                    return launch_prep(pc, mode, nullptr, nullptr, momentum, bc.xh[0], bc.xl[0], bc.part, reset, s,
-                                       &tab);
+                    return launch_prep(pc, mode, nullptr, nullptr, momentum, bc.xh[0], bc.xl[0],
+                                       cfg.ns_steps == 0 ? bc.part : nullptr, reset, s, &tab);
                 });
                 if (e != hipSuccess) return hip_fail(e, "k_prep launch");
             }
-            const hipError_t e = timed(MUON_KERNEL_NORM_FINALIZE, s, [&] {
-                return launch_norm_finalize(p, bufs[gi].part, bufs[gi].scale, cfg.eps, s);
-            });
-            if (e != hipSuccess) return hip_fail(e, "k_norm_finalize launch");
+            // With NS iterations the first Gram yields the norm; without, the
+            // prep's sums of squares give it.
+            if (cfg.ns_steps == 0) {
+                const hipError_t e = timed(MUON_KERNEL_NORM_FINALIZE, s, [&] {
+                    return launch_norm_finalize(p, bufs[gi].part, bufs[gi].scale, cfg.eps, s);
+                });
+                if (e != hipSuccess) return hip_fail(e, "k_norm_finalize launch");
+            }
         }
 
         // NS iterations: products of equal reduction length share launches.
@@ -932,8 +958,9 @@ muon_status muon_step_multi(const muon_matrix* mats, int32_t count, float lr, fl
             for (size_t gi : wave) fl += ns_flops(groups[gi].plan, cfg.ns_steps);
             const std::vector<NsLoopProblem>& lps = wave_lps[w];
             const hipError_t e = timed(MUON_KERNEL_NS_LOOP, s, [&] {
-                return launch_ns_loop(lps.data(), int(lps.size()), cfg.ns_steps, cfg.a, cfg.b, cfg.c, ch,
-                                      reinterpret_cast<uint2*>(ws + waves[w].items_off), waves[w].items_cap, status, s);
+                return launch_ns_loop(lps.data(), int(lps.size()), cfg.ns_steps, cfg.a, cfg.b, cfg.c, cfg.eps, ch,
+                                      reinterpret_cast<uint2*>(ws + waves[w].items_off), waves[w].items_cap, status,
+                                      false, s);
             }, fl);
             if (e != hipSuccess) return hip_fail(e, "k_ns_loop launch");
         }
@@ -944,11 +971,11 @@ muon_status muon_step_multi(const muon_matrix* mats, int32_t count, float lr, fl
                 double fl = 0.0;
                 for (size_t k = 0; k < bk.size(); ++k) {
                     const Buffers& b = bufs[bk[k]];
-                    ops[k] = GramOp{&groups[bk[k]].plan, b.xh[cur], b.a, it == 0 ? b.scale : nullptr};
+                    ops[k] = GramOp{&groups[bk[k]].plan, b.xh[cur], b.a, it == 0 ? b.trace : nullptr};
                     fl += product_flops(groups[bk[k]].plan, MUON_KERNEL_GRAM);
                 }
                 const hipError_t e =
-                    timed(MUON_KERNEL_GRAM, s, [&] { return launch_gram(ops, int(bk.size()), s); }, fl);
+                    timed(MUON_KERNEL_GRAM, s, [&] { return launch_gram(ops, int(bk.size()), nullptr, s); }, fl);
                 if (e != hipSuccess) return hip_fail(e, "k_gemm<gram> launch");
             }
             for (const auto& bk : by_mp) {
@@ -956,11 +983,11 @@ muon_status muon_step_multi(const muon_matrix* mats, int32_t count, float lr, fl
                 double fl = 0.0;
                 for (size_t k = 0; k < bk.size(); ++k) {
                     const Buffers& b = bufs[bk[k]];
-                    ops[k] = PolyOp{&groups[bk[k]].plan, b.a, b.bh, b.bl};
+                    ops[k] = PolyOp{&groups[bk[k]].plan, b.a, b.bh, b.bl, it == 0 ? b.trace : nullptr};
                     fl += product_flops(groups[bk[k]].plan, MUON_KERNEL_POLY);
                 }
                 const hipError_t e = timed(MUON_KERNEL_POLY, s, [&] {
-                    return launch_poly(ops, int(bk.size()), cfg.a, cfg.b, cfg.c, s);
+                    return launch_poly(ops, int(bk.size()), cfg.a, cfg.b, cfg.c, cfg.eps, s);
                 }, fl);
                 if (e != hipSuccess) return hip_fail(e, "k_gemm<poly> launch");
             }
@@ -970,10 +997,11 @@ muon_status muon_step_multi(const muon_matrix* mats, int32_t count, float lr, fl
                 for (size_t k = 0; k < bk.size(); ++k) {
                     const Buffers& b = bufs[bk[k]];
                     ops[k] = BxOp{&groups[bk[k]].plan, b.bh, b.bl, b.xh[cur], b.xl[cur], b.xh[cur ^ 1],
-                                  b.xl[cur ^ 1], it == 0 ? b.scale : nullptr};
+                                  b.xl[cur ^ 1], it == 0 ? b.trace : nullptr};
                     fl += product_flops(groups[bk[k]].plan, MUON_KERNEL_BX);
                 }
-                const hipError_t e = timed(MUON_KERNEL_BX, s, [&] { return launch_bx(ops, int(bk.size()), s); }, fl);
+                const hipError_t e =
+                    timed(MUON_KERNEL_BX, s, [&] { return launch_bx(ops, int(bk.size()), cfg.eps, s); }, fl);
                 if (e != hipSuccess) return hip_fail(e, "k_gemm<bx> launch");
             }
         }

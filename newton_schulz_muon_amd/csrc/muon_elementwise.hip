@@ -39,7 +39,7 @@ struct PrepArgs {
     uint16_t* dl;
     uint16_t* th;          // padded transposed copy [cp][rp] (hi, lo)
     uint16_t* tl;
-    float* part;           // [nb][ew_tiles]
+    float* part;           // [nb][ew_tiles] sums of squares, or null (not needed)
     int64_t r, c;          // stored block shape
     int64_t rp, cp;        // padded stored-orientation shape
     int64_t be;            // r * c
@@ -243,8 +243,10 @@ __global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
         }
     }
 
-    const float tot = block_sum_256(ss, red);
-    if (t == 0) a.part[blk * a.ew_tiles + tile] = tot;
+    if (a.part != nullptr) {   // uniform: the sums of squares only where the norm is taken here
+        const float tot = block_sum_256(ss, red);
+        if (t == 0) a.part[blk * a.ew_tiles + tile] = tot;
+    }
 }
 
 __global__ __launch_bounds__(256) void k_norm_finalize(const float* part, float* scales,
@@ -454,7 +456,7 @@ hipError_t run_prep(const Plan& p, const PrepArgs& a, hipStream_t s) {
         c.dl = a.dl ? a.dl + b0 * pad : nullptr;
         c.th = a.th ? a.th + b0 * pad : nullptr;
         c.tl = a.tl ? a.tl + b0 * pad : nullptr;
-        c.part = a.part + b0 * p.ew_tiles;
+        c.part = a.part ? a.part + b0 * p.ew_tiles : nullptr;
         k_prep<MODE, VEC, SPLIT, TALL><<<dim3(static_cast<unsigned>(p.ew_tiles), cnt), dim3(256), 0, s>>>(c);
     });
 }

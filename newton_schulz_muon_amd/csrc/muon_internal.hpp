@@ -38,6 +38,7 @@ struct Plan {
     int64_t mp = 0, np = 0;      // padded oriented shape
     int32_t precision = MUON_PRECISION_FAST;
     int64_t ew_tiles = 0;        // 64 x 64 tiles per padded block (norm partial slots)
+    int64_t trace_stride = 0;    // floats per block of the trace partials (mp / 32 rounded up to 32)
     // workspace byte offsets
     size_t off_x[2] = {0, 0};    // iterate ping-pong, bf16 [nb][mp][np] (hi plane)
     size_t off_xlo[2] = {0, 0};  // ACCURATE: lo planes
@@ -45,7 +46,8 @@ struct Plan {
     size_t off_b = 0;            // polynomial, bf16 [nb][mp][mp] (hi plane)
     size_t off_blo = 0;          // ACCURATE: lo plane of B
     size_t off_part = 0;         // fp32 [nb][ew_tiles] partial sums of squares
-    size_t off_scale = 0;        // fp32 [nb][2]: 1/s, 1/s^2
+    size_t off_scale = 0;        // fp32 [nb][2]: 1/s, 1/s^2 (the zero-iteration normalisation)
+    size_t off_trace = 0;        // fp32 [nb][trace_stride]: traces of X X^T's diagonal 32 x 32 blocks
     size_t off_sync = 0;         // u32 counters of the persistent NS loop (ns_loop_sync_bytes)
     size_t total = 0;
 };
@@ -111,17 +113,21 @@ hipError_t launch_finish(const Plan& p, const uint16_t* x_hi, const uint16_t* x_
 // MFMA kernels (ns_gemm.hip).  Each launcher takes 1 to 4 products of one
 // kind that share the reduction length; their tiles run in one launch (two
 // when the last round is split into quadrants).
+// In the first NS iteration `trace` points to the plan's norm partials (the
+// Gram writes the traces of its diagonal 32 x 32 blocks there; the
+// polynomial and B X derive s^-1 = 1 / (|X|_F + eps) from them); null later.
 struct GramOp {
     const Plan* plan;
     const uint16_t* x;
     uint16_t* a;
-    const float* scale2;
+    float* trace;
 };
 struct PolyOp {
     const Plan* plan;
     const uint16_t* a;
     uint16_t* b_hi;
     uint16_t* b_lo;
+    const float* trace;
 };
 struct BxOp {
     const Plan* plan;
@@ -131,26 +137,29 @@ struct BxOp {
     const uint16_t* x_lo;
     uint16_t* out_hi;
     uint16_t* out_lo;
-    const float* scale1;
+    const float* trace;
 };
 constexpr int kMaxGemmProblems = 4;
 // MFMA flops the GEMM launchers below (and the persistent loop) enqueue,
 // added up on the calling thread (timing diagnostics reset and read it).
 double& last_exec_flops();
-hipError_t launch_gram(const GramOp* ops, int n, hipStream_t s);
-hipError_t launch_poly(const PolyOp* ops, int n, float ca, float cb, float cc, hipStream_t s);
-hipError_t launch_bx(const BxOp* ops, int n, hipStream_t s);
-// Single-product forms.
-// A = scale2 * X X^T   (upper tiles computed, mirrored; scale2 may be null)
-hipError_t launch_gram(const Plan& p, const uint16_t* x, uint16_t* a, const float* scale2,
+// status: null, or the call's two status words, which the Gram launch clears.
+hipError_t launch_gram(const GramOp* ops, int n, uint32_t* status, hipStream_t s);
+hipError_t launch_poly(const PolyOp* ops, int n, float ca, float cb, float cc, float eps, hipStream_t s);
+hipError_t launch_bx(const BxOp* ops, int n, float eps, hipStream_t s);
+// Single-product forms.  With `trace` (the first iteration), s^-1 = 1 / (sqrt(sum of the
+// partials) + eps) as above.
+// A = X X^T   (upper tiles computed, mirrored; with trace also the norm partials)
+hipError_t launch_gram(const Plan& p, const uint16_t* x, uint16_t* a, float* trace, uint32_t* status,
                        hipStream_t s);
-// B' = a I + b A + c A A   (A symmetric; b_lo != nullptr stores the rounding residual)
+// B' = a I + b A + c A A, with trace a I + b s^-2 A + c s^-4 A A   (A symmetric; b_lo != nullptr
+// stores the rounding residual)
 hipError_t launch_poly(const Plan& p, const uint16_t* a, uint16_t* b_hi, uint16_t* b_lo,
-                       float ca, float cb, float cc, hipStream_t s);
-// X' = scale1 * B' X   (scale1 may be null; a X is carried by the diagonal of B').
-// ACCURATE when b_lo is given: X' = scale1 * (Bh Xh + Bh Xl + Bl Xh), stored as hi + lo.
+                       float ca, float cb, float cc, const float* trace, float eps, hipStream_t s);
+// X' = B' X, with trace s^-1 B' X   (a X is carried by the diagonal of B').
+// ACCURATE when b_lo is given: X' = (s^-1) (Bh Xh + Bh Xl + Bl Xh), stored as hi + lo.
 hipError_t launch_bx(const Plan& p, const uint16_t* b_hi, const uint16_t* b_lo, const uint16_t* x_hi,
-                     const uint16_t* x_lo, uint16_t* out_hi, uint16_t* out_lo, const float* scale1,
+                     const uint16_t* x_lo, uint16_t* out_hi, uint16_t* out_lo, const float* trace, float eps,
                      hipStream_t s);
 
 // Persistent NS loop (ns_gemm.hip): every iteration of the three products
@@ -159,8 +168,8 @@ hipError_t launch_bx(const Plan& p, const uint16_t* b_hi, const uint16_t* b_lo, 
 // completion counters.  Each problem brings a sync region of
 // ns_loop_sync_bytes(nb) (the launch zeroes it first).  Iteration 0 reads x0,
 // iteration t > 0 reads x[t % 2]; every iteration but the last writes
-// x[(t + 1) % 2] and the last writes xlast; the first one applies `scale` as
-// the per-product launches do.  ACCURATE adds the lo planes: iteration t
+// x[(t + 1) % 2] and the last writes xlast; the first one writes and reads
+// the norm partials `trace` as the per-product launches do.  ACCURATE adds the lo planes: iteration t
 // reads xlo[t % 2] and writes xlo[(t + 1) % 2] (so x0 = x[0], xlast =
 // x[ns_steps % 2] there), and B' is stored as b + blo.
 struct NsLoopProblem {
@@ -170,7 +179,7 @@ struct NsLoopProblem {
     uint16_t* xlast;
     uint16_t* a;
     uint16_t* b;
-    const float* scale;
+    float* trace;           // the plan's norm partials (iteration 0)
     uint32_t* sync;
     uint16_t* xlo[2];       // ACCURATE: lo planes of the iterates (null for FAST)
     uint16_t* blo;          // ACCURATE: lo plane of B' (null for FAST)
@@ -203,9 +212,11 @@ size_t ns_loop_sync_bytes(int64_t total_blocks);
 // host copy into items_ws, which holds items_cap entries) and the loop.  An
 // interrupted run NaN-fills the final iterates of the blocks it left
 // incomplete and adds their count and its error flags to status[0], status[1].
-hipError_t launch_ns_loop(const NsLoopProblem* probs, int n, int ns_steps, float ca, float cb, float cc,
+// clear_status: the setup kernel clears the two status words first (when
+// this launch is the call's first kernel).
+hipError_t launch_ns_loop(const NsLoopProblem* probs, int n, int ns_steps, float ca, float cb, float cc, float eps,
                           const NsChoice& choice, uint2* items_ws, uint64_t items_cap, uint32_t* status,
-                          hipStream_t s);
+                          bool clear_status, hipStream_t s);
 // 0: automatic per set of shapes (default); 1: per-product launches only;
 // 2: the persistent loop wherever eligible.
 void set_ns_schedule(int mode);

@@ -460,7 +460,13 @@ struct GemmProblem {
     const uint16_t* p[2];     // row operands (hi, lo): X, A or B'
     const uint16_t* q[2];     // column operands (hi, lo): X or A or X
     uint16_t* out[2];         // row-major output (hi, lo)
-    const float* scale;       // [nb][2] or null
+    // The first iteration's Frobenius norm, from the trace of X X^T: the
+    // Gram writes one partial per 32-row block of each block's diagonal
+    // (trace + blk * trace_stride), the polynomial and B X read them.  Null
+    // in later iterations.
+    float* trace;
+    int64_t trace_stride;
+    int ntrace;               // partials per block: padded rows / 32
     int64_t p_stride, q_stride, out_stride;
     int64_t K;                // reduction length (row pitch of k-contiguous operands)
     int64_t ldq;              // row pitch of a k-major column operand
@@ -478,11 +484,12 @@ struct GemmArgs {
     GemmProblem pr[kMaxProblems];
     int n;                    // problems in this launch
     uint32_t total;           // workgroups of this launch
+    uint32_t* status;         // null, or the call's two status words, which workgroup 0 clears
     // Quadrant mode (128-wide kernel finishing the last partial round of a
     // 256-wide tiling): workgroup L computes quadrant L % 4 of 256-wide tile
     // big_base + L / 4.
     uint32_t quad, big_base;
-    float ca, cb, cc;
+    float ca, cb, cc, eps;
 };
 
 // One output tile of one product, its pointers already offset to the block.
@@ -490,7 +497,11 @@ struct TileJob {
     const uint16_t* p[2];     // row operands (hi, lo): X, A or B'
     const uint16_t* q[2];     // column operands (hi, lo): X, A or X
     uint16_t* out[2];         // row-major output (hi, lo)
-    const float* scale;       // epilogue factor of X X^T or B X, or null (1)
+    // The first iteration's norm partials of this block (one per 32 rows of
+    // the diagonal: the Gram writes them, the polynomial and B X read them),
+    // or null in later iterations.
+    float* trace;
+    int ntrace;
     uint32_t p_bytes, q_bytes;
     int64_t K;                // reduction length (row pitch of k-contiguous operands)
     int64_t ldq;              // row pitch of a k-major column operand
@@ -514,6 +525,73 @@ struct NoHook {
     __device__ __forceinline__ void operator()() const {}
 };
 
+// 1 / (sqrt(sum of the n partials) + eps), the same value in every lane and
+// every caller: lane k adds partials k, k + 64, ... in order, then the lanes'
+// sums are added in a fixed tree to lane 0 and broadcast.
+__device__ __forceinline__ float norm_inverse(const float* part, int n, float eps) {
+    const int lane = static_cast<int>(threadIdx.x & 63);
+    float v = 0.f;
+    for (int i = lane; i < n; i += 64) v += part[i];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_down(v, off, 64);
+    const float tot = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+    return 1.0f / (sqrtf(tot) + eps);
+}
+
+// Sum of the diagonal of a 32 x 32 accumulator block, valid in lane 0, in a
+// fixed order.  Lane l holds row l % 32 and, in element 4 g + e, column
+// 8 g + 4 (l / 32) + e, so diagonal entry c sits in lane c + 32 ((c / 4) % 2),
+// element 4 (c / 8) + c % 4.
+__device__ __forceinline__ float diag_sum32(const f32x16& acc, int lane) {
+    const int c = lane & 31;
+    const bool has = ((c >> 2) & 1) == (lane >> 5);
+    const int idx = ((c >> 3) << 2) | (c & 3);
+    float v = 0.f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+        if (q == idx) v = acc[q];
+    v = has ? v : 0.f;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_down(v, off, 64);
+    return v;
+}
+
+// The operand loaders of one tile of KIND at width BT.
+template <int KIND, int BT>
+struct TileTypes {
+    using Cfg = TileCfg<BT, ring_pipeline<BT, KIND>()>;
+    static constexpr bool SPLIT_IN = KIND == kBxSplit;                // hi/lo planes of both operands
+    // Operand layouts: X X^T reads rows of X (k-contiguous).  A and B' are
+    // symmetric, so their row panels are also column panels, and X of B X is
+    // k-major as stored.  A k-major slice row is a whole 2 BT-byte run of full
+    // cache lines, where a k-contiguous slice row is only 2 BK bytes; a
+    // k-contiguous fragment is one 16-byte LDS read per lane, a k-major one
+    // two transposing reads.  Measured per launch: the 128-wide polynomial
+    // runs about 6% faster k-contiguous (two-stage pipeline, BK = 64), the
+    // 64-wide one 20% slower, the 256-wide one within noise in the loop; B X
+    // with k-contiguous B' rows is up to 13% slower.
+    static constexpr bool KMAJOR_A = KIND != kGram && !((KIND == kPoly || KIND == kPolySplit) && BT == 128);
+    static constexpr bool KMAJOR_B = KMAJOR_A;
+    static constexpr int BK = Cfg::BK, NW = Cfg::NW;
+    // split B X: the row operand reads its lo plane in segment 2, the column operand in segment 1
+    using ALoader = typename std::conditional<KMAJOR_A, ColDma<BT, BK, NW, SPLIT_IN ? 2 : -1>, RowDma<BT, BK, NW>>::type;
+    using BLoader = typename std::conditional<KMAJOR_B, ColDma<BT, BK, NW, SPLIT_IN ? 1 : -1>, RowDma<BT, BK, NW>>::type;
+    using Ops = Operands<BT, 1, 1, ALoader, BLoader>;
+    static constexpr int STAGE = Ops::STAGE;
+
+    __device__ __forceinline__ static void init(Ops& ops, const TileJob& a, int tid) {
+        const int row0 = a.ti * BT, col0 = a.tj * BT;
+        if constexpr (SPLIT_IN) {
+            // segments: Bh Xh, Bh Xl, Bl Xh
+            ops.a[0].init(a.p[0], a.p_bytes, a.K, row0, tid, a.p[1], static_cast<int>(a.K));
+            ops.b[0].init(a.q[0], a.q_bytes, a.ldq, col0, tid, a.q[1], static_cast<int>(a.K));
+        } else {
+            ops.a[0].init(a.p[0], a.p_bytes, a.K, row0, tid);   // K = ld (square when k-major)
+            ops.b[0].init(a.q[0], a.q_bytes, KMAJOR_B ? a.ldq : a.K, col0, tid);
+        }
+    }
+};
+
 // Computes one BT x BT output tile with the NW waves of the workgroup,
 // using `lds` (tile_lds_bytes<KIND, BT>() bytes) for the operand stages and
 // the epilogue.  All LDS traffic of the previous use of `lds` must be
@@ -521,33 +599,24 @@ struct NoHook {
 // epilogue, after the last global load it waits for (so that a memory
 // operation the hook issues is not waited for by the rest of the tile).
 template <int KIND, int BT, bool OPAQUE_TID = false, typename Hook = NoHook>
-__device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca, float cb, float cc,
+__device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca, float cb, float cc, float eps,
                                           const Hook& hook = Hook()) {
     // In a loop over tiles the thread index is made opaque per tile, so that
     // the compiler does not hoist the lane-dependent address arithmetic of
     // every product out of the loop (and spill it).
     int tid = static_cast<int>(threadIdx.x);
     if constexpr (OPAQUE_TID) asm volatile("" : "+v"(tid));
-    using Cfg = TileCfg<BT, ring_pipeline<BT, KIND>()>;
+    using TT = TileTypes<KIND, BT>;
+    using Cfg = typename TT::Cfg;
     constexpr int FA = Cfg::FA, FB = Cfg::FB, TWR = Cfg::TWR, TWC = Cfg::TWC, NW = Cfg::NW;
     constexpr bool SYM = KIND == kGram || KIND == kPoly || KIND == kPolySplit;
     constexpr bool POLY = KIND == kPoly || KIND == kPolySplit;
-    constexpr bool SPLIT_IN = KIND == kBxSplit;                       // hi/lo planes of both operands
+    constexpr bool SPLIT_IN = TT::SPLIT_IN;
     constexpr bool SPLIT_OUT = KIND == kPolySplit || KIND == kBxSplit;
-    // Operand layouts: X X^T reads rows of X (k-contiguous).  The other
-    // products read k-major panels only: A, B' are symmetric, so their row
-    // panels are the column panels of the same matrix, and X of B X is
-    // k-major as stored.  A k-major slice row is a whole 2 BT-byte run of
-    // full cache lines, where a k-contiguous slice row is only 2 BK bytes.
-    constexpr bool KMAJOR_A = KIND != kGram;
-    constexpr bool KMAJOR_B = KIND != kGram;
-    constexpr int NA = 1, NB = 1;
+    constexpr bool KMAJOR_A = TT::KMAJOR_A, KMAJOR_B = TT::KMAJOR_B;
     constexpr int NSEG = SPLIT_IN ? 3 : 1;            // reduction segments (split B X: Bh Xh, Bh Xl, Bl Xh)
     constexpr int BK = Cfg::BK;
-    // split B X: the row operand reads its lo plane in segment 2, the column operand in segment 1
-    using ALoader = typename std::conditional<KMAJOR_A, ColDma<BT, BK, NW, SPLIT_IN ? 2 : -1>, RowDma<BT, BK, NW>>::type;
-    using BLoader = typename std::conditional<KMAJOR_B, ColDma<BT, BK, NW, SPLIT_IN ? 1 : -1>, RowDma<BT, BK, NW>>::type;
-    using Ops = Operands<BT, NA, NB, ALoader, BLoader>;
+    using Ops = typename TT::Ops;
     constexpr int STAGE = Ops::STAGE;
     constexpr int LDS_BYTES = Cfg::NS * STAGE;
     static_assert(LDS_BYTES == tile_lds_bytes<KIND, BT>(), "LDS size");
@@ -557,20 +626,23 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
     const int wr0 = (wave / Cfg::WC) * TWR, wc0 = (wave % Cfg::WC) * TWC;
 
     Ops ops;
-    if constexpr (SPLIT_IN) {
-        // segments: Bh Xh, Bh Xl, Bl Xh
-        ops.a[0].init(a.p[0], a.p_bytes, a.K, row0, tid, a.p[1], static_cast<int>(a.K));
-        ops.b[0].init(a.q[0], a.q_bytes, a.ldq, col0, tid, a.q[1], static_cast<int>(a.K));
-    } else {
-        ops.a[0].init(a.p[0], a.p_bytes, a.K, row0, tid);   // K = ld (square when k-major)
-        ops.b[0].init(a.q[0], a.q_bytes, KMAJOR_B ? a.ldq : a.K, col0, tid);
-    }
+    TT::init(ops, a, tid);
 
     f32x16 acc[FA][FB];
     zero_acc<FA, FB>(acc);
-    // The epilogue's factor, loaded with the operand prologue, so that the
-    // epilogue waits for no global load of its own.
-    const float sc = a.scale ? *a.scale : 1.0f;
+    // The first iteration scales by s^-1 = 1 / (|X|_F + eps) (B X) or uses
+    // s^-2, s^-4 (the polynomial of the unscaled X X^T).  The norm partials
+    // are loaded with the operand prologue, so that the epilogue waits for
+    // no global load of its own.
+    float sc = 1.0f;
+    if constexpr (KIND != kGram) {
+        if (a.trace != nullptr) sc = norm_inverse(a.trace, a.ntrace, eps);
+    }
+    if constexpr (POLY) {
+        const float s2 = sc * sc;
+        cb *= s2;
+        cc *= s2 * s2;
+    }
 
     // A K step is U sub-slices (16 deep); the fragments of sub-slice u + 1 are
     // read from LDS while the MFMAs of u run.
@@ -666,15 +738,36 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
     // of one wave complete in order, so no barrier is needed.
     const int lane = tid & 63;
     const int lr = lane & 31, lk = lane >> 5;
+    if constexpr (KIND == kGram) {
+        // The first iteration's norm partials: the traces of the 32 x 32
+        // blocks on the block's diagonal, taken from the fp32 accumulators
+        // (each such block lies in one wave's tile).
+        if (a.trace != nullptr && ti == tj) {
+#pragma unroll
+            for (int i = 0; i < FA; ++i)
+#pragma unroll
+                for (int j = 0; j < FB; ++j)
+                    if (wr0 + 32 * i == wc0 + 32 * j) {
+                        const float v = diag_sum32(acc[i][j], lane);
+                        if (lane == 0) a.trace[(row0 + wr0 + 32 * i) >> 5] = v;
+                    }
+        }
+    }
     const uint16_t* amat = POLY ? a.p[0] : nullptr;
     uint16_t* out0 = a.out[0];
     uint16_t* out1 = SPLIT_OUT ? a.out[1] : nullptr;
+    // Staging per wave: the fp32 chunk, and for a symmetric tile the bf16
+    // chunk of the mirror store.  Without split outputs the bf16 chunk
+    // overlays the fp32 one: bf16 row r occupies the bytes of fp32 row r / 2,
+    // which every lane has read (in an earlier or the same read-back
+    // instruction, and one wave's LDS accesses complete in order) before any
+    // lane writes there.  The split products keep both bf16 planes apart.
     constexpr int ST_F32 = 32 * TWC * 4;
     constexpr int ST_BF = SYM ? 32 * TWC * 2 : 0;
-    constexpr int WAVE_LDS = ST_F32 + ST_BF * (SPLIT_OUT ? 2 : 1);
+    constexpr int WAVE_LDS = SPLIT_OUT ? ST_F32 + 2 * ST_BF : ST_F32;
     static_assert(NW * WAVE_LDS <= LDS_BYTES, "epilogue staging must fit in LDS");
     char* sf = lds + wave * WAVE_LDS;
-    char* sb = sf + ST_F32;
+    char* sb = SPLIT_OUT ? sf + ST_F32 : sf;
     char* sb_lo = sb + ST_BF;
     const bool mirror = SYM && ti != tj;
     constexpr int LPR = TWC / 4;      // lanes per row on read-back (4 values each)
@@ -851,12 +944,8 @@ __global__ __launch_bounds__(tile_threads<BT>()) void k_gemm(GemmArgs args) {
     j.q[1] = SPLIT_IN ? a.q[1] + blk * a.q_stride : nullptr;
     j.out[0] = a.out[0] + blk * a.out_stride;
     j.out[1] = SPLIT_OUT ? a.out[1] + blk * a.out_stride : nullptr;
-    j.scale = nullptr;
-    if constexpr (KIND == kGram) {
-        if (a.scale) j.scale = a.scale + 2 * blk + 1;
-    } else if constexpr (KIND == kBx || KIND == kBxSplit) {
-        if (a.scale) j.scale = a.scale + 2 * blk;
-    }
+    j.trace = a.trace ? a.trace + blk * a.trace_stride : nullptr;
+    j.ntrace = a.ntrace;
     j.p_bytes = a.p_bytes;
     j.q_bytes = a.q_bytes;
     j.K = a.K;
@@ -864,7 +953,8 @@ __global__ __launch_bounds__(tile_threads<BT>()) void k_gemm(GemmArgs args) {
     j.ldo = a.ldo;
     j.ti = ti;
     j.tj = tj;
-    gemm_tile<KIND, BT>(j, lds, args.ca, args.cb, args.cc);
+    if (args.status != nullptr && blockIdx.x == 0 && threadIdx.x < 2) args.status[threadIdx.x] = 0u;
+    gemm_tile<KIND, BT>(j, lds, args.ca, args.cb, args.cc, args.eps);
 }
 
 // ---------------------------------------------------------------- persistent NS loop
@@ -893,7 +983,8 @@ struct PersistProblem {
     uint16_t* a;
     uint16_t* b;
     uint16_t* blo;            // ACCURATE: lo plane of B'
-    const float* scale;
+    float* trace;             // iteration 0's norm partials (Gram writes, polynomial and B X read)
+    int64_t trace_stride;     // floats between blocks' partials (a multiple of 32: 128-byte lines)
     uint32_t* done;           // [nb] completion counters, kSyncStride words apart
     int32_t mp, np;
     uint32_t first_blk;       // global index of its first block
@@ -912,7 +1003,7 @@ struct PersistArgs {
     uint32_t* sync;           // queue heads 0..7, then the error word and the exit counter
     uint32_t* status;         // the call's status words: [0] blocks left incomplete, [1] error flags
     uint64_t spin_ticks;      // longest dependency wait (ticks of the 100 MHz real-time counter)
-    float ca, cb, cc;
+    float ca, cb, cc, eps;
 };
 
 // Counters of the loop each sit on their own 128-byte line (kSyncStride
@@ -1130,18 +1221,14 @@ __global__ __launch_bounds__(tile_threads<256>()) void k_ns_loop(PersistArgs arg
         const int64_t xs = int64_t(pr.mp) * pr.np, as = int64_t(pr.mp) * pr.mp;
         const uint16_t* const xin = (t == 0 ? pr.x0 : pr.xb[t & 1]) + blk * xs;
         const uint16_t* const xin_lo = SPLIT ? pr.xlo[t & 1] + blk * xs : nullptr;
-        for (int c = 0; c < ntiles; ++c) {
-            if (c > 0) __syncthreads();    // the previous tile's epilogue is done with LDS
-            const bool last = c + 1 == ntiles;
-            const auto claim = [&]() {
-                if (wave == 0 && last && lane0)
-                    idx_v = __hip_atomic_fetch_add(head, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            };
+        // Tile c of the item (every tile of an item is of one product).
+        const auto job = [&](int c) {
             int id = static_cast<int>(ity & 0x3fffffu) + c;
             TileJob j;
             j.p[1] = j.q[1] = nullptr;
             j.out[1] = nullptr;
-            j.scale = nullptr;
+            j.trace = t == 0 && pr.trace ? pr.trace + blk * pr.trace_stride : nullptr;
+            j.ntrace = pr.mp / 32;
             if (ph < 2) {
                 int r = 0, len = pr.mp / 256;
                 while (id >= len) { id -= len; ++r; --len; }
@@ -1154,30 +1241,22 @@ __global__ __launch_bounds__(tile_threads<256>()) void k_ns_loop(PersistArgs arg
             if (ph == 0) {
                 j.p[0] = j.q[0] = xin;
                 j.out[0] = pr.a + blk * as;
-                if (t == 0 && pr.scale) j.scale = pr.scale + 2 * blk + 1;
                 j.p_bytes = j.q_bytes = static_cast<uint32_t>(xs * 2);
                 j.K = pr.np;
                 j.ldq = pr.np;
                 j.ldo = pr.mp;
-                gemm_tile<kGram, 256, true>(j, lds, args.ca, args.cb, args.cc, claim);
             } else if (ph == 1) {
                 j.p[0] = j.q[0] = pr.a + blk * as;
                 j.out[0] = pr.b + blk * as;
+                if constexpr (SPLIT) j.out[1] = pr.blo + blk * as;
                 j.p_bytes = j.q_bytes = static_cast<uint32_t>(as * 2);
                 j.K = pr.mp;
                 j.ldq = pr.mp;
                 j.ldo = pr.mp;
-                if constexpr (SPLIT) {
-                    j.out[1] = pr.blo + blk * as;
-                    gemm_tile<kPolySplit, 256, true>(j, lds, args.ca, args.cb, args.cc, claim);
-                } else {
-                    gemm_tile<kPoly, 256, true>(j, lds, args.ca, args.cb, args.cc, claim);
-                }
             } else {
                 j.p[0] = pr.b + blk * as;
                 j.q[0] = xin;
                 j.out[0] = (t + 1 == args.steps ? pr.xlast : pr.xb[(t + 1) & 1]) + blk * xs;
-                if (t == 0 && pr.scale) j.scale = pr.scale + 2 * blk;
                 j.p_bytes = static_cast<uint32_t>(as * 2);
                 j.q_bytes = static_cast<uint32_t>(xs * 2);
                 j.K = pr.mp;
@@ -1187,10 +1266,30 @@ __global__ __launch_bounds__(tile_threads<256>()) void k_ns_loop(PersistArgs arg
                     j.p[1] = pr.blo + blk * as;
                     j.q[1] = xin_lo;
                     j.out[1] = pr.xlo[(t + 1) & 1] + blk * xs;
-                    gemm_tile<kBxSplit, 256, true>(j, lds, args.ca, args.cb, args.cc, claim);
-                } else {
-                    gemm_tile<kBx, 256, true>(j, lds, args.ca, args.cb, args.cc, claim);
                 }
+            }
+            return j;
+        };
+        for (int c = 0; c < ntiles; ++c) {
+            if (c > 0) __syncthreads();    // the previous tile's epilogue is done with LDS
+            const bool last = c + 1 == ntiles;
+            const auto claim = [&]() {
+                if (wave == 0 && last && lane0)
+                    idx_v = __hip_atomic_fetch_add(head, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            };
+            const TileJob j = job(c);
+            if (ph == 0) {
+                gemm_tile<kGram, 256, true>(j, lds, args.ca, args.cb, args.cc, args.eps, claim);
+            } else if (ph == 1) {
+                if constexpr (SPLIT)
+                    gemm_tile<kPolySplit, 256, true>(j, lds, args.ca, args.cb, args.cc, args.eps, claim);
+                else
+                    gemm_tile<kPoly, 256, true>(j, lds, args.ca, args.cb, args.cc, args.eps, claim);
+            } else {
+                if constexpr (SPLIT)
+                    gemm_tile<kBxSplit, 256, true>(j, lds, args.ca, args.cb, args.cc, args.eps, claim);
+                else
+                    gemm_tile<kBx, 256, true>(j, lds, args.ca, args.cb, args.cc, args.eps, claim);
             }
         }
         // Every wave's stores (and wave 0's claim) complete before the barrier.
@@ -1223,6 +1322,7 @@ struct SetupArgs {
     const uint2* src;         // host (pinned, device-readable)
     uint2* dst;               // workspace
     uint32_t items;
+    uint32_t* status;         // null, or the call's two status words to clear
 };
 
 __global__ void k_loop_setup(SetupArgs z) {
@@ -1230,6 +1330,7 @@ __global__ void k_loop_setup(SetupArgs z) {
     for (int r = 0; r < z.count; ++r)
         if (i < z.n[r]) z.p[r][i] = 0u;
     if (i < z.items) z.dst[i] = z.src[i];
+    if (z.status != nullptr && i < 2) z.status[i] = 0u;
 }
 
 // Every kernel instantiation is named explicitly: with implicit instantiation
@@ -1561,11 +1662,12 @@ hipError_t run(const Plan* const* plans, GemmArgs a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_gram(const GramOp* ops, int n, hipStream_t s) {
+hipError_t launch_gram(const GramOp* ops, int n, uint32_t* status, hipStream_t s) {
     if (n < 1 || n > kMaxProblems) return hipErrorInvalidValue;
     GemmArgs a{};
     const Plan* plans[kMaxProblems];
     a.n = n;
+    a.status = status;
     for (int i = 0; i < n; ++i) {
         const Plan& p = *ops[i].plan;
         GemmProblem& g = a.pr[i];
@@ -1573,7 +1675,9 @@ hipError_t launch_gram(const GramOp* ops, int n, hipStream_t s) {
         g.p[0] = ops[i].x;
         g.q[0] = ops[i].x;
         g.out[0] = ops[i].a;
-        g.scale = ops[i].scale2;
+        g.trace = ops[i].trace;
+        g.trace_stride = p.trace_stride;
+        g.ntrace = static_cast<int>(p.mp / 32);
         g.p_stride = g.q_stride = p.mp * p.np;
         g.out_stride = p.mp * p.mp;
         g.K = p.np;
@@ -1583,7 +1687,7 @@ hipError_t launch_gram(const GramOp* ops, int n, hipStream_t s) {
     return run<kGram>(plans, a, s);
 }
 
-hipError_t launch_poly(const PolyOp* ops, int n, float ca, float cb, float cc, hipStream_t s) {
+hipError_t launch_poly(const PolyOp* ops, int n, float ca, float cb, float cc, float eps, hipStream_t s) {
     if (n < 1 || n > kMaxProblems) return hipErrorInvalidValue;
     GemmArgs a{};
     const Plan* plans[kMaxProblems];
@@ -1591,6 +1695,7 @@ hipError_t launch_poly(const PolyOp* ops, int n, float ca, float cb, float cc, h
     a.ca = ca;
     a.cb = cb;
     a.cc = cc;
+    a.eps = eps;
     const bool split = ops[0].b_lo != nullptr;
     for (int i = 0; i < n; ++i) {
         const Plan& p = *ops[i].plan;
@@ -1601,6 +1706,9 @@ hipError_t launch_poly(const PolyOp* ops, int n, float ca, float cb, float cc, h
         g.q[0] = ops[i].a;
         g.out[0] = ops[i].b_hi;
         g.out[1] = ops[i].b_lo;
+        g.trace = const_cast<float*>(ops[i].trace);
+        g.trace_stride = p.trace_stride;
+        g.ntrace = static_cast<int>(p.mp / 32);
         g.p_stride = g.q_stride = p.mp * p.mp;
         g.out_stride = p.mp * p.mp;
         g.K = p.mp;
@@ -1611,11 +1719,12 @@ hipError_t launch_poly(const PolyOp* ops, int n, float ca, float cb, float cc, h
     return split ? run<kPolySplit>(plans, a, s) : run<kPoly>(plans, a, s);
 }
 
-hipError_t launch_bx(const BxOp* ops, int n, hipStream_t s) {
+hipError_t launch_bx(const BxOp* ops, int n, float eps, hipStream_t s) {
     if (n < 1 || n > kMaxProblems) return hipErrorInvalidValue;
     GemmArgs a{};
     const Plan* plans[kMaxProblems];
     a.n = n;
+    a.eps = eps;
     const bool split = ops[0].b_lo != nullptr;
     for (int i = 0; i < n; ++i) {
         const Plan& p = *ops[i].plan;
@@ -1628,7 +1737,9 @@ hipError_t launch_bx(const BxOp* ops, int n, hipStream_t s) {
         g.q[1] = ops[i].x_lo;
         g.out[0] = ops[i].out_hi;
         g.out[1] = ops[i].out_lo;
-        g.scale = ops[i].scale1;
+        g.trace = const_cast<float*>(ops[i].trace);
+        g.trace_stride = p.trace_stride;
+        g.ntrace = static_cast<int>(p.mp / 32);
         g.p_stride = p.mp * p.mp;
         g.q_stride = p.mp * p.np;
         g.out_stride = p.mp * p.np;
@@ -1641,22 +1752,23 @@ hipError_t launch_bx(const BxOp* ops, int n, hipStream_t s) {
     return split ? run<kBxSplit>(plans, a, s) : run<kBx>(plans, a, s);
 }
 
-hipError_t launch_gram(const Plan& p, const uint16_t* x, uint16_t* a_out, const float* scale2, hipStream_t s) {
-    const GramOp op{&p, x, a_out, scale2};
-    return launch_gram(&op, 1, s);
+hipError_t launch_gram(const Plan& p, const uint16_t* x, uint16_t* a_out, float* trace, uint32_t* status,
+                       hipStream_t s) {
+    const GramOp op{&p, x, a_out, trace};
+    return launch_gram(&op, 1, status, s);
 }
 
 hipError_t launch_poly(const Plan& p, const uint16_t* a_in, uint16_t* b_hi, uint16_t* b_lo, float ca, float cb,
-                       float cc, hipStream_t s) {
-    const PolyOp op{&p, a_in, b_hi, b_lo};
-    return launch_poly(&op, 1, ca, cb, cc, s);
+                       float cc, const float* trace, float eps, hipStream_t s) {
+    const PolyOp op{&p, a_in, b_hi, b_lo, trace};
+    return launch_poly(&op, 1, ca, cb, cc, eps, s);
 }
 
 hipError_t launch_bx(const Plan& p, const uint16_t* b_hi, const uint16_t* b_lo, const uint16_t* x_hi,
-                     const uint16_t* x_lo, uint16_t* out_hi, uint16_t* out_lo, const float* scale1,
+                     const uint16_t* x_lo, uint16_t* out_hi, uint16_t* out_lo, const float* trace, float eps,
                      hipStream_t s) {
-    const BxOp op{&p, b_hi, b_lo, x_hi, x_lo, out_hi, out_lo, scale1};
-    return launch_bx(&op, 1, s);
+    const BxOp op{&p, b_hi, b_lo, x_hi, x_lo, out_hi, out_lo, trace};
+    return launch_bx(&op, 1, eps, s);
 }
 
 // ---------------------------------------------------------------- persistent NS loop (host)
@@ -1878,9 +1990,9 @@ size_t ns_loop_sync_bytes(int64_t total_blocks) {
     return (size_t(kSyncLines + total_blocks) * kSyncStride * 4 + 255) & ~size_t(255);
 }
 
-hipError_t launch_ns_loop(const NsLoopProblem* probs, int n, int ns_steps, float ca, float cb, float cc,
+hipError_t launch_ns_loop(const NsLoopProblem* probs, int n, int ns_steps, float ca, float cb, float cc, float eps,
                           const NsChoice& choice, uint2* items_ws, uint64_t items_cap, uint32_t* status,
-                          hipStream_t s) {
+                          bool clear_status, hipStream_t s) {
     if (!choice.persistent || choice.sched == nullptr || !ns_loop_eligible(probs, n, ns_steps) || status == nullptr)
         return hipErrorInvalidValue;
     const Schedule& sc = *static_cast<const Schedule*>(choice.sched);
@@ -1893,6 +2005,7 @@ hipError_t launch_ns_loop(const NsLoopProblem* probs, int n, int ns_steps, float
     a.ca = ca;
     a.cb = cb;
     a.cc = cc;
+    a.eps = eps;
     a.sync = probs[0].sync;
     a.status = status;
     const int fault = g_loop_fault.load();
@@ -1918,7 +2031,8 @@ hipError_t launch_ns_loop(const NsLoopProblem* probs, int n, int ns_steps, float
         pr.blo = probs[i].blo;
         if (split != (probs[i].blo != nullptr && probs[i].xlo[0] != nullptr && probs[i].xlo[1] != nullptr))
             return hipErrorInvalidValue;
-        pr.scale = probs[i].scale;
+        pr.trace = probs[i].trace;
+        pr.trace_stride = p.trace_stride;
         pr.done = probs[i].sync + kSyncLines * kSyncStride;
         z.p[i] = probs[i].sync;
         z.n[i] = uint32_t((kSyncLines + p.nb) * kSyncStride);
@@ -1937,7 +2051,8 @@ hipError_t launch_ns_loop(const NsLoopProblem* probs, int n, int ns_steps, float
     z.src = sc.host_items;
     z.dst = items_ws;
     z.items = sc.count;
-    const uint32_t work = std::max(zmax, sc.count);
+    z.status = clear_status ? status : nullptr;
+    const uint32_t work = std::max(std::max(zmax, sc.count), 2u);
     k_loop_setup<<<dim3((work + 255) / 256), dim3(256), 0, s>>>(z);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

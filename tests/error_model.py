@@ -11,8 +11,12 @@ Newton-Schulz iteration of the parameter-golf walkthrough, Part 1
 coefficients of the "Muon Custom Sizing" walkthrough, section 2.3, written
 the way the kernels arrange it:
 
-* the Frobenius normalisation is folded into the first iteration's two
-  products (A = s^-2 X X^T, X1 = s^-1 B' X), so X0 = U / s is never rounded;
+* the Frobenius normalisation is folded into the first iteration: the Gram
+  stores the unscaled A0 = X X^T and yields s^2 = trace(X X^T) (the sum of
+  the squares of the bf16 values X holds; for ACCURATE those of the hi plane),
+  the polynomial forms a I + b s^-2 A0 + c s^-4 A0 A0 and B X scales by s^-1,
+  so X0 = U / s is never rounded (with zero iterations the update is U / s
+  with s from U itself);
 * aX rides on B''s diagonal (aX + BX = (aI + B) X), so a is rounded with B;
 * FAST keeps every operand in bf16; ACCURATE keeps B' and X as bf16 hi + lo
   pairs and forms B' X as Bh Xh + Bh Xl + Bl Xh (the Gram uses Xh only).
@@ -60,21 +64,21 @@ def ns_model(U, steps: int = 5, coeffs=COEFFS, eps: float = EPS, precision: str 
     eye = np.eye(m)
     if precision == "fast":
         X = rnd(Y)
-        s = np.sqrt(np.sum(X * X)) + eps           # the squares of the values X holds
+        s = np.sqrt(np.sum(X * X)) + eps           # trace(X X^T): the squares of the values X holds
         for t in range(steps):
             sc = 1.0 / s if t == 0 else 1.0
-            A = rnd((X @ X.T) * sc * sc)
-            B = rnd(a * eye + b * A + c * (A @ A))
+            A = rnd(X @ X.T)
+            B = rnd(a * eye + b * sc * sc * A + c * sc ** 4 * (A @ A))
             X = rnd((B @ X) * sc)
         O = X
     else:
         Xh = rnd(Y)
         Xl = 0.0 * Xh if drop_lo else rnd(Y - Xh)
-        s = np.sqrt(np.sum(Y * Y)) + eps
+        s = np.sqrt(np.sum(Xh * Xh)) + eps         # trace(Xh Xh^T): the Gram reads the hi plane
         for t in range(steps):
             sc = 1.0 / s if t == 0 else 1.0
-            A = rnd((Xh @ Xh.T) * sc * sc)
-            v = a * eye + b * A + c * (A @ A)
+            A = rnd(Xh @ Xh.T)
+            v = a * eye + b * sc * sc * A + c * sc ** 4 * (A @ A)
             Bh = rnd(v)
             Bl = 0.0 * Bh if drop_lo else rnd(v - Bh)
             v = (Bh @ Xh + Bh @ Xl + Bl @ Xh) * sc
@@ -82,7 +86,8 @@ def ns_model(U, steps: int = 5, coeffs=COEFFS, eps: float = EPS, precision: str 
             Xl = 0.0 * Xh if drop_lo else rnd(v - Xh)
         O = rnd(Xh + Xl)
     if steps == 0:
-        O = rnd(X / s) if precision == "fast" else rnd((Xh + Xl) / s)
+        # the prep's sums of squares: of the bf16 values (FAST), of U (ACCURATE)
+        O = rnd(X / s) if precision == "fast" else rnd((Xh + Xl) / (np.sqrt(np.sum(Y * Y)) + eps))
     return O.T if tall else O
 
 

@@ -63,10 +63,12 @@ def _regions(nb, m, n, split=False):
     xb = _up(nb * mp * np_ * 2, 256)
     ab = _up(nb * mp * mp * 2, 256)
     tiles = (mp // 64) * (np_ // 64)
-    # iterate ping-pong (and lo planes when split); A; B (+ lo); partials; scales;
-    # counters of the persistent NS loop (9 + one per block, each on a 128-byte line)
+    trace = _up(mp // 32, 32)          # floats per block: a 128-byte multiple
+    # iterate ping-pong (and lo planes when split); A; B (+ lo); sums of squares; scales;
+    # trace partials of the norm; counters of the persistent NS loop (9 + one per block,
+    # each on a 128-byte line)
     return ((4 if split else 2) * xb + (3 if split else 2) * ab + _up(nb * tiles * 4, 256) + _up(nb * 8, 256)
-            + _up((9 + nb) * 128, 256))
+            + _up(nb * trace * 4, 256) + _up((9 + nb) * 128, 256))
 
 
 def _queue_entries(nb, m, n, steps=5, split=False):
