@@ -112,7 +112,10 @@ size_t muon_workspace_bytes(int64_t batch, int64_t rows, int64_t cols,
  *   out      out, bf16 [batch, rows, cols]; may be x itself (exact alias),
  *            must not overlap it otherwise
  *   cfg      NULL = defaults
- * Each NS block is normalised by its own Frobenius norm.
+ * Each NS block is normalised by its own Frobenius norm s = |X|_F + eps,
+ * taken as sqrt(trace(X X^T)) from the first Gram product's fp32 diagonal
+ * (FAST: of the bf16 values; ACCURATE: of the hi plane; with ns_steps = 0
+ * from the sum of squares of x); the first polynomial and B X apply it.
  */
 muon_status ns_orthogonalize_batched(const void* x, void* out,
                                      int64_t batch, int64_t rows, int64_t cols,
@@ -349,8 +352,8 @@ muon_status muon_set_gemm_tiling(int32_t width);
 
 /* Kernel timing (diagnostics).  Kernel families of the library: */
 typedef enum muon_kernel_kind {
-    MUON_KERNEL_PREP = 0,           /* momentum + cast + tile norms            */
-    MUON_KERNEL_NORM_FINALIZE = 1,  /* per-block 1/|X|_F                       */
+    MUON_KERNEL_PREP = 0,           /* momentum + cast (+ tile norms, 0 steps) */
+    MUON_KERNEL_NORM_FINALIZE = 1,  /* per-block 1/|X|_F (ns_steps = 0 only)   */
     MUON_KERNEL_GRAM = 2,           /* A = X X^T                               */
     MUON_KERNEL_POLY = 3,           /* B = b A + c A A                         */
     MUON_KERNEL_BX = 4,             /* X <- a X + B X                          */
