@@ -479,6 +479,8 @@ def main():
     ap.add_argument("--ns-schedule", choices=("auto", "persistent", "per_product"), default="auto",
                     help="auto: the library's per-shape choice (default); persistent: all NS iterations of "
                          "a call in one launch; per_product: three launches per iteration")
+    ap.add_argument("--extras-only", action="store_true",
+                    help="skip the headline call and print the extras alone (for per-extra kernel profiles)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run a plain device copy of MIB MiB first (HBM counter calibration)")
     args = ap.parse_args()
@@ -507,6 +509,22 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    if args.extras_only:
+        want = set(x.strip() for x in args.extras.split(",") if x.strip())
+        result = {"extras_only": True, "extras": sorted(want)}
+        if "step" in want:
+            result["gpt124m_step"] = gpt124m_step(nsm, args, dev)
+        if "shares" in want:
+            result["rank_share_8way"] = rank_shares(nsm, args, dev)
+        if "c4" in want:
+            result["gpt2_medium_step"] = large_step(nsm, args, dev, "gpt2_medium")
+        if "c5" in want:
+            result["large_dense_step"] = large_step(nsm, args, dev, "large_dense")
+        if "adamw" in want:
+            result["adamw_gpt124m"] = adamw_gpt124m(nsm, args, dev)
+        print(json.dumps(result), flush=True)
+        return
 
     h = headline(nsm, args, dev)
     value = h["nominal"] / (h["ms"] / 1e3) / 1e12
