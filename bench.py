@@ -375,12 +375,26 @@ def rank_shares(nsm, args, dev):
         with Timer(nsm, nsm.KERNEL_KINDS) as t:
             for _ in range(args.steps):
                 step()
+        # The same step captured once into a HIP graph and replayed (the launch
+        # gaps of its ~17 dependent launches are most of what a share waits for).
+        graph = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            graph.replay()
+        ms_graph = timed_region(graph.replay, args.steps)
         flops = 2 * g.view_blocks * ns_flops(*g.block_shape)
         out[name] = {"blocks": f"{2 * g.view_blocks} x {g.block_shape[0]}x{g.block_shape[1]}",
                      "ms": round(ms, 4), "tflops_nominal": round(flops / (ms / 1e3) / 1e12, 2),
                      "mfma_peak_frac_nominal": round(flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                     "kernel_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in t.result.items()}}
-        del P, G, M
+                     "kernel_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in t.result.items()},
+                     "graph_replay": {"ms": round(ms_graph, 4),
+                                      "tflops_nominal": round(flops / (ms_graph / 1e3) / 1e12, 2),
+                                      "mfma_peak_frac_nominal": round(flops / (ms_graph / 1e3) / 1e12
+                                                                      / PEAK_BF16_TFLOPS, 4)}}
+        del P, G, M, graph
     return out
 
 

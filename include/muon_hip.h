@@ -141,6 +141,9 @@ muon_status ns_orthogonalize_batched(const void* x, void* out,
  *   Every call on one GPU shares its scratch, so calls that overlap on one
  *   GPU (different streams or host threads without ordering) race; calls on
  *   one stream are ordered and safe.
+ *   The first call on a device looks up the scratch's device address
+ *   (hipGetSymbolAddress); make it outside stream capture.  Later calls can
+ *   be captured into a HIP graph.
  */
 muon_status ns_orthogonalize_batched_noalloc(const void* x, void* out,
                                              int64_t batch, int64_t rows, int64_t cols,
@@ -326,6 +329,10 @@ muon_status muon_debug_set_loop_fault(int32_t mode);
  * workspace on its stream.  Beyond 64 such sets (256 for the automatic
  * choice), calls with a new set use the per-product schedule.  With 8 queues
  * a workgroup serves the queue of the XCD it runs on.
+ * Under stream capture (hipStreamBeginCapture on the call's stream) a call
+ * allocates, times and synchronises nothing: it reuses the schedule an
+ * earlier call settled for the set (and its cached queue), else runs per
+ * product; captured calls replay to the eager results bit for bit.
  * Returns MUON_ERR_INVALID_ARG for any other mode. */
 muon_status muon_set_ns_schedule(int32_t mode);
 

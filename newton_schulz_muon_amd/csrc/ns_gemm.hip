@@ -1877,13 +1877,15 @@ void release_events(AutoState& st) {
             }
 }
 
-// The cached schedule of this set of shapes, built on first use; null when
-// the cache is full or building failed (the caller then runs per product).
-const Schedule* find_schedule(const NsLoopProblem* probs, int n, int ns_steps, int dev, int cus) {
+// The cached schedule of this set of shapes, built on first use (not under
+// stream capture: building allocates pinned host memory); null when the
+// cache is full, building failed or was not allowed (the caller then runs per
+// product).
+const Schedule* find_schedule(const NsLoopProblem* probs, int n, int ns_steps, int dev, int cus, bool may_build) {
     const std::vector<int64_t> key = schedule_key(probs, n, ns_steps, dev, cus);
     auto it = g_sched.find(key);
     if (it != g_sched.end()) return &it->second;
-    if (g_sched.size() >= kMaxSchedules) return nullptr;
+    if (!may_build || g_sched.size() >= kMaxSchedules) return nullptr;
     std::vector<LoopDims> dims;
     std::vector<int64_t> nbs;
     for (int i = 0; i < n; ++i) {
@@ -1907,10 +1909,15 @@ NsChoice ns_schedule_begin(const NsLoopProblem* probs, int n, int ns_steps, hipS
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
         return c;
+    // Under stream capture nothing is allocated or timed: a settled choice
+    // (and the queue it needs) is reused, anything else runs per product.
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    const bool capturing = hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone;
     std::lock_guard<std::mutex> lock(g_sched_mu);
-    // The loop needs its queue: without one (cache full, or no pinned host
-    // memory) the call runs per product, which gives the same results.
-    const Schedule* sched = find_schedule(probs, n, ns_steps, dev, cus);
+    // The loop needs its queue: without one (cache full, no pinned host
+    // memory, or capture) the call runs per product, which gives the same
+    // results.
+    const Schedule* sched = find_schedule(probs, n, ns_steps, dev, cus, !capturing);
     if (sched == nullptr) return c;
     c.sched = sched;
     c.cus = cus;
@@ -1920,6 +1927,10 @@ NsChoice ns_schedule_begin(const NsLoopProblem* probs, int n, int ns_steps, hipS
     }
     const std::vector<int64_t> key = schedule_key(probs, n, ns_steps, dev, cus);
     auto it = g_auto.find(key);
+    if (capturing) {
+        c.persistent = it != g_auto.end() && it->second.decided == 1;
+        return c;
+    }
     if (it == g_auto.end()) {
         if (g_auto.size() >= kMaxAutoSets) return c;
         it = g_auto.emplace(key, AutoState()).first;
