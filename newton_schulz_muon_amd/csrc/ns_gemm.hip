@@ -608,7 +608,7 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
     if constexpr (OPAQUE_TID) asm volatile("" : "+v"(tid));
     using TT = TileTypes<KIND, BT>;
     using Cfg = typename TT::Cfg;
-    constexpr int FA = Cfg::FA, FB = Cfg::FB, TWR = Cfg::TWR, TWC = Cfg::TWC, NW = Cfg::NW;
+    constexpr int FB = Cfg::FB, TWR = Cfg::TWR, TWC = Cfg::TWC, NW = Cfg::NW;
     constexpr bool SYM = KIND == kGram || KIND == kPoly || KIND == kPolySplit;
     constexpr bool POLY = KIND == kPoly || KIND == kPolySplit;
     constexpr bool SPLIT_IN = TT::SPLIT_IN;
@@ -623,13 +623,10 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
     const int ti = a.ti, tj = a.tj;
     const int row0 = ti * BT, col0 = tj * BT;
     const int wave = tid >> 6;
-    const int wr0 = (wave / Cfg::WC) * TWR, wc0 = (wave % Cfg::WC) * TWC;
 
     Ops ops;
     TT::init(ops, a, tid);
 
-    f32x16 acc[FA][FB];
-    zero_acc<FA, FB>(acc);
     // The first iteration scales by s^-1 = 1 / (|X|_F + eps) (B X) or uses
     // s^-2, s^-4 (the polynomial of the unscaled X X^T).  The norm partials
     // are loaded with the operand prologue, so that the epilogue waits for
@@ -643,6 +640,16 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
         cb *= s2;
         cc *= s2 * s2;
     }
+
+    // The K loop and epilogue of one wave, which computes FA x FB blocks of
+    // 32 x 32 at rows wr0, columns wc0 of the tile, and stores their mirror
+    // (the transposed block at the transposed place) with `mirror`.  Every
+    // wave runs the same K loop structure (one wait, barrier and stage of DMA
+    // per step) whatever its FA.
+    const auto body = [&](auto fa_tag, const int wr0, const int wc0, const bool mirror) {
+    constexpr int FA = decltype(fa_tag)::value;
+    f32x16 acc[FA][FB];
+    zero_acc<FA, FB>(acc);
 
     // A K step is U sub-slices (16 deep); the fragments of sub-slice u + 1 are
     // read from LDS while the MFMAs of u run.
@@ -769,7 +776,6 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
     char* sf = lds + wave * WAVE_LDS;
     char* sb = SPLIT_OUT ? sf + ST_F32 : sf;
     char* sb_lo = sb + ST_BF;
-    const bool mirror = SYM && ti != tj;
     constexpr int LPR = TWC / 4;      // lanes per row on read-back (4 values each)
     constexpr int RPI = 64 / LPR;     // rows per read-back instruction
     const int rrow = lane / LPR, rcol = (lane % LPR) * 4;
@@ -896,6 +902,25 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
             }
         }
     }
+    };
+    // A diagonal 256-wide tile of a symmetric product: its lower-left
+    // quadrant is the transpose of the upper-right one, so no wave computes
+    // it.  Waves 0-3 take the upper-right quadrant as 64 x 64 pieces and store
+    // each piece twice (itself and, transposed, the lower-left quadrant);
+    // waves 4-7 take the two diagonal quadrants as 128 x 64 pieces.  Wave w
+    // shares a SIMD with wave w + 4, so every SIMD issues 12 of the 16
+    // MFMA blocks per sub-slice it would otherwise.
+    if constexpr (SYM && NW == 8) {
+        if (ti == tj) {
+            if (wave < 4)
+                body(std::integral_constant<int, 2>(), (wave >> 1) * 64, 128 + (wave & 1) * 64, true);
+            else
+                body(std::integral_constant<int, 4>(), (wave & 2) ? 128 : 0, ((wave & 2) ? 128 : 0) + (wave & 1) * 64,
+                     false);
+            return;
+        }
+    }
+    body(std::integral_constant<int, Cfg::FA>(), (wave / Cfg::WC) * TWR, (wave % Cfg::WC) * TWC, SYM && ti != tj);
 }
 
 // Threads of a tile's workgroup.
@@ -1564,12 +1589,23 @@ hipError_t run(const Plan* const* plans, GemmArgs a, hipStream_t s) {
     };
     // Executed MFMA flops of the launches (for the timing diagnostics): every
     // workgroup computes a bt x bt tile over the reduction, except the lower
-    // quadrants of diagonal 256-wide tiles in quadrant mode, which return.
+    // quadrants of diagonal 256-wide tiles in quadrant mode, which return,
+    // and diagonal 256-wide tiles, which compute three quadrants.
     auto launch = [&](int bt, int64_t total, uint32_t quad, uint32_t base) {
         a.quad = quad;
         a.big_base = base;
         a.total = static_cast<uint32_t>(total);
-        int64_t tiles = total;
+        double tiles = double(total);
+        if (SYM && bt == 256 && !quad) {
+            for (int64_t t = 0; t < total; ++t) {
+                int pi = 0;
+                for (int i = 1; i < a.n; ++i)
+                    if (t >= int64_t(a.pr[i].first)) pi = i;
+                int id = static_cast<int>((t - a.pr[pi].first) % a.pr[pi].tiles), len = a.pr[pi].T;
+                while (id > 0 && id >= len) { id -= len; --len; }
+                if (id == 0) tiles -= 0.25;     // the row's diagonal tile
+            }
+        }
         if (quad && SYM) {
             tiles = 0;
             for (int64_t t = base; t < int64_t(base) + total / 4; ++t) {
@@ -1581,7 +1617,7 @@ hipError_t run(const Plan* const* plans, GemmArgs a, hipStream_t s) {
                 tiles += id == 0 ? 3 : 4;     // id == 0: the row's diagonal tile
             }
         }
-        last_exec_flops() += double(tiles) * 2.0 * double(bt) * double(bt) * double(Kc);
+        last_exec_flops() += tiles * 2.0 * double(bt) * double(bt) * double(Kc);
         if (bt == 256) {
             k_gemm<KIND, 256><<<dim3(a.total), dim3(tile_threads<256>()), 0, s>>>(a);
         } else if (bt == 128) {
@@ -2070,8 +2106,10 @@ hipError_t launch_ns_loop(const NsLoopProblem* probs, int n, int ns_steps, float
     double ex = 0.0;
     for (int i = 0; i < n; ++i) {
         const PersistProblem& pr = a.pr[i];
+        // diagonal tiles of the symmetric products compute three quadrants
+        const double sym = double(pr.nsym) - 0.25 * double(pr.mp / 256);
         ex += double(pr.nb) * double(ns_steps) * 2.0 * 256.0 * 256.0 *
-              (double(pr.nsym) * pr.np + double(pr.nsym) * pr.mp + double(pr.nbx) * pr.mp * (split ? 3.0 : 1.0));
+              (sym * pr.np + sym * pr.mp + double(pr.nbx) * pr.mp * (split ? 3.0 : 1.0));
     }
     last_exec_flops() += ex;
     if (split)
