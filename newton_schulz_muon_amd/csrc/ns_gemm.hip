@@ -146,23 +146,6 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
                  static_cast<int>(bytes), 0x00020000};
 }
 
-// The same descriptor as a buffer resource for the epilogue's loads and
-// stores (the compiler's buffer instructions: a per-lane 32-bit offset plus
-// a uniform offset in a scalar register, where a flat address would cost
-// 64-bit arithmetic per lane and instruction).  Offsets past `bytes` read 0
-// and write nothing.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t epi_rsrc(const void* base, uint32_t bytes) {
-    const uint64_t b = reinterpret_cast<uint64_t>(base);
-    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b)));
-    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32)));
-    void* const p = reinterpret_cast<void*>(uint64_t(lo) | (uint64_t(hi) << 32));
-    return __builtin_amdgcn_make_buffer_rsrc(p, 0, static_cast<int>(__builtin_amdgcn_readfirstlane(bytes)),
-                                             0x00020000);
-}
-__device__ __forceinline__ uint32_t uniform(uint32_t v) {
-    return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(v));
-}
-
 // One buffer_load_dwordx4 ... lds: lane L's 16 bytes at rsrc + voff + soff go to
 // LDS byte address lds + 16 L.  It is issued as inline assembly so that the
 // compiler does not track it: the compiler would otherwise make every
@@ -520,7 +503,6 @@ struct TileJob {
     float* trace;
     int ntrace;
     uint32_t p_bytes, q_bytes;
-    uint32_t out_bytes;       // bytes of the block's output (per plane)
     int64_t K;                // reduction length (row pitch of k-contiguous operands)
     int64_t ldq;              // row pitch of a k-major column operand
     int64_t ldo;              // output row pitch
@@ -761,11 +743,7 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
     // the polynomial) cover whole row segments instead of the MFMA layout's
     // 4-column pieces of 32 rows.  All staging is wave-private; LDS accesses
     // of one wave complete in order, so no barrier is needed.
-    // The epilogue's per-lane offsets are derived here (an opaque lane
-    // index), so that none is computed ahead of the K loop and held in a
-    // register through it.
-    int lane = tid & 63;
-    asm volatile("" : "+v"(lane));
+    const int lane = tid & 63;
     const int lr = lane & 31, lk = lane >> 5;
     if constexpr (KIND == kGram) {
         // The first iteration's norm partials: the traces of the 32 x 32
@@ -801,15 +779,7 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
     constexpr int LPR = TWC / 4;      // lanes per row on read-back (4 values each)
     constexpr int RPI = 64 / LPR;     // rows per read-back instruction
     const int rrow = lane / LPR, rcol = (lane % LPR) * 4;
-    const int gcol = col0 + wc0 + rcol;
-    // Byte offsets in the block's output (and A): row r, column c of the
-    // tile chunk at uniform + per-lane parts.
-    const uint32_t ldb = uniform(static_cast<uint32_t>(a.ldo) * 2u);
-    const __amdgpu_buffer_rsrc_t ro0 = epi_rsrc(out0, a.out_bytes);
-    const __amdgpu_buffer_rsrc_t ro1 = epi_rsrc(SPLIT_OUT ? out1 : out0, a.out_bytes);
-    const __amdgpu_buffer_rsrc_t ra = epi_rsrc(POLY ? amat : out0, POLY ? a.p_bytes : a.out_bytes);
-    const uint32_t vrow = static_cast<uint32_t>(wr0 + rrow) * ldb + static_cast<uint32_t>(wc0 + rcol) * 2u;
-    const auto srow = [&](int r) { return uniform(static_cast<uint32_t>(row0 + r) * ldb + static_cast<uint32_t>(col0) * 2u); };
+    const int64_t gcol = col0 + wc0 + rcol;
     // The polynomial's A values of chunk i + 1 are loaded while chunk i is
     // finished (double buffer), so their latency is exposed once, not per row.
     constexpr int NT = 32 / RPI;      // read-back instructions per chunk
@@ -817,7 +787,8 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
     auto load_a = [&](int i, u32x2 (&dst)[NT]) {
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-            dst[t] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(ra, vrow, srow(i * 32 + t * RPI), 0));
+            dst[t] = *reinterpret_cast<const u32x2*>(amat + (int64_t)(row0 + wr0 + i * 32 + t * RPI + rrow) * a.ldo +
+                                                     gcol);
     };
     if constexpr (POLY)
         load_a(0, abuf[0]);
@@ -841,13 +812,12 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
             __builtin_amdgcn_sched_barrier(0);
             constexpr int CH = TWC / 8, RPB = 64 / CH;
             const int brow = lane / CH, bch = lane % CH;
-            const uint32_t vb = static_cast<uint32_t>(wr0 + brow) * ldb + static_cast<uint32_t>(wc0 + 8 * bch) * 2u;
 #pragma unroll
             for (int t = 0; t < 32 / RPB; ++t) {
                 const int rr = t * RPB + brow;
                 u32x4 v = *reinterpret_cast<const u32x4*>(sf + rr * (TWC * 2) + ((bch ^ (rr & (CH - 1))) << 4));
                 if ((rr / CH) & 1) v = u32x4{v[2], v[3], v[0], v[1]};
-                __builtin_amdgcn_raw_buffer_store_b128(v, ro0, vb, srow(i * 32 + t * RPB), 0);
+                *reinterpret_cast<u32x4*>(out0 + (int64_t)(row0 + wr0 + i * 32 + rr) * a.ldo + col0 + wc0 + 8 * bch) = v;
             }
             continue;
         }
@@ -867,13 +837,12 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const int rr = t * RPI + rrow;
-            const int grow = row0 + wr0 + i * 32 + rr;
-            const uint32_t so = srow(i * 32 + t * RPI);
+            const int64_t grow = row0 + wr0 + i * 32 + rr;
+            const int64_t o = grow * a.ldo + gcol;
             const f32x4 x = *reinterpret_cast<const f32x4*>(sf + f32_off<TWC>(rr, rcol));
             float am[4] = {0.f, 0.f, 0.f, 0.f};
             if constexpr (POLY) {
-                u32x2 av = abuf[i & 1][t];
-                asm volatile("" : "+v"(av));    // converted here, not all ahead of the chunk
+                const u32x2 av = abuf[i & 1][t];
                 am[0] = bf16_to_f32(uint16_t(av[0] & 0xffffu));
                 am[1] = bf16_to_f32(uint16_t(av[0] >> 16));
                 am[2] = bf16_to_f32(uint16_t(av[1] & 0xffffu));
@@ -892,8 +861,8 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
                 hb[e] = f32_to_bf16(v);
                 if constexpr (SPLIT_OUT) lb[e] = f32_to_bf16(v - bf16_to_f32(hb[e]));
             }
-            __builtin_amdgcn_raw_buffer_store_b64(pack4(hb), ro0, vrow, so, 0);
-            if constexpr (SPLIT_OUT) __builtin_amdgcn_raw_buffer_store_b64(pack4(lb), ro1, vrow, so, 0);
+            *reinterpret_cast<u32x2*>(out0 + o) = pack4(hb);
+            if constexpr (SPLIT_OUT) *reinterpret_cast<u32x2*>(out1 + o) = pack4(lb);
             if constexpr (SYM) {
                 if (mirror) {
                     *reinterpret_cast<u32x2*>(sb + mir_off<TWC>(rr, rcol)) = pack4(hb);
@@ -911,28 +880,23 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
             // rows 8 g4 .. 8 g4 + 7 of column cb + L, stored as 16 bytes.
             if (mirror) {
                 const int L = lane & 15, g4 = lane >> 4;
-                const int mrow = 8 * g4 + (L >> 2);
-                const uint32_t vm = static_cast<uint32_t>(wc0 + L) * ldb + static_cast<uint32_t>(wr0 + 8 * g4) * 2u;
+                const int srow = 8 * g4 + (L >> 2);
 #pragma unroll
                 for (int cb = 0; cb < TWC; cb += 16) {
                     const int scol = cb + 4 * (L & 3);
-                    const uint32_t sm = uniform(static_cast<uint32_t>(col0 + cb) * ldb +
-                                                static_cast<uint32_t>(row0 + i * 32) * 2u);
+                    const int64_t o = (int64_t)(col0 + wc0 + cb + L) * a.ldo + row0 + wr0 + i * 32 + 8 * g4;
                     const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) i16x4*)(sb + mir_off<TWC>(mrow, scol)));
+                        (__attribute__((address_space(3))) i16x4*)(sb + mir_off<TWC>(srow, scol)));
                     const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) i16x4*)(sb + mir_off<TWC>(mrow + 4, scol)));
-                    __builtin_amdgcn_raw_buffer_store_b128(
-                        __builtin_bit_cast(u32x4, i16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]}),
-                        ro0, vm, sm, 0);
+                        (__attribute__((address_space(3))) i16x4*)(sb + mir_off<TWC>(srow + 4, scol)));
+                    *reinterpret_cast<i16x8*>(out0 + o) = i16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
                     if constexpr (SPLIT_OUT) {
                         const i16x4 w0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) i16x4*)(sb_lo + mir_off<TWC>(mrow, scol)));
+                            (__attribute__((address_space(3))) i16x4*)(sb_lo + mir_off<TWC>(srow, scol)));
                         const i16x4 w1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) i16x4*)(sb_lo + mir_off<TWC>(mrow + 4, scol)));
-                        __builtin_amdgcn_raw_buffer_store_b128(
-                            __builtin_bit_cast(u32x4, i16x8{w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]}),
-                            ro1, vm, sm, 0);
+                            (__attribute__((address_space(3))) i16x4*)(sb_lo + mir_off<TWC>(srow + 4, scol)));
+                        *reinterpret_cast<i16x8*>(out1 + o) =
+                            i16x8{w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
                     }
                 }
             }
@@ -1009,7 +973,6 @@ __global__ __launch_bounds__(tile_threads<BT>()) void k_gemm(GemmArgs args) {
     j.ntrace = a.ntrace;
     j.p_bytes = a.p_bytes;
     j.q_bytes = a.q_bytes;
-    j.out_bytes = static_cast<uint32_t>(a.out_stride * 2);
     j.K = a.K;
     j.ldq = a.ldq;
     j.ldo = a.ldo;
@@ -1304,7 +1267,6 @@ __global__ __launch_bounds__(tile_threads<256>()) void k_ns_loop(PersistArgs arg
                 j.p[0] = j.q[0] = xin;
                 j.out[0] = pr.a + blk * as;
                 j.p_bytes = j.q_bytes = static_cast<uint32_t>(xs * 2);
-                j.out_bytes = static_cast<uint32_t>(as * 2);
                 j.K = pr.np;
                 j.ldq = pr.np;
                 j.ldo = pr.mp;
@@ -1313,7 +1275,6 @@ __global__ __launch_bounds__(tile_threads<256>()) void k_ns_loop(PersistArgs arg
                 j.out[0] = pr.b + blk * as;
                 if constexpr (SPLIT) j.out[1] = pr.blo + blk * as;
                 j.p_bytes = j.q_bytes = static_cast<uint32_t>(as * 2);
-                j.out_bytes = static_cast<uint32_t>(as * 2);
                 j.K = pr.mp;
                 j.ldq = pr.mp;
                 j.ldo = pr.mp;
@@ -1323,7 +1284,6 @@ __global__ __launch_bounds__(tile_threads<256>()) void k_ns_loop(PersistArgs arg
                 j.out[0] = (t + 1 == args.steps ? pr.xlast : pr.xb[(t + 1) & 1]) + blk * xs;
                 j.p_bytes = static_cast<uint32_t>(as * 2);
                 j.q_bytes = static_cast<uint32_t>(xs * 2);
-                j.out_bytes = static_cast<uint32_t>(xs * 2);
                 j.K = pr.mp;
                 j.ldq = pr.np;
                 j.ldo = pr.np;

@@ -74,6 +74,7 @@ CASES = [
     (3, 300, 700, 1, 5, "accurate"),
     (2, 512, 1024, 1, 2, "accurate"),
     (2, 1024, 512, 1, 5, "accurate"),   # tall
+    (8, 1280, 1280, 1, 1, "accurate"),  # many mirrored 128-wide polynomial tiles per block
 ]
 
 
@@ -160,3 +161,24 @@ def test_tilings_multi_bitwise(nsm):
         for a, b in zip(outs[64], outs[w]):
             np.testing.assert_array_equal(a, b, err_msg=f"64-wide vs {w}-wide")
 
+
+
+@pytest.mark.parametrize("shape", [(8, 1280, 1280), (2, 2048, 2048)])
+def test_tilings_accurate_repeatable(nsm, shape):
+    # ACCURATE keeps the lo planes of B' and X, which expose fp32-level
+    # differences that bf16 rounding hides: every width gives the same bits on
+    # every call (a store of the mirror tile racing with its offset register
+    # once made the 128-wide split polynomial differ between calls by one ulp
+    # in a few elements of the lo plane)
+    b, r, c = shape
+    print(f"[tiling] ACCURATE repeatability batch={b} shape={(r, c)}", flush=True)
+    x = workloads.to_device_bf16(workloads.gaussian_bits(shape, seed=b * 7 + r + c))
+
+    def run():
+        return [torch_bf16_to_bits(nsm.ns_orthogonalize_batched(x, ns_steps=1, precision="accurate"))
+                for _ in range(4)]
+
+    outs, _ = _widths(nsm, run, [64, 128, 256])
+    for w, runs in outs.items():
+        for i, o in enumerate(runs):
+            np.testing.assert_array_equal(o, outs[64][0], err_msg=f"{w}-wide call {i} vs 64-wide call 0")
