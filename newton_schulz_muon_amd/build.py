@@ -36,7 +36,8 @@ COMMON_FLAGS = [
 # persistent loop's queue claim into an atomic followed by an immediate wait;
 # its kernels' resource usage is reported so that the build can reject
 # scratch use (its hand-counted vmcnt waits assume no compiler-placed vector
-# memory operation, and scratch accesses are such operations).
+# memory operation, and scratch accesses are such operations).  Its device
+# assembly is also scanned for LDS DMA hazards (dma_sgpr_hazards).
 SOURCE_FLAGS = {"ns_gemm.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
                                 "-Rpass-analysis=kernel-resource-usage"]}
 NO_SCRATCH_SOURCES = ("ns_gemm.hip",)
@@ -62,7 +63,16 @@ def _kernels_with_scratch(out: str):
     return found
 
 
-def _check_no_scratch(src: str, out: str, cc: str, flags) -> None:
+def _device_asm(src: str, cc: str, flags) -> str:
+    """The gfx950 assembly that `src` compiles to."""
+    asm = subprocess.run([cc, *flags, "--cuda-device-only", "-S", "-o", "-", os.path.join(CSRC, src)],
+                         stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
+    if asm.returncode != 0:
+        raise RuntimeError(f"{src}: device assembly failed")
+    return asm.stdout
+
+
+def _check_no_scratch(src: str, out: str, asm: str) -> None:
     """Raises if a kernel of `src` accesses scratch memory.  A kernel may
     reserve a private segment that its code never touches (the register
     allocator's emergency slot beside SGPR spills to VGPR lanes); such a
@@ -70,17 +80,94 @@ def _check_no_scratch(src: str, out: str, cc: str, flags) -> None:
     found = _kernels_with_scratch(out)
     if not found:
         return
-    asm = subprocess.run([cc, *flags, "--cuda-device-only", "-S", "-o", "-", os.path.join(CSRC, src)],
-                         stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
-    if asm.returncode != 0:
-        raise RuntimeError(f"{src}: device assembly failed")
     for name in found:
-        body = asm.stdout.split(f"\n{name}:", 1)
+        body = asm.split(f"\n{name}:", 1)
         if len(body) < 2:
             raise RuntimeError(f"{src}: kernel {name} not found in the device assembly")
         code = body[1].split("s_endpgm", 1)[0]
         if re.search(r"\bscratch_|\bbuffer_\w+ [^\n]*s\[0:3\]|flat_\w+", code):
             raise RuntimeError(f"{src}: kernel {name} accesses scratch memory")
+
+
+# Wait states that gfx9 requires between a VALU write of an SGPR and a vector
+# memory instruction that reads it.
+VMEM_SGPR_WAIT_STATES = 5
+
+
+def _sgprs(tok: str):
+    tok = tok.strip().rstrip(",")
+    m = re.fullmatch(r"s\[(\d+):(\d+)\]", tok)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.fullmatch(r"s(\d+)", tok)
+    if m:
+        return {int(m.group(1))}
+    if tok in ("vcc", "vcc_lo", "vcc_hi"):
+        return {106, 107} if tok == "vcc" else ({106} if tok == "vcc_lo" else {107})
+    return set()
+
+
+def _valu_sgpr_defs(inst: str):
+    """SGPRs written by the VALU instruction `inst` (empty if none)."""
+    parts = inst.replace(",", " ").split()
+    op = parts[0]
+    defs = _sgprs(parts[1]) if len(parts) > 1 else set()
+    if op.startswith(("v_add_co_", "v_sub_co_", "v_subrev_co_", "v_addc_co_", "v_subb_co_", "v_subbrev_co_",
+                      "v_mad_u64_u32", "v_mad_i64_i32", "v_div_scale_")) and len(parts) > 2:
+        defs |= _sgprs(parts[2])
+    if op.endswith("_e32") and (op.startswith(("v_cmp", "v_add_co_", "v_sub_co_", "v_subrev_co_", "v_addc_co_",
+                                               "v_subb_co_", "v_subbrev_co_"))):
+        defs |= {106, 107}                                       # implicit VCC
+    return defs
+
+
+def dma_sgpr_hazards(asm: str, need: int = VMEM_SGPR_WAIT_STATES):
+    """LDS DMA instructions (buffer_load ... lds, written as inline assembly,
+    which the compiler's hazard recognizer does not see) that read an SGPR
+    written by a VALU instruction fewer than `need` wait states before, or
+    that follow a branch target within that distance.  Each instruction
+    counts one wait state, s_nop N counts N + 1."""
+    insts = []
+    for line in asm.splitlines():
+        t = line.split(";")[0].strip()
+        if not t:
+            continue
+        if t.endswith(":"):
+            insts.append(("label", t))
+        elif not t.startswith("."):
+            insts.append(("inst", t))
+    found = []
+    for i, (kind, text) in enumerate(insts):
+        if kind != "inst":
+            continue
+        m = re.match(r"buffer_load_\w+\s+\S+,\s+(s\[\d+:\d+\]),\s+(\S+)\s+offen\s+lds", text)
+        if not m:
+            continue
+        regs = _sgprs(m.group(1)) | _sgprs(m.group(2))
+        ws = 0
+        j = i - 1
+        while j >= 0 and ws < need:
+            pkind, ptext = insts[j]
+            if pkind == "label":
+                found.append(f"{text}: branch target {ptext} {ws} wait states before")
+                break
+            op = ptext.split()[0]
+            if op.startswith("s_nop"):
+                ws += int(ptext.split()[1], 0) + 1
+            else:
+                if op.startswith("v_") and _valu_sgpr_defs(ptext) & regs:
+                    found.append(f"{text}: {ws} wait states after {ptext}")
+                ws += 1
+            j -= 1
+    return found
+
+
+def _check_dma_hazards(src: str, asm: str) -> None:
+    found = dma_sgpr_hazards(asm)
+    if not any(re.search(r"buffer_load_\w+\s[^\n]*\slds", l) for l in asm.splitlines()):
+        raise RuntimeError(f"{src}: no LDS DMA instruction found in the device assembly")
+    if found:
+        raise RuntimeError(f"{src}: LDS DMA reads an SGPR too soon after a VALU write:\n  " + "\n  ".join(found[:10]))
 
 
 def hipcc() -> str:
@@ -111,8 +198,10 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
         outs = list(ex.map(_run, cmds))
     for src, out in zip(SOURCES, outs):
         if src in NO_SCRATCH_SOURCES:
-            _check_no_scratch(src, out, cc, [f for f in COMMON_FLAGS + SOURCE_FLAGS.get(src, [])
-                                             if not f.startswith("-Rpass")])
+            asm = _device_asm(src, cc, [f for f in COMMON_FLAGS + SOURCE_FLAGS.get(src, [])
+                                        if not f.startswith("-Rpass")])
+            _check_no_scratch(src, out, asm)
+            _check_dma_hazards(src, asm)
     if verbose:
         for o in outs:
             if o.strip():

@@ -152,9 +152,25 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
 // transposing LDS read (which carries no alias information) wait for all of
 // this wave's outstanding DMA, which collapses the pipeline.  The kernel
 // orders DMA and LDS reads itself with explicit vmcnt waits and barriers.
+//
+// Inline assembly is also outside the compiler's hazard recognizer, so the
+// statement carries the wait states that gfx9 requires before a vector
+// memory instruction: one after a scalar write of M0 (the LDS address), and
+// five after a VALU write of an SGPR that it reads (the buffer descriptor and
+// offset; v_readfirstlane, or v_readlane restoring a spilled SGPR), without
+// which the load can read the SGPR's previous value and fetch from the wrong
+// place.  VALU_SGPR: the caller's SGPR operands come from v_readfirstlane.
+// The build scans the generated code and rejects any other DMA that follows
+// a VALU write of one of its SGPRs by fewer than five wait states.
+template <bool VALU_SGPR = false>
 __device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t voff, uint32_t soff, char* lds) {
     const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)lds));
-    asm volatile("buffer_load_dwordx4 %1, %2, %3 offen lds" ::"{m0}"(m0), "v"(voff), "s"(rsrc), "s"(soff) : "memory");
+    if constexpr (VALU_SGPR)
+        asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"{m0}"(m0), "v"(voff), "s"(rsrc),
+                     "s"(soff) : "memory");
+    else
+        asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"{m0}"(m0), "v"(voff), "s"(rsrc),
+                     "s"(soff) : "memory");
 }
 
 // An R x BK slice of a k-contiguous matrix fetched straight into LDS by the
@@ -250,7 +266,7 @@ struct ColDma {
             const uint32_t b_hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(bp >> 32)));
             const uint64_t bs = uint64_t(b_lo) | (uint64_t(b_hi) << 32);
             const uint32_t soff = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(k0 - s * seg_k) * ldb);
-            dma16(make_rsrc(reinterpret_cast<const void*>(bs), bytes), voff[q], soff, lds + (w * PW + q) * 1024);
+            dma16<true>(make_rsrc(reinterpret_cast<const void*>(bs), bytes), voff[q], soff, lds + (w * PW + q) * 1024);
         } else {
             dma16(make_rsrc(base, bytes), voff[q], static_cast<uint32_t>(k0) * ldb, lds + (w * PW + q) * 1024);
         }
