@@ -153,15 +153,17 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
 // this wave's outstanding DMA, which collapses the pipeline.  The kernel
 // orders DMA and LDS reads itself with explicit vmcnt waits and barriers.
 //
-// Inline assembly is also outside the compiler's hazard recognizer, so the
-// statement carries the wait states that gfx9 requires before a vector
-// memory instruction: one after a scalar write of M0 (the LDS address), and
-// five after a VALU write of an SGPR that it reads (the buffer descriptor and
-// offset; v_readfirstlane, or v_readlane restoring a spilled SGPR), without
-// which the load can read the SGPR's previous value and fetch from the wrong
-// place.  VALU_SGPR: the caller's SGPR operands come from v_readfirstlane.
-// The build scans the generated code and rejects any other DMA that follows
-// a VALU write of one of its SGPRs by fewer than five wait states.
+// Inline assembly is also outside the compiler's hazard recognizer.  A
+// vector memory instruction that reads an SGPR shortly after a VALU wrote it
+// (v_readfirstlane, or v_readlane restoring a spilled SGPR) can use the
+// SGPR's previous value and fetch from the wrong place: measured on gfx950
+// with in-bounds buffer loads, 77% of loads one instruction after the
+// v_readfirstlane of their offset and 52% two instructions after used the
+// old offset; none from three on.  VALU_SGPR (the caller's descriptor or
+// offset comes from v_readfirstlane) puts five wait states, the figure
+// documented for gfx9, before the load.  The build scans the generated code
+// and rejects any other DMA within five wait states of a VALU write of its
+// SGPRs.  A scalar write of M0 right before the load needs none.
 template <bool VALU_SGPR = false>
 __device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t voff, uint32_t soff, char* lds) {
     const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)lds));
@@ -169,8 +171,8 @@ __device__ __forceinline__ void dma16(const i32x4& rsrc, uint32_t voff, uint32_t
         asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"{m0}"(m0), "v"(voff), "s"(rsrc),
                      "s"(soff) : "memory");
     else
-        asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"{m0}"(m0), "v"(voff), "s"(rsrc),
-                     "s"(soff) : "memory");
+        asm volatile("buffer_load_dwordx4 %1, %2, %3 offen lds" ::"{m0}"(m0), "v"(voff), "s"(rsrc), "s"(soff)
+                     : "memory");
 }
 
 // An R x BK slice of a k-contiguous matrix fetched straight into LDS by the
