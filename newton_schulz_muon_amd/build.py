@@ -89,8 +89,10 @@ def _check_no_scratch(src: str, out: str, asm: str) -> None:
             raise RuntimeError(f"{src}: kernel {name} accesses scratch memory")
 
 
-# Wait states that gfx9 requires between a VALU write of an SGPR and a vector
-# memory instruction that reads it.
+# Wait states required between a VALU write of an SGPR and a vector memory
+# instruction that reads it: five, the figure documented for gfx9 (on gfx950
+# tests/test_gpu_dma_hazard.py finds loads one instruction after the write
+# using the old value, and none from two on).
 VMEM_SGPR_WAIT_STATES = 5
 
 
