@@ -7,8 +7,9 @@ v_readfirstlane puts five wait states before its loads.  A test-only kernel
 (tests/kernels/sgpr_hazard_probe.hip) counts which offset each load used,
 for v_readfirstlane and for v_readlane (the restore of a spilled SGPR), with
 0, 1, 2 and 5 instructions between the write and the load; only the last is
-asserted, the others are printed (measured on gfx950: with 0 and 1 between,
-most or half of the loads used the old value; with 2, none)."""
+asserted, the others are printed (measured on gfx950: with none between,
+40-76% of the loads used the old value, with one between 2-52%, varying from
+run to run, with two or more none)."""
 import ctypes
 import os
 
