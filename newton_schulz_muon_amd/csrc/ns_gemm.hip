@@ -139,7 +139,8 @@ struct TileCfg {
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // Raw buffer descriptor of `bytes` bytes at `base` (stride 0; loads past the
-// end return zero).
+// end return zero without accessing memory, so `bytes` = 0 makes a load that
+// fetches nothing but still counts in vmcnt).
 __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
     const uint64_t b = reinterpret_cast<uint64_t>(base);
     return i32x4{static_cast<int>(static_cast<uint32_t>(b)), static_cast<int>((b >> 32) & 0xffffu),
@@ -157,9 +158,10 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
 // vector memory instruction that reads an SGPR shortly after a VALU wrote it
 // (v_readfirstlane, or v_readlane restoring a spilled SGPR) can use the
 // SGPR's previous value and fetch from the wrong place: measured on gfx950
-// with in-bounds buffer loads, 77% of loads one instruction after the
-// v_readfirstlane of their offset and 52% two instructions after used the
-// old offset; none from three on.  VALU_SGPR (the caller's descriptor or
+// with in-bounds buffer loads, 40-77% of loads directly after the
+// v_readfirstlane of their offset and 2-52% one instruction later (varying
+// from run to run) used the old offset; none from two instructions between
+// on.  VALU_SGPR (the caller's descriptor or
 // offset comes from v_readfirstlane) puts five wait states, the figure
 // documented for gfx9, before the load.  The build scans the generated code
 // and rejects any other DMA within five wait states of a VALU write of its
@@ -202,10 +204,13 @@ struct RowDma {
             voff[q] = static_cast<uint32_t>(((int64_t)(row0 + row) * ld + chunk * 8) * 2);
         }
     }
-    // Window q of this wave (1 KB) of the slice at K offset k0.
+    // Window q of this wave (1 KB) of the slice at K offset k0 (k0 < 0: an
+    // empty range, which fetches nothing).
     __device__ __forceinline__ void load_q(char* lds, int k0, int q, int tid) const {
         const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-        dma16(make_rsrc(base, bytes), voff[q], static_cast<uint32_t>(k0 * 2), lds + (w * PW + q) * 1024);
+        const bool live = k0 >= 0;
+        dma16(make_rsrc(base, live ? bytes : 0u), voff[q], static_cast<uint32_t>((live ? k0 : 0) * 2),
+              lds + (w * PW + q) * 1024);
     }
 };
 
@@ -256,8 +261,11 @@ struct ColDma {
             voff[q] = static_cast<uint32_t>(((int64_t)row * ld + col0 + chunk * 8) * 2);
         }
     }
+    // As RowDma::load_q (k0 < 0: an empty range).
     __device__ __forceinline__ void load_q(char* lds, int k0, int q, int tid) const {
         const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const bool live = k0 >= 0;
+        if (!live) k0 = 0;
         if constexpr (LO_SEG >= 0) {
             // k0 is uniform: the segment and its base are kept in scalar registers
             const int s = (k0 >= seg_k) + (k0 >= 2 * seg_k);
@@ -268,9 +276,10 @@ struct ColDma {
             const uint32_t b_hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(bp >> 32)));
             const uint64_t bs = uint64_t(b_lo) | (uint64_t(b_hi) << 32);
             const uint32_t soff = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(k0 - s * seg_k) * ldb);
-            dma16<true>(make_rsrc(reinterpret_cast<const void*>(bs), bytes), voff[q], soff, lds + (w * PW + q) * 1024);
+            dma16<true>(make_rsrc(reinterpret_cast<const void*>(bs), live ? bytes : 0u), voff[q], soff,
+                        lds + (w * PW + q) * 1024);
         } else {
-            dma16(make_rsrc(base, bytes), voff[q], static_cast<uint32_t>(k0) * ldb, lds + (w * PW + q) * 1024);
+            dma16(make_rsrc(base, live ? bytes : 0u), voff[q], static_cast<uint32_t>(k0) * ldb, lds + (w * PW + q) * 1024);
         }
     }
 };
@@ -289,7 +298,8 @@ struct Operands {
     __device__ __forceinline__ static char* b_tile(char* stage, int j) {
         return stage + (NA + j) * OP_BYTES;
     }
-    // DMA instruction w (0 <= w < WINDOWS) of this wave for the slice at k0.
+    // DMA instruction w (0 <= w < WINDOWS) of this wave for the slice at k0
+    // (k0 < 0: an empty range).
     __device__ __forceinline__ void load_window(char* stage, int k0, int w, int tid) const {
         constexpr int PA = ALoader::PW, PB = BLoader::PW;
         if (w < NA * PA) {
@@ -693,10 +703,11 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
         // free (step kt - 1 consumed all its reads) and slice kt + NS - 1 is
         // fetched into it, spread over the last sub-slice, whose reads are
         // the first fragments of slice kt + 1.  Every step issues exactly one
-        // stage of loads (in the tail an in-bounds slice whose copy is never
-        // read), so the wait count is fixed.
+        // stage of loads, so the wait count is fixed: past the last slice the
+        // loads name K offset -1, which the loaders turn into an empty
+        // buffer range (no memory access; the stage, never read, gets zeros).
 #pragma unroll
-        for (int st = 0; st < NS - 1; ++st) ops.load(lds + st * STAGE, (st < nk ? st : 0) * BK, tid);
+        for (int st = 0; st < NS - 1; ++st) ops.load(lds + st * STAGE, st < nk ? st * BK : -1, tid);
         wait_dma_and_barrier<(NS - 2) * W>();
         frags(lds, 0, fa[0], fb[0]);
         for (int kt = 0; kt < nk; ++kt) {
@@ -718,7 +729,7 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
                     const int kn = kt + NS - 1;
                     load_frags<FA, FB, KMAJOR_A, KMAJOR_B, BT, BK, true, FA + FB>(
                         Ops::a_tile(nxt, 0), Ops::b_tile(nxt, 0), wr0, wc0, 0, fa[c ^ 1], fb[c ^ 1], tid, &ops,
-                        lds + (kn % NS) * STAGE, (kn < nk ? kn : kt) * BK, 0);
+                        lds + (kn % NS) * STAGE, kn < nk ? kn * BK : -1, 0);
                 }
                 mfma_block<FA, FB>(fa[c], fb[c], acc);
                 interleave<NM, NREAD, SPREAD>();
@@ -735,7 +746,7 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
         for (int kt = 0; kt < nk; ++kt) {
             char* cur = lds + (kt & 1) * STAGE;
             char* nxt = lds + ((kt + 1) & 1) * STAGE;
-            const int k1 = (kt + 1 < nk ? kt + 1 : kt) * BK;
+            const int k1 = kt + 1 < nk ? (kt + 1) * BK : -1;
             frags(cur, 0, fa[0], fb[0]);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
