@@ -291,6 +291,7 @@ template <int BT, int NA, int NB, typename ALoader, typename BLoader>
 struct Operands {
     ALoader a[NA];
     BLoader b[NB];
+    bool b_empty = false;     // the column operand's loads fetch nothing (it is read from the row operand's tile)
     static constexpr int OP_BYTES = BT * ALoader::BK * 2;   // one operand tile
     static constexpr int STAGE = (NA + NB) * OP_BYTES;
     static constexpr int WINDOWS = NA * ALoader::PW + NB * BLoader::PW;   // DMA instructions per wave
@@ -306,7 +307,7 @@ struct Operands {
             a[w / PA].load_q(a_tile(stage, w / PA), k0, w % PA, tid);
         } else {
             const int v = w - NA * PA;
-            b[v / PB].load_q(b_tile(stage, v / PB), k0, v % PB, tid);
+            b[v / PB].load_q(b_tile(stage, v / PB), b_empty ? -1 : k0, v % PB, tid);
         }
     }
     __device__ __forceinline__ void load(char* stage, int k0, int tid) const {
@@ -654,6 +655,14 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
 
     Ops ops;
     TT::init(ops, a, tid);
+    // A diagonal tile of a symmetric product reads the same rows as both
+    // operands (X X^T: rows of X; A A: rows of A): only the row operand is
+    // fetched, the column operand's loads go through an empty range (same
+    // instruction count, so the same waits), and the column fragments are
+    // read from the row operand's tile.
+    const bool same_ops = SYM && ti == tj;
+    ops.b_empty = same_ops;
+    const int bsel = same_ops ? 0 : Ops::OP_BYTES;
 
     // The first iteration scales by s^-1 = 1 / (|X|_F + eps) (B X) or uses
     // s^-2, s^-4 (the polynomial of the unscaled X X^T).  The norm partials
@@ -693,7 +702,7 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
     bf16x8 fa[2][FA], fb[2][FB];
     auto frags = [&](const char* st, int u, bf16x8 (&xa)[FA], bf16x8 (&xb)[FB]) {
         load_frags<FA, FB, KMAJOR_A, KMAJOR_B, BT, BK>(Ops::a_tile(const_cast<char*>(st), 0),
-                                              Ops::b_tile(const_cast<char*>(st), 0), wr0, wc0, u, xa, xb, tid);
+                                              const_cast<char*>(st) + bsel, wr0, wc0, u, xa, xb, tid);
     };
 
     if constexpr (NS >= 3) {
@@ -728,7 +737,7 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
                     wait_dma_and_barrier<(NS - 3) * W>();
                     const int kn = kt + NS - 1;
                     load_frags<FA, FB, KMAJOR_A, KMAJOR_B, BT, BK, true, FA + FB>(
-                        Ops::a_tile(nxt, 0), Ops::b_tile(nxt, 0), wr0, wc0, 0, fa[c ^ 1], fb[c ^ 1], tid, &ops,
+                        Ops::a_tile(nxt, 0), nxt + bsel, wr0, wc0, 0, fa[c ^ 1], fb[c ^ 1], tid, &ops,
                         lds + (kn % NS) * STAGE, kn < nk ? kn * BK : -1, 0);
                 }
                 mfma_block<FA, FB>(fa[c], fb[c], acc);
@@ -754,7 +763,7 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
                 const int c = u & 1;
                 if (u + 1 < U) {
                     load_frags<FA, FB, KMAJOR_A, KMAJOR_B, BT, BK, true, (U - 1) * (FA + FB)>(
-                        Ops::a_tile(cur, 0), Ops::b_tile(cur, 0), wr0, wc0, u + 1,
+                        Ops::a_tile(cur, 0), cur + bsel, wr0, wc0, u + 1,
                         fa[c ^ 1], fb[c ^ 1], tid, &ops, nxt, k1, u * (FA + FB));
                 }
                 mfma_block<FA, FB>(fa[c], fb[c], acc);
