@@ -287,11 +287,13 @@ struct ColDma {
 // The operands of one kernel: NA tiles for the output rows and NB tiles for
 // the output columns, each either k-contiguous rows (RowDma) or k-major
 // columns (ColDma).
-template <int BT, int NA, int NB, typename ALoader, typename BLoader>
+template <int BT, int NA, int NB, typename ALoader, typename BLoader, bool SHARE_B = false>
 struct Operands {
     ALoader a[NA];
     BLoader b[NB];
-    bool b_empty = false;     // the column operand's loads fetch nothing (it is read from the row operand's tile)
+    // SHARE_B (symmetric products): with b_empty set, the column operand's
+    // loads fetch nothing (it is read from the row operand's tile).
+    bool b_empty = false;
     static constexpr int OP_BYTES = BT * ALoader::BK * 2;   // one operand tile
     static constexpr int STAGE = (NA + NB) * OP_BYTES;
     static constexpr int WINDOWS = NA * ALoader::PW + NB * BLoader::PW;   // DMA instructions per wave
@@ -307,7 +309,7 @@ struct Operands {
             a[w / PA].load_q(a_tile(stage, w / PA), k0, w % PA, tid);
         } else {
             const int v = w - NA * PA;
-            b[v / PB].load_q(b_tile(stage, v / PB), b_empty ? -1 : k0, v % PB, tid);
+            b[v / PB].load_q(b_tile(stage, v / PB), SHARE_B && b_empty ? -1 : k0, v % PB, tid);
         }
     }
     __device__ __forceinline__ void load(char* stage, int k0, int tid) const {
@@ -605,7 +607,7 @@ struct TileTypes {
     // split B X: the row operand reads its lo plane in segment 2, the column operand in segment 1
     using ALoader = typename std::conditional<KMAJOR_A, ColDma<BT, BK, NW, SPLIT_IN ? 2 : -1>, RowDma<BT, BK, NW>>::type;
     using BLoader = typename std::conditional<KMAJOR_B, ColDma<BT, BK, NW, SPLIT_IN ? 1 : -1>, RowDma<BT, BK, NW>>::type;
-    using Ops = Operands<BT, 1, 1, ALoader, BLoader>;
+    using Ops = Operands<BT, 1, 1, ALoader, BLoader, KIND == kGram || KIND == kPoly || KIND == kPolySplit>;
     static constexpr int STAGE = Ops::STAGE;
 
     __device__ __forceinline__ static void init(Ops& ops, const TileJob& a, int tid) {
@@ -627,7 +629,7 @@ struct TileTypes {
 // finished (a barrier) before the call.  Each wave calls hook() once in its
 // epilogue, after the last global load it waits for (so that a memory
 // operation the hook issues is not waited for by the rest of the tile).
-template <int KIND, int BT, bool OPAQUE_TID = false, typename Hook = NoHook>
+template <int KIND, int BT, bool OPAQUE_TID = false, typename Hook = NoHook, bool SHARE_DIAG = true>
 __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca, float cb, float cc, float eps,
                                           const Hook& hook = Hook()) {
     // In a loop over tiles the thread index is made opaque per tile, so that
@@ -659,9 +661,13 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
     // operands (X X^T: rows of X; A A: rows of A): only the row operand is
     // fetched, the column operand's loads go through an empty range (same
     // instruction count, so the same waits), and the column fragments are
-    // read from the row operand's tile.
-    const bool same_ops = SYM && ti == tj;
-    ops.b_empty = same_ops;
+    // read from the row operand's tile.  SHARE_DIAG = false keeps both
+    // fetches: the ACCURATE persistent loop, whose split B'X phase ran
+    // 2-7% slower on 2048- and 4096-row blocks when the diagonal tiles
+    // before it were shortened (measured; the per-product launches and the
+    // FAST loop gain).
+    const bool same_ops = SYM && SHARE_DIAG && ti == tj;
+    if constexpr (SYM) ops.b_empty = same_ops;
     const int bsel = same_ops ? 0 : Ops::OP_BYTES;
 
     // The first iteration scales by s^-1 = 1 / (|X|_F + eps) (B X) or uses
@@ -1342,10 +1348,11 @@ __global__ __launch_bounds__(tile_threads<256>()) void k_ns_loop(PersistArgs arg
             };
             const TileJob j = job(c);
             if (ph == 0) {
-                gemm_tile<kGram, 256, true>(j, lds, args.ca, args.cb, args.cc, args.eps, claim);
+                gemm_tile<kGram, 256, true, decltype(claim), !SPLIT>(j, lds, args.ca, args.cb, args.cc, args.eps, claim);
             } else if (ph == 1) {
                 if constexpr (SPLIT)
-                    gemm_tile<kPolySplit, 256, true>(j, lds, args.ca, args.cb, args.cc, args.eps, claim);
+                    gemm_tile<kPolySplit, 256, true, decltype(claim), false>(j, lds, args.ca, args.cb, args.cc, args.eps,
+                                                                             claim);
                 else
                     gemm_tile<kPoly, 256, true>(j, lds, args.ca, args.cb, args.cc, args.eps, claim);
             } else {
