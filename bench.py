@@ -56,6 +56,8 @@ FAMILY_NAMES = {"ns_loop": "k_ns_loop (all NS iterations of a call in one launch
                 "bx": "k_gemm<kBx> (X <- B' X)"}
 SETTLE_CALLS = 12              # calls before warm-up that let the automatic NS schedule choose
 NS_STEPS = 5
+# the quintic's coefficients (the parameter-golf walkthrough, Part 1; the library's defaults)
+NS_COEFFS = (3.4445, -4.7750, 2.0315)
 
 
 def ns_flops(m: int, n: int, steps: int = NS_STEPS) -> float:
@@ -480,6 +482,50 @@ def adamw_gpt124m(nsm, args, dev):
             "traffic": load_profile("k_adamw_gpt124m_traffic", ADAM_SOURCE, "bytes_per_launch")}
 
 
+def library_baseline(nsm, args, dev, headline_ms=None):
+    """The same NS call written as plain PyTorch on the GPU (torch.bmm on
+    hipBLASLt, bf16 operands, the pages' five quintic iterations with the
+    Gram of the short side), and one large square bf16 GEMM as the rate the
+    vendor library reaches when nothing but a single product is asked of it.
+    A comparison leg only: the library's own path never calls torch."""
+    import torch
+    import workloads
+    wl = workloads.get_workload("metric32")
+    g = wl.groups[0]
+    x = workloads.grads_device(wl, g, 0, dev)
+    a, b, c = NS_COEFFS
+
+    def torch_ns():
+        y = (x.float() / (torch.linalg.vector_norm(x.float(), dim=(1, 2), keepdim=True) + 1e-7)).to(x.dtype)
+        for _ in range(NS_STEPS):
+            gram = torch.bmm(y, y.transpose(1, 2).contiguous())
+            poly = b * gram + c * torch.bmm(gram, gram)
+            y = a * y + torch.bmm(poly, y)
+        return y
+
+    for _ in range(args.warmup):
+        torch_ns()
+    torch.cuda.synchronize()
+    ms = timed_region(torch_ns, args.steps)
+    nominal = g.count * ns_flops(g.rows, g.cols)
+    res = {"what": "the same 32 x 768x3072 NS in PyTorch eager (torch.bmm / hipBLASLt, bf16), 5 iterations",
+           "ms": round(ms, 4), "tflops_nominal": round(nominal / (ms / 1e3) / 1e12, 2)}
+    if headline_ms:
+        res["speedup_of_this_library"] = round(ms / headline_ms, 2)
+    del x
+    n = 8192
+    p = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    q = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        p @ q
+    torch.cuda.synchronize()
+    ms = timed_region(lambda: p @ q, args.steps)
+    res["gemm_8192_bf16"] = {"ms": round(ms, 4), "tflops": round(2 * n ** 3 / (ms / 1e3) / 1e12, 2),
+                             "frac_of_peak": round(2 * n ** 3 / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    del p, q
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -488,9 +534,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="the headline call only")
-    ap.add_argument("--extras", default="step,shares,c4,c5,adamw",
+    ap.add_argument("--extras", default="step,shares,c4,c5,adamw,library",
                     help="comma-separated extras: step (124M Muon step), shares (one GPU's 8-way share), "
-                         "c4 (96 x 1024x4096 step), c5 (large dense ACCURATE step), adamw")
+                         "c4 (96 x 1024x4096 step), c5 (large dense ACCURATE step), adamw, "
+                         "library (the same NS call in PyTorch eager on hipBLASLt)")
     ap.add_argument("--ns-schedule", choices=("auto", "persistent", "per_product"), default="auto",
                     help="auto: the library's per-shape choice (default); persistent: all NS iterations of "
                          "a call in one launch; per_product: three launches per iteration")
@@ -538,6 +585,8 @@ def main():
             result["large_dense_step"] = large_step(nsm, args, dev, "large_dense")
         if "adamw" in want:
             result["adamw_gpt124m"] = adamw_gpt124m(nsm, args, dev)
+        if "library" in want:
+            result["library_baseline"] = library_baseline(nsm, args, dev)
         print(json.dumps(result), flush=True)
         return
 
@@ -574,6 +623,8 @@ def main():
             result["large_dense_step"] = large_step(nsm, args, dev, "large_dense")
         if "adamw" in want:
             result["adamw_gpt124m"] = adamw_gpt124m(nsm, args, dev)
+        if "library" in want:
+            result["library_baseline"] = library_baseline(nsm, args, dev, h["ms"])
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -11,12 +11,18 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "newton_schulz_muon_amd", "csrc")
 
 
-def test_schedule_invariants(tmp_path):
+# The second build runs the same checker under AddressSanitizer and
+# UndefinedBehaviorSanitizer (host code only: the scheduler is plain C++).
+SANITIZE = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
+
+
+@pytest.mark.parametrize("flags", [[], SANITIZE], ids=["plain", "asan_ubsan"])
+def test_schedule_invariants(tmp_path, flags):
     cxx = shutil.which("g++")
     if cxx is None:
         pytest.skip("g++ not available")
     exe = str(tmp_path / "ns_schedule_check")
-    build = subprocess.run([cxx, "-std=c++17", "-O2", "-Wall", "-Werror", "-I", CSRC,
+    build = subprocess.run([cxx, "-std=c++17", "-O2", "-Wall", "-Werror", *flags, "-I", CSRC,
                             os.path.join(ROOT, "tests", "ns_schedule_check.cpp"),
                             os.path.join(CSRC, "ns_schedule.cpp"), "-o", exe],
                            capture_output=True, text=True)
