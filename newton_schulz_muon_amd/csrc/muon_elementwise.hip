@@ -44,7 +44,7 @@ struct PrepArgs {
     int64_t rp, cp;        // padded stored-orientation shape
     int64_t be;            // r * c
     int64_t ew_tiles;
-    int tiles_j;           // cp / 64
+    int tiles_j;           // cp / TC (tiles per padded row)
     float mu, omm;
 };
 
@@ -139,13 +139,22 @@ __device__ __forceinline__ void load_update8_scalar(const PrepArgs& a, const uin
     }
 }
 
-// One 64 x 64 tile of the padded stored-orientation block per workgroup.  The
-// oriented iterate X is that block for wide blocks (written through dh/dl)
-// and its transpose for tall ones (TALL: written through th/tl, via LDS).
-// Both rows' loads are issued before any store, so a thread has its whole
-// share of HBM reads in flight at once.
-template <int MODE, bool VEC, bool SPLIT, bool TALL>
+// One tile of 4096 elements of the padded stored-orientation block per
+// workgroup: TR x TC with TC = T for tall blocks (64 x 64, transposed through
+// LDS) and the scalar path, and row strips up to 4 x 1024 for wide blocks,
+// whose longer row pieces stream from HBM faster (measured with a probe of
+// this access pattern: 5.1 TB/s as 64 x 64 tiles, 5.6 as 16 x 256, 5.7 as
+// 4 x 1024).  The oriented iterate X is that block for wide blocks (written
+// through dh/dl) and its transpose for tall ones (TALL: written through
+// th/tl, via LDS).  Both passes' loads are issued before any store, so a
+// thread has its whole share of HBM reads in flight at once.
+template <int MODE, bool VEC, bool SPLIT, bool TALL, int TC = T>
 __global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
+    static_assert(TC == T || (!TALL && VEC), "row strips only on the wide vector path");
+    constexpr int TR = T * T / TC;    // tile rows
+    constexpr int TPR = TC / 8;       // threads per tile row (8 elements each)
+    constexpr int RPP = 256 / TPR;    // rows per pass; two passes
+    static_assert(2 * RPP == TR, "a tile is two passes of the workgroup");
     __shared__ uint16_t lds_hi[TALL ? T : 1][T + 2];
     __shared__ uint16_t lds_lo[(TALL && SPLIT) ? T : 1][T + 2];
     __shared__ float red[4];
@@ -171,21 +180,21 @@ __global__ __launch_bounds__(256) void k_prep(PrepArgs a) {
     uint16_t* dl = (!TALL && SPLIT) ? a.dl + blk * pad : nullptr;
     uint16_t* th = TALL ? a.th + blk * pad : nullptr;
     uint16_t* tl = (TALL && SPLIT) ? a.tl + blk * pad : nullptr;
-    const int rl = t >> 3;
-    const int cl = (t & 7) * 8;
+    const int rl = t / TPR;
+    const int cl = (t % TPR) * 8;
     float ss = 0.f;
 
     Raw8 raw[2];
     if constexpr (VEC) {
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-            raw[h] = load8<MODE>(a, src, mom, (int64_t)si * T + rl + 32 * h, (int64_t)sj * T + cl);
+            raw[h] = load8<MODE>(a, src, mom, (int64_t)si * TR + rl + RPP * h, (int64_t)sj * TC + cl);
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        const int row = rl + 32 * h;
-        const int64_t bi = (int64_t)si * T + row;
-        const int64_t bj0 = (int64_t)sj * T + cl;
+        const int row = rl + RPP * h;
+        const int64_t bi = (int64_t)si * TR + row;
+        const int64_t bj0 = (int64_t)sj * TC + cl;
         float u[8];
         bool ok[8];
         if constexpr (VEC) update8<MODE>(a, raw[h], mom, bi, bj0, u, ok);
@@ -273,7 +282,7 @@ struct FinArgs {
     float* P;              // stored fp32 parameters (update mode)
     uint16_t* out;         // stored bf16 output (NS output, or optional O)
     int64_t r, c, mp, np, be;
-    int tiles_j;           // ceil(n / 64)
+    int tiles_j;           // ceil(n / TC)
     float decay, step;
 };
 
@@ -335,12 +344,19 @@ __device__ __forceinline__ void finish_store8(const FinArgs& a, float* P, uint16
     }
 }
 
-// One 64 x 64 tile of the oriented block per workgroup; both rows' loads (the
-// final iterate, and for the update the parameters) are issued before any
-// store.  (Non-temporal loads and stores here measured slower: 5.0-5.3 TB/s
-// against 5.6.)
-template <bool UPDATE, bool TALL, bool VEC, bool SPLIT>
+// One tile of 4096 elements of the oriented block per workgroup (TR x TC as
+// in k_prep: 64 x 64 for tall blocks and the scalar path, row strips for
+// wide blocks); both passes' loads (the final iterate, and for the update
+// the parameters) are issued before any store.  (Non-temporal loads and
+// stores here measured slower: 5.0-5.3 TB/s against 5.6, and again 4.8-4.9
+// against 5.3-5.4 with the momentum kernel's also non-temporal.)
+template <bool UPDATE, bool TALL, bool VEC, bool SPLIT, int TC = T>
 __global__ __launch_bounds__(256) void k_finish(FinArgs a) {
+    static_assert(TC == T || (!TALL && VEC), "row strips only on the wide vector path");
+    constexpr int TR = T * T / TC;    // tile rows
+    constexpr int TPR = TC / 8;       // threads per tile row (8 elements each)
+    constexpr int RPP = 256 / TPR;    // rows per pass; two passes
+    static_assert(2 * RPP == TR, "a tile is two passes of the workgroup");
     __shared__ float lds[TALL ? T : 1][T + 1];
     __shared__ uint16_t ldsb[TALL ? T : 1][T + 2];
     const int t = threadIdx.x;
@@ -365,24 +381,25 @@ __global__ __launch_bounds__(256) void k_finish(FinArgs a) {
     }
     const float sc = a.scale ? a.scale[2 * blk] : 1.0f;
     const bool exact_bits = !SPLIT && a.scale == nullptr;
-    const int rl = t >> 3;
-    const int cl = (t & 7) * 8;
+    const int rl = t / TPR;
+    const int cl = (t % TPR) * 8;
 
     u32x4 vh[2], vl[2];
     P8 pv[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        const int64_t o = ((int64_t)ti * T + rl + 32 * h) * a.np + (int64_t)tj * T + cl;   // inside the padded buffer
+        const int64_t o = ((int64_t)ti * TR + rl + RPP * h) * a.np + (int64_t)tj * TC + cl;   // inside the padded buffer
         vh[h] = *reinterpret_cast<const u32x4*>(xhi + o);
         vl[h] = u32x4{0u, 0u, 0u, 0u};
         if constexpr (SPLIT) vl[h] = *reinterpret_cast<const u32x4*>(xlo + o);
-        if constexpr (!TALL) pv[h] = load_p8<UPDATE, VEC>(a, P, (int64_t)ti * T + rl + 32 * h, (int64_t)tj * T + cl);
+        if constexpr (!TALL)
+            pv[h] = load_p8<UPDATE, VEC>(a, P, (int64_t)ti * TR + rl + RPP * h, (int64_t)tj * TC + cl);
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        const int row = rl + 32 * h;
-        const int64_t oi = (int64_t)ti * T + row;
-        const int64_t oj = (int64_t)tj * T + cl;
+        const int row = rl + RPP * h;
+        const int64_t oi = (int64_t)ti * TR + row;
+        const int64_t oj = (int64_t)tj * TC + cl;
         float v[8];
         uint16_t bits[8];
 #pragma unroll
@@ -442,12 +459,23 @@ hipError_t for_block_chunks(int64_t nb, F&& f) {
     return hipSuccess;
 }
 
-template <int MODE, bool VEC, bool SPLIT, bool TALL>
+// Widest row strip (columns, up to 1024) whose width divides the padded
+// columns `cols` (a multiple of 128): every tile then lies inside the padded
+// block.
+inline int strip_cols(int64_t cols) {
+    return cols % 1024 == 0 ? 1024 : cols % 512 == 0 ? 512 : cols % 256 == 0 ? 256 : 128;
+}
+
+template <int MODE, bool VEC, bool SPLIT, bool TALL, int TC = T>
 hipError_t run_prep(const Plan& p, const PrepArgs& a, hipStream_t s) {
     const int64_t be = p.r * p.c;
     const int64_t pad = p.mp * p.np;
+    // the padded block's rows (a multiple of 128) and columns (of TC) tile exactly
+    if (a.rp % (T * T / TC) != 0 || a.cp % TC != 0 || (a.rp / (T * T / TC)) * (a.cp / TC) != p.ew_tiles)
+        return hipErrorInvalidValue;
     return for_block_chunks(p.nb, [&](int64_t b0, unsigned cnt) {
         PrepArgs c = a;
+        c.tiles_j = static_cast<int>(a.cp / TC);
         c.b0 = b0;
         c.status = b0 == 0 ? a.status : nullptr;
         c.src = a.src ? a.src + b0 * be : nullptr;
@@ -457,14 +485,25 @@ hipError_t run_prep(const Plan& p, const PrepArgs& a, hipStream_t s) {
         c.th = a.th ? a.th + b0 * pad : nullptr;
         c.tl = a.tl ? a.tl + b0 * pad : nullptr;
         c.part = a.part ? a.part + b0 * p.ew_tiles : nullptr;
-        k_prep<MODE, VEC, SPLIT, TALL><<<dim3(static_cast<unsigned>(p.ew_tiles), cnt), dim3(256), 0, s>>>(c);
+        k_prep<MODE, VEC, SPLIT, TALL, TC><<<dim3(static_cast<unsigned>(p.ew_tiles), cnt), dim3(256), 0, s>>>(c);
     });
+}
+
+template <int MODE, bool SPLIT>
+hipError_t prep_strips(const Plan& p, const PrepArgs& a, hipStream_t s) {
+    switch (strip_cols(a.cp)) {
+        case 1024: return run_prep<MODE, true, SPLIT, false, 1024>(p, a, s);
+        case 512: return run_prep<MODE, true, SPLIT, false, 512>(p, a, s);
+        case 256: return run_prep<MODE, true, SPLIT, false, 256>(p, a, s);
+        default: return run_prep<MODE, true, SPLIT, false, 128>(p, a, s);
+    }
 }
 
 template <int MODE, bool TALL>
 hipError_t prep_orient(const Plan& p, const PrepArgs& a, hipStream_t s) {
     const bool vec = (p.c % 8) == 0;
     const bool split = a.dl != nullptr || a.tl != nullptr;
+    if (vec && !TALL) return split ? prep_strips<MODE, true>(p, a, s) : prep_strips<MODE, false>(p, a, s);
     if (vec) return split ? run_prep<MODE, true, true, TALL>(p, a, s) : run_prep<MODE, true, false, TALL>(p, a, s);
     return split ? run_prep<MODE, false, true, TALL>(p, a, s) : run_prep<MODE, false, false, TALL>(p, a, s);
 }
@@ -474,21 +513,27 @@ hipError_t prep_mode(const Plan& p, const PrepArgs& a, hipStream_t s) {
     return p.tall ? prep_orient<MODE, true>(p, a, s) : prep_orient<MODE, false>(p, a, s);
 }
 
-template <bool UPDATE, bool TALL, bool VEC, bool SPLIT>
+template <bool UPDATE, bool TALL, bool VEC, bool SPLIT, int TC = T>
 hipError_t run_finish(const Plan& p, const FinArgs& a, hipStream_t s) {
     const int64_t be = p.r * p.c;
     const int64_t pad = p.mp * p.np;
-    const int64_t ti = (p.m + T - 1) / T;
-    const int64_t tiles = ti * a.tiles_j;
+    constexpr int TR = T * T / TC;
+    // the tiles cover rows up to ceil(m / TR) TR <= mp and columns up to
+    // ceil(n / TC) TC <= np (mp is a multiple of 128, np of TC)
+    if (p.mp % TR != 0 || p.np % TC != 0) return hipErrorInvalidValue;
+    const int64_t ti = (p.m + TR - 1) / TR;
+    const int tiles_j = static_cast<int>((p.n + TC - 1) / TC);
+    const int64_t tiles = ti * tiles_j;
     return for_block_chunks(p.nb, [&](int64_t b0, unsigned cnt) {
         FinArgs c = a;
+        c.tiles_j = tiles_j;
         c.b0 = b0;
         c.xhi = a.xhi + b0 * pad;
         c.xlo = a.xlo ? a.xlo + b0 * pad : nullptr;
         c.scale = a.scale ? a.scale + 2 * b0 : nullptr;
         c.P = a.P ? a.P + b0 * be : nullptr;
         c.out = a.out ? a.out + b0 * be : nullptr;
-        k_finish<UPDATE, TALL, VEC, SPLIT><<<dim3(static_cast<unsigned>(tiles), cnt), dim3(256), 0, s>>>(c);
+        k_finish<UPDATE, TALL, VEC, SPLIT, TC><<<dim3(static_cast<unsigned>(tiles), cnt), dim3(256), 0, s>>>(c);
     });
 }
 
@@ -500,7 +545,18 @@ hipError_t finish_mode(const Plan& p, const FinArgs& a, hipStream_t s) {
         if (vec) return split ? run_finish<UPDATE, true, true, true>(p, a, s) : run_finish<UPDATE, true, true, false>(p, a, s);
         return split ? run_finish<UPDATE, true, false, true>(p, a, s) : run_finish<UPDATE, true, false, false>(p, a, s);
     }
-    if (vec) return split ? run_finish<UPDATE, false, true, true>(p, a, s) : run_finish<UPDATE, false, true, false>(p, a, s);
+    if (vec) {
+        switch (strip_cols(p.np)) {
+            case 1024: return split ? run_finish<UPDATE, false, true, true, 1024>(p, a, s)
+                                    : run_finish<UPDATE, false, true, false, 1024>(p, a, s);
+            case 512: return split ? run_finish<UPDATE, false, true, true, 512>(p, a, s)
+                                   : run_finish<UPDATE, false, true, false, 512>(p, a, s);
+            case 256: return split ? run_finish<UPDATE, false, true, true, 256>(p, a, s)
+                                   : run_finish<UPDATE, false, true, false, 256>(p, a, s);
+            default: return split ? run_finish<UPDATE, false, true, true, 128>(p, a, s)
+                                  : run_finish<UPDATE, false, true, false, 128>(p, a, s);
+        }
+    }
     return split ? run_finish<UPDATE, false, false, true>(p, a, s) : run_finish<UPDATE, false, false, false>(p, a, s);
 }
 
