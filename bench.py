@@ -75,12 +75,12 @@ def ns_flops_symmetric(m: int, n: int, steps: int = NS_STEPS) -> float:
 def loop_executed_flops(m: int, n: int, steps: int = NS_STEPS) -> float:
     """MFMA flops the persistent loop executes for one block: 256-wide tiles of
     the padded oriented block (mp x np), upper-triangle tiles of the symmetric
-    products (T (T + 1) / 2 of them, the T diagonal ones computing three of
-    their four quadrants), every tile of B' X."""
+    products (T (T + 1) / 2 of them, the T diagonal ones computing 10 of
+    their 16 64 x 64 blocks), every tile of B' X."""
     m, n = min(m, n), max(m, n)
     mp, np_ = -(-m // 128) * 128, -(-n // 128) * 128
     t, tn = mp // 256, np_ // 256
-    nsym, nbx = t * (t + 1) // 2 - 0.25 * t, t * tn
+    nsym, nbx = t * (t + 1) // 2 - 0.375 * t, t * tn
     return float(steps) * 2.0 * 256 * 256 * (nsym * np_ + nsym * mp + nbx * mp)
 
 

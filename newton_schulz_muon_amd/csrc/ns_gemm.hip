@@ -686,10 +686,11 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
 
     // The K loop and epilogue of one wave, which computes FA x FB blocks of
     // 32 x 32 at rows wr0, columns wc0 of the tile, and stores their mirror
-    // (the transposed block at the transposed place) with `mirror`.  Every
+    // (the transposed block at the transposed place) for its first
+    // `mirror_chunks` 32-row chunks.  Every
     // wave runs the same K loop structure (one wait, barrier and stage of DMA
     // per step) whatever its FA.
-    const auto body = [&](auto fa_tag, const int wr0, const int wc0, const bool mirror) {
+    const auto body = [&](auto fa_tag, const int wr0, const int wc0, const int mirror_chunks) {
     constexpr int FA = decltype(fa_tag)::value;
     f32x16 acc[FA][FB];
     zero_acc<FA, FB>(acc);
@@ -908,7 +909,7 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
             *reinterpret_cast<u32x2*>(out0 + o) = pack4(hb);
             if constexpr (SPLIT_OUT) *reinterpret_cast<u32x2*>(out1 + o) = pack4(lb);
             if constexpr (SYM) {
-                if (mirror) {
+                if (i < mirror_chunks) {
                     *reinterpret_cast<u32x2*>(sb + mir_off<TWC>(rr, rcol)) = pack4(hb);
                     if constexpr (SPLIT_OUT) *reinterpret_cast<u32x2*>(sb_lo + mir_off<TWC>(rr, rcol)) = pack4(lb);
                 }
@@ -922,7 +923,7 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
             // Mirror: output row (col0 + wc0 + c) gets this chunk's 32 values of
             // column c.  Two transposing reads give lane L of 16-lane group g4
             // rows 8 g4 .. 8 g4 + 7 of column cb + L, stored as 16 bytes.
-            if (mirror) {
+            if (i < mirror_chunks) {
                 const int L = lane & 15, g4 = lane >> 4;
                 const int srow = 8 * g4 + (L >> 2);
 #pragma unroll
@@ -950,21 +951,31 @@ __device__ __forceinline__ void gemm_tile(const TileJob& a, char* lds, float ca,
     // A diagonal 256-wide tile of a symmetric product: its lower-left
     // quadrant is the transpose of the upper-right one, so no wave computes
     // it.  Waves 0-3 take the upper-right quadrant as 64 x 64 pieces and store
-    // each piece twice (itself and, transposed, the lower-left quadrant);
-    // waves 4-7 take the two diagonal quadrants as 128 x 64 pieces.  Wave w
-    // shares a SIMD with wave w + 4, so every SIMD issues 12 of the 16
-    // MFMA blocks per sub-slice it would otherwise.
+    // each piece twice (itself and, transposed, the lower-left quadrant).
+    // Each diagonal 128 x 128 quadrant is symmetric too: the odd wave of its
+    // pair (5, 7) takes its right 128 x 64 half and stores the upper 64 x 64
+    // of it twice (itself and, transposed, the quadrant's lower-left block),
+    // the even wave (4, 6) only its upper-left 64 x 64 diagonal block.  Wave
+    // w shares a SIMD with wave w + 4, so the SIMDs issue 8, 12, 8 and 12 of
+    // the 16 MFMA blocks per sub-slice (10 of 16 64 x 64 blocks executed in
+    // all).  The mirrored blocks are bitwise the directly computed ones (the
+    // same products, summed in the same order), and with fewer MFMAs the
+    // tile draws less power: the 32 x 768x3072 NS call runs about 1% faster
+    // than with the diagonal quadrants computed whole.
     if constexpr (SYM && NW == 8) {
         if (ti == tj) {
+            const int q0 = (wave & 2) ? 128 : 0;
             if (wave < 4)
-                body(std::integral_constant<int, 2>(), (wave >> 1) * 64, 128 + (wave & 1) * 64, true);
+                body(std::integral_constant<int, 2>(), (wave >> 1) * 64, 128 + (wave & 1) * 64, 2);
+            else if ((wave & 1) == 0)
+                body(std::integral_constant<int, 2>(), q0, q0, 0);
             else
-                body(std::integral_constant<int, 4>(), (wave & 2) ? 128 : 0, ((wave & 2) ? 128 : 0) + (wave & 1) * 64,
-                     false);
+                body(std::integral_constant<int, 4>(), q0, q0 + 64, 2);
             return;
         }
     }
-    body(std::integral_constant<int, Cfg::FA>(), (wave / Cfg::WC) * TWR, (wave % Cfg::WC) * TWC, SYM && ti != tj);
+    body(std::integral_constant<int, Cfg::FA>(), (wave / Cfg::WC) * TWR, (wave % Cfg::WC) * TWC,
+         SYM && ti != tj ? Cfg::FA : 0);
 }
 
 // Threads of a tile's workgroup.
@@ -1635,7 +1646,7 @@ hipError_t run(const Plan* const* plans, GemmArgs a, hipStream_t s) {
     // Executed MFMA flops of the launches (for the timing diagnostics): every
     // workgroup computes a bt x bt tile over the reduction, except the lower
     // quadrants of diagonal 256-wide tiles in quadrant mode, which return,
-    // and diagonal 256-wide tiles, which compute three quadrants.
+    // and diagonal 256-wide tiles, which compute 10 of their 16 64 x 64 blocks.
     auto launch = [&](int bt, int64_t total, uint32_t quad, uint32_t base) {
         a.quad = quad;
         a.big_base = base;
@@ -1648,7 +1659,7 @@ hipError_t run(const Plan* const* plans, GemmArgs a, hipStream_t s) {
                     if (t >= int64_t(a.pr[i].first)) pi = i;
                 int id = static_cast<int>((t - a.pr[pi].first) % a.pr[pi].tiles), len = a.pr[pi].T;
                 while (id > 0 && id >= len) { id -= len; --len; }
-                if (id == 0) tiles -= 0.25;     // the row's diagonal tile
+                if (id == 0) tiles -= 0.375;    // the row's diagonal tile
             }
         }
         if (quad && SYM) {
@@ -2151,8 +2162,8 @@ hipError_t launch_ns_loop(const NsLoopProblem* probs, int n, int ns_steps, float
     double ex = 0.0;
     for (int i = 0; i < n; ++i) {
         const PersistProblem& pr = a.pr[i];
-        // diagonal tiles of the symmetric products compute three quadrants
-        const double sym = double(pr.nsym) - 0.25 * double(pr.mp / 256);
+        // diagonal tiles of the symmetric products compute 10 of 16 64 x 64 blocks
+        const double sym = double(pr.nsym) - 0.375 * double(pr.mp / 256);
         ex += double(pr.nb) * double(ns_steps) * 2.0 * 256.0 * 256.0 *
               (sym * pr.np + sym * pr.mp + double(pr.nbx) * pr.mp * (split ? 3.0 : 1.0));
     }

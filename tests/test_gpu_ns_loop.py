@@ -329,9 +329,9 @@ def test_timing_reports_nominal_flops(nsm, sched, shape):
     executed = sum(e for _, _, _, e in k.values())
     assert b * v * 5 * (3.0 * m * m * n + m ** 3) <= executed <= b * v * 5 * (4.0 * mp * mp * np_ + 2.0 * mp ** 3)
     if loop:
-        # diagonal tiles of the symmetric products compute three of their four quadrants
+        # diagonal tiles of the symmetric products compute 10 of their 16 64 x 64 blocks
         t, tn = mp // 256, np_ // 256
-        sym = t * (t + 1) // 2 - 0.25 * t
+        sym = t * (t + 1) // 2 - 0.375 * t
         assert executed == pytest.approx(b * v * 5 * 2.0 * 256 * 256 * (sym * np_ + sym * mp + t * tn * mp),
                                          rel=1e-12)
 

@@ -58,9 +58,9 @@ def _padded(n):
 
 
 def _gram_tiles(mp, bt):
-    # upper-triangle tiles; a diagonal 256-wide tile computes three of its quadrants
+    # upper-triangle tiles; a diagonal 256-wide tile computes 10 of its 16 64 x 64 blocks
     t = mp // bt
-    return t * (t + 1) // 2 - (0.25 * t if bt == 256 else 0.0)
+    return t * (t + 1) // 2 - (0.375 * t if bt == 256 else 0.0)
 
 
 # (batch, rows, cols, view_blocks, ns_steps, precision)
