@@ -237,3 +237,42 @@ def test_step_rank_share(nsm, group):
         lr_eff = float(np.float32(wl.lr)) * oracle.aspect_factor(grp.rows, grp.cols)
         bound += NS_REL_TOL * lr_eff * np.linalg.norm(O_ref) + 4 * 2.0 ** -24 * np.linalg.norm(P_ref)
         assert np.linalg.norm(P.cpu().numpy() - P_ref) <= bound
+
+
+# Wide blocks go through the element-wise kernels in row strips of 4096
+# elements whose width is the widest of 1024, 512, 256, 128 columns dividing
+# the padded columns: one shape per width, row counts that leave a ragged
+# last strip, an attn view and ACCURATE precision.
+STRIP_CASES = [
+    (3, 200, 640, 1, "fast"),       # padded columns 640: 128-wide strips (32 rows)
+    (2, 130, 1280, 1, "accurate"),  # 1280: 256-wide (16 rows)
+    (2, 260, 2560, 1, "fast"),      # 2560: 512-wide (8 rows)
+    (2, 102, 2048, 1, "fast"),      # 2048: 1024-wide (4 rows)
+    (2, 256, 3072, 4, "fast"),      # attn view: 256 x 768 blocks, 256-wide
+]
+
+
+@pytest.mark.parametrize("b,r,c,v,precision", STRIP_CASES)
+def test_step_row_strip_widths(nsm, b, r, c, v, precision):
+    import torch
+    rng = np.random.default_rng(1000 + r + c)
+    P_host = (rng.standard_normal((b, r, c)) / np.sqrt(c)).astype(np.float32)
+    M_host = (rng.standard_normal((b, r, c)) * 1e-3).astype(np.float32)
+    gbits = workloads.gaussian_bits((b, r, c), seed=77 + r, std=1e-2)
+    P = torch.from_numpy(P_host).cuda()
+    M = torch.from_numpy(M_host).cuda()
+    O = torch.empty((b, r, c), dtype=torch.bfloat16, device="cuda")
+    print(f"[strip parity] {b}x{r}x{c} view={v} {precision}", flush=True)
+    nsm.muon_step_batched(P, workloads.to_device_bf16(gbits), M, lr=0.05, weight_decay=0.01, momentum=0.95,
+                          view_blocks=v, precision=precision, update_out=O)
+    torch.cuda.synchronize()
+    P_ref, M_ref, O_ref = oracle.muon_step(P_host.astype(np.float64), bits_to_f64(gbits),
+                                           M_host.astype(np.float64), lr=0.05, weight_decay=0.01,
+                                           momentum=0.95, view_blocks=v)
+    O_got = bits_to_f64(torch_bf16_to_bits(O))
+    for i in range(b):
+        assert_ns_close(O_got[i], O_ref[i], v, label=f"strip {r}x{c}[{i}]")
+        assert rel_fro(M.cpu().numpy()[i], M_ref[i]) <= MOMENTUM_TOL
+    lr_eff = float(np.float32(0.05)) * oracle.aspect_factor(r, c)
+    bound = NS_REL_TOL * lr_eff * np.linalg.norm(O_ref) + 4 * 2.0 ** -24 * np.linalg.norm(P_ref)
+    assert np.linalg.norm(P.cpu().numpy() - P_ref) <= bound
